@@ -1,0 +1,448 @@
+/*
+ * qref.c — the oracle (see qref.h). TEST INFRASTRUCTURE ONLY: only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg may load it.
+ *
+ * What it follows, page by page:
+ *  - Bit layout and dequantization: emily lib/emily/quantization.ex,
+ *    `dequantize_defn/1` docs and `dequantize_impl` (lane i sits at bit
+ *    offset i*bits of the row's u32 stream, masked to `bits` bits; group
+ *    g = i div group_size; w = lane * scales[g] + biases[g]), and the
+ *    cross-word unpack (`unpack_cross_word_lanes`, `build_word_indices`:
+ *    read the word holding the lane and the next one, clamped to the last
+ *    word, as one 64-bit value, shift right by i*bits mod 32, mask).
+ *  - Quantizer: the pages call MLX's quantizer without printing its body
+ *    (ollama x/create/client/quantize.go, `loadAndQuantizeArray`; emily
+ *    `QuantizedWeight.from_dense/2` in the `quantized_matmul/2` example).
+ *    The formula used here is the plain affine one: per group,
+ *    scale = (max - min) / (2^bits - 1), bias = min, q = round((w-bias)/scale).
+ *    The readings where the pages are silent follow the per-tensor int8
+ *    quantizer of mlex src/quant.rs (`quantize_dynamic_int8`): the scale is
+ *    floored at FLT_EPSILON, codes use round-half-away-from-zero and are
+ *    clamped to the code range. Codes are computed from the scale and bias
+ *    AS STORED (rounded to the storage type, a zero bias stored as +0), so
+ *    dequantization sees the nearest grid point.
+ *    Parity with MLX's own quantizer: parity unpinned (no values printed).
+ *  - The product: emily `quantized_matmul/2` docs (x @ W^T with the packed
+ *    W laid out [N, K], transpose = true).
+ *  - MoE: ferrum-kernels src/stacked_expert.rs, `gemv_moe_id` and
+ *    `gemv_moe_id_batched` docs (pair p reads a[(p/top_k)*outer +
+ *    (p%top_k)*inner] and expert ids[p]), and the CPU fallback in the module
+ *    docs (per-expert Linear calls): here, one dot product per pair and row.
+ *    `gemv_moe_id_gate_up_silu` docs: SiLU(gate) * up.
+ *
+ * Arithmetic: fp32 for quantize and dequantize (compiled with
+ * -ffp-contract=off, so a*b+c is a multiply then an add), fp64 for every
+ * product sum. Each output's sum runs sequentially in k order, so the OpenMP
+ * loops over outputs give the same bits at any thread count.
+ */
+#include "qref.h"
+
+#include <float.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ */
+/* Floating-point formats                                              */
+/* ------------------------------------------------------------------ */
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* Round a >= 0 (finite) to the nearest integer multiple of `quantum` (a power
+ * of two), ties to the even multiple. Every step is exact in fp64 for the
+ * fp32 inputs used here. */
+static double round_to_multiple_even(double a, double quantum)
+{
+    double t = a / quantum;
+    double lo = floor(t);
+    double frac = t - lo;
+    double r;
+    if (frac > 0.5)
+        r = lo + 1.0;
+    else if (frac < 0.5)
+        r = lo;
+    else
+        r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;
+    return r * quantum;
+}
+
+/* A binary format with `mant_bits` explicit mantissa bits, exponent bias
+ * `bias`, and `exp_bits` exponent bits (IEEE layout, subnormals, inf/NaN). */
+struct fmt16 { int mant_bits, exp_bits, bias; };
+static const struct fmt16 FMT_BF16 = {7, 8, 127};
+static const struct fmt16 FMT_F16 = {10, 5, 15};
+
+static uint16_t encode_rne(float f, struct fmt16 F)
+{
+    uint32_t u = f32_bits(f);
+    uint16_t sign = (uint16_t)((u >> 31) << 15);
+    uint16_t exp_all_ones = (uint16_t)(((1u << F.exp_bits) - 1u) << F.mant_bits);
+    if (isnan(f))
+        return (uint16_t)(sign | exp_all_ones | (1u << (F.mant_bits - 1)));
+    double a = fabs((double)f);
+    if (isinf(f))
+        return (uint16_t)(sign | exp_all_ones);
+    if (a == 0.0)
+        return sign;
+    int emin = 1 - F.bias;                    /* smallest normal exponent */
+    int emax = (1 << F.exp_bits) - 2 - F.bias; /* largest finite exponent */
+    int e2;
+    (void)frexp(a, &e2);                      /* a = f * 2^e2, 0.5 <= f < 1 */
+    int e = e2 - 1;                           /* a = m * 2^e, 1 <= m < 2 */
+    if (e < emin)
+        e = emin;                             /* subnormal range: fixed quantum */
+    double quantum = ldexp(1.0, e - F.mant_bits);
+    double v = round_to_multiple_even(a, quantum);
+    if (v >= ldexp(1.0, emax + 1))            /* rounded past the largest finite */
+        return (uint16_t)(sign | exp_all_ones);
+    if (v < ldexp(1.0, emin)) {               /* subnormal (or zero) */
+        uint32_t mant = (uint32_t)(v / ldexp(1.0, emin - F.mant_bits));
+        return (uint16_t)(sign | mant);
+    }
+    (void)frexp(v, &e2);
+    e = e2 - 1;
+    uint32_t mant = (uint32_t)((v / ldexp(1.0, e) - 1.0) * ldexp(1.0, F.mant_bits));
+    return (uint16_t)(sign | ((uint32_t)(e + F.bias) << F.mant_bits) | mant);
+}
+
+uint16_t qref_f32_to_bf16(float f) { return encode_rne(f, FMT_BF16); }
+uint16_t qref_f32_to_f16(float f) { return encode_rne(f, FMT_F16); }
+
+/* bf16 is, by definition, the upper 16 bits of an fp32. */
+float qref_bf16_to_f32(uint16_t h) { return f32_from_bits((uint32_t)h << 16); }
+
+float qref_f16_to_f32(uint16_t h)
+{
+    int sign = h >> 15;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return (float)(sign ? -v : v);
+}
+
+void qref_f32_to_bf16_n(const float* in, uint16_t* out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = qref_f32_to_bf16(in[i]);
+}
+
+void qref_f32_to_f16_n(const float* in, uint16_t* out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = qref_f32_to_f16(in[i]);
+}
+
+void qref_bf16_to_f32_n(const uint16_t* in, float* out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = qref_bf16_to_f32(in[i]);
+}
+
+void qref_f16_to_f32_n(const uint16_t* in, float* out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = qref_f16_to_f32(in[i]);
+}
+
+/* Value of element `idx` of an array of element type `dtype`. */
+static float load_elem(const void* p, int dtype, int64_t idx)
+{
+    switch (dtype) {
+    case QREF_F32: return ((const float*)p)[idx];
+    case QREF_F16: return qref_f16_to_f32(((const uint16_t*)p)[idx]);
+    case QREF_BF16: return qref_bf16_to_f32(((const uint16_t*)p)[idx]);
+    }
+    abort();
+}
+
+/* Round fp32 `v` to element type `dtype`, store it, and return the stored value. */
+static float store_elem(void* p, int dtype, int64_t idx, float v)
+{
+    switch (dtype) {
+    case QREF_F32: ((float*)p)[idx] = v; return v;
+    case QREF_F16: {
+        uint16_t h = qref_f32_to_f16(v);
+        ((uint16_t*)p)[idx] = h;
+        return qref_f16_to_f32(h);
+    }
+    case QREF_BF16: {
+        uint16_t h = qref_f32_to_bf16(v);
+        ((uint16_t*)p)[idx] = h;
+        return qref_bf16_to_f32(h);
+    }
+    }
+    abort();
+}
+
+/* ------------------------------------------------------------------ */
+/* Packing                                                             */
+/* ------------------------------------------------------------------ */
+
+static int bits_ok(int bits)
+{
+    return bits == 2 || bits == 3 || bits == 4 || bits == 6 || bits == 8;
+}
+
+/* Packed row length; the packing needs k*bits to be a multiple of 32. */
+static int64_t words_per_row(int64_t k, int bits) { return k * bits / 32; }
+
+/* Lane i of a row: word i*bits div 32 and the next word (clamped to the
+ * row's last word) read as one 64-bit value, shifted right by
+ * i*bits mod 32, masked to `bits` bits. For bits dividing 32 the lane never
+ * leaves its word and this is the plain (word >> (lane*bits)) & mask. */
+static uint32_t unpack_lane(const uint32_t* row, int64_t words, int64_t i, int bits)
+{
+    int64_t w = (i * bits) / 32;
+    int64_t w_next = (w + 1 < words) ? w + 1 : words - 1;
+    uint64_t window = (uint64_t)row[w] | ((uint64_t)row[w_next] << 32);
+    uint64_t shifted = window >> ((i * bits) % 32);
+    return (uint32_t)(shifted & ((1u << bits) - 1u));
+}
+
+int qref_pack(const uint8_t* codes, int64_t n, int64_t k, int bits, uint32_t* wq)
+{
+    if (!bits_ok(bits) || n < 0 || k < 0 || (k * bits) % 32 != 0)
+        return -1;
+    int64_t words = words_per_row(k, bits);
+    for (int64_t r = 0; r < n; ++r) {
+        uint32_t* row = wq + r * words;
+        for (int64_t w = 0; w < words; ++w)
+            row[w] = 0;
+        for (int64_t i = 0; i < k; ++i) {
+            uint32_t q = codes[r * k + i] & ((1u << bits) - 1u);
+            int64_t bit = i * bits;
+            int64_t w = bit / 32;
+            int off = (int)(bit % 32);
+            row[w] |= q << off;
+            if (off + bits > 32) /* the lane runs on into the next word */
+                row[w + 1] |= q >> (32 - off);
+        }
+    }
+    return 0;
+}
+
+int qref_unpack(const uint32_t* wq, int64_t n, int64_t k, int bits, uint8_t* codes)
+{
+    if (!bits_ok(bits) || n < 0 || k < 0 || (k * bits) % 32 != 0)
+        return -1;
+    int64_t words = words_per_row(k, bits);
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t i = 0; i < k; ++i)
+            codes[r * k + i] = (uint8_t)unpack_lane(wq + r * words, words, i, bits);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Quantize / dequantize                                               */
+/* ------------------------------------------------------------------ */
+
+static int args_ok(int64_t n, int64_t k, int bits, int group_size, int dtype)
+{
+    if (!bits_ok(bits) || n < 0 || k < 0 || group_size <= 0)
+        return 0;
+    if (k % group_size != 0 || (k * bits) % 32 != 0)
+        return 0;
+    return dtype == QREF_F32 || dtype == QREF_F16 || dtype == QREF_BF16;
+}
+
+int qref_quantize(const float* w, int64_t n, int64_t k, int bits, int group_size,
+                  int sb_dtype, uint32_t* wq, void* scales, void* biases)
+{
+    if (!args_ok(n, k, bits, group_size, sb_dtype))
+        return -1;
+    int64_t groups = k / group_size;
+    int64_t words = words_per_row(k, bits);
+    float qmax = (float)((1 << bits) - 1);
+    uint8_t* codes = (uint8_t*)malloc((size_t)(k > 0 ? k : 1));
+    if (!codes)
+        return -1;
+    for (int64_t r = 0; r < n; ++r) {
+        const float* wr = w + r * k;
+        for (int64_t g = 0; g < groups; ++g) {
+            const float* wg = wr + g * group_size;
+            float mn = wg[0], mx = wg[0];
+            for (int i = 1; i < group_size; ++i) {
+                if (wg[i] < mn) mn = wg[i];
+                if (wg[i] > mx) mx = wg[i];
+            }
+            float s = (mx - mn) / qmax;
+            if (!(s >= FLT_EPSILON)) /* constant group: floor the scale */
+                s = FLT_EPSILON;
+            float sq = store_elem(scales, sb_dtype, r * groups + g, s);
+            float bq = store_elem(biases, sb_dtype, r * groups + g, mn);
+            if (bq == 0.0f) /* a zero bias is stored as +0 */
+                bq = store_elem(biases, sb_dtype, r * groups + g, 0.0f);
+            for (int i = 0; i < group_size; ++i) {
+                float t = roundf((wg[i] - bq) / sq);
+                if (t < 0.0f) t = 0.0f;
+                if (t > qmax) t = qmax;
+                codes[g * group_size + i] = (uint8_t)t;
+            }
+        }
+        qref_pack(codes, 1, k, bits, wq + r * words);
+    }
+    free(codes);
+    return 0;
+}
+
+/* Dequantized weight (n_row's element i) in fp32: fp32(q) * s' + b'. */
+static float dequant_elem(const uint32_t* row_wq, int64_t words, const void* scales,
+                          const void* biases, int sb_dtype, int64_t sb_row_off, int64_t i,
+                          int bits, int group_size)
+{
+    uint32_t q = unpack_lane(row_wq, words, i, bits);
+    int64_t g = i / group_size;
+    float s = load_elem(scales, sb_dtype, sb_row_off + g);
+    float b = load_elem(biases, sb_dtype, sb_row_off + g);
+    float prod = (float)q * s;
+    return prod + b;
+}
+
+int qref_dequantize(const uint32_t* wq, const void* scales, const void* biases,
+                    int sb_dtype, int64_t n, int64_t k, int bits, int group_size,
+                    float* w_out)
+{
+    if (!args_ok(n, k, bits, group_size, sb_dtype))
+        return -1;
+    int64_t groups = k / group_size, words = words_per_row(k, bits);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t i = 0; i < k; ++i)
+            w_out[r * k + i] = dequant_elem(wq + r * words, words, scales, biases, sb_dtype,
+                                            r * groups, i, bits, group_size);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Products                                                            */
+/* ------------------------------------------------------------------ */
+
+/* One output: sum over k of x_row[k] * w'[row, k] (fp64, k order). */
+static void dot_row(const void* x, int x_dtype, int64_t x_off, const uint32_t* row_wq,
+                    const void* scales, const void* biases, int sb_dtype, int64_t sb_off,
+                    int64_t k, int bits, int group_size, double* y, double* S)
+{
+    int64_t words = words_per_row(k, bits);
+    double acc = 0.0, mag = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        double xv = (double)load_elem(x, x_dtype, x_off + i);
+        double wv = (double)dequant_elem(row_wq, words, scales, biases, sb_dtype, sb_off, i,
+                                         bits, group_size);
+        acc += xv * wv;
+        mag += fabs(xv) * fabs(wv);
+    }
+    *y = acc;
+    *S = mag;
+}
+
+int qref_qmatmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint32_t* wq,
+                 const void* scales, const void* biases, int sb_dtype, int64_t n, int bits,
+                 int group_size, double* y, double* S)
+{
+    if (!args_ok(n, k, bits, group_size, sb_dtype) || m < 0 || x_dtype < 0 || x_dtype > 2)
+        return -1;
+    int64_t groups = k / group_size, words = words_per_row(k, bits);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t c = 0; c < n; ++c)
+            dot_row(x, x_dtype, r * k, wq + c * words, scales, biases, sb_dtype, c * groups, k,
+                    bits, group_size, &y[r * n + c], &S[r * n + c]);
+    return 0;
+}
+
+int qref_qmatmul_sampled(const void* x, int x_dtype, int64_t m, int64_t k, const uint32_t* wq,
+                         const void* scales, const void* biases, int sb_dtype, int64_t n,
+                         int bits, int group_size, const int64_t* mi, const int64_t* ni,
+                         int64_t count, double* y, double* S)
+{
+    if (!args_ok(n, k, bits, group_size, sb_dtype) || m < 0 || x_dtype < 0 || x_dtype > 2)
+        return -1;
+    for (int64_t c = 0; c < count; ++c)
+        if (mi[c] < 0 || mi[c] >= m || ni[c] < 0 || ni[c] >= n)
+            return -1;
+    int64_t groups = k / group_size, words = words_per_row(k, bits);
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < count; ++c)
+        dot_row(x, x_dtype, mi[c] * k, wq + ni[c] * words, scales, biases, sb_dtype,
+                ni[c] * groups, k, bits, group_size, &y[c], &S[c]);
+    return 0;
+}
+
+static int moe_args_ok(const int32_t* ids, int64_t pairs, int64_t num_experts)
+{
+    for (int64_t p = 0; p < pairs; ++p)
+        if (ids[p] < 0 || ids[p] >= num_experts)
+            return 0;
+    return 1;
+}
+
+int qref_moe(const void* a, int a_dtype, const int32_t* ids, int64_t n_tokens, int64_t top_k,
+             int64_t a_outer, int64_t a_inner, const uint32_t* wq, const void* scales,
+             const void* biases, int sb_dtype, int64_t num_experts, int64_t n_rows,
+             int64_t n_cols, int bits, int group_size, double* out, double* S)
+{
+    if (!args_ok(n_rows, n_cols, bits, group_size, sb_dtype) || n_tokens < 0 || top_k < 0)
+        return -1;
+    int64_t pairs = n_tokens * top_k;
+    if (!moe_args_ok(ids, pairs, num_experts))
+        return -2;
+    int64_t groups = n_cols / group_size, words = words_per_row(n_cols, bits);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t p = 0; p < pairs; ++p)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t a_off = (p / top_k) * a_outer + (p % top_k) * a_inner;
+            int64_t row = (int64_t)ids[p] * n_rows + r; /* expert-major row index */
+            dot_row(a, a_dtype, a_off, wq + row * words, scales, biases, sb_dtype,
+                    row * groups, n_cols, bits, group_size, &out[p * n_rows + r],
+                    &S[p * n_rows + r]);
+        }
+    return 0;
+}
+
+/* SiLU(z) = z * sigmoid(z) = z / (1 + e^-z). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+int qref_moe_gate_up_silu(const void* a, int a_dtype, const int32_t* ids, int64_t n_tokens,
+                          int64_t top_k, int64_t a_outer, int64_t a_inner,
+                          const uint32_t* gate_wq, const void* gate_s, const void* gate_b,
+                          const uint32_t* up_wq, const void* up_s, const void* up_b,
+                          int sb_dtype, int64_t num_experts, int64_t n_rows, int64_t n_cols,
+                          int bits, int group_size, double* silu_out, double* g, double* u,
+                          double* Sg, double* Su)
+{
+    int rc = qref_moe(a, a_dtype, ids, n_tokens, top_k, a_outer, a_inner, gate_wq, gate_s,
+                      gate_b, sb_dtype, num_experts, n_rows, n_cols, bits, group_size, g, Sg);
+    if (rc)
+        return rc;
+    rc = qref_moe(a, a_dtype, ids, n_tokens, top_k, a_outer, a_inner, up_wq, up_s, up_b,
+                  sb_dtype, num_experts, n_rows, n_cols, bits, group_size, u, Su);
+    if (rc)
+        return rc;
+    int64_t total = n_tokens * top_k * n_rows;
+    for (int64_t i = 0; i < total; ++i)
+        silu_out[i] = silu(g[i]) * u[i];
+    return 0;
+}
+
+int qref_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,101 @@
+/*
+ * qref.h — the oracle: a plain, slow CPU implementation of affine group
+ * quantization, bit packing, dequantization and the quantized matmul / MoE
+ * products.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link,
+ * load or call this code; only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark do. It shares no code, header or table with
+ * the HIP library.
+ *
+ * Element-type codes used by every function below (the oracle's own
+ * numbering, independent of the library's):
+ *   0 = fp32, 1 = fp16 (IEEE binary16), 2 = bf16 (top half of an fp32).
+ *
+ * Parity pins: every function here is pinned by the CPU tests (closed forms,
+ * printed examples, brute force, library routines), except agreement with the
+ * MLX quantizer itself, which the pages never print values for ("parity
+ * unpinned": the readings in qref.c fix our own quantizer, not MLX's).
+ */
+#ifndef QREF_H
+#define QREF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { QREF_F32 = 0, QREF_F16 = 1, QREF_BF16 = 2 };
+
+/* Scalar conversions. fp32 -> 16-bit formats round to nearest, ties to even. */
+uint16_t qref_f32_to_bf16(float f);
+uint16_t qref_f32_to_f16(float f);
+float qref_bf16_to_f32(uint16_t h);
+float qref_f16_to_f32(uint16_t h);
+/* Bulk forms (for exhaustive checks). */
+void qref_f32_to_bf16_n(const float* in, uint16_t* out, int64_t n);
+void qref_f32_to_f16_n(const float* in, uint16_t* out, int64_t n);
+void qref_bf16_to_f32_n(const uint16_t* in, float* out, int64_t n);
+void qref_f16_to_f32_n(const uint16_t* in, float* out, int64_t n);
+
+/* Codes <-> packed little-endian u32 stream, row by row.
+ * codes: [n, k] u8 (values < 2^bits); wq: [n, k*bits/32] u32. */
+int qref_pack(const uint8_t* codes, int64_t n, int64_t k, int bits, uint32_t* wq);
+int qref_unpack(const uint32_t* wq, int64_t n, int64_t k, int bits, uint8_t* codes);
+
+/* Affine group quantization of w[n,k] (fp32) into packed codes plus one
+ * scale and one bias per group, stored in element type sb_dtype.
+ * scales, biases: [n, k/group_size]. Returns 0, or -1 on bad arguments. */
+int qref_quantize(const float* w, int64_t n, int64_t k, int bits, int group_size,
+                  int sb_dtype, uint32_t* wq, void* scales, void* biases);
+
+/* Dequantize to fp32: w'[n,k] = fp32(q) * s' + b' (multiply, then add). */
+int qref_dequantize(const uint32_t* wq, const void* scales, const void* biases,
+                    int sb_dtype, int64_t n, int64_t k, int bits, int group_size,
+                    float* w_out);
+
+/* y[m,n] = sum_k x[m,k] * w'[n,k] in fp64, in k order, plus
+ * S[m,n] = sum_k |x[m,k]| * |w'[n,k]| (the scale of the error bound).
+ * x: [m,k] of element type x_dtype. y, S: [m,n] fp64. */
+int qref_qmatmul(const void* x, int x_dtype, int64_t m, int64_t k,
+                 const uint32_t* wq, const void* scales, const void* biases,
+                 int sb_dtype, int64_t n, int bits, int group_size,
+                 double* y, double* S);
+
+/* The same product at `count` sampled output positions (mi[c], ni[c]). */
+int qref_qmatmul_sampled(const void* x, int x_dtype, int64_t m, int64_t k,
+                         const uint32_t* wq, const void* scales, const void* biases,
+                         int sb_dtype, int64_t n, int bits, int group_size,
+                         const int64_t* mi, const int64_t* ni, int64_t count,
+                         double* y, double* S);
+
+/* MoE over stacked experts, one (token, slot) pair at a time.
+ * Pair p = t*top_k + j reads the activation row a + t*a_outer + j*a_inner
+ * (element offsets) and expert ids[p]'s weights:
+ *   wq: [E, n_rows, n_cols*bits/32], scales/biases: [E, n_rows, n_cols/gs].
+ * out, S: [n_tokens*top_k, n_rows] fp64. Returns -2 if an id is out of range. */
+int qref_moe(const void* a, int a_dtype, const int32_t* ids, int64_t n_tokens,
+             int64_t top_k, int64_t a_outer, int64_t a_inner,
+             const uint32_t* wq, const void* scales, const void* biases, int sb_dtype,
+             int64_t num_experts, int64_t n_rows, int64_t n_cols, int bits,
+             int group_size, double* out, double* S);
+
+/* Fused gate/up: silu_out[p,r] = SiLU(g) * u with g, u the gate and up
+ * products of pair p, row r (fp64). Also returns g, u and their S terms. */
+int qref_moe_gate_up_silu(const void* a, int a_dtype, const int32_t* ids,
+                          int64_t n_tokens, int64_t top_k, int64_t a_outer,
+                          int64_t a_inner,
+                          const uint32_t* gate_wq, const void* gate_s, const void* gate_b,
+                          const uint32_t* up_wq, const void* up_s, const void* up_b,
+                          int sb_dtype, int64_t num_experts, int64_t n_rows,
+                          int64_t n_cols, int bits, int group_size,
+                          double* silu_out, double* g, double* u, double* Sg, double* Su);
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int qref_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
