@@ -1,0 +1,166 @@
+/*
+ * qpack.h — C ABI of libqpack.so: weight-only quantized linear layers on
+ * MI355X (gfx950).
+ *
+ *   y = x @ dequant(W)^T,   dequant(W)[n, k] = q[n, k] * scale[n, g] + bias[n, g],
+ *   g = k / group_size,
+ *
+ * with W stored as packed b-bit codes (b in {2, 3, 4, 6, 8}) and one scale and
+ * one bias per group of `group_size` consecutive elements along K.
+ *
+ * Sources (the surveyed pages):
+ *  - emily lib/emily/quantization.ex, `quantized_matmul/2` docs: the product
+ *    x @ W^T with W packed row-major [N, K] ("transpose = true"), and the rule
+ *    that the input dtype must equal the scales dtype (affine mode).
+ *  - same page, `dequantize_defn/1` docs and its unpack helpers: lane i of a
+ *    row sits at bit offset i*bits of the row's little-endian u32 stream,
+ *    masked to `bits` bits; 3- and 6-bit lanes may straddle two words; the
+ *    packed length must satisfy K*bits % 32 == 0; groups run along the last
+ *    axis (K % group_size == 0).
+ *  - ollama x/create/client/quantize.go, `quantizeParams` and
+ *    `loadAndQuantizeArray`: quantize(w, group_size, bits, mode) returns
+ *    (codes, scales, biases); int4 = {64, 4, affine}, int8 = {64, 8, affine}.
+ *  - ferrum-kernels src/stacked_expert.rs, `StackedExpertGgufLinear` docs:
+ *    the MoE calls `gemv_moe_id` / `gemv_moe_id_batched` (pair p reads
+ *    a[(p/top_k)*outer + (p%top_k)*inner] and expert ids[p]) and
+ *    `gemv_moe_id_gate_up_silu` (SiLU(gate) * up in one dispatch).
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" are HIP device (or managed) memory; the caller
+ *    allocates and frees every buffer. The library never allocates device
+ *    memory.
+ *  - Calls are asynchronous on `stream` (0 = the null stream): they validate
+ *    on the host, enqueue kernels and return. There is no host synchronisation
+ *    and no device-to-host copy.
+ *  - Errors are returned as qp_status; nothing is thrown. On an error no work
+ *    is enqueued and qpack_last_error() (thread-local) describes it. Argument
+ *    checks run before any HIP call, so they work without a GPU.
+ *  - All arrays are row-major and densely packed (no row strides except the
+ *    MoE activation strides).
+ *  - Element types: QP_F32, QP_F16 (IEEE binary16), QP_BF16. 16-bit outputs
+ *    are rounded to nearest even from an fp32 accumulator.
+ */
+#ifndef QPACK_H
+#define QPACK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qp_status {
+    QP_OK = 0,
+    QP_ERR_INVALID_ARG = 1,    /* null pointer, negative size, size overflow */
+    QP_ERR_UNSUPPORTED = 2,    /* bits not in {2,3,4,6,8}, group_size not in {32,64,128} */
+    QP_ERR_DTYPE_MISMATCH = 3, /* activation dtype != scales dtype */
+    QP_ERR_SHAPE = 4,          /* K % group_size != 0, K*bits % 32 != 0, gate/up mismatch */
+    QP_ERR_ALIGN = 5,          /* a pointer not aligned to its element size */
+    QP_ERR_WORKSPACE = 6,      /* MoE workspace too small */
+    QP_ERR_HIP = 7             /* a HIP launch failed */
+} qp_status;
+
+typedef enum qp_dtype { QP_F32 = 0, QP_F16 = 1, QP_BF16 = 2 } qp_dtype;
+
+/*
+ * Affine group quantization (ollama quantize.go `loadAndQuantizeArray`,
+ * emily `QuantizedWeight.from_dense/2`), computed on the device.
+ *   w       device, fp32 [n, k]                       (input)
+ *   wq      device, u32 [n, k*bits/32]                (output, packed codes)
+ *   scales  device, sb_dtype [n, k/group_size]        (output)
+ *   biases  device, sb_dtype [n, k/group_size]        (output)
+ * Per row and group: mn/mx = group min/max; s = (mx - mn) / (2^bits - 1) in
+ * fp32, floored at FLT_EPSILON; stored s' = RNE(s), b' = RNE(mn) (a zero bias
+ * is stored as +0); q = clamp(round_half_away((w - b') / s'), 0, 2^bits - 1);
+ * lane i of the row goes to bits [i*bits, i*bits + bits) of the row's u32
+ * stream. Inputs must be finite; with fp16 storage, |scale| and |bias| must
+ * stay below 65504. Deterministic: the output does not depend on the launch.
+ * n == 0 or k == 0 is a no-op.
+ */
+qp_status qpack_quantize(const float* w, int64_t n, int64_t k, int32_t bits,
+                         int32_t group_size, qp_dtype sb_dtype, uint32_t* wq,
+                         void* scales, void* biases, hipStream_t stream);
+
+/*
+ * Quantized linear (emily `quantized_matmul/2`, transpose = true):
+ *   y[m, n] = sum_k x[m, k] * (q[n, k] * s'[n, k/gs] + b'[n, k/gs])
+ *   x       device, x_dtype [m, k]
+ *   wq      device, u32 [n, k*bits/32]
+ *   scales, biases  device, sb_dtype [n, k/group_size]; sb_dtype must equal
+ *           x_dtype (QP_ERR_DTYPE_MISMATCH otherwise)
+ *   y       device, x_dtype [m, n] (output)
+ * fp32 accumulation. m <= 16 runs the decode GEMV (VALU, weights streamed
+ * once); m > 16 with 16-bit activations runs the MFMA prefill GEMM. k == 0
+ * writes zeros; m == 0 or n == 0 is a no-op.
+ */
+qp_status qmatmul(const void* x, qp_dtype x_dtype, int64_t m, int64_t k,
+                  const uint32_t* wq, const void* scales, const void* biases,
+                  qp_dtype sb_dtype, int64_t n, int32_t bits, int32_t group_size,
+                  void* y, hipStream_t stream);
+
+/*
+ * Workspace (bytes) the MoE calls need for n_pairs = n_tokens * top_k pairs
+ * over num_experts experts (routing tables, written by the device).
+ */
+size_t qgemv_moe_workspace_bytes(int64_t n_pairs, int64_t num_experts);
+
+/*
+ * MoE over stacked experts (ferrum-kernels stacked_expert.rs,
+ * `gemv_moe_id` / `gemv_moe_id_batched`):
+ *   for p in [0, n_tokens*top_k):  t = p / top_k, j = p % top_k,
+ *     out[p, :] = a_row(p) @ dequant(W[ids[p]])^T,
+ *     a_row(p) = a + t*a_outer_stride + j*a_inner_stride   (elements)
+ *   a        device, a_dtype, rows of n_cols elements at the strides above
+ *   ids      device, int32 [n_tokens*top_k], each in [0, num_experts)
+ *   wq       device, u32 [num_experts, n_rows, n_cols*bits/32] (expert-major)
+ *   scales, biases  device, sb_dtype [num_experts, n_rows, n_cols/group_size]
+ *   out      device, a_dtype [n_tokens*top_k, n_rows] (output)
+ *   workspace device, >= qgemv_moe_workspace_bytes(n_tokens*top_k, num_experts)
+ * The single-token form of the page is n_tokens = 1, top_k = n_selected,
+ * a_outer_stride = 0, a_inner_stride = src1_stride; its offset form is
+ * pointer arithmetic on `a` and `ids`. Pairs are sorted by expert on the
+ * device, so each expert's weights are streamed once per launch. A pair whose
+ * id is out of range is skipped (its output row is left unwritten).
+ */
+qp_status qgemv_moe_id(const void* a, qp_dtype a_dtype, const int32_t* ids,
+                       int64_t n_tokens, int64_t top_k, int64_t a_outer_stride,
+                       int64_t a_inner_stride, const uint32_t* wq, const void* scales,
+                       const void* biases, qp_dtype sb_dtype, int64_t num_experts,
+                       int64_t n_rows, int64_t n_cols, int32_t bits, int32_t group_size,
+                       void* out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * Fused gate/up MoE product (ferrum-kernels stacked_expert.rs,
+ * `gemv_moe_id_gate_up_silu` and its batched form): one launch computes,
+ * for every pair p and row r,
+ *   silu_out[p, r] = SiLU(g) * u,  g = a_row(p) . gate_W[ids[p], r, :],
+ *                                  u = a_row(p) . up_W[ids[p], r, :],
+ *   SiLU(z) = z / (1 + exp(-z)),
+ * with both stacks of identical shape, bits and group size. Arguments as in
+ * qgemv_moe_id; silu_out is a_dtype [n_tokens*top_k, n_rows].
+ */
+qp_status qgemv_moe_id_gate_up_silu(const void* a, qp_dtype a_dtype, const int32_t* ids,
+                                    int64_t n_tokens, int64_t top_k,
+                                    int64_t a_outer_stride, int64_t a_inner_stride,
+                                    const uint32_t* gate_wq, const void* gate_scales,
+                                    const void* gate_biases, const uint32_t* up_wq,
+                                    const void* up_scales, const void* up_biases,
+                                    qp_dtype sb_dtype, int64_t num_experts, int64_t n_rows,
+                                    int64_t n_cols, int32_t bits, int32_t group_size,
+                                    void* silu_out, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* Description of the calling thread's last error ("" if none). */
+const char* qpack_last_error(void);
+
+/* Library version string. */
+const char* qpack_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QPACK_H */

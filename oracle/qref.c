@@ -267,10 +267,17 @@ int qref_quantize(const float* w, int64_t n, int64_t k, int bits, int group_size
     int64_t groups = k / group_size;
     int64_t words = words_per_row(k, bits);
     float qmax = (float)((1 << bits) - 1);
+    int failed = 0;
+    /* Rows are independent; each thread packs its own rows. */
+#pragma omp parallel reduction(| : failed)
+    {
     uint8_t* codes = (uint8_t*)malloc((size_t)(k > 0 ? k : 1));
     if (!codes)
-        return -1;
+        failed = 1;
+#pragma omp for schedule(static)
     for (int64_t r = 0; r < n; ++r) {
+        if (!codes)
+            continue;
         const float* wr = w + r * k;
         for (int64_t g = 0; g < groups; ++g) {
             const float* wg = wr + g * group_size;
@@ -296,7 +303,8 @@ int qref_quantize(const float* w, int64_t n, int64_t k, int bits, int group_size
         qref_pack(codes, 1, k, bits, wq + r * words);
     }
     free(codes);
-    return 0;
+    }
+    return failed ? -1 : 0;
 }
 
 /* Dequantized weight (n_row's element i) in fp32: fp32(q) * s' + b'. */

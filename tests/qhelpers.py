@@ -1,0 +1,91 @@
+"""Shared helpers for the GPU parity tests: moving seeded inputs between numpy
+(the oracle's side) and device tensors (the library's side), and the error
+bound every floating-point comparison uses.
+
+Bound (per output element): |y_gpu - y_ref| <= tau * S + half_ulp_out(y_ref),
+with S = sum_k |x| |w'| from the oracle, tau = 2e-3 for 16-bit activations and
+1e-5 for fp32, and half_ulp_out bounded by |y_ref| * 2^-(p+1) for the output
+format's p fraction bits (bf16: 7, fp16: 10, fp32: 23). The half-ulp term
+covers the final rounding of the fp32 accumulator to the output type.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import qref
+
+F32, F16, BF16 = qref.F32, qref.F16, qref.BF16
+TORCH_DT = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
+TAU = {F32: 1e-5, F16: 2e-3, BF16: 2e-3}
+HALF_ULP = {F32: 2.0 ** -24, F16: 2.0 ** -11, BF16: 2.0 ** -8}
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def to_device(a: np.ndarray, dt: int) -> torch.Tensor:
+    """numpy storage (fp32 values, or uint16 bit patterns) -> device tensor."""
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32).copy()).to(dev())
+    if dt == F32:
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy())
+    return t.view(TORCH_DT[dt]).to(dev())
+
+
+def to_numpy(t: torch.Tensor) -> np.ndarray:
+    """device tensor -> numpy storage (fp32 values, uint16 bits or uint32 words)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.int32:
+        return t.numpy().view(np.uint32)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def values(t: torch.Tensor) -> np.ndarray:
+    """fp64 values of a device tensor."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def activations(shape, dt: int, seed: int, sigma: float = 1.0):
+    """Seeded N(0, sigma^2) activations rounded (RNE) to dt: (oracle storage, device tensor)."""
+    from weight_only_quantized_qgemv_amd import synth
+    x = synth.normal_f32(shape, sigma, seed)
+    t = torch.from_numpy(x).to(TORCH_DT[dt])
+    return to_numpy(t), t.to(dev())
+
+
+def assert_within(y_gpu: torch.Tensor, y_ref: np.ndarray, S: np.ndarray, dt: int, what: str,
+                  tau: float | None = None) -> None:
+    tau = TAU[dt] if tau is None else tau
+    y = values(y_gpu).reshape(y_ref.shape)
+    bound = tau * S + np.abs(y_ref) * HALF_ULP[dt]
+    err = np.abs(y - y_ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err - bound, -np.inf)), y_ref.shape)
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} outside the bound; worst at {i}: "
+            f"gpu={y[i]!r} ref={y_ref[i]!r} err={err[i]:.3e} bound={bound[i]:.3e}")
+    assert np.isfinite(y).all()
+
+
+def rne_to_bits(y_ref: np.ndarray, dt: int) -> np.ndarray:
+    """Oracle value rounded to the output type (oracle's converters): bits."""
+    f = y_ref.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), y_ref), "value not exact in fp32"
+    if dt == F32:
+        return f.view(np.uint32)
+    return qref.f32_to_bf16(f) if dt == BF16 else qref.f32_to_f16(f)
+
+
+def bits_of(t: torch.Tensor, dt: int) -> np.ndarray:
+    a = to_numpy(t)
+    return a.view(np.uint32) if dt == F32 else a

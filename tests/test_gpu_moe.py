@@ -1,0 +1,178 @@
+"""GPU parity of the MoE calls (qgemv_moe_id, qgemv_moe_id_gate_up_silu)
+against the oracle's per-pair products, through the C ABI.
+
+Bounds: the plain product uses tau*S + half an output ulp. The fused form uses
+the first-order propagation of that bound through SiLU(g)*u:
+  |d| <= tau * (1.1 |u| S_g + |SiLU(g)| S_u) + half_ulp(out),
+where 1.1 >= max |SiLU'(z)| (about 1.0998 near z = 2.4). The down projection is
+checked on identical inputs: the oracle's SiLU output rounded to bf16 is fed
+to both sides.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import weight_only_quantized_qgemv_amd as qp
+from oracle import qref
+from qhelpers import (BF16, F16, F32, HALF_ULP, TAU, TORCH_DT, activations, assert_within, dev,
+                      log, to_device, to_numpy, values)
+from weight_only_quantized_qgemv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def stack(E, R, C, bits, gs, dt, seed):
+    """Oracle-quantized expert stack (numpy) and its device copy."""
+    w = synth.normal_f32((E * R, C), 0.02, seed)
+    wq, s, b = qref.quantize(w, bits, gs, dt)
+    host = (wq.reshape(E, R, -1), s.reshape(E, R, -1), b.reshape(E, R, -1))
+    return host, tuple(to_device(t, dt) for t in host)
+
+
+def fused_bound(ref, dt):
+    sig = 1.0 / (1.0 + np.exp(-ref["g"]))
+    return (TAU[dt] * (1.1 * np.abs(ref["u"]) * ref["Sg"] + np.abs(ref["g"] * sig) * ref["Su"])
+            + np.abs(ref["silu_out"]) * HALF_ULP[dt])
+
+
+def check_fused(out, ref, dt, what, rows=None):
+    y = values(out)
+    if rows is not None:
+        y = y[rows]
+    err = np.abs(y - ref["silu_out"])
+    bound = fused_bound(ref, dt)
+    bad = ~(err <= bound)
+    assert not bad.any(), f"{what}: {int(bad.sum())} outside; worst excess {(err - bound).max():.3e}"
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
+@pytest.mark.parametrize("dt", [F32, F16, BF16])
+@pytest.mark.parametrize("T,top_k,E", [(1, 4, 6), (5, 3, 6), (40, 4, 8)])
+def test_moe_gate_up_and_down_small(bits, dt, T, top_k, E):
+    R, C, gs = 64, 256, 64        # gate/up: [E, R, C]; down: [E, C, R]
+    log(f"moe small bits={bits} dt={dt} T={T} top_k={top_k} E={E}")
+    gate_h, gate_d = stack(E, R, C, bits, gs, dt, 51 + bits)
+    up_h, up_d = stack(E, R, C, bits, gs, dt, 52 + bits)
+    down_h, down_d = stack(E, C, R, bits, 32, dt, 53 + bits)
+    ids = synth.moe_ids(T, top_k, E, seed=55).ravel()
+    ids_d = torch.from_numpy(ids).to(dev())
+    a_s, a_d = activations((T, C), dt, 54)
+    # gate/up: every slot of a token reads the token's row (outer = C, inner = 0)
+    out = qp.qgemv_moe_id_gate_up_silu(a_d, ids_d, T, top_k, C, 0, gate_d, up_d, bits, gs)
+    torch.cuda.synchronize()
+    ref = qref.moe_gate_up_silu(a_s, dt, ids, T, top_k, C, 0, gate_h, up_h, dt, E, R, C, bits, gs)
+    check_fused(out, ref, dt, "gate_up")
+    # plain product with the gate stack
+    g = qp.qgemv_moe_id(a_d, ids_d, T, top_k, C, 0, *gate_d, bits, gs)
+    torch.cuda.synchronize()
+    assert_within(g, ref["g"], ref["Sg"], dt, "moe plain")
+    # down: pair p reads its own row of the oracle's SiLU output, rounded to dt
+    h_f32 = ref["silu_out"].astype(np.float32)
+    h_s = h_f32 if dt == F32 else (qref.f32_to_bf16(h_f32) if dt == BF16 else qref.f32_to_f16(h_f32))
+    h_d = to_device(np.ascontiguousarray(h_s), dt)
+    out_d = qp.qgemv_moe_id(h_d, ids_d, T, top_k, top_k * R, R, *down_d, bits, 32)
+    torch.cuda.synchronize()
+    ref_d, S_d = qref.moe(h_s, dt, ids, T, top_k, top_k * R, R, *down_h, dt, E, C, R, bits, 32)
+    assert_within(out_d, ref_d, S_d, dt, "moe down")
+
+
+def moe_config(T, seed_ids=55):
+    E, top_k = 128, 8
+    gate_h, gate_d = stack(E, 768, 2048, 4, 64, BF16, 51)
+    up_h, up_d = stack(E, 768, 2048, 4, 64, BF16, 52)
+    down_h, down_d = stack(E, 2048, 768, 4, 64, BF16, 53)
+    ids = synth.moe_ids(T, top_k, E, seed=seed_ids).ravel()
+    a_s, a_d = activations((T, 2048), BF16, 54)
+    return E, top_k, ids, a_s, a_d, (gate_h, gate_d), (up_h, up_d), (down_h, down_d)
+
+
+@pytest.mark.parametrize("T", [1, 64, 512])
+def test_moe_config_sampled(T):
+    """128 experts, top-8, gate/up [128, 768, 2048], down [128, 2048, 768], 4-bit
+    gs64 bf16; tokens x bf16 [T, 2048]; fused SiLU(gate)*up then down."""
+    log(f"moe config T={T}")
+    E, top_k, ids, a_s, a_d, gate, up, down = moe_config(T)
+    P = T * top_k
+    ids_d = torch.from_numpy(ids).to(dev())
+    out = qp.qgemv_moe_id_gate_up_silu(a_d, ids_d, T, top_k, 2048, 0, gate[1], up[1], 4, 64)
+    torch.cuda.synchronize()
+    # Oracle on a sample of pairs (all pairs of the sampled tokens).
+    g = synth.rng(T)
+    toks = np.unique(np.concatenate([g.integers(0, T, min(T, 6)), [0, T - 1]]))
+    sel = np.concatenate([np.arange(t * top_k, (t + 1) * top_k) for t in toks])
+    a_sub = np.ascontiguousarray(a_s[toks])
+    ref = qref.moe_gate_up_silu(a_sub, BF16, ids[sel], len(toks), top_k, 2048, 0, gate[0], up[0],
+                                BF16, E, 768, 2048, 4, 64)
+    check_fused(out, ref, BF16, "config gate_up", rows=sel)
+    # Down on identical inputs: oracle SiLU output (all pairs would be costly on
+    # the CPU, so the sampled pairs' rows are fed, the rest kept from the GPU).
+    h = to_numpy(out).copy()
+    h[sel] = qref.f32_to_bf16(ref["silu_out"].astype(np.float32))
+    h_d = to_device(h, BF16)
+    out_d = qp.qgemv_moe_id(h_d, ids_d, T, top_k, top_k * 768, 768, *down[1], 4, 64)
+    torch.cuda.synchronize()
+    h_sub = np.ascontiguousarray(h[sel])
+    ref_d, S_d = qref.moe(h_sub, BF16, ids[sel], len(sel), 1, 768, 0, *down[0], BF16, E, 2048,
+                          768, 4, 64)
+    assert_within(out_d[torch.from_numpy(sel).to(dev())], ref_d, S_d, BF16, "config down")
+
+
+def test_moe_single_token_and_offset_forms():
+    """Single-token form (n_tokens=1, top_k=n_selected, outer=0, inner=src1_stride)
+    and the offset form (pointer arithmetic on a and ids) equal the batched form."""
+    E, R, C, bits, gs = 8, 32, 128, 4, 32
+    h, d = stack(E, R, C, bits, gs, BF16, 71)
+    rows_s, rows_d = activations((6, C), BF16, 72)
+    ids = np.array([3, 1, 7, 0, 5, 2], dtype=np.int32)
+    ids_d = torch.from_numpy(ids).to(dev())
+    full = qp.qgemv_moe_id(rows_d, ids_d, 6, 1, C, 0, *d, bits, gs)
+    single = qp.qgemv_moe_id(rows_d, ids_d, 1, 6, 0, C, *d, bits, gs)
+    off = qp.qgemv_moe_id(rows_d[2:], ids_d[2:], 1, 4, 0, C, *d, bits, gs)
+    torch.cuda.synchronize()
+    assert torch.equal(full, single)
+    assert torch.equal(full[2:], off)
+    ref, S = qref.moe(rows_s, BF16, ids, 1, 6, 0, C, *h, BF16, E, R, C, bits, gs)
+    assert_within(single, ref, S, BF16, "single-token")
+
+
+def test_moe_permutation_of_pairs_permutes_outputs():
+    E, R, C, bits, gs = 16, 64, 256, 4, 64
+    h, d = stack(E, R, C, bits, gs, BF16, 81)
+    P = 64
+    ids = synth.random_ints((P,), 0, E - 1, 82).astype(np.int32)
+    a_s, a_d = activations((P, C), BF16, 83)
+    out = qp.qgemv_moe_id(a_d, torch.from_numpy(ids).to(dev()), P, 1, C, 0, *d, bits, gs)
+    perm = synth.rng(84).permutation(P)
+    out_p = qp.qgemv_moe_id(a_d[torch.from_numpy(perm).to(dev())].contiguous(),
+                            torch.from_numpy(ids[perm]).to(dev()), P, 1, C, 0, *d, bits, gs)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out[torch.from_numpy(perm).to(dev())])
+
+
+def test_moe_invalid_ids_are_skipped():
+    E, R, C, bits, gs = 4, 16, 64, 4, 64
+    h, d = stack(E, R, C, bits, gs, BF16, 91)
+    ids = np.array([1, -1, 4, 2], dtype=np.int32)
+    a_s, a_d = activations((4, C), BF16, 92)
+    out = torch.full((4, R), 123.0, dtype=torch.bfloat16, device=dev())
+    qp.qgemv_moe_id(a_d, torch.from_numpy(ids).to(dev()), 4, 1, C, 0, *d, bits, gs, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out[1] == 123.0) and torch.all(out[2] == 123.0)
+    ref, S = qref.moe(np.ascontiguousarray(a_s[[0, 3]]), BF16, ids[[0, 3]], 2, 1, C, 0, *h, BF16,
+                      E, R, C, bits, gs)
+    assert_within(out[[0, 3]], ref, S, BF16, "valid rows")
+
+
+def test_moe_expert_with_many_pairs_spans_tiles():
+    """All pairs on one expert: several tiles of the same expert."""
+    E, R, C, bits, gs = 4, 48, 512, 4, 64
+    h, d = stack(E, R, C, bits, gs, BF16, 95)
+    P = 37
+    ids = np.full(P, 2, dtype=np.int32)
+    a_s, a_d = activations((P, C), BF16, 96)
+    out = qp.qgemv_moe_id(a_d, torch.from_numpy(ids).to(dev()), P, 1, C, 0, *d, bits, gs)
+    torch.cuda.synchronize()
+    ref, S = qref.moe(a_s, BF16, ids, P, 1, C, 0, *h, BF16, E, R, C, bits, gs)
+    assert_within(out, ref, S, BF16, "one expert")

@@ -1,0 +1,233 @@
+"""GPU parity of qpack_quantize and qmatmul against the oracle, through the C ABI.
+
+Quantize: bit-exact codes, scales and biases. qmatmul: element by element
+within tau*S + half an output ulp (see qhelpers), and bit-exact on inputs
+whose arithmetic is exact in fp32. Weights fed to the library's products are
+always the oracle's quantization of the seeded fp32 W (never the device's).
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import weight_only_quantized_qgemv_amd as qp
+from oracle import qref
+from qhelpers import (BF16, F16, F32, TORCH_DT, activations, assert_within, bits_of, dev, log,
+                      rne_to_bits, to_device, to_numpy, values)
+from weight_only_quantized_qgemv_amd import synth
+
+pytestmark = pytest.mark.gpu
+ALL_BITS = [2, 3, 4, 6, 8]
+
+
+def quantize_both(w: np.ndarray, bits: int, gs: int, dt: int):
+    """Oracle and device quantization of w; asserts they agree bit for bit and
+    returns the oracle's (wq, s, b) as numpy plus device copies of them."""
+    rq, rs, rb = qref.quantize(w, bits, gs, dt)
+    gq, gs_, gb = qp.qpack_quantize(torch.from_numpy(w).to(dev()), bits, gs, TORCH_DT[dt])
+    torch.cuda.synchronize()
+    bits_view = np.uint32 if dt == F32 else np.uint16
+    assert np.array_equal(to_numpy(gq), rq), "codes differ"
+    assert np.array_equal(to_numpy(gs_).view(bits_view), rs.view(bits_view)), "scales differ"
+    assert np.array_equal(to_numpy(gb).view(bits_view), rb.view(bits_view)), "biases differ"
+    return (rq, rs, rb), (to_device(rq, dt), to_device(rs, dt), to_device(rb, dt))
+
+
+# ------------------------------------------------------------------ quantize
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("dt", [F32, F16, BF16])
+def test_quantize_bit_exact_small(bits, gs, dt):
+    log(f"quantize bits={bits} gs={gs} dt={dt} [97, 384]")
+    w = synth.normal_f32((97, 384), 0.02, seed=100 + bits + gs + dt)
+    w[3, :gs] = 0.5            # constant group
+    w[5, gs:2 * gs] *= 400.0   # large range
+    w[7] += 3.0                # far from zero (bias rounding matters)
+    quantize_both(w, bits, gs, dt)
+
+
+def test_quantize_iota_example():
+    w = synth.iota_f32((4, 128))
+    (rq, rs, rb), _ = quantize_both(w, 4, 64, F32)
+    assert np.all(rs == np.float32(63) / np.float32(15))
+
+
+@pytest.mark.parametrize("shape,bits,gs,dt,seed", [
+    ((256, 1024), 4, 64, F32, 11),
+    ((14336, 4096), 4, 64, BF16, 21),
+    ((14336, 4096), 8, 64, BF16, 21),
+    ((14336, 4096), 2, 64, BF16, 21),
+    ((4096, 4096), 3, 32, F16, 31), ((4096, 4096), 3, 64, F16, 31), ((4096, 4096), 3, 128, F16, 31),
+    ((4096, 4096), 6, 32, F16, 31), ((4096, 4096), 6, 64, F16, 31), ((4096, 4096), 6, 128, F16, 31),
+])
+def test_quantize_bit_exact_full_configs(shape, bits, gs, dt, seed):
+    log(f"quantize full {shape} bits={bits} gs={gs} dt={dt}")
+    quantize_both(synth.normal_f32(shape, 0.02, seed), bits, gs, dt)
+
+
+def test_quantize_empty_is_noop():
+    w = torch.empty((0, 64), dtype=torch.float32, device=dev())
+    wq, s, b = qp.qpack_quantize(w, 4, 64)
+    assert wq.shape == (0, 8)
+
+
+# ------------------------------------------------------------------ qmatmul
+
+def run_case(n, k, m, bits, gs, dt, seed):
+    w = synth.normal_f32((n, k), 0.02, seed)
+    (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, bits, gs, dt)
+    xs, xt = activations((m, k), dt, seed + 1)
+    y = qp.qmatmul(xt, gq, gs_, gb, bits, gs)
+    torch.cuda.synchronize()
+    y_ref, S = qref.qmatmul(xs, dt, rq, rs, rb, dt, k, bits, gs)
+    return y, y_ref, S
+
+
+SMALL = list(itertools.product(ALL_BITS, [F32, F16, BF16]))
+
+
+@pytest.mark.parametrize("bits,dt", SMALL)
+@pytest.mark.parametrize("k,m", [(32, 1), (96, 3), (768, 2), (1024, 5), (2048, 8), (4096, 16),
+                                 (4096, 1), (1024, 13)])
+def test_qmatmul_parity_small(bits, dt, k, m):
+    gs = {32: 32, 96: 32, 768: 64, 1024: 128, 2048: 64, 4096: 64}[k]
+    n = 301  # not a multiple of any block's row count
+    log(f"qmatmul bits={bits} dt={dt} n={n} k={k} m={m} gs={gs}")
+    y, y_ref, S = run_case(n, k, m, bits, gs, dt, seed=1000 + 7 * bits + k + m + dt)
+    assert_within(y, y_ref, S, dt, f"qmatmul b{bits} dt{dt} k{k} m{m}")
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("dt", [F32, F16, BF16])
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_qmatmul_exact_arithmetic_is_bit_exact(bits, dt, m):
+    """s' = 1/16, b' = -2^(bits-1)/16, integer x in [-8, 8]: every partial sum
+    is exact in fp32, so y must be the output rounding of the exact result."""
+    n, k, gs = 203, 4096, 64
+    log(f"exact bits={bits} dt={dt} m={m}")
+    codes = synth.random_codes((n, k), bits, seed=2000 + bits)
+    rq = qref.pack(codes, bits)
+    sv = np.full((n, k // gs), 1 / 16, dtype=np.float32)
+    bv = np.full((n, k // gs), -(2 ** (bits - 1)) / 16, dtype=np.float32)
+    rs = sv if dt == F32 else (qref.f32_to_bf16(sv) if dt == BF16 else qref.f32_to_f16(sv))
+    rb = bv if dt == F32 else (qref.f32_to_bf16(bv) if dt == BF16 else qref.f32_to_f16(bv))
+    x = synth.random_ints((m, k), -8, 8, seed=2100 + bits).astype(np.float32)
+    xs = x if dt == F32 else (qref.f32_to_bf16(x) if dt == BF16 else qref.f32_to_f16(x))
+    y = qp.qmatmul(to_device(xs, dt), to_device(rq, dt), to_device(rs, dt), to_device(rb, dt),
+                   bits, gs)
+    torch.cuda.synchronize()
+    y_ref, _ = qref.qmatmul(xs, dt, rq, rs, rb, dt, k, bits, gs)
+    assert np.array_equal(bits_of(y, dt), rne_to_bits(y_ref, dt))
+
+
+def test_qmatmul_iota_example_shape_and_values():
+    w = synth.iota_f32((4, 128))
+    x = synth.iota_f32((3, 128))
+    (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, 4, 64, F32)
+    y = qp.qmatmul(torch.from_numpy(x).to(dev()), gq, gs_, gb, 4, 64)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (3, 4)
+    y_ref, S = qref.qmatmul(x, F32, rq, rs, rb, F32, 128, 4, 64)
+    assert_within(y, y_ref, S, F32, "iota")
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_qmatmul_tiny_config_full(m):
+    """W fp32 [256, 1024] N(0, 0.02) (seed 11), 4-bit gs64, fp32 scales; x fp32 N(0, 1)."""
+    log(f"tiny config m={m}")
+    w = synth.normal_f32((256, 1024), 0.02, 11)
+    (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, 4, 64, F32)
+    xs, xt = activations((m, 1024), F32, 12 if m == 1 else 13)
+    y = qp.qmatmul(xt, gq, gs_, gb, 4, 64)
+    torch.cuda.synchronize()
+    y_ref, S = qref.qmatmul(xs, F32, rq, rs, rb, F32, 1024, 4, 64)
+    assert_within(y, y_ref, S, F32, "tiny")
+
+
+def sampled_check(y, xs, dt, rq, rs, rb, k, bits, gs, n_samples=3000, seed=0, tau=None):
+    m, n = y.shape
+    g = synth.rng(seed)
+    mi = g.integers(0, m, n_samples)
+    ni = g.integers(0, n, n_samples)
+    # Always include the corners and the last row (ragged tails).
+    mi = np.concatenate([mi, [0, m - 1, 0, m - 1]])
+    ni = np.concatenate([ni, [0, 0, n - 1, n - 1]])
+    y_ref, S = qref.qmatmul_sampled(xs, dt, rq, rs, rb, dt, k, bits, gs, mi, ni)
+    yv = values(y)[mi, ni]
+    assert_within(torch.from_numpy(yv), y_ref, S, dt, "sampled", tau=tau)
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_qmatmul_decode_config_sampled(bits, m):
+    """W [14336, 4096] N(0, 0.02) (seed 21), gs64, bf16 scales; x bf16 [m, 4096] (seed 22)."""
+    log(f"decode config bits={bits} m={m}")
+    w = synth.normal_f32((14336, 4096), 0.02, 21)
+    (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, bits, 64, BF16)
+    xs, xt = activations((m, 4096), BF16, 22)
+    y = qp.qmatmul(xt, gq, gs_, gb, bits, 64)
+    torch.cuda.synchronize()
+    sampled_check(y, xs, BF16, rq, rs, rb, 4096, bits, 64, seed=bits * 100 + m)
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("m", [1, 8])
+def test_qmatmul_cross_word_config_sampled(bits, gs, m):
+    """W [4096, 4096] N(0, 0.02) (seed 31), fp16 scales; x fp16 [m, 4096] (seed 32)."""
+    log(f"cross-word config bits={bits} gs={gs} m={m}")
+    w = synth.normal_f32((4096, 4096), 0.02, 31)
+    (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, bits, gs, F16)
+    xs, xt = activations((m, 4096), F16, 32)
+    y = qp.qmatmul(xt, gq, gs_, gb, bits, gs)
+    torch.cuda.synchronize()
+    sampled_check(y, xs, F16, rq, rs, rb, 4096, bits, gs, seed=bits * 10 + gs + m)
+
+
+@pytest.mark.parametrize("m", [17, 64, 100])
+def test_qmatmul_prefill_sizes_small(m):
+    log(f"prefill small m={m}")
+    y, y_ref, S = run_case(130, 512, m, 4, 64, BF16, seed=3000 + m)
+    assert_within(y, y_ref, S, BF16, f"prefill m{m}")
+
+
+@pytest.mark.parametrize("shape_x,shape_w,xseed,wseed", [
+    ((2048, 4096), (14336, 4096), 43, 41),
+    ((2048, 14336), (4096, 14336), 44, 42),
+])
+def test_qmatmul_prefill_config_sampled(shape_x, shape_w, xseed, wseed):
+    log(f"prefill config x={shape_x} w={shape_w}")
+    w = synth.normal_f32(shape_w, 0.02, wseed)
+    (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, 4, 64, BF16)
+    xs, xt = activations(shape_x, BF16, xseed)
+    y = qp.qmatmul(xt, gq, gs_, gb, 4, 64)
+    torch.cuda.synchronize()
+    sampled_check(y, xs, BF16, rq, rs, rb, shape_w[1], 4, 64, seed=xseed)
+
+
+def test_qmatmul_k_zero_writes_zeros():
+    x = torch.ones((3, 0), dtype=torch.bfloat16, device=dev())
+    wq = torch.empty((5, 0), dtype=torch.int32, device=dev())
+    s = torch.empty((5, 0), dtype=torch.bfloat16, device=dev())
+    y = torch.full((3, 5), 7.0, dtype=torch.bfloat16, device=dev())
+    qp.qmatmul(x, wq, s, s, 4, 64, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
+def test_qmatmul_empty_m_or_n():
+    w = synth.normal_f32((8, 64), 0.02, 5)
+    _, (gq, gs_, gb) = quantize_both(w, 4, 64, BF16)
+    y = qp.qmatmul(torch.empty((0, 64), dtype=torch.bfloat16, device=dev()), gq, gs_, gb, 4, 64)
+    assert y.shape == (0, 8)
+
+
+def test_qmatmul_dtype_mismatch_raises():
+    w = synth.normal_f32((8, 64), 0.02, 5)
+    _, (gq, gs_, gb) = quantize_both(w, 4, 64, BF16)
+    with pytest.raises(qp.QpackError, match="DTYPE_MISMATCH"):
+        qp.qmatmul(torch.zeros((1, 64), dtype=torch.float16, device=dev()), gq, gs_, gb, 4, 64)

@@ -1,0 +1,266 @@
+// api.cpp — the C ABI of libqpack.so (declared in include/qpack.h): argument
+// validation on the host, then kernel selection and launch on the caller's
+// stream. Every check runs before any HIP call, so the error paths work on a
+// machine without a GPU.
+//
+// Rules enforced, by source:
+//  - bits in {2, 3, 4, 6, 8}: emily lib/emily/quantization.ex,
+//    `defn_supported_bits/0` and `validate_defn_bits!`;
+//  - K * bits % 32 == 0 and K % group_size == 0: same page,
+//    `build_word_indices` (the packing invariant) and `group_last_axis`;
+//  - activation dtype == scales dtype in affine mode: same page,
+//    `validate_dtype_match!`;
+//  - gate and up stacks of one shape: ferrum-kernels src/stacked_expert.rs,
+//    `gemv_moe_id_gate_up_silu` docs ("must match shape").
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/qpack.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qp_status fail(qp_status s, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+qp_status ok()
+{
+    g_last_error.clear();
+    return QP_OK;
+}
+
+qp_status hip_result(hipError_t e, const char* what)
+{
+    if (e != hipSuccess)
+        return fail(QP_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+    return ok();
+}
+
+bool bits_ok(int32_t b) { return b == 2 || b == 3 || b == 4 || b == 6 || b == 8; }
+bool gs_ok(int32_t g) { return g == 32 || g == 64 || g == 128; }
+bool dtype_ok(int d) { return d == QP_F32 || d == QP_F16 || d == QP_BF16; }
+size_t esize(int d) { return d == QP_F32 ? 4 : 2; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// a * b without int64 overflow (both non-negative).
+bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / a; }
+
+// Checks shared by every call: bits, group size, K divisibility.
+qp_status check_layout(int64_t k, int32_t bits, int32_t gs)
+{
+    if (!bits_ok(bits))
+        return fail(QP_ERR_UNSUPPORTED, "bits=%d not supported (2, 3, 4, 6, 8)", bits);
+    if (!gs_ok(gs))
+        return fail(QP_ERR_UNSUPPORTED, "group_size=%d not supported (32, 64, 128)", gs);
+    if (k % gs != 0)
+        return fail(QP_ERR_SHAPE, "K=%lld is not a multiple of group_size=%d", (long long)k, gs);
+    if ((k * bits) % 32 != 0)
+        return fail(QP_ERR_SHAPE, "K*bits=%lld is not a multiple of 32", (long long)(k * bits));
+    return QP_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char* qpack_last_error(void) { return g_last_error.c_str(); }
+
+const char* qpack_version(void) { return "qpack 0.1.0 (gfx950)"; }
+
+qp_status qpack_quantize(const float* w, int64_t n, int64_t k, int32_t bits, int32_t group_size,
+                         qp_dtype sb_dtype, uint32_t* wq, void* scales, void* biases,
+                         hipStream_t stream)
+{
+    if (n < 0 || k < 0)
+        return fail(QP_ERR_INVALID_ARG, "negative size (n=%lld, k=%lld)", (long long)n,
+                    (long long)k);
+    if (!dtype_ok(sb_dtype))
+        return fail(QP_ERR_INVALID_ARG, "unknown scales dtype %d", (int)sb_dtype);
+    if (qp_status s = check_layout(k, bits, group_size); s != QP_OK)
+        return s;
+    if (!mul_ok(n, k))
+        return fail(QP_ERR_INVALID_ARG, "n*k overflows");
+    if (n == 0 || k == 0)
+        return ok();
+    if (!w || !wq || !scales || !biases)
+        return fail(QP_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(w, 4) || !aligned(wq, 4) || !aligned(scales, esize(sb_dtype)) ||
+        !aligned(biases, esize(sb_dtype)))
+        return fail(QP_ERR_ALIGN, "pointer not aligned to its element size");
+    qp::QuantizeArgs a{w, n, k, bits, group_size, (int)sb_dtype, wq, scales, biases};
+    return hip_result(qp::launch_quantize(a, stream), "qpack_quantize");
+}
+
+qp_status qmatmul(const void* x, qp_dtype x_dtype, int64_t m, int64_t k, const uint32_t* wq,
+                  const void* scales, const void* biases, qp_dtype sb_dtype, int64_t n,
+                  int32_t bits, int32_t group_size, void* y, hipStream_t stream)
+{
+    if (m < 0 || k < 0 || n < 0)
+        return fail(QP_ERR_INVALID_ARG, "negative size (m=%lld, k=%lld, n=%lld)", (long long)m,
+                    (long long)k, (long long)n);
+    if (!dtype_ok(x_dtype) || !dtype_ok(sb_dtype))
+        return fail(QP_ERR_INVALID_ARG, "unknown dtype (x=%d, scales=%d)", (int)x_dtype,
+                    (int)sb_dtype);
+    if (qp_status s = check_layout(k, bits, group_size); s != QP_OK)
+        return s;
+    if (x_dtype != sb_dtype)
+        return fail(QP_ERR_DTYPE_MISMATCH,
+                    "input dtype %d must match scales dtype %d (affine mode)", (int)x_dtype,
+                    (int)sb_dtype);
+    if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n))
+        return fail(QP_ERR_INVALID_ARG, "size product overflows");
+    if (m == 0 || n == 0)
+        return ok();
+    if (!y)
+        return fail(QP_ERR_INVALID_ARG, "null output pointer");
+    const size_t es = esize(x_dtype);
+    if (!aligned(y, es))
+        return fail(QP_ERR_ALIGN, "y not aligned to its element size");
+    if (k == 0)
+        return hip_result(qp::launch_fill_zero(y, (int)x_dtype, m * n, stream), "qmatmul");
+    if (!x || !wq || !scales || !biases)
+        return fail(QP_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(x, es) || !aligned(wq, 4) || !aligned(scales, es) || !aligned(biases, es))
+        return fail(QP_ERR_ALIGN, "pointer not aligned to its element size");
+    qp::GemvArgs a{x, (int)x_dtype, m, k, n, wq, scales, biases, bits, group_size, y};
+    if (m <= 16 || x_dtype == QP_F32)
+        return hip_result(qp::launch_qgemv(a, stream), "qmatmul");
+    return hip_result(qp::launch_qgemm(a, stream), "qmatmul");
+}
+
+size_t qgemv_moe_workspace_bytes(int64_t n_pairs, int64_t num_experts)
+{
+    if (n_pairs < 0 || num_experts < 0)
+        return 0;
+    return qp::moe_workspace_bytes(n_pairs, num_experts);
+}
+
+static qp_status moe_common(const qp::MoeArgs& a, const char* what)
+{
+    if (a.n_tokens < 0 || a.top_k < 0 || a.E < 0 || a.n_rows < 0 || a.n_cols < 0 ||
+        a.a_outer < 0 || a.a_inner < 0)
+        return fail(QP_ERR_INVALID_ARG, "%s: negative size or stride", what);
+    if (!dtype_ok(a.dt))
+        return fail(QP_ERR_INVALID_ARG, "%s: unknown dtype", what);
+    if (qp_status s = check_layout(a.n_cols, a.bits, a.gs); s != QP_OK)
+        return s;
+    if (a.E > 4096)
+        return fail(QP_ERR_UNSUPPORTED, "%s: num_experts=%lld above 4096", what, (long long)a.E);
+    if (!mul_ok(a.n_tokens, a.top_k) || a.n_tokens * a.top_k > (int64_t)INT32_MAX / 2)
+        return fail(QP_ERR_INVALID_ARG, "%s: too many pairs", what);
+    const int64_t P = a.n_tokens * a.top_k;
+    if (!mul_ok(a.E, a.n_rows) || !mul_ok(a.E * a.n_rows, a.n_cols) || !mul_ok(P, a.n_rows))
+        return fail(QP_ERR_INVALID_ARG, "%s: size product overflows", what);
+    if (P == 0 || a.n_rows == 0)
+        return QP_OK;
+    if (a.E == 0)
+        return fail(QP_ERR_INVALID_ARG, "%s: no experts for %lld pairs", what, (long long)P);
+    if (!a.ids || !a.out || !a.workspace)
+        return fail(QP_ERR_INVALID_ARG, "%s: null pointer", what);
+    if (a.ws_bytes < qp::moe_workspace_bytes(P, a.E))
+        return fail(QP_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", what, a.ws_bytes,
+                    qp::moe_workspace_bytes(P, a.E));
+    const size_t es = esize(a.dt);
+    if (!aligned(a.out, es) || !aligned(a.ids, 4) || !aligned(a.workspace, 16))
+        return fail(QP_ERR_ALIGN, "%s: pointer not aligned", what);
+    if (a.n_cols > 0) {
+        if (!a.a)
+            return fail(QP_ERR_INVALID_ARG, "%s: null activation pointer", what);
+        if (!aligned(a.a, es))
+            return fail(QP_ERR_ALIGN, "%s: activations not aligned", what);
+        for (int t = 0; t < (a.fused_silu ? 2 : 1); ++t) {
+            if (!a.wq[t] || !a.scales[t] || !a.biases[t])
+                return fail(QP_ERR_INVALID_ARG, "%s: null weight pointer", what);
+            if (!aligned(a.wq[t], 4) || !aligned(a.scales[t], es) || !aligned(a.biases[t], es))
+                return fail(QP_ERR_ALIGN, "%s: weight pointer not aligned", what);
+        }
+    }
+    return QP_OK;
+}
+
+qp_status qgemv_moe_id(const void* a, qp_dtype a_dtype, const int32_t* ids, int64_t n_tokens,
+                       int64_t top_k, int64_t a_outer_stride, int64_t a_inner_stride,
+                       const uint32_t* wq, const void* scales, const void* biases,
+                       qp_dtype sb_dtype, int64_t num_experts, int64_t n_rows, int64_t n_cols,
+                       int32_t bits, int32_t group_size, void* out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream)
+{
+    if (dtype_ok(a_dtype) && dtype_ok(sb_dtype) && a_dtype != sb_dtype)
+        return fail(QP_ERR_DTYPE_MISMATCH, "qgemv_moe_id: input dtype must match scales dtype");
+    qp::MoeArgs m{};
+    m.a = a; m.dt = (int)a_dtype; m.ids = ids;
+    m.n_tokens = n_tokens; m.top_k = top_k; m.a_outer = a_outer_stride; m.a_inner = a_inner_stride;
+    m.wq[0] = m.wq[1] = wq; m.scales[0] = m.scales[1] = scales; m.biases[0] = m.biases[1] = biases;
+    m.E = num_experts; m.n_rows = n_rows; m.n_cols = n_cols; m.bits = bits; m.gs = group_size;
+    m.fused_silu = false; m.out = out; m.workspace = workspace; m.ws_bytes = workspace_bytes;
+    if (qp_status s = moe_common(m, "qgemv_moe_id"); s != QP_OK)
+        return s;
+    const int64_t P = n_tokens * top_k;
+    if (P == 0 || n_rows == 0)
+        return ok();
+    if (n_cols == 0)
+        return hip_result(qp::launch_fill_zero(out, (int)a_dtype, P * n_rows, stream),
+                          "qgemv_moe_id");
+    return hip_result(qp::launch_moe(m, stream), "qgemv_moe_id");
+}
+
+qp_status qgemv_moe_id_gate_up_silu(const void* a, qp_dtype a_dtype, const int32_t* ids,
+                                    int64_t n_tokens, int64_t top_k, int64_t a_outer_stride,
+                                    int64_t a_inner_stride, const uint32_t* gate_wq,
+                                    const void* gate_scales, const void* gate_biases,
+                                    const uint32_t* up_wq, const void* up_scales,
+                                    const void* up_biases, qp_dtype sb_dtype,
+                                    int64_t num_experts, int64_t n_rows, int64_t n_cols,
+                                    int32_t bits, int32_t group_size, void* silu_out,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (dtype_ok(a_dtype) && dtype_ok(sb_dtype) && a_dtype != sb_dtype)
+        return fail(QP_ERR_DTYPE_MISMATCH,
+                    "qgemv_moe_id_gate_up_silu: input dtype must match scales dtype");
+    qp::MoeArgs m{};
+    m.a = a; m.dt = (int)a_dtype; m.ids = ids;
+    m.n_tokens = n_tokens; m.top_k = top_k; m.a_outer = a_outer_stride; m.a_inner = a_inner_stride;
+    m.wq[0] = gate_wq; m.scales[0] = gate_scales; m.biases[0] = gate_biases;
+    m.wq[1] = up_wq; m.scales[1] = up_scales; m.biases[1] = up_biases;
+    m.E = num_experts; m.n_rows = n_rows; m.n_cols = n_cols; m.bits = bits; m.gs = group_size;
+    m.fused_silu = true; m.out = silu_out; m.workspace = workspace; m.ws_bytes = workspace_bytes;
+    if (qp_status s = moe_common(m, "qgemv_moe_id_gate_up_silu"); s != QP_OK)
+        return s;
+    const int64_t P = n_tokens * top_k;
+    if (P == 0 || n_rows == 0)
+        return ok();
+    if (n_cols == 0) // g = u = 0, SiLU(0) * 0 = 0
+        return hip_result(qp::launch_fill_zero(silu_out, (int)a_dtype, P * n_rows, stream),
+                          "qgemv_moe_id_gate_up_silu");
+    return hip_result(qp::launch_moe(m, stream), "qgemv_moe_id_gate_up_silu");
+}
+
+} // extern "C"
+
+namespace qp {
+
+hipError_t launch_qgemv(const GemvArgs& a, hipStream_t stream)
+{
+    switch (a.bits) {
+    case 2: return launch_qgemv_b2(a, stream);
+    case 3: return launch_qgemv_b3(a, stream);
+    case 4: return launch_qgemv_b4(a, stream);
+    case 6: return launch_qgemv_b6(a, stream);
+    case 8: return launch_qgemv_b8(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+} // namespace qp

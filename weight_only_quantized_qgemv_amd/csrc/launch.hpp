@@ -1,0 +1,89 @@
+// launch.hpp — host-side launchers implemented by the kernel files and
+// called by the C ABI layer (api.cpp). Arguments are validated by the caller;
+// every launcher returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qp {
+
+struct GemvArgs {
+    const void* x;          // [M, K] activations
+    int dt;                 // element type of x, scales, biases and y
+    int64_t M, K, N;
+    const uint32_t* wq;     // [N, K*bits/32]
+    const void* scales;     // [N, K/gs]
+    const void* biases;     // [N, K/gs]
+    int bits, gs;
+    void* y;                // [M, N]
+};
+
+#define QP_CAT_(a, b) a##b
+#define QP_CAT(a, b) QP_CAT_(a, b)
+
+// Decode GEMV (M <= 16): weights streamed once per launch group. One entry
+// point per bit width (each in its own translation unit), plus a dispatcher.
+hipError_t launch_qgemv_b2(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_qgemv_b3(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_qgemv_b4(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_qgemv_b6(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_qgemv_b8(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_qgemv(const GemvArgs& a, hipStream_t stream);
+
+// Prefill GEMM (M > 16, 16-bit activations): bf16/f16 MFMA.
+hipError_t launch_qgemm(const GemvArgs& a, hipStream_t stream);
+
+// Writes zeros to `n` elements of `dt` (used for K == 0).
+hipError_t launch_fill_zero(void* p, int dt, int64_t n, hipStream_t stream);
+
+struct QuantizeArgs {
+    const float* w;         // [N, K]
+    int64_t N, K;
+    int bits, gs, dt;       // dt: storage type of scales / biases
+    uint32_t* wq;
+    void* scales;
+    void* biases;
+};
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
+
+struct MoeArgs {
+    const void* a;          // activations
+    int dt;
+    const int32_t* ids;     // [P]
+    int64_t n_tokens, top_k, a_outer, a_inner;
+    const uint32_t* wq[2];  // expert stacks: [E, n_rows, n_cols*bits/32]; [1] = up (fused)
+    const void* scales[2];
+    const void* biases[2];
+    int64_t E, n_rows, n_cols;
+    int bits, gs;
+    bool fused_silu;        // out = SiLU(gate) * up
+    void* out;              // [P, n_rows]
+    void* workspace;
+    size_t ws_bytes;
+};
+size_t moe_workspace_bytes(int64_t n_pairs, int64_t num_experts);
+// Routing (moe.hip) and the per-(bits, fused) compute entry points
+// (moe_compute.hip, one translation unit each).
+struct MoeRouting {
+    const int32_t* n_tiles; // device tile count
+    const int32_t* perm;    // pair indices in expert order
+    const void* tiles;      // TileDesc list
+    int mt;                 // tile height
+    int64_t max_tiles;      // upper bound of the tile count
+};
+hipError_t launch_moe_route(const MoeArgs& a, int mt, MoeRouting* r, hipStream_t stream);
+int moe_tile_height(int64_t n_pairs, int64_t num_experts, int bits, int dt);
+#define QP_MOE_DECL(B)                                                                          \
+    hipError_t launch_moe_b##B##_n1(const MoeArgs& a, const MoeRouting& r, hipStream_t stream); \
+    hipError_t launch_moe_b##B##_n2(const MoeArgs& a, const MoeRouting& r, hipStream_t stream);
+QP_MOE_DECL(2)
+QP_MOE_DECL(3)
+QP_MOE_DECL(4)
+QP_MOE_DECL(6)
+QP_MOE_DECL(8)
+#undef QP_MOE_DECL
+hipError_t launch_moe(const MoeArgs& a, hipStream_t stream);
+
+} // namespace qp

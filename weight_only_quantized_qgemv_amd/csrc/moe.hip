@@ -1,0 +1,198 @@
+// moe.hip — MoE over stacked experts (ferrum-kernels src/stacked_expert.rs,
+// `gemv_moe_id`, `gemv_moe_id_batched`, `gemv_moe_id_gate_up_silu` docs):
+//   out[p, :] = a_row(p) @ dequant(W[ids[p]])^T,
+//   a_row(p) = a + (p/top_k)*outer + (p%top_k)*inner,
+// optionally fused as SiLU(gate) * up.
+//
+// Two launches, no host synchronisation (the page's point about removing the
+// device-to-host read of tokens-per-expert before the GEMM):
+//  1. routing: one block counts pairs per expert (LDS atomics), scans the
+//     counts, writes a tile list (each tile: up to MT pairs of one expert) and
+//     scatters the pair indices into expert order, all in the workspace;
+//  2. compute: the streaming GEMV of gemv_core.hpp over the tile list; blocks
+//     past the device-written tile count exit at once. Each tile streams its
+//     expert's weights once, so an expert's weights are read once per launch
+//     when its pairs fit one tile.
+// Each pair's accumulation order does not depend on its slot in a tile, so the
+// (unordered) scatter cannot change any output value.
+#include "gemv_core.hpp"
+#include "launch.hpp"
+
+namespace qp {
+
+namespace {
+
+constexpr int ROUTE_THREADS = 1024;
+constexpr int kMaxExperts = 4096;
+
+struct WsLayout {
+    size_t hdr, perm, tiles, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int64_t P, int64_t E)
+{
+    WsLayout l{};
+    l.hdr = 0;
+    l.perm = align256(16);
+    l.tiles = l.perm + align256((size_t)(P > 0 ? P : 1) * 4);
+    l.total = l.tiles + align256((size_t)(P + E + 1) * sizeof(TileDesc));
+    return l;
+}
+
+} // namespace
+
+// Exclusive scan of one value per thread over a block of ROUTE_THREADS.
+__device__ int block_exclusive_scan(int v, int* s_tmp, int* total)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off, 64);
+        if (lane >= off)
+            incl += t;
+    }
+    if (lane == 63)
+        s_tmp[wave] = incl;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int w = 0; w < ROUTE_THREADS / 64; ++w) {
+            const int t = s_tmp[w];
+            s_tmp[w] = run;
+            run += t;
+        }
+        s_tmp[ROUTE_THREADS / 64] = run;
+    }
+    __syncthreads();
+    const int excl = incl - v + s_tmp[wave];
+    *total = s_tmp[ROUTE_THREADS / 64];
+    __syncthreads();
+    return excl;
+}
+
+// hdr[0] = number of tiles, hdr[1] = number of pairs with an invalid id.
+__global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int MT, int32_t* __restrict__ hdr,
+    int32_t* __restrict__ perm, TileDesc* __restrict__ tiles)
+{
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int s_cur[kMaxExperts];
+    __shared__ int s_tmp[ROUTE_THREADS / 64 + 1];
+    __shared__ int s_invalid;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += ROUTE_THREADS)
+        s_cnt[e] = 0;
+    if (tid == 0)
+        s_invalid = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += ROUTE_THREADS) {
+        const int e = ids[p];
+        if (e >= 0 && e < E)
+            atomicAdd(&s_cnt[e], 1);
+        else
+            atomicAdd(&s_invalid, 1);
+    }
+    __syncthreads();
+
+    // Each thread owns a contiguous run of experts; scan pair and tile counts.
+    const int ept = (E + ROUTE_THREADS - 1) / ROUTE_THREADS;
+    const int e0 = tid * ept;
+    int my_pairs = 0, my_tiles = 0;
+    for (int e = e0; e < e0 + ept && e < E; ++e) {
+        my_pairs += s_cnt[e];
+        my_tiles += (s_cnt[e] + MT - 1) / MT;
+    }
+    int tot_pairs, tot_tiles;
+    int pair_off = block_exclusive_scan(my_pairs, s_tmp, &tot_pairs);
+    int tile_off = block_exclusive_scan(my_tiles, s_tmp, &tot_tiles);
+    for (int e = e0; e < e0 + ept && e < E; ++e) {
+        const int c = s_cnt[e];
+        for (int j = 0; j * MT < c; ++j) {
+            TileDesc d;
+            d.expert = e;
+            d.start = pair_off + j * MT;
+            d.count = (c - j * MT) < MT ? (c - j * MT) : MT;
+            tiles[tile_off++] = d;
+        }
+        s_cur[e] = pair_off;
+        pair_off += c;
+    }
+    if (tid == 0) {
+        hdr[0] = tot_tiles;
+        hdr[1] = s_invalid;
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += ROUTE_THREADS) {
+        const int e = ids[p];
+        if (e >= 0 && e < E)
+            perm[atomicAdd(&s_cur[e], 1)] = p;
+    }
+}
+
+size_t moe_workspace_bytes(int64_t n_pairs, int64_t num_experts)
+{
+    return ws_layout(n_pairs, num_experts).total;
+}
+
+namespace {
+
+int pick_mt(int64_t P, int64_t E, int mtmax)
+{
+    int mt = 1;
+    while (mt < mtmax && (int64_t)mt * E < P)
+        mt <<= 1;
+    return mt;
+}
+
+} // namespace
+
+int moe_tile_height(int64_t n_pairs, int64_t num_experts, int bits, int dt)
+{
+    // The register-resident kernel holds up to 8 activation rows with the dot2
+    // path, 2 with the fp32 path (fp32 activations, 8-bit codes with bf16).
+    const bool dot2 = dt != DT_F32 && !(bits == 8 && dt == DT_BF16);
+    return pick_mt(n_pairs, num_experts, dot2 ? 8 : 2);
+}
+
+hipError_t launch_moe_route(const MoeArgs& a, int mt, MoeRouting* r, hipStream_t st)
+{
+    const int64_t P = a.n_tokens * a.top_k;
+    WsLayout l = ws_layout(P, a.E);
+    char* ws = static_cast<char*>(a.workspace);
+    int32_t* hdr = reinterpret_cast<int32_t*>(ws + l.hdr);
+    int32_t* perm = reinterpret_cast<int32_t*>(ws + l.perm);
+    TileDesc* tiles = reinterpret_cast<TileDesc*>(ws + l.tiles);
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, st, a.ids, (int)P,
+                       (int)a.E, mt, hdr, perm, tiles);
+    r->n_tiles = hdr;
+    r->perm = perm;
+    r->tiles = tiles;
+    r->mt = mt;
+    // Each tile holds >= 1 pair and each expert leaves at most one partial tile.
+    int64_t max_tiles = (P + mt - 1) / mt + a.E;
+    r->max_tiles = max_tiles < P ? max_tiles : P;
+    return hipGetLastError();
+}
+
+hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
+{
+    MoeRouting r{};
+    const int64_t P = a.n_tokens * a.top_k;
+    hipError_t e = launch_moe_route(a, moe_tile_height(P, a.E, a.bits, a.dt), &r, st);
+    if (e != hipSuccess)
+        return e;
+    const bool f = a.fused_silu;
+    switch (a.bits) {
+    case 2: return f ? launch_moe_b2_n2(a, r, st) : launch_moe_b2_n1(a, r, st);
+    case 3: return f ? launch_moe_b3_n2(a, r, st) : launch_moe_b3_n1(a, r, st);
+    case 4: return f ? launch_moe_b4_n2(a, r, st) : launch_moe_b4_n1(a, r, st);
+    case 6: return f ? launch_moe_b6_n2(a, r, st) : launch_moe_b6_n1(a, r, st);
+    case 8: return f ? launch_moe_b8_n2(a, r, st) : launch_moe_b8_n1(a, r, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+} // namespace qp

@@ -1,0 +1,125 @@
+// moe_compute.hip — the compute launch of the MoE path over the device-written
+// tile list (see moe.hip for the routing). Compiled once per bit width
+// (QP_BITS) and per form (QP_NMAT: 1 = plain product, 2 = fused
+// SiLU(gate) * up), so the kernel instantiations spread over parallel
+// translation units.
+#include "gemv_core.hpp"
+#include "launch.hpp"
+
+#if !defined(QP_BITS) || !defined(QP_NMAT)
+#error "moe_compute.hip needs QP_BITS and QP_NMAT"
+#endif
+
+namespace qp {
+
+namespace {
+
+template <int BITS, int DT, int MT, int U, int NMAT>
+hipError_t run_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
+{
+    const int RP = GEMV_THREADS / k.KL;
+    const int64_t passes = (k.R + RP - 1) / RP;
+    int64_t gy = max_tiles < 65535 ? max_tiles : 65535;
+    if (gy < 1)
+        gy = 1;
+    int64_t gx = 4096 / gy;
+    gx = gx < 1 ? 1 : gx;
+    gx = gx < passes ? gx : passes;
+    hipLaunchKernelGGL((qgemv_stream_kernel<BITS, DT, MT, U, NMAT>), dim3((int)gx, (int)gy),
+                       dim3(GEMV_THREADS), 0, st, k);
+    return hipGetLastError();
+}
+
+template <int BITS, int DT, int NMAT>
+hipError_t run_generic(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
+{
+    int64_t gy = max_tiles < 65535 ? max_tiles : 65535;
+    if (gy < 1)
+        gy = 1;
+    int64_t gx = (k.R + 3) / 4;
+    int64_t cap = 4096 / gy;
+    cap = cap < 1 ? 1 : cap;
+    gx = gx < cap ? gx : cap;
+    k.KL = 64;
+    hipLaunchKernelGGL((qgemv_generic_kernel<BITS, DT, NMAT>), dim3((int)gx, (int)gy), dim3(256),
+                       0, st, k);
+    return hipGetLastError();
+}
+
+template <int BITS, int DT, int MT, int NMAT>
+hipError_t run_mt(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
+{
+    // At most one wave per row; the widest slice that splits K evenly.
+    if constexpr (MT <= 2) {
+        if (int kl = gemv_lanes_per_row(k.K, 2); kl && kl <= 64) {
+            k.KL = kl;
+            return run_tiles<BITS, DT, MT, 2, NMAT>(k, max_tiles, st);
+        }
+    }
+    if (int kl = gemv_lanes_per_row(k.K, 1); kl && kl <= 64) {
+        k.KL = kl;
+        return run_tiles<BITS, DT, MT, 1, NMAT>(k, max_tiles, st);
+    }
+    if constexpr (MT <= 2) {
+        if (int kl = gemv_lanes_per_row(k.K, 3); kl && kl <= 64) {
+            k.KL = kl;
+            return run_tiles<BITS, DT, MT, 3, NMAT>(k, max_tiles, st);
+        }
+    }
+    return run_generic<BITS, DT, NMAT>(k, max_tiles, st);
+}
+
+template <int BITS, int DT, int NMAT>
+hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
+{
+    GemvKernelArgs k{};
+    k.x = a.a;
+    k.top_k = a.top_k;
+    k.outer = a.a_outer;
+    k.inner = a.a_inner;
+    k.perm = r.perm;
+    k.tiles = static_cast<const TileDesc*>(r.tiles);
+    k.n_tiles = r.n_tiles;
+    k.M = 0;
+    for (int t = 0; t < 2; ++t) {
+        const int src = NMAT == 2 ? t : 0;
+        k.wq[t] = a.wq[src];
+        k.scales[t] = a.scales[src];
+        k.biases[t] = a.biases[src];
+    }
+    k.R = a.n_rows;
+    k.K = a.n_cols;
+    k.gs = a.gs;
+    k.out = a.out;
+    if constexpr (DT == DT_F32) {
+        return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
+    } else {
+        constexpr int MTMAX = gemv_max_mt<BITS, DT>();
+        switch (r.mt) {
+        case 1: return run_mt<BITS, DT, 1, NMAT>(k, r.max_tiles, st);
+        case 2: return run_mt<BITS, DT, 2, NMAT>(k, r.max_tiles, st);
+        }
+        if constexpr (MTMAX >= 8) {
+            if (r.mt == 4)
+                return run_mt<BITS, DT, 4, NMAT>(k, r.max_tiles, st);
+            return run_mt<BITS, DT, 8, NMAT>(k, r.max_tiles, st);
+        }
+        return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
+    }
+}
+
+} // namespace
+
+hipError_t QP_CAT(QP_CAT(QP_CAT(launch_moe_b, QP_BITS), _n), QP_NMAT)(const MoeArgs& a,
+                                                                       const MoeRouting& r,
+                                                                       hipStream_t st)
+{
+    switch (a.dt) {
+    case DT_F32: return run_moe<QP_BITS, DT_F32, QP_NMAT>(a, r, st);
+    case DT_F16: return run_moe<QP_BITS, DT_F16, QP_NMAT>(a, r, st);
+    case DT_BF16: return run_moe<QP_BITS, DT_BF16, QP_NMAT>(a, r, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+} // namespace qp
