@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace qp {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -48,6 +50,61 @@ template <> struct Elem<DT_BF16> {
     }
 };
 
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so the body sees
+// I as a compile-time constant (table lookups fold, register arrays are
+// indexed statically).
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>)
+{
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// One DPP-moved copy of v (gfx9 data-parallel primitives); lanes whose row is
+// masked off, or whose source is out of range, read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, ROW_MASK, 0xF, true));
+}
+
+// Sum over aligned segments of `seg` lanes (1, 2, 4, ..., 64) with DPP adds.
+// The total is valid in every lane of the segment for seg <= 16, and in the
+// segment's last lane for seg = 32 or 64 (see segment_writer).
+__device__ __forceinline__ float segment_reduce(float v, int seg)
+{
+    if (seg >= 2) v += dpp_f32<0xB1>(v);         // quad_perm [1,0,3,2]: lane ^ 1
+    if (seg >= 4) v += dpp_f32<0x4E>(v);         // quad_perm [2,3,0,1]: lane ^ 2
+    if (seg >= 8) v += dpp_f32<0x141>(v);        // row_half_mirror: i <-> 7 - i
+    if (seg >= 16) v += dpp_f32<0x140>(v);       // row_mirror: i <-> 15 - i
+    if (seg >= 32) v += dpp_f32<0x142, 0xA>(v);  // row_bcast15 into rows 1, 3
+    if (seg >= 64) v += dpp_f32<0x143, 0xC>(v);  // row_bcast31 into rows 2, 3
+    return v;
+}
+__device__ __forceinline__ bool segment_writer(int lane_in_seg, int seg)
+{
+    return seg <= 16 ? lane_in_seg == 0 : lane_in_seg == seg - 1;
+}
+
+// segment_reduce for N independent values at once and a compile-time segment
+// width: the steps are interleaved across the values, so consecutive DPP reads
+// never depend on the instruction just before them.
+template <int N, int SEG>
+__device__ __forceinline__ void reduce_slots(float* v)
+{
+    if constexpr (SEG >= 2) { for (int i = 0; i < N; ++i) v[i] += dpp_f32<0xB1>(v[i]); }
+    if constexpr (SEG >= 4) { for (int i = 0; i < N; ++i) v[i] += dpp_f32<0x4E>(v[i]); }
+    if constexpr (SEG >= 8) { for (int i = 0; i < N; ++i) v[i] += dpp_f32<0x141>(v[i]); }
+    if constexpr (SEG >= 16) { for (int i = 0; i < N; ++i) v[i] += dpp_f32<0x140>(v[i]); }
+    if constexpr (SEG >= 32) { for (int i = 0; i < N; ++i) v[i] += dpp_f32<0x142, 0xA>(v[i]); }
+    if constexpr (SEG >= 64) { for (int i = 0; i < N; ++i) v[i] += dpp_f32<0x143, 0xC>(v[i]); }
+}
+
 // Sum over aligned segments of SEG lanes (SEG a power of two <= 64); every
 // lane of a segment ends with the segment's total.
 template <int SEG>
@@ -83,15 +140,16 @@ __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint3
     }
 }
 
-// Code `c` (0..31) of a 32-code unit held in BITS consecutive words.
-template <int BITS>
-__device__ __forceinline__ uint32_t unit_code(const uint32_t* w, int c)
+// Code C (0..31) of a 32-code unit held in BITS consecutive words.
+template <int BITS, int C>
+__device__ __forceinline__ uint32_t unit_code(const uint32_t* w)
 {
-    const int bit = c * BITS, wi = bit / 32, sh = bit % 32;
-    const uint32_t mask = (1u << BITS) - 1u;
-    if (sh + BITS <= 32)
+    constexpr int bit = C * BITS, wi = bit / 32, sh = bit % 32;
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+    if constexpr (sh + BITS <= 32)
         return (w[wi] >> sh) & mask;
-    return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & mask;
+    else
+        return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & mask;
 }
 
 } // namespace qp

@@ -35,6 +35,18 @@
 
 namespace qp {
 
+// (a & mask) | magic as one v_and_or_b32. Written out because a VOP3
+// instruction on gfx9 cannot take a literal and reads at most one SGPR, so the
+// compiler would otherwise split it into a v_and and a v_or with literals; the
+// mask is kept in a VGPR (materialised once, outside the loops) and the magic
+// constant comes from an SGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask), "s"(magic));
+    return r;
+}
+
 template <int DT> struct Dot2Traits;
 template <> struct Dot2Traits<DT_BF16> {
     static constexpr int MANT = 7;
@@ -79,11 +91,13 @@ constexpr bool use_dot2()
         return make_unpack_plan(BITS, Dot2Traits<DT>::MANT).feasible;
 }
 
-// Largest tile height (activation rows per launch) the register budget allows.
+// Largest tile height (activation rows per launch) the register budget allows:
+// activations take MT * 32 * U / 2 VGPRs on the dot2 path (bf16/fp16 pairs),
+// MT * 32 * U on the fp32 path, for U <= 2 units of 32 codes per lane.
 template <int BITS, int DT>
 constexpr int gemv_max_mt()
 {
-    return use_dot2<BITS, DT>() ? 8 : 2;
+    return use_dot2<BITS, DT>() ? 4 : 2;
 }
 
 constexpr int GEMV_THREADS = 256;
@@ -91,7 +105,7 @@ constexpr int GEMV_THREADS = 256;
 template <int BITS, int DT, bool DOT2> struct UnitX;
 
 // Activations of one 32-code unit for the dot2 path: pre-scaled pairs, the
-// magic-offset sum and the plain sum.
+// negated magic-offset sum and the plain sum.
 template <int BITS, int DT> struct UnitX<BITS, DT, true> {
     using T = Dot2Traits<DT>;
     static constexpr UnpackPlan P = make_unpack_plan(BITS, T::MANT);
@@ -106,48 +120,48 @@ template <int BITS, int DT> struct UnitX<BITS, DT, true> {
             s += xv[c];
         xsum = s;
         float off = 0.f;
-#pragma unroll
-        for (int j = 0; j < P.n_pair; ++j) {
-            const PlanPair pp = P.pair[j];
-            float lo = pp.lo >= 0 ? xv[pp.lo] * (1.0f / float(1 << pp.lo_off)) : 0.f;
-            float hi = pp.hi >= 0 ? xv[pp.hi] * (1.0f / float(1 << pp.hi_off)) : 0.f;
-            xp[j] = T::make(lo, hi);
-            off += T::lo_f(xp[j]) + T::hi_f(xp[j]);
-        }
-        xoff = off * T::MAGIC;
+        static_for<P.n_pair>([&](auto J) {
+            constexpr PlanPair pp = P.pair[J];
+            constexpr float lo_scale = 1.0f / float(1 << pp.lo_off);
+            constexpr float hi_scale = 1.0f / float(1 << pp.hi_off);
+            const float lo = pp.lo >= 0 ? xv[pp.lo >= 0 ? pp.lo : 0] * lo_scale : 0.f;
+            const float hi = pp.hi >= 0 ? xv[pp.hi >= 0 ? pp.hi : 0] * hi_scale : 0.f;
+            xp[J] = T::make(lo, hi);
+            off += T::lo_f(xp[J]) + T::hi_f(xp[J]);
+        });
+        xoff = -(off * T::MAGIC);
     }
 
-    // Sum over the unit's 32 codes of q * x.
-    __device__ __forceinline__ float qdot(const uint32_t* w) const
+    // acc + (sum over the unit's 32 codes of (magic + q * 2^o) * x * 2^-o); the
+    // caller starts the chain at -(magic offset sums) of the units it covers.
+    __device__ __forceinline__ float qdot(const uint32_t* w, float acc) const
     {
         uint32_t win[P.n_win];
-#pragma unroll
-        for (int i = 0; i < P.n_win; ++i) {
-            const int wb = P.win_bit[i], wi = wb / 32, sh = wb % 32;
-            if (sh == 0)
-                win[i] = w[wi];
-            else if (wi + 1 < BITS)
-                win[i] = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh);
+        static_for<P.n_win>([&](auto I) {
+            constexpr int wb = P.win_bit[I], wi = wb / 32, sh = wb % 32;
+            if constexpr (sh == 0)
+                win[I] = w[wi];
+            else if constexpr (wi + 1 < BITS)
+                win[I] = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh);
             else
-                win[i] = w[wi] >> sh;
-        }
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < P.n_pair; ++j) {
-            const PlanPair pp = P.pair[j];
+                win[I] = w[wi] >> sh;
+        });
+        static_for<P.n_pair>([&](auto J) {
+            constexpr PlanPair pp = P.pair[J];
             constexpr uint32_t cm = (1u << BITS) - 1u;
-            const uint32_t mask = (pp.lo >= 0 ? cm << pp.lo_off : 0u) |
-                                  (pp.hi >= 0 ? cm << (16 + pp.hi_off) : 0u);
-            const uint32_t v = (win[pp.win] & mask) | T::MAGIC2;
-            acc = T::dot(v, xp[j], acc);
-        }
-        return acc - xoff;
+            constexpr uint32_t mask = (pp.lo >= 0 ? cm << pp.lo_off : 0u) |
+                                      (pp.hi >= 0 ? cm << (16 + pp.hi_off) : 0u);
+            const uint32_t v = and_or(win[pp.win], mask, T::MAGIC2);
+            acc = T::dot(v, xp[J], acc);
+        });
+        return acc;
     }
 };
 
 // fp32 path: activations as fp32, one conversion and one FMA per code.
 template <int BITS, int DT> struct UnitX<BITS, DT, false> {
     float xf[32];
+    float xoff = 0.f; // no magic offset on this path
     float xsum;
 
     __device__ __forceinline__ void load(const float (&xv)[32])
@@ -161,12 +175,12 @@ template <int BITS, int DT> struct UnitX<BITS, DT, false> {
         xsum = s;
     }
 
-    __device__ __forceinline__ float qdot(const uint32_t* w) const
+    // acc + sum over the unit's 32 codes of q * x.
+    __device__ __forceinline__ float qdot(const uint32_t* w, float acc) const
     {
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < 32; ++c)
-            acc = __builtin_fmaf((float)unit_code<BITS>(w, c), xf[c], acc);
+        static_for<32>([&](auto C) {
+            acc = __builtin_fmaf((float)unit_code<BITS, C>(w), xf[C], acc);
+        });
         return acc;
     }
 };
@@ -194,6 +208,7 @@ struct GemvKernelArgs {
     int gs;
     int KL;                  // lanes per row
     void* out;               // [pairs, R]
+    uint32_t out_bytes;      // size of `out` in bytes (< 2^31)
 };
 
 __device__ __forceinline__ float silu_f32(float z)
@@ -201,199 +216,327 @@ __device__ __forceinline__ float silu_f32(float z)
     return z / (1.0f + expf(-z));
 }
 
-template <int BITS, int DT, int MT, int U, int NMAT>
-__global__ __launch_bounds__(GEMV_THREADS) void qgemv_stream_kernel(GemvKernelArgs a)
+// Buffer resource over `bytes` bytes at `p` (raw, untyped). Loads past the end
+// return zeros and stores past the end are dropped, which is what lets the
+// kernels below run without bounds branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Byte offset that is always past the end of a resource (its stores drop).
+constexpr uint32_t OOB = 0x80000000u;
+
+template <int NW>
+__device__ __forceinline__ void buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                             uint32_t (&w)[NW])
+{
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW; i += 4) {
+            const u32x4_t v = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0));
+            w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+        }
+    } else if constexpr (NW % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW; i += 2) {
+            const u32x2_t v = __builtin_bit_cast(
+                u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * i, 0, 0));
+            w[i] = v.x; w[i + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, 0);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ typename Elem<DT>::storage buffer_elem(__amdgpu_buffer_rsrc_t r,
+                                                                  uint32_t off)
+{
+    if constexpr (DT == DT_F32)
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    else
+        return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ void buffer_store_elem(typename Elem<DT>::storage v,
+                                                  __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    if constexpr (DT == DT_F32)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+
+// Activation words per unit in the block's table: dot2 pairs, or fp32 values.
+template <int BITS, int DT>
+constexpr int unit_table_words()
+{
+    if constexpr (use_dot2<BITS, DT>())
+        return make_unpack_plan(BITS, Dot2Traits<DT>::MANT).n_pair;
+    else
+        return 32;
+}
+
+// Ring depth that fits the register budget of a kernel instance: activation
+// registers (pairs or fp32 values per unit, two sums per group) plus D ring
+// slots of weight words and scale/bias values, plus about 40 for addressing
+// and accumulators.
+template <int BITS, int DT, int MT, int U, int G, int NMAT, int BUDGET>
+constexpr int ring_depth()
+{
+    constexpr bool dot2 = use_dot2<BITS, DT>();
+    int per_unit = 40; // 32 fp32 values and conversion temporaries
+    if constexpr (dot2)
+        per_unit = make_unpack_plan(BITS, Dot2Traits<DT>::MANT).n_pair;
+    const int xr = MT * U * per_unit + MT * G * 2;
+    const int slot = NMAT * (U * BITS + 2 * G);
+    for (int d = 4; d > 1; --d)
+        if (xr + d * slot + 56 + 8 * MT <= BUDGET)
+            return d;
+    return 1;
+}
+
+// One wave streams whole rows: a row is spread over KL lanes (KL a power of
+// two <= 64), so a wave covers RPW = 64 / KL rows per pass. Waves take passes
+// p = gw, gw + GW, ... (gw = global wave id, GW = waves along the grid's x).
+// Each lane owns U units of 32 codes; they fall into G groups (G = 1 when the
+// whole slice lies in one quantization group, else G = U).
+//
+//  1. The block prepares the tile's activation table (dot2 pairs, magic-offset
+//     and plain sums for every lane slot and activation row) in LDS, each
+//     thread one (row, unit, lane slot) item, so the conversion work is done
+//     once per block rather than once per wave.
+//  2. Every wave keeps D passes of weight words in flight (a ring refilled as
+//     it is consumed). The activation loads are issued first and the ring
+//     right after, so waiting for the activations never waits for weights.
+//  3. All loads and stores are raw buffer accesses: rows past the end read
+//     zeros and their stores are dropped, so the loop has no bounds branches
+//     and the compiler's memory-counter waits cover exactly one ring slot.
+//  4. The D slots' partial sums are reduced together (interleaved DPP steps)
+//     and stored at the end of each ring cycle.
+template <int BITS, int DT, int MT, int U, int G, int KL, int NMAT, int MAXT>
+__global__ __launch_bounds__(MAXT) void qgemv_stream_kernel(GemvKernelArgs a)
 {
     using E = Elem<DT>;
     using St = typename E::storage;
     constexpr bool DOT2 = use_dot2<BITS, DT>();
+    using UX = UnitX<BITS, DT, DOT2>;
+    static_assert(G == 1 || G == U, "a lane slice is one group or one group per unit");
+    constexpr int UPG = U / G;                              // units per group
+    constexpr int D = ring_depth<BITS, DT, MT, U, G, NMAT, (131072 / MAXT < 512 ? 131072 / MAXT : 512)>();
     constexpr int NW = U * BITS;
-    __shared__ float red[GEMV_THREADS / 64][NMAT][MT];
+    constexpr int RPW = 64 / KL;
+    constexpr int NP = unit_table_words<BITS, DT>();        // table words per unit
+    constexpr int UWORDS = NP + 2;                          // + offset sum, plain sum
+    constexpr int ITEMS = MT * U * KL;                      // table items per tile
+    constexpr int XV = 32 * (int)sizeof(St) / 16;           // 16-byte vectors per unit
+    constexpr int SB = (int)sizeof(St);
+    __shared__ uint32_t table[MT * U * UWORDS * KL];       // [m][u][word][kl]
 
-    // Tiles: blocks stride over them along y (block-uniform bounds, so every
-    // barrier below is reached by the whole block).
+    const int lane = threadIdx.x & 63;
+    const int kl = lane & (KL - 1);
+    const int sub = lane / KL;
+    const uint32_t row_bytes = (uint32_t)(a.K * BITS / 8);
+    const uint32_t groups_row = (uint32_t)(a.K / a.gs);
+    const int R = (int)a.R;
+    const int nthreads = (int)blockDim.x; // a multiple of 64, >= 256, <= MAXT
+    const int gw = (int)blockIdx.x * (nthreads / 64) + (int)(threadIdx.x / 64);
+    const int GW = (int)gridDim.x * (nthreads / 64);
+    const int passes = (R + RPW - 1) / RPW;
+    uint32_t sboff[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        sboff[g] = (uint32_t)(((kl * U + g * UPG) * 32) / a.gs) * SB;
+    const St* xs = static_cast<const St*>(a.x);
+
     const int ntiles = a.tiles != nullptr ? *a.n_tiles : 1;
     for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
-    int expert = 0, start = 0, count = a.M;
-    if (a.tiles != nullptr) {
-        const TileDesc d = a.tiles[tile];
-        expert = d.expert;
-        start = d.start;
-        count = d.count;
-    }
-
-    const int KL = a.KL;
-    const int tid = threadIdx.x;
-    const int kl = tid & (KL - 1);
-    const int slot = tid / KL;
-    const int RP = GEMV_THREADS / KL;
-    const int64_t K = a.K, R = a.R;
-    const int64_t words_row = K * BITS / 32;
-    const int64_t groups_row = K / a.gs;
-
-    int64_t pair[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        int64_t p = -1;
-        if (m < count)
-            p = a.perm != nullptr ? (int64_t)a.perm[start + m] : (int64_t)(start + m);
-        pair[m] = p;
-    }
-
-    // Prologue: this lane's activations for every row of the tile.
-    UnitX<BITS, DT, DOT2> ux[MT][U];
-    const St* xs = static_cast<const St*>(a.x);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const St* xrow = nullptr;
-        if (pair[m] >= 0)
-            xrow = xs + (pair[m] / a.top_k) * a.outer + (pair[m] % a.top_k) * a.inner;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float xv[32];
-            const int64_t k0 = ((int64_t)kl * U + u) * 32;
-#pragma unroll
-            for (int c = 0; c < 32; ++c)
-                xv[c] = xrow != nullptr ? E::to_f32(xrow[k0 + c]) : 0.f;
-            ux[m][u].load(xv);
+        int expert = 0, start = 0, count = a.M;
+        if (a.tiles != nullptr) {
+            const TileDesc d = a.tiles[tile];
+            expert = d.expert;
+            start = d.start;
+            count = d.count;
         }
-    }
-    int64_t gidx[U];
+        int64_t pair[MT];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-        gidx[u] = (((int64_t)kl * U + u) * 32) / a.gs;
-
-    const uint32_t* wbase[NMAT];
-    const St* sbase[NMAT];
-    const St* bbase[NMAT];
-#pragma unroll
-    for (int t = 0; t < NMAT; ++t) {
-        wbase[t] = a.wq[t] + (int64_t)expert * R * words_row + (int64_t)kl * NW;
-        sbase[t] = static_cast<const St*>(a.scales[t]) + (int64_t)expert * R * groups_row;
-        bbase[t] = static_cast<const St*>(a.biases[t]) + (int64_t)expert * R * groups_row;
-    }
-
-    const int64_t stride_rows = (int64_t)gridDim.x * RP;
-    int64_t row = (int64_t)blockIdx.x * RP + slot;
-
-    uint32_t w[NMAT][NW];
-    St sv[NMAT][U], bv[NMAT][U];
-    auto fetch = [&](int64_t r, uint32_t (&dw)[NMAT][NW], St (&ds)[NMAT][U], St (&db)[NMAT][U]) {
-#pragma unroll
-        for (int t = 0; t < NMAT; ++t) {
-            load_words<NW>(wbase[t] + r * words_row, dw[t]);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                ds[t][u] = sbase[t][r * groups_row + gidx[u]];
-                db[t][u] = bbase[t][r * groups_row + gidx[u]];
-            }
+        for (int m = 0; m < MT; ++m) {
+            int64_t p = -1;
+            if (m < count)
+                p = a.perm != nullptr ? (int64_t)a.perm[start + m] : (int64_t)(start + m);
+            pair[m] = p;
         }
-    };
-    if (row < R)
-        fetch(row, w, sv, bv);
 
-    St* outs = static_cast<St*>(a.out);
-    for (int64_t base = (int64_t)blockIdx.x * RP; base < R; base += stride_rows) {
-        const int64_t nrow = row + stride_rows;
-        uint32_t wn[NMAT][NW];
-        St svn[NMAT][U], bvn[NMAT][U];
-        if (nrow < R)
-            fetch(nrow, wn, svn, bvn);
-
-        float acc[NMAT][MT];
+        // 1a. Activation loads for this thread's table items (clamped so every
+        //     thread issues the same loads; only in-range items are stored).
+        constexpr int IPT = (ITEMS + 255) / 256;
+        u32x4_t xraw[IPT][XV];
+        bool it_live[IPT];
 #pragma unroll
-        for (int t = 0; t < NMAT; ++t)
+        for (int i = 0; i < IPT; ++i) {
+            int item = (int)threadIdx.x + i * nthreads;
+            item = item < ITEMS ? item : ITEMS - 1;
+            const int it_kl = item % KL, it_u = (item / KL) % U, it_m = item / (KL * U);
+            int64_t it_pair = pair[0];
+            bool live = false;
 #pragma unroll
             for (int m = 0; m < MT; ++m)
-                acc[t][m] = 0.f;
-        if (row < R) {
-#pragma unroll
-            for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const float s = E::to_f32(sv[t][u]), b = E::to_f32(bv[t][u]);
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        const float qx = ux[m][u].qdot(w[t] + u * BITS);
-                        acc[t][m] =
-                            __builtin_fmaf(s, qx, __builtin_fmaf(b, ux[m][u].xsum, acc[t][m]));
-                    }
+                if (m == it_m && pair[m] >= 0) {
+                    it_pair = pair[m];
+                    live = true;
                 }
+            it_live[i] = live;
+            const St* xrow = xs + (it_pair / a.top_k) * a.outer + (it_pair % a.top_k) * a.inner;
+            const u32x4_t* p =
+                reinterpret_cast<const u32x4_t*>(xrow + (int64_t)(it_kl * U + it_u) * 32);
+#pragma unroll
+            for (int v = 0; v < XV; ++v)
+                xraw[i][v] = p[v];
         }
-        // Reduce over the KL lanes of the row.
-        bool have = false;
-        if (KL <= 64) {
-#pragma unroll
-            for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    for (int off = 1; off < KL; off <<= 1)
-                        acc[t][m] += __shfl_xor(acc[t][m], off, 64);
-            have = kl == 0 && row < R;
-        } else {
-#pragma unroll
-            for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    acc[t][m] = segment_sum<64>(acc[t][m]);
-            const int wave = tid / 64;
-            if ((tid & 63) == 0)
-#pragma unroll
-                for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-                    for (int m = 0; m < MT; ++m)
-                        red[wave][t][m] = acc[t][m];
-            __syncthreads();
-            if (kl == 0) {
-                const int wpr = KL / 64;
-#pragma unroll
-                for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        float s = 0.f;
-                        for (int i = 0; i < wpr; ++i)
-                            s += red[wave + i][t][m];
-                        acc[t][m] = s;
-                    }
-            }
-            __syncthreads();
-            have = kl == 0 && row < R;
-        }
-        if (have) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                if (pair[m] >= 0) {
-                    float v = acc[0][m];
-                    if constexpr (NMAT == 2)
-                        v = silu_f32(acc[0][m]) * acc[1][m];
-                    outs[pair[m] * R + row] = E::from_f32(v);
-                }
-            }
-        }
-        row = nrow;
+
+        // 2. The weight ring.
+        __amdgpu_buffer_rsrc_t rw[NMAT], rs[NMAT], rb[NMAT];
 #pragma unroll
         for (int t = 0; t < NMAT; ++t) {
+            const uint64_t erow = (uint64_t)expert * (uint64_t)R;
+            rw[t] = make_rsrc(reinterpret_cast<const char*>(a.wq[t]) + erow * row_bytes,
+                              (uint32_t)R * row_bytes);
+            rs[t] = make_rsrc(static_cast<const char*>(a.scales[t]) + erow * groups_row * SB,
+                              (uint32_t)R * groups_row * SB);
+            rb[t] = make_rsrc(static_cast<const char*>(a.biases[t]) + erow * groups_row * SB,
+                              (uint32_t)R * groups_row * SB);
+        }
+        const uint32_t lane_off = (uint32_t)(kl * NW * 4);
+        uint32_t w[D][NMAT][NW];
+        St sv[D][NMAT][G], bv[D][NMAT][G];
+        auto fetch = [&](int p, uint32_t (&dw)[NMAT][NW], St (&ds)[NMAT][G],
+                         St (&db)[NMAT][G]) {
+            const uint32_t r = (uint32_t)(p * RPW + sub);
 #pragma unroll
-            for (int i = 0; i < NW; ++i)
-                w[t][i] = wn[t][i];
+            for (int t = 0; t < NMAT; ++t) {
+                buffer_words<NW>(rw[t], r * row_bytes + lane_off, dw[t]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                sv[t][u] = svn[t][u];
-                bv[t][u] = bvn[t][u];
+                for (int g = 0; g < G; ++g) {
+                    ds[t][g] = buffer_elem<DT>(rs[t], r * groups_row * SB + sboff[g]);
+                    db[t][g] = buffer_elem<DT>(rb[t], r * groups_row * SB + sboff[g]);
+                }
+            }
+        };
+        static_for<D>([&](auto J) { fetch(gw + J * GW, w[J], sv[J], bv[J]); });
+
+        // 1b. Build the table items and share them through LDS.
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            const int item = (int)threadIdx.x + i * nthreads;
+            const int it_kl = item % KL, it_u = (item / KL) % U, it_m = item / (KL * U);
+            float xv[32];
+            const St* e = reinterpret_cast<const St*>(&xraw[i][0]);
+            const bool live = it_live[i];
+            static_for<32>([&](auto C) { xv[C] = live ? E::to_f32(e[C]) : 0.f; });
+            UX ux;
+            ux.load(xv);
+            if (item < ITEMS) {
+                uint32_t* dst = table + ((it_m * U + it_u) * UWORDS) * KL + it_kl;
+                if constexpr (DOT2) {
+                    static_for<NP>([&](auto J) {
+                        dst[J * KL] = __builtin_bit_cast(uint32_t, ux.xp[J]);
+                    });
+                } else {
+                    static_for<32>([&](auto C) {
+                        dst[C * KL] = __builtin_bit_cast(uint32_t, ux.xf[C]);
+                    });
+                }
+                dst[NP * KL] = __builtin_bit_cast(uint32_t, ux.xoff);
+                dst[(NP + 1) * KL] = __builtin_bit_cast(uint32_t, ux.xsum);
             }
         }
-    }
+        __syncthreads();
+        UX ux[MT][U];
+        float goff[MT][G], gsum[MT][G];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                goff[m][g] = gsum[m][g] = 0.f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t* src = table + ((m * U + u) * UWORDS) * KL + kl;
+                if constexpr (DOT2) {
+                    static_for<NP>([&](auto J) {
+                        ux[m][u].xp[J] =
+                            __builtin_bit_cast(typename UX::T::pair_t, src[J * KL]);
+                    });
+                } else {
+                    static_for<32>([&](auto C) {
+                        ux[m][u].xf[C] = __builtin_bit_cast(float, src[C * KL]);
+                    });
+                }
+                goff[m][u / UPG] += __builtin_bit_cast(float, src[NP * KL]);
+                gsum[m][u / UPG] += __builtin_bit_cast(float, src[(NP + 1) * KL]);
+            }
+        }
+
+        // Output resource; non-writer lanes store out of range (dropped).
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out, a.out_bytes);
+        const bool writer = segment_writer(kl, KL);
+
+        // 3. Stream.
+        for (int p0 = gw; p0 < passes; p0 += D * GW) {
+            float acc[D][NMAT][MT];
+            static_for<D>([&](auto J) {
+#pragma unroll
+                for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        float r = 0.f;
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            float c = goff[m][g];
+#pragma unroll
+                            for (int u = g * UPG; u < (g + 1) * UPG; ++u)
+                                c = ux[m][u].qdot(w[J][t] + u * BITS, c);
+                            r = __builtin_fmaf(E::to_f32(sv[J][t][g]), c,
+                                               __builtin_fmaf(E::to_f32(bv[J][t][g]),
+                                                              gsum[m][g], r));
+                        }
+                        acc[J][t][m] = r;
+                    }
+                fetch(p0 + (J + D) * GW, w[J], sv[J], bv[J]);
+            });
+            // 4. Reduce the D slots together, then store.
+            reduce_slots<D * NMAT * MT, KL>(&acc[0][0][0]);
+            static_for<D>([&](auto J) {
+                const int row = (p0 + J * GW) * RPW + sub;
+                const bool ok = writer && row < R && p0 + J * GW < passes;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    float v = acc[J][0][m];
+                    if constexpr (NMAT == 2)
+                        v = silu_f32(acc[J][0][m]) * acc[J][1][m];
+                    const uint32_t off = (ok && pair[m] >= 0)
+                        ? (uint32_t)((pair[m] * a.R + row) * SB) : OOB;
+                    buffer_store_elem<DT>(E::from_f32(v), ro, off);
+                }
+            });
+        }
+        __syncthreads(); // the table is rebuilt for the next tile
     } // tiles
 }
 
-// Lanes per row for slices of U units; 0 when K does not split into a power of
-// two lane count that fits one block.
+// Lanes per row for slices of U units; 0 unless K splits into a power-of-two
+// lane count that fits one wave.
 inline int gemv_lanes_per_row(int64_t K, int U)
 {
     if (K <= 0 || K % (32 * U) != 0)
         return 0;
     int64_t kl = K / (32 * U);
-    if (kl < 1 || kl > GEMV_THREADS || (kl & (kl - 1)) != 0)
+    if (kl < 1 || kl > 64 || (kl & (kl - 1)) != 0)
         return 0;
     return (int)kl;
 }
@@ -454,15 +597,14 @@ __global__ __launch_bounds__(256) void qgemv_generic_kernel(GemvKernelArgs a)
                 const int64_t g = (u * 32) / a.gs;
                 const float s = E::to_f32(srow[g]);
                 const float b = E::to_f32(brow[g]);
-#pragma unroll
-                for (int c = 0; c < 32; ++c) {
-                    const float wv = (float)unit_code<BITS>(w, c) * s + b;
+                static_for<32>([&](auto C) {
+                    const float wv = (float)unit_code<BITS, C>(w) * s + b;
 #pragma unroll
                     for (int m = 0; m < 16; ++m)
                         if (m < count)
-                            acc[t][m] = __builtin_fmaf(E::to_f32(xrow[m][u * 32 + c]), wv,
+                            acc[t][m] = __builtin_fmaf(E::to_f32(xrow[m][u * 32 + C]), wv,
                                                        acc[t][m]);
-                }
+                });
             }
         }
 #pragma unroll

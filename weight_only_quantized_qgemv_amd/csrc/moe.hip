@@ -151,10 +151,10 @@ int pick_mt(int64_t P, int64_t E, int mtmax)
 
 int moe_tile_height(int64_t n_pairs, int64_t num_experts, int bits, int dt)
 {
-    // The register-resident kernel holds up to 8 activation rows with the dot2
+    // The register-resident kernel holds up to 4 activation rows with the dot2
     // path, 2 with the fp32 path (fp32 activations, 8-bit codes with bf16).
     const bool dot2 = dt != DT_F32 && !(bits == 8 && dt == DT_BF16);
-    return pick_mt(n_pairs, num_experts, dot2 ? 8 : 2);
+    return pick_mt(n_pairs, num_experts, dot2 ? 4 : 2);
 }
 
 hipError_t launch_moe_route(const MoeArgs& a, int mt, MoeRouting* r, hipStream_t st)

@@ -14,19 +14,26 @@ namespace qp {
 
 namespace {
 
-template <int BITS, int DT, int MT, int U, int NMAT>
+template <int DT> using St = typename Elem<DT>::storage;
+
+// Grid: y strides over the device-written tiles (bounded by max_tiles), x
+// spreads each tile's row passes over waves; about 4096 waves in total.
+template <int BITS, int DT, int MT, int U, int KL, int NMAT>
 hipError_t run_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 {
-    const int RP = GEMV_THREADS / k.KL;
-    const int64_t passes = (k.R + RP - 1) / RP;
+    constexpr int D = ring_depth<BITS, DT, MT, U, U, NMAT, 512>();
+    constexpr int RPW = 64 / KL;
+    const int64_t passes = (k.R + RPW - 1) / RPW;
     int64_t gy = max_tiles < 65535 ? max_tiles : 65535;
     if (gy < 1)
         gy = 1;
-    int64_t gx = 4096 / gy;
-    gx = gx < 1 ? 1 : gx;
-    gx = gx < passes ? gx : passes;
-    hipLaunchKernelGGL((qgemv_stream_kernel<BITS, DT, MT, U, NMAT>), dim3((int)gx, (int)gy),
-                       dim3(GEMV_THREADS), 0, st, k);
+    int64_t waves = (passes + D - 1) / D;
+    const int64_t cap = (4096 + gy - 1) / gy;
+    waves = waves < cap ? waves : cap;
+    const int64_t gx = (waves + 3) / 4;
+    k.KL = KL;
+    hipLaunchKernelGGL((qgemv_stream_kernel<BITS, DT, MT, U, U, KL, NMAT, GEMV_THREADS>),
+                       dim3((int)gx, (int)gy), dim3(GEMV_THREADS), 0, st, k);
     return hipGetLastError();
 }
 
@@ -49,23 +56,11 @@ hipError_t run_generic(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 template <int BITS, int DT, int MT, int NMAT>
 hipError_t run_mt(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 {
-    // At most one wave per row; the widest slice that splits K evenly.
-    if constexpr (MT <= 2) {
-        if (int kl = gemv_lanes_per_row(k.K, 2); kl && kl <= 64) {
-            k.KL = kl;
-            return run_tiles<BITS, DT, MT, 2, NMAT>(k, max_tiles, st);
-        }
-    }
-    if (int kl = gemv_lanes_per_row(k.K, 1); kl && kl <= 64) {
-        k.KL = kl;
-        return run_tiles<BITS, DT, MT, 1, NMAT>(k, max_tiles, st);
-    }
-    if constexpr (MT <= 2) {
-        if (int kl = gemv_lanes_per_row(k.K, 3); kl && kl <= 64) {
-            k.KL = kl;
-            return run_tiles<BITS, DT, MT, 3, NMAT>(k, max_tiles, st);
-        }
-    }
+    // One wave per row at K = 2048, eight rows per wave at K = 768.
+    if (k.K == 32 * 64)
+        return run_tiles<BITS, DT, MT, 1, 64, NMAT>(k, max_tiles, st);
+    if (k.K == 3 * 32 * 8)
+        return run_tiles<BITS, DT, MT, 3, 8, NMAT>(k, max_tiles, st);
     return run_generic<BITS, DT, NMAT>(k, max_tiles, st);
 }
 
@@ -91,18 +86,29 @@ hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     k.K = a.n_cols;
     k.gs = a.gs;
     k.out = a.out;
+    // The streaming kernel reads activation rows as 16-byte vectors and uses
+    // 32-bit offsets inside one expert matrix and the output.
+    const int64_t es = (int64_t)sizeof(St<DT>);
+    const int64_t P = a.n_tokens * a.top_k;
+    const bool x_vec = reinterpret_cast<uintptr_t>(a.a) % 16 == 0 &&
+                       (a.a_outer * es) % 16 == 0 && (a.a_inner * es) % 16 == 0 &&
+                       a.n_rows * (a.n_cols * BITS / 8) < (int64_t(1) << 31) &&
+                       a.n_rows * (a.n_cols / a.gs) * es < (int64_t(1) << 31) &&
+                       P * a.n_rows * es < (int64_t(1) << 31);
+    k.out_bytes = (uint32_t)(x_vec ? P * a.n_rows * es : 0);
     if constexpr (DT == DT_F32) {
         return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
     } else {
+        if (!x_vec)
+            return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
         constexpr int MTMAX = gemv_max_mt<BITS, DT>();
         switch (r.mt) {
         case 1: return run_mt<BITS, DT, 1, NMAT>(k, r.max_tiles, st);
         case 2: return run_mt<BITS, DT, 2, NMAT>(k, r.max_tiles, st);
         }
-        if constexpr (MTMAX >= 8) {
+        if constexpr (MTMAX >= 4) {
             if (r.mt == 4)
                 return run_mt<BITS, DT, 4, NMAT>(k, r.max_tiles, st);
-            return run_mt<BITS, DT, 8, NMAT>(k, r.max_tiles, st);
         }
         return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
     }

@@ -3,6 +3,8 @@
 // the streaming GEMV of gemv_core.hpp with a single tile holding the M
 // activation rows; M above the register budget of one tile is split into
 // chunks, each streaming the weights once.
+#include <stdlib.h>
+
 #include "gemv_core.hpp"
 #include "launch.hpp"
 
@@ -43,58 +45,117 @@ GemvKernelArgs dense_args(const GemvArgs& a, int64_t m0, int mc, int elem_size, 
     k.gs = a.gs;
     k.KL = KL;
     k.out = static_cast<char*>(a.y) + m0 * a.N * elem_size;
+    k.out_bytes = (uint32_t)(mc * a.N * elem_size);
     return k;
 }
 
-template <int BITS, int DT, int MT, int U>
-hipError_t run_fast(const GemvArgs& a, int64_t m0, int mc, int KL, hipStream_t st)
+#ifdef QP_TUNING
+// Launch-shape override for tuning builds only (never defined in the library).
+int tuning_env(const char* name, int dflt)
 {
-    const int RP = GEMV_THREADS / KL;
-    const int64_t passes = (a.N + RP - 1) / RP;
-    const int blocks = (int)(passes < kMaxBlocks ? passes : kMaxBlocks);
+    const char* v = getenv(name);
+    return v ? atoi(v) : dflt;
+}
+#endif
+
+// Launch shape: at most one block per CU (256 blocks) holding W waves
+// (4 <= W <= 10) so that all CUs get the same share; each wave keeps D rows
+// (the ring depth the register budget allows) in flight and loops over the
+// ring for the rest.
+constexpr int kCUs = 256;
+
+template <int BITS, int DT, int MT, int U, int G, int KL>
+hipError_t run_fast(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
+{
+    // 1024-thread blocks (128 VGPRs per lane) for the lean dot2 kernel at one
+    // activation row; 512 threads (256 VGPRs) for the heavier variants.
+    constexpr int MAXT = (MT == 1 && use_dot2<BITS, DT>() && U != 3) ? 1024
+                         : (U == 3 || MT == 4) ? 256 : 512;
+    // Waves per block: 10 measured best for the 14336 x 4096 decode shape.
+    constexpr int WMAX = MAXT / 64 < 10 ? MAXT / 64 : 10;
+    constexpr int D = ring_depth<BITS, DT, MT, U, G, 1, (131072 / MAXT < 512 ? 131072 / MAXT : 512)>();
+    constexpr int RPW = 64 / KL;
+    const int64_t passes = (a.N + RPW - 1) / RPW;
+    const int64_t waves = (passes + D - 1) / D;
+    int64_t W = (waves + kCUs - 1) / kCUs;
+    W = W < 4 ? 4 : (W > WMAX ? WMAX : W);
+    int64_t blocks = (waves + W - 1) / W;
+    blocks = blocks < kCUs ? blocks : kCUs;
+#ifdef QP_TUNING
+    W = tuning_env("QP_GEMV_W", (int)W);
+    blocks = tuning_env("QP_GEMV_BLOCKS", (int)blocks);
+#endif
     GemvKernelArgs k = dense_args(a, m0, mc, (int)sizeof(St<DT>), KL);
-    hipLaunchKernelGGL((qgemv_stream_kernel<BITS, DT, MT, U, 1>), dim3(blocks),
-                       dim3(GEMV_THREADS), 0, st, k);
+    hipLaunchKernelGGL((qgemv_stream_kernel<BITS, DT, MT, U, G, KL, 1, MAXT>),
+                       dim3((int)blocks), dim3((int)W * 64), 0, st, k);
     return hipGetLastError();
 }
 
+// The lane slice of U units lies in one quantization group when the group
+// size is a multiple of the slice.
+template <int BITS, int DT, int MT, int U, int KL>
+hipError_t run_slice(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
+{
+    if constexpr (U > 1) {
+        if (a.gs % (32 * U) == 0)
+            return run_fast<BITS, DT, MT, U, 1, KL>(a, m0, mc, st);
+        return run_fast<BITS, DT, MT, U, U, KL>(a, m0, mc, st);
+    } else {
+        return run_fast<BITS, DT, MT, 1, 1, KL>(a, m0, mc, st);
+    }
+}
+
+// Shapes with a one-wave-per-row (or finer) register-resident kernel; others
+// take the generic kernel.
 template <int BITS, int DT, int MT>
 hipError_t run_chunk(const GemvArgs& a, int64_t m0, int mc, hipStream_t st, bool* done)
 {
     *done = true;
-    // Prefer slices that put 64 lanes (one wave) on a row; widest slice first.
-    if constexpr (MT == 1) {
-        if (int kl = gemv_lanes_per_row(a.K, 2); kl == 64) return run_fast<BITS, DT, MT, 2>(a, m0, mc, kl, st);
-        if (int kl = gemv_lanes_per_row(a.K, 4); kl == 64) return run_fast<BITS, DT, MT, 4>(a, m0, mc, kl, st);
-        if (int kl = gemv_lanes_per_row(a.K, 1); kl == 64) return run_fast<BITS, DT, MT, 1>(a, m0, mc, kl, st);
-        if (int kl = gemv_lanes_per_row(a.K, 4)) return run_fast<BITS, DT, MT, 4>(a, m0, mc, kl, st);
-        if (int kl = gemv_lanes_per_row(a.K, 2)) return run_fast<BITS, DT, MT, 2>(a, m0, mc, kl, st);
-    } else if constexpr (MT == 2) {
-        if (int kl = gemv_lanes_per_row(a.K, 2); kl == 64) return run_fast<BITS, DT, MT, 2>(a, m0, mc, kl, st);
-        if (int kl = gemv_lanes_per_row(a.K, 2)) return run_fast<BITS, DT, MT, 2>(a, m0, mc, kl, st);
+    const int64_t K = a.K;
+    if (K == 2 * 32 * 64) return run_slice<BITS, DT, MT, 2, 64>(a, m0, mc, st);
+    if (K == 1 * 32 * 64) return run_slice<BITS, DT, MT, 1, 64>(a, m0, mc, st);
+    if (K == 3 * 32 * 8) return run_fast<BITS, DT, MT, 3, 3, 8>(a, m0, mc, st);
+    if constexpr (MT <= 2) {
+        if (K == 32 * 32) return run_slice<BITS, DT, MT, 1, 32>(a, m0, mc, st);
     }
-    if (int kl = gemv_lanes_per_row(a.K, 1)) return run_fast<BITS, DT, MT, 1>(a, m0, mc, kl, st);
+    if constexpr (MT == 1 && DT != DT_F32) {
+        if (K == 4 * 32 * 64) return run_slice<BITS, DT, MT, 4, 64>(a, m0, mc, st);
+    }
     *done = false;
     return hipSuccess;
 }
 
+// Any K and any activation alignment; up to 16 rows per launch.
 template <int BITS, int DT>
 hipError_t run_generic(const GemvArgs& a, hipStream_t st)
 {
     int64_t blocks = (a.N + 3) / 4;
     if (blocks > kMaxBlocks)
         blocks = kMaxBlocks;
-    GemvKernelArgs k = dense_args(a, 0, (int)a.M, (int)sizeof(St<DT>), 64);
-    hipLaunchKernelGGL((qgemv_generic_kernel<BITS, DT, 1>), dim3((int)blocks), dim3(256), 0, st,
-                       k);
-    return hipGetLastError();
+    for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
+        const int mc = (int)((a.M - m0) < 16 ? (a.M - m0) : 16);
+        GemvKernelArgs k = dense_args(a, m0, mc, (int)sizeof(St<DT>), 64);
+        hipLaunchKernelGGL((qgemv_generic_kernel<BITS, DT, 1>), dim3((int)blocks), dim3(256), 0,
+                           st, k);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 template <int BITS, int DT>
 hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
 {
     constexpr int MTMAX = gemv_max_mt<BITS, DT>();
-    if (gemv_lanes_per_row(a.K, 1) == 0)
+    // The streaming kernel reads activations as 16-byte vectors.
+    const bool x_vec = reinterpret_cast<uintptr_t>(a.x) % 16 == 0;
+    // Raw buffer accesses address each matrix and the output with 32-bit
+    // offsets.
+    const int64_t es = (int64_t)sizeof(St<DT>);
+    const bool small = a.N * (a.K * BITS / 8) < (int64_t(1) << 31) &&
+                       a.N * (a.K / a.gs) * es < (int64_t(1) << 31) &&
+                       a.M * a.N * es < (int64_t(1) << 31);
+    if (!x_vec || !small)
         return run_generic<BITS, DT>(a, st);
     for (int64_t m0 = 0; m0 < a.M;) {
         const int mc = (int)((a.M - m0) < MTMAX ? (a.M - m0) : MTMAX);
@@ -104,11 +165,8 @@ hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
             e = run_chunk<BITS, DT, 1>(a, m0, mc, st, &done);
         } else if (mc == 2) {
             e = run_chunk<BITS, DT, 2>(a, m0, mc, st, &done);
-        } else if constexpr (MTMAX >= 8) {
-            if (mc <= 4)
-                e = run_chunk<BITS, DT, 4>(a, m0, mc, st, &done);
-            else
-                e = run_chunk<BITS, DT, 8>(a, m0, mc, st, &done);
+        } else if constexpr (MTMAX >= 4) {
+            e = run_chunk<BITS, DT, 4>(a, m0, mc, st, &done);
         } else {
             e = hipErrorInvalidValue; // unreachable: mc <= MTMAX = 2
         }
