@@ -103,7 +103,7 @@ def test_qmatmul_parity_small(bits, dt, k, m):
 
 @pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("dt", [F32, F16, BF16])
-@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("m", [1, 4, 16, 64, 300])
 def test_qmatmul_exact_arithmetic_is_bit_exact(bits, dt, m):
     """s' = 1/16, b' = -2^(bits-1)/16, integer x in [-8, 8]: every partial sum
     is exact in fp32, so y must be the output rounding of the exact result."""
@@ -188,11 +188,13 @@ def test_qmatmul_cross_word_config_sampled(bits, gs, m):
     sampled_check(y, xs, F16, rq, rs, rb, 4096, bits, gs, seed=bits * 10 + gs + m)
 
 
-@pytest.mark.parametrize("m", [17, 64, 100])
-def test_qmatmul_prefill_sizes_small(m):
-    log(f"prefill small m={m}")
-    y, y_ref, S = run_case(130, 512, m, 4, 64, BF16, seed=3000 + m)
-    assert_within(y, y_ref, S, BF16, f"prefill m{m}")
+@pytest.mark.parametrize("m", [17, 64, 100, 257])
+@pytest.mark.parametrize("bits,dt,gs", [(4, BF16, 64), (2, BF16, 32), (3, F16, 128), (6, F16, 64),
+                                        (8, BF16, 64)])
+def test_qmatmul_prefill_sizes_small(m, bits, dt, gs):
+    log(f"prefill small m={m} bits={bits} dt={dt}")
+    y, y_ref, S = run_case(300, 512, m, bits, gs, dt, seed=3000 + m + bits)
+    assert_within(y, y_ref, S, dt, f"prefill m{m} b{bits}")
 
 
 @pytest.mark.parametrize("shape_x,shape_w,xseed,wseed", [
