@@ -1,69 +1,165 @@
-"""Benchmark: decode GEMV and prefill GEMM of weight-only quantized linear layers
-on one MI355X.
+"""Benchmark: weight-only quantized linear layers (qGEMV decode, qGEMM prefill,
+routed MoE) on one MI355X.
 
-Headline (the JSON `value`): 4-bit gs64 qGEMV weight GB/s, decode W[14336, 4096]
-(8B-class MLP shape) with bf16 scales/biases and x bf16 [1, 4096]. One step =
-one qmatmul call (the whole hot path of the decode step: stream + unpack +
-affine + reduce). Weight bytes = codes + scales + biases = 33,030,144 B.
-The timed region cycles through >= 512 MB of distinct weight copies so every
-launch streams from HBM, not from the 256 MB Infinity Cache.
+Headline (the JSON `value`): 4-bit gs64 qGEMV weight GB/s on the decode shape
+W[14336, 4096] (8B-class MLP) with bf16 scales/biases and x bf16 [1, 4096].
+One step = one qmatmul call: the whole hot path of a decode linear layer
+(stream the packed codes, unpack, affine dequant, contract, reduce, store).
+Weight bytes = codes + scales + biases = 33,030,144 B per call. The timed
+region cycles through >= 512 MB of distinct weight copies (more than twice the
+256 MB Infinity Cache), so every launch streams its weights from HBM.
 
-Secondary (in `secondary`): 4-bit prefill qGEMM TFLOP/s on x bf16 [2048, 4096]
-x W[14336, 4096]^T, against the bf16 dense MFMA peak.
+Every other row of the hot path is measured too, in `rows`: decode at 2/4/8
+bits and M = 1/4/16, the cross-word 3/6-bit layouts over three group sizes,
+both prefill GEMM shapes against the bf16 MFMA peak, and the MoE gate+up+SiLU
+and down calls at T = 1/64/512 tokens.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
+  python bench.py --copy-calibration   # plain 1 GiB copies, to scale HBM counters
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 MALL_BYTES = 256 << 20
+ROTATE_BYTES = 2 * MALL_BYTES
+CSRC = os.path.join(ROOT, "weight_only_quantized_qgemv_amd", "csrc")
+
+# HBM traffic of the headline kernel per launch, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE) of `bench.py --steps 20 --warmup 2 --no-rows
+# --no-cpu-baseline`, each scaled by the same counter on a plain 1 GiB copy.
+# It holds only while the decode kernel's sources are the ones it was taken on.
+TRAFFIC = {"src_sha": "7b1d5a1d46400a66", "fetch_bytes": 33220843, "write_bytes": 68992,
+           "fetch_scale": 2.0, "write_scale": 1.0}
+DECODE_SOURCES = ("gemv_core.hpp", "common.hpp", "unpack_plan.hpp", "qgemv.hip")
+
+
+def decode_src_sha() -> str:
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def weight_bytes(n, k, bits, gs, sb_bytes):
     return n * k * bits // 8 + 2 * n * (k // gs) * sb_bytes
 
 
-def make_weights(n, k, bits, gs, copies, seed, dev):
+def make_weights(n, k, bits, gs, sb_dtype, copies, seed, dev):
     import torch
     import weight_only_quantized_qgemv_amd as qp
     from weight_only_quantized_qgemv_amd import synth
     w = torch.from_numpy(synth.normal_f32((n, k), 0.02, seed)).to(dev)
-    base = qp.qpack_quantize(w, bits, gs, torch.bfloat16)
+    base = qp.qpack_quantize(w, bits, gs, sb_dtype)
     del w
     sets = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
     torch.cuda.synchronize()
     return sets
 
 
-def time_calls(fn, steps, warmup, stream):
-    """Average ms per call over `steps` back-to-back calls, events on `stream`."""
+def copies_for(nbytes):
+    return max(2, -(-ROTATE_BYTES // nbytes))
+
+
+def time_calls(fn, steps, warmup, stream, reps=5):
+    """Median over `reps` of the mean ms per call over `steps` back-to-back
+    calls, HIP events recorded on `stream` (the stream the kernels run on)."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        fn(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    out = []
+    for _ in range(reps):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            fn(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        out.append(start.elapsed_time(end) / steps)
+    return statistics.median(out)
 
 
-def cpu_baseline(n, k, bits, gs, budget_s=10.0):
-    """The oracle (plain C, OpenMP over outputs) on the same decode workload:
-    whole M=1 calls on the full weight matrix, repeated for ~budget_s."""
+def bench_dense(N, K, M, bits, gs, dt, steps, warmup, stream, dev, seed=21):
+    import torch
+    import weight_only_quantized_qgemv_amd as qp
+    from weight_only_quantized_qgemv_amd import synth
+    es = torch.finfo(dt).bits // 8
+    wb = weight_bytes(N, K, bits, gs, es)
+    copies = copies_for(wb)
+    sets = make_weights(N, K, bits, gs, dt, copies, seed, dev)
+    x = torch.from_numpy(synth.normal_f32((M, K), 1.0, seed + 1)).to(dt).to(dev)
+    y = torch.empty((M, N), dtype=dt, device=dev)
+
+    def step(i):
+        wq, s, b = sets[i % copies]
+        qp.qmatmul(x, wq, s, b, bits, gs, out=y)
+
+    ms = time_calls(step, steps, warmup, stream)
+    del sets
+    torch.cuda.empty_cache()
+    return ms, wb, copies
+
+
+def bench_moe(T, steps, warmup, stream, dev):
+    """Gate+up+SiLU then down of a 128-expert top-8 MoE block (d = 2048,
+    ffn = 768), 4-bit gs64 bf16; two weight sets alternate."""
+    import numpy as np
+    import torch
+    import weight_only_quantized_qgemv_amd as qp
+    from weight_only_quantized_qgemv_amd import synth
+    E, top_k, D, F, bits, gs = 128, 8, 2048, 768, 4, 64
+    wsets = []
+    for c in range(2):
+        g = [t.reshape(E, F, -1) for t in make_weights(E * F, D, bits, gs, torch.bfloat16, 1,
+                                                       51 + 10 * c, dev)[0]]
+        u = [t.reshape(E, F, -1) for t in make_weights(E * F, D, bits, gs, torch.bfloat16, 1,
+                                                       52 + 10 * c, dev)[0]]
+        d = [t.reshape(E, D, -1) for t in make_weights(E * D, F, bits, gs, torch.bfloat16, 1,
+                                                       53 + 10 * c, dev)[0]]
+        wsets.append((g, u, d))
+    ids_np = synth.moe_ids(T, top_k, E, seed=55).ravel()
+    ids = torch.from_numpy(ids_np).to(dev)
+    a = torch.from_numpy(synth.normal_f32((T, D), 1.0, 54)).to(torch.bfloat16).to(dev)
+    P = T * top_k
+    h = torch.empty((P, F), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((P, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(qp.qgemv_moe_workspace_bytes(P, E), dtype=torch.uint8, device=dev)
+
+    def gate_up(i):
+        g, u, _ = wsets[i % 2]
+        qp.qgemv_moe_id_gate_up_silu(a, ids, T, top_k, D, 0, g, u, bits, gs, out=h, workspace=ws)
+
+    def down(i):
+        _, _, d = wsets[i % 2]
+        qp.qgemv_moe_id(h, ids, T, top_k, top_k * F, F, *d, bits, gs, out=o, workspace=ws)
+
+    ms_gu = time_calls(gate_up, steps, warmup, stream)
+    ms_d = time_calls(down, steps, warmup, stream)
+    touched = len(np.unique(ids_np))
+    per_expert = weight_bytes(F, D, bits, gs, 2)   # one [768, 2048] matrix
+    del wsets
+    torch.cuda.empty_cache()
+    return ms_gu, ms_d, touched, per_expert
+
+
+def cpu_baseline(n, k, bits, gs, budget_s=12.0):
+    """The oracle (plain C, OpenMP over outputs) on the headline decode workload:
+    whole M=1 calls on the full weight matrix, repeated for about budget_s."""
     import numpy as np
     import torch
     from oracle import qref
@@ -82,8 +178,24 @@ def cpu_baseline(n, k, bits, gs, budget_s=10.0):
     wb = weight_bytes(n, k, bits, gs, 2)
     return {"value": round(wb * runs / el / 1e9, 4), "unit": "GB/s", "cores": qref.num_threads(),
             "kind": "oracle",
-            "sample": f"{runs} whole decode calls (M=1, W[{n},{k}] {bits}-bit gs{gs} bf16), "
-                      f"{el:.1f} s; dequant + fp64 dot per output, OpenMP over outputs"}
+            "sample": f"{runs} whole decode calls (M=1, W[{n},{k}] {bits}-bit gs{gs} bf16 "
+                      f"scales/biases), {el:.1f} s wall; dequant + fp64 dot per output, "
+                      f"OpenMP over outputs"}
+
+
+def copy_calibration():
+    """Plain device copies of a known size: the reference that scales the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    dev = torch.device("cuda:0")
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
 def main():
@@ -92,34 +204,30 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (no multi-GPU path); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path in this library "
+              "(see the sharding design); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
-    import weight_only_quantized_qgemv_amd as qp
-    from weight_only_quantized_qgemv_amd import synth
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    bf16 = torch.bfloat16
     N, K, BITS, GS = 14336, 4096, 4, 64
-    wb = weight_bytes(N, K, BITS, GS, 2)
-    copies = max(2, -(-2 * MALL_BYTES // wb))   # > 2x the Infinity Cache in total
-    sets = make_weights(N, K, BITS, GS, copies, 21, dev)
-    x = torch.from_numpy(synth.normal_f32((1, K), 1.0, 22)).to(torch.bfloat16).to(dev)
-    y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
-
-    def step(i):
-        wq, s, b = sets[i % copies]
-        qp.qmatmul(x, wq, s, b, BITS, GS, out=y)
-
-    ms = time_calls(step, args.steps, args.warmup, stream)
+    ms, wb, copies = bench_dense(N, K, 1, BITS, GS, bf16, args.steps, args.warmup, stream, dev)
     gbs = wb / (ms * 1e-3) / 1e9
+    traffic = None
+    if TRAFFIC is not None and TRAFFIC.get("src_sha") == decode_src_sha():
+        traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
     result = {
-        "metric": "4-bit gs64 qGEMV weight GB/s (% HBM peak); qGEMM TFLOP/s (% bf16 MFMA)",
+        "metric": "4-bit gs64 qGEMV weight GB/s (decode W[14336,4096], M=1)",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -130,38 +238,62 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) weights quantized on device, N(0,1) activations)",
-        "config": {"workload": "decode qGEMV W[14336,4096] 4-bit gs64 bf16 scales/biases, "
+        "data": "synthetic: seeded N(0,0.02) fp32 weights quantized on the device, "
+                "N(0,1) bf16 activations",
+        "config": {"workload": "decode qGEMV W[14336,4096] 4-bit gs64, bf16 scales/biases, "
                                "x bf16 [1,4096], fp32 accumulation",
                    "weight_bytes_per_call": wb, "weight_copies": copies,
                    "rotation_bytes": wb * copies},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "qgemv_stream_kernel (4-bit, bf16, MT=1, U=2)",
-                     "us_per_launch": round(ms * 1e3, 3)},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "qgemv_stream_kernel<4, bf16, MT=1, U=2, G=1, KL=64, NMAT=1>",
+                     "us_per_launch": round(ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": wb},
     }
-    del sets
-    torch.cuda.empty_cache()
+    del_steps = max(20, args.steps // 4)
 
-    if not args.no_secondary:
-        # Prefill qGEMM: x bf16 [2048, 4096] x W[14336, 4096]^T (4-bit gs64).
-        M = 2048
-        psets = make_weights(N, K, BITS, GS, 2, 41, dev)
-        xp = torch.from_numpy(synth.normal_f32((M, K), 1.0, 43)).to(torch.bfloat16).to(dev)
-        yp = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-
-        def pstep(i):
-            wq, s, b = psets[i % 2]
-            qp.qmatmul(xp, wq, s, b, BITS, GS, out=yp)
-
-        pms = time_calls(pstep, max(5, args.steps // 20), 3, stream)
-        tflops = 2.0 * M * N * K / (pms * 1e-3) / 1e12
-        result["secondary"] = {
-            "qgemm_prefill": {"workload": "x bf16 [2048,4096] x W[14336,4096]^T 4-bit gs64",
-                              "tflops": round(tflops, 2), "ms": round(pms, 4),
-                              "frac_of_bf16_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
-        del psets
-        torch.cuda.empty_cache()
+    if not args.no_rows:
+        rows = {}
+        # Decode rows: W[14336,4096] gs64 bf16 at 4/8/2 bits, M = 1/4/16.
+        for bits in (4, 8, 2):
+            for M in (1, 4, 16):
+                ms_r, wb_r, _ = bench_dense(N, K, M, bits, 64, bf16, del_steps, 5, stream, dev)
+                g = wb_r / (ms_r * 1e-3) / 1e9
+                rows[f"decode_b{bits}_m{M}"] = {
+                    "us": round(ms_r * 1e3, 3), "weight_GBps": round(g, 1),
+                    "frac_hbm": round(g / HBM_PEAK_GBS, 4),
+                    "tokens_per_s": round(M / (ms_r * 1e-3), 1)}
+        # Cross-word rows: W[4096,4096] fp16 at 3/6 bits over gs 32/64/128, M = 1/8.
+        for bits in (3, 6):
+            for gs in (32, 64, 128):
+                for M in (1, 8):
+                    ms_r, wb_r, _ = bench_dense(4096, 4096, M, bits, gs, torch.float16,
+                                                del_steps, 5, stream, dev, seed=31)
+                    g = wb_r / (ms_r * 1e-3) / 1e9
+                    rows[f"crossword_b{bits}_gs{gs}_m{M}"] = {
+                        "us": round(ms_r * 1e3, 3), "weight_GBps": round(g, 1),
+                        "frac_hbm": round(g / HBM_PEAK_GBS, 4)}
+        # Prefill rows: x bf16 [2048, K] against the two MLP shapes.
+        for (n, k) in ((14336, 4096), (4096, 14336)):
+            ms_r, _, _ = bench_dense(n, k, 2048, 4, 64, bf16, 20, 3, stream, dev, seed=41)
+            tf = 2.0 * 2048 * n * k / (ms_r * 1e-3) / 1e12
+            rows[f"prefill_m2048_n{n}_k{k}"] = {
+                "us": round(ms_r * 1e3, 2), "tflops": round(tf, 1),
+                "frac_bf16_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "tokens_per_s": round(2048 / (ms_r * 1e-3), 1)}
+        # MoE rows: 128 experts, top-8, 4-bit gs64 bf16.
+        for T in (1, 64, 512):
+            ms_gu, ms_d, touched, per_expert = bench_moe(T, del_steps, 5, stream, dev)
+            gu_bytes, d_bytes = 2 * touched * per_expert, touched * per_expert
+            rows[f"moe_t{T}"] = {
+                "experts_touched": touched,
+                "gate_up_silu_us": round(ms_gu * 1e3, 3),
+                "gate_up_weight_GBps": round(gu_bytes / (ms_gu * 1e-3) / 1e9, 1),
+                "down_us": round(ms_d * 1e3, 3),
+                "down_weight_GBps": round(d_bytes / (ms_d * 1e-3) / 1e9, 1),
+                "tflops_total": round(2.0 * T * 8 * 3 * 768 * 2048 / ((ms_gu + ms_d) * 1e-3)
+                                      / 1e12, 2)}
+        result["rows"] = rows
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(N, K, BITS, GS)
