@@ -78,6 +78,38 @@ def test_moe_gate_up_and_down_small(bits, dt, T, top_k, E):
     assert_within(out_d, ref_d, S_d, dt, "moe down")
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("T,top_k,E,R,C,gs", [
+    (32, 2, 16, 200, 352, 32),    # 4 pairs per expert: 16-pair tiles
+    (64, 4, 8, 96, 256, 64),      # 32 per expert: 32-pair tiles
+    (200, 2, 4, 130, 256, 128),   # 100 per expert: 64-pair tiles, several per expert
+])
+def test_moe_matrix_core_tiles(bits, dt, T, top_k, E, R, C, gs):
+    """Enough pairs per expert for the matrix-core tiles, with row counts that
+    are not multiples of a row group and K not a multiple of 128."""
+    log(f"moe tiles bits={bits} dt={dt} T={T} top_k={top_k} E={E} R={R} C={C}")
+    gate_h, gate_d = stack(E, R, C, bits, gs, dt, 61 + bits)
+    up_h, up_d = stack(E, R, C, bits, gs, dt, 62 + bits)
+    Rd = 96 if R % 32 else R      # the down projection's K (a multiple of its group size)
+    down_h, down_d = stack(E, C, Rd, bits, 32, dt, 63 + bits)
+    ids = synth.moe_ids(T, top_k, E, seed=65).ravel()
+    ids_d = torch.from_numpy(ids).to(dev())
+    a_s, a_d = activations((T, C), dt, 64)
+    out = qp.qgemv_moe_id_gate_up_silu(a_d, ids_d, T, top_k, C, 0, gate_d, up_d, bits, gs)
+    g = qp.qgemv_moe_id(a_d, ids_d, T, top_k, C, 0, *gate_d, bits, gs)
+    torch.cuda.synchronize()
+    ref = qref.moe_gate_up_silu(a_s, dt, ids, T, top_k, C, 0, gate_h, up_h, dt, E, R, C, bits, gs)
+    check_fused(out, ref, dt, "tiles gate_up")
+    assert_within(g, ref["g"], ref["Sg"], dt, "tiles plain")
+    # Down projection over the pairs' own rows (inner stride = row length).
+    h_s, h_d = activations((T * top_k, Rd), dt, 66)
+    out_d = qp.qgemv_moe_id(h_d, ids_d, T, top_k, top_k * Rd, Rd, *down_d, bits, 32)
+    torch.cuda.synchronize()
+    ref_d, S_d = qref.moe(h_s, dt, ids, T, top_k, top_k * Rd, Rd, *down_h, dt, E, C, Rd, bits, 32)
+    assert_within(out_d, ref_d, S_d, dt, "tiles down")
+
+
 def moe_config(T, seed_ids=55):
     E, top_k = 128, 8
     gate_h, gate_d = stack(E, 768, 2048, 4, 64, BF16, 51)

@@ -101,9 +101,22 @@ def test_qmatmul_parity_small(bits, dt, k, m):
     assert_within(y, y_ref, S, dt, f"qmatmul b{bits} dt{dt} k{k} m{m}")
 
 
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("n,k,m,gs", [(301, 14336, 16, 128), (50, 14336, 7, 64),
+                                      (130, 160, 11, 32), (1000, 4096, 2, 64)])
+def test_qmatmul_skinny_tiles(bits, dt, n, k, m, gs):
+    """2..16 activation rows: ragged row counts, K not a multiple of the
+    K-split quads, and K long enough that the activation rows go to LDS in
+    several chunks (K = 14336)."""
+    log(f"skinny bits={bits} dt={dt} n={n} k={k} m={m} gs={gs}")
+    y, y_ref, S = run_case(n, k, m, bits, gs, dt, seed=5000 + n + k + m + bits)
+    assert_within(y, y_ref, S, dt, f"skinny b{bits} n{n} k{k} m{m}")
+
+
 @pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("dt", [F32, F16, BF16])
-@pytest.mark.parametrize("m", [1, 4, 16, 64, 300])
+@pytest.mark.parametrize("m", [1, 2, 4, 16, 64, 300])
 def test_qmatmul_exact_arithmetic_is_bit_exact(bits, dt, m):
     """s' = 1/16, b' = -2^(bits-1)/16, integer x in [-8, 8]: every partial sum
     is exact in fp32, so y must be the output rounding of the exact result."""

@@ -72,9 +72,16 @@ struct MoeRouting {
     const void* tiles;      // TileDesc list
     int mt;                 // tile height
     int64_t max_tiles;      // upper bound of the tile count
+    int nb;                 // > 0: matrix-core tiles of 16 * nb pairs (mt == 16 * nb)
 };
 hipError_t launch_moe_route(const MoeArgs& a, int mt, MoeRouting* r, hipStream_t stream);
 int moe_tile_height(int64_t n_pairs, int64_t num_experts, int bits, int dt);
+// Column blocks of 16 pairs per matrix-core tile for this call, or 0 when the
+// streaming kernel takes it (fp32 activations, few pairs per expert, or
+// operands the 16-byte / 32-bit-offset accesses cannot cover).
+int moe_mfma_nb(const MoeArgs& a);
+// LDS budget of the matrix-core tile kernels.
+constexpr unsigned kMfmaLdsBytes = 160 * 1024;
 #define QP_MOE_DECL(B)                                                                          \
     hipError_t launch_moe_b##B##_n1(const MoeArgs& a, const MoeRouting& r, hipStream_t stream); \
     hipError_t launch_moe_b##B##_n2(const MoeArgs& a, const MoeRouting& r, hipStream_t stream);

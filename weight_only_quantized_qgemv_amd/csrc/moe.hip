@@ -16,6 +16,7 @@
 // Each pair's accumulation order does not depend on its slot in a tile, so the
 // (unordered) scatter cannot change any output value.
 #include "gemv_core.hpp"
+#include "mfma_gemv.hpp"
 #include "launch.hpp"
 
 namespace qp {
@@ -177,13 +178,45 @@ hipError_t launch_moe_route(const MoeArgs& a, int mt, MoeRouting* r, hipStream_t
     return hipGetLastError();
 }
 
+int moe_mfma_nb(const MoeArgs& a)
+{
+    if (a.dt == DT_F32)
+        return 0;
+    const int64_t P = a.n_tokens * a.top_k;
+    // Matrix-core tiles pay off once experts see a few pairs each on average.
+    if (P < 2 * a.E || P < 32)
+        return 0;
+    const int64_t es = 2;
+    const bool vec = reinterpret_cast<uintptr_t>(a.a) % 16 == 0 && (a.a_outer * es) % 16 == 0 &&
+                     (a.a_inner * es) % 16 == 0;
+    const bool small = a.n_rows * (a.n_cols * a.bits / 8) < (int64_t(1) << 31) &&
+                       a.n_rows * (a.n_cols / a.gs) * es < (int64_t(1) << 31) &&
+                       P * a.n_rows * es < (int64_t(1) << 31);
+    if (!vec || !small)
+        return 0;
+    const int64_t kpad = (a.n_cols + 127) / 128 * 128;
+    const int64_t avg = (P + a.E - 1) / a.E;
+    int nb = 0;
+    for (int c = 1; c <= 4; c *= 2) {
+        if (mfma_lds_bytes(512, c, a.fused_silu ? 2 : 1, (int)kpad, 1, a.gs) > kMfmaLdsBytes)
+            break;
+        nb = c;
+        if (16 * c >= avg)
+            break;
+    }
+    return nb;
+}
+
 hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
 {
     MoeRouting r{};
     const int64_t P = a.n_tokens * a.top_k;
-    hipError_t e = launch_moe_route(a, moe_tile_height(P, a.E, a.bits, a.dt), &r, st);
+    const int nb = moe_mfma_nb(a);
+    hipError_t e = launch_moe_route(a, nb > 0 ? 16 * nb : moe_tile_height(P, a.E, a.bits, a.dt),
+                                    &r, st);
     if (e != hipSuccess)
         return e;
+    r.nb = nb;
     const bool f = a.fused_silu;
     switch (a.bits) {
     case 2: return f ? launch_moe_b2_n2(a, r, st) : launch_moe_b2_n1(a, r, st);

@@ -4,6 +4,7 @@
 // SiLU(gate) * up), so the kernel instantiations spread over parallel
 // translation units.
 #include "gemv_core.hpp"
+#include "mfma_gemv.hpp"
 #include "launch.hpp"
 
 #if !defined(QP_BITS) || !defined(QP_NMAT)
@@ -64,6 +65,33 @@ hipError_t run_mt(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
     return run_generic<BITS, DT, NMAT>(k, max_tiles, st);
 }
 
+// Matrix-core tiles of up to 16 * NB pairs: grid x over row groups of 128
+// rows of an expert matrix (8 waves of 16 rows), y over the device-written
+// tiles.
+constexpr int kMoeMfmaThreads = 512;
+
+template <int BITS, int DT, int NB, int NMAT>
+hipError_t run_mfma_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
+{
+    static bool attr_set = false; // per instantiation; set before its first launch
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&qgemv_mfma_kernel<BITS, DT, NB, NMAT, kMoeMfmaThreads>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaLdsBytes);
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    const int kpad = (int)((k.K + 127) / 128 * 128);
+    const int n_rg = (int)((k.R + 127) / 128);
+    int64_t gy = max_tiles < 65535 ? max_tiles : 65535;
+    gy = gy < 1 ? 1 : gy;
+    const uint32_t lds = mfma_lds_bytes(kMoeMfmaThreads, NB, NMAT, kpad, 1, k.gs);
+    hipLaunchKernelGGL((qgemv_mfma_kernel<BITS, DT, NB, NMAT, kMoeMfmaThreads>),
+                       dim3(n_rg, (int)gy), dim3(kMoeMfmaThreads), lds, st, k, kpad, 1, n_rg);
+    return hipGetLastError();
+}
+
 template <int BITS, int DT, int NMAT>
 hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
 {
@@ -99,6 +127,11 @@ hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     if constexpr (DT == DT_F32) {
         return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
     } else {
+        switch (r.nb) {
+        case 1: return run_mfma_tiles<BITS, DT, 1, NMAT>(k, r.max_tiles, st);
+        case 2: return run_mfma_tiles<BITS, DT, 2, NMAT>(k, r.max_tiles, st);
+        case 4: return run_mfma_tiles<BITS, DT, 4, NMAT>(k, r.max_tiles, st);
+        }
         if (!x_vec)
             return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
         constexpr int MTMAX = gemv_max_mt<BITS, DT>();

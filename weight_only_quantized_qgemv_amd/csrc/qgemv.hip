@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include "gemv_core.hpp"
+#include "mfma_gemv.hpp"
 #include "launch.hpp"
 
 namespace qp {
@@ -143,6 +144,56 @@ hipError_t run_generic(const GemvArgs& a, hipStream_t st)
     return hipSuccess;
 }
 
+// Tiles of 2..16 activation rows (16-bit activations) on the matrix cores:
+// 8-wave blocks, one per CU (the activation table takes most of the LDS).
+// KS waves split each row block's K range; KS is picked so that the row
+// groups of 16 * 8 / KS rows cover the CUs with the least padding of K.
+constexpr int kMfmaThreads = 512;
+
+template <int BITS, int DT>
+hipError_t run_mfma(const GemvArgs& a, hipStream_t st, bool* done)
+{
+    *done = false;
+    constexpr int WAVES = kMfmaThreads / 64;
+    const int64_t n16 = (a.N + 15) / 16;
+    const int64_t quads = (a.K + 127) / 128;
+    int KS = 1;
+    double best = -1.0;
+    for (int ks : {1, 2, 4, 8}) {
+        if (ks > 1 && quads < ks)
+            break;
+        const int64_t rg = (n16 + WAVES / ks - 1) / (WAVES / ks);
+        const int64_t kp = (a.K + 128 * ks - 1) / (128 * ks) * (128 * ks);
+        const double fill = (double)rg / (double)(kCUs * ((rg + kCUs - 1) / kCUs));
+        const double score = fill * (double)a.K / (double)kp;
+        if (score > best + 1e-9) {
+            best = score;
+            KS = ks;
+        }
+    }
+    const int kpad = (int)((a.K + 128 * KS - 1) / (128 * KS) * (128 * KS));
+    const uint64_t lds = mfma_lds_bytes(kMfmaThreads, 1, 1, kpad, KS, a.gs);
+    if (lds > kMfmaLdsBytes)
+        return hipSuccess;   // the streaming kernel takes this shape
+    static bool attr_set = false; // per instantiation; set before its first launch
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&qgemv_mfma_kernel<BITS, DT, 1, 1, kMfmaThreads>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaLdsBytes);
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    const int n_rg = (int)((n16 + WAVES / KS - 1) / (WAVES / KS));
+    GemvKernelArgs k = dense_args(a, 0, (int)a.M, (int)sizeof(St<DT>), 0);
+    hipLaunchKernelGGL((qgemv_mfma_kernel<BITS, DT, 1, 1, kMfmaThreads>), dim3(n_rg),
+                       dim3(kMfmaThreads), (uint32_t)lds, st, k, kpad, KS, n_rg);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess)
+        return e;
+    *done = true;
+    return hipSuccess;
+}
+
 template <int BITS, int DT>
 hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
 {
@@ -157,6 +208,19 @@ hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
                        a.M * a.N * es < (int64_t(1) << 31);
     if (!x_vec || !small)
         return run_generic<BITS, DT>(a, st);
+    if constexpr (DT != DT_F32) {
+#ifdef QP_TUNING
+        const int min_m = tuning_env("QP_MFMA_MIN_M", 2);
+#else
+        constexpr int min_m = 2;
+#endif
+        if (a.M >= min_m) {
+            bool done = false;
+            hipError_t e = run_mfma<BITS, DT>(a, st, &done);
+            if (e != hipSuccess || done)
+                return e;
+        }
+    }
     for (int64_t m0 = 0; m0 < a.M;) {
         const int mc = (int)((a.M - m0) < MTMAX ? (a.M - m0) : MTMAX);
         bool done = false;
