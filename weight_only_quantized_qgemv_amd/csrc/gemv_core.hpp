@@ -428,7 +428,15 @@ __global__ __launch_bounds__(MAXT) void qgemv_stream_kernel(GemvKernelArgs a)
                 }
             }
         };
-        static_for<D>([&](auto J) { fetch(gw + J * GW, w[J], sv[J], bv[J]); });
+        // Scheduling barriers keep each ring slot's loads together and in slot
+        // order, here and in the stream loop: if the scheduler sinks a slot's
+        // scale/bias loads behind later slots, the memory-counter wait before
+        // that slot's use has to drain nearly the whole ring.
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<D>([&](auto J) {
+            fetch(gw + J * GW, w[J], sv[J], bv[J]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
 
         // 1b. Build the table items and share them through LDS.
 #pragma unroll
@@ -490,6 +498,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_stream_kernel(GemvKernelArgs a)
         for (int p0 = gw; p0 < passes; p0 += D * GW) {
             float acc[D][NMAT][MT];
             static_for<D>([&](auto J) {
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int t = 0; t < NMAT; ++t)
 #pragma unroll
@@ -508,6 +517,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_stream_kernel(GemvKernelArgs a)
                         acc[J][t][m] = r;
                     }
                 fetch(p0 + (J + D) * GW, w[J], sv[J], bv[J]);
+                __builtin_amdgcn_sched_barrier(0);
             });
             // 4. Reduce the D slots together, then store.
             reduce_slots<D * NMAT * MT, KL>(&acc[0][0][0]);
