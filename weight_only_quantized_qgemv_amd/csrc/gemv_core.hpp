@@ -146,13 +146,23 @@ template <int BITS, int DT> struct UnitX<BITS, DT, true> {
             else
                 win[I] = w[wi] >> sh;
         });
-        static_for<P.n_pair>([&](auto J) {
-            constexpr PlanPair pp = P.pair[J];
+        // Each pair is formed one step before its dot product, so no pair is
+        // consumed by the instruction right after the one that wrote it (that
+        // adjacency costs a hazard wait state).
+        auto make = [&](auto J) {
+            constexpr PlanPair pp = P.pair[decltype(J)::value];
             constexpr uint32_t cm = (1u << BITS) - 1u;
             constexpr uint32_t mask = (pp.lo >= 0 ? cm << pp.lo_off : 0u) |
                                       (pp.hi >= 0 ? cm << (16 + pp.hi_off) : 0u);
-            const uint32_t v = and_or(win[pp.win], mask, T::MAGIC2);
-            acc = T::dot(v, xp[J], acc);
+            return and_or(win[pp.win], mask, T::MAGIC2);
+        };
+        uint32_t v = make(std::integral_constant<int, 0>{});
+        static_for<P.n_pair>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const uint32_t cur = v;
+            if constexpr (j + 1 < P.n_pair)
+                v = make(std::integral_constant<int, j + 1>{});
+            acc = T::dot(cur, xp[J], acc);
         });
         return acc;
     }
