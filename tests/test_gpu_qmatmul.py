@@ -210,6 +210,16 @@ def test_qmatmul_prefill_sizes_small(m, bits, dt, gs):
     assert_within(y, y_ref, S, dt, f"prefill m{m} b{bits}")
 
 
+@pytest.mark.parametrize("k", [96, 160, 544])
+@pytest.mark.parametrize("bits,dt", [(4, BF16), (3, F16), (8, BF16)])
+def test_qmatmul_many_rows_k_not_multiple_of_64(k, bits, dt):
+    """More than 16 activation rows with K an odd multiple of 32: every code
+    of the last half k-step must count."""
+    log(f"many rows k={k} bits={bits} dt={dt}")
+    y, y_ref, S = run_case(150, k, 40, bits, 32, dt, seed=3500 + k + bits)
+    assert_within(y, y_ref, S, dt, f"k{k} b{bits}")
+
+
 @pytest.mark.parametrize("shape_x,shape_w,xseed,wseed", [
     ((2048, 4096), (14336, 4096), 43, 41),
     ((2048, 14336), (4096, 14336), 44, 42),

@@ -187,11 +187,12 @@ __global__ __launch_bounds__(THREADS) void qgemm_kernel(const void* __restrict__
     const int b_r = tid % BN;
     const int u0 = (tid / BN) * UPT;
     const uint32_t b_soff = n0 + b_r < N ? (uint32_t)(n0 + b_r) * groups * 2 : 0x80000000u;
+    const uint32_t gshift = (uint32_t)__builtin_ctz((unsigned)gs);
     uint16_t s_next[UPT], b_next[UPT];
     auto load_sb = [&](int kt) {
 #pragma unroll
         for (int u = 0; u < UPT; ++u) {
-            const uint32_t g = (uint32_t)(kt * BK + (u0 + u) * 32) / (uint32_t)gs;
+            const uint32_t g = (uint32_t)(kt * BK + (u0 + u) * 32) >> gshift;
             s_next[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, b_soff + g * 2, 0, 0);
             b_next[u] = __builtin_amdgcn_raw_buffer_load_b16(rb, b_soff + g * 2, 0, 0);
         }
@@ -359,9 +360,10 @@ hipError_t run_gemm_dt(const GemvArgs& a, hipStream_t st)
 
 hipError_t launch_qgemm(const GemvArgs& a, hipStream_t stream)
 {
-    // 32-bit buffer offsets: every operand below 2 GB; otherwise the GEMV
-    // path (in chunks of activation rows) covers the shape.
-    const bool fits = a.M * a.K * 2 < (int64_t(1) << 31) &&
+    // 32-bit buffer offsets: every operand below 2 GB, and whole 64-wide k
+    // steps; otherwise the GEMV path (in chunks of activation rows) covers
+    // the shape.
+    const bool fits = a.K % BK == 0 && a.M * a.K * 2 < (int64_t(1) << 31) &&
                       a.N * (a.K * a.bits / 8) < (int64_t(1) << 31) &&
                       a.M * a.N * 2 < (int64_t(1) << 31) && a.K < (int64_t(1) << 30);
     if (!fits)
