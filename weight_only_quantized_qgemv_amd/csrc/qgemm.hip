@@ -15,8 +15,8 @@
 //    issued before the current step's MFMAs and written to the other stage
 //    interleaved with them (one barrier per step, no branch in the loop body);
 //  - LDS rows are 128 bytes (64 x 16-bit); 16-byte chunks are XOR-swizzled by
-//    row % 8 so that the MFMA fragment reads (eight rows, one chunk) hit
-//    distinct banks;
+//    (row / 2) % 8 so that the 16 rows one 16-lane phase of a fragment read
+//    touches at one chunk hit distinct banks;
 //  - all global accesses are raw buffer accesses: rows past M or N read zeros
 //    and their stores drop, so ragged shapes need no branches;
 //  - blocks are mapped to tiles XCD by XCD (block b runs on XCD b % 8), each
@@ -65,9 +65,11 @@ constexpr int ROW_BYTES = 128;  // one LDS row of activations / weights: 64 x 16
 constexpr int THREADS = 256;
 
 // Byte offset of 16-byte chunk c (0..7) of LDS row r: chunks are XOR-swizzled
-// by r % 8, so the eight rows an MFMA fragment read touches at one chunk land
-// on eight different 16-byte bank groups.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * ROW_BYTES + ((c ^ (r & 7)) << 4); }
+// by (r / 2) % 8. Two 128-byte rows fill one 256-byte sweep of the banks, so
+// the 16 rows a 16-lane phase of a fragment read (or of a dequantized-weight
+// write) touches at one chunk land on 16 different 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * ROW_BYTES + ((c ^ swz(r)) << 4); }
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t voff)
 {
@@ -147,12 +149,12 @@ __global__ __launch_bounds__(THREADS) void qgemm_kernel(const void* __restrict__
     // DMA plan. Activations: wave w's instruction i moves rows 8g..8g+7 of the
     // tile (g = 8w + i for BM = 256) into 1 KB of LDS; lane l lands in slot l
     // = (row 8g + l/8, physical chunk l%8), so it reads logical chunk
-    // (l%8) ^ (row%8) of that row. Rows past M read zeros.
+    // (l%8) ^ swz(row) of that row. Rows past M read zeros.
     uint32_t a_goff[A_INSTR];
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
         const int g = wave * A_INSTR + i, r = 8 * g + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
+        const int c = (lane & 7) ^ swz(r);
         a_goff[i] = m0 + r < M ? (uint32_t)(m0 + r) * xrow_bytes + c * 16 : 0x80000000u;
     }
     // Codes: flat chunk q = 64 * (wave * C_INSTR + i) + lane -> row q / CPR,
