@@ -59,59 +59,6 @@ template <> struct Mfma16<DT_F16> {
     }
 };
 
-// x & mask, opaque to the optimizer: the byte reads below must stay byte
-// conversions (v_cvt_f32_ubyteN) instead of being folded into bit-field
-// extracts of the unmasked word.
-__device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t mask)
-{
-    uint32_t r;
-    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(mask));
-    return r;
-}
-
-// A unit's 32 codes as bytes, so that each converts with one v_cvt_f32_ubyteN:
-// 8-bit codes already are bytes; 4-bit (2-bit) words are split into 2 (4)
-// words of one code per byte. 3- and 6-bit codes keep the word form and are
-// extracted with a bit-field read.
-template <int BITS> struct CodeBytes {
-    static constexpr bool BYTEWISE = BITS == 2 || BITS == 4 || BITS == 8;
-    static constexpr int NBW = BYTEWISE ? 8 : BITS;   // words after splitting
-    static __device__ __forceinline__ void split(const uint32_t (&w)[BITS], uint32_t (&bw)[NBW])
-    {
-        if constexpr (BITS == 8) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) bw[i] = w[i];
-        } else if constexpr (BITS == 4) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bw[2 * i] = and_opaque(w[i], 0x0F0F0F0Fu);
-                bw[2 * i + 1] = and_opaque(w[i] >> 4, 0x0F0F0F0Fu);
-            }
-        } else if constexpr (BITS == 2) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int h = 0; h < 4; ++h) bw[4 * i + h] = and_opaque(w[i] >> (2 * h), 0x03030303u);
-        } else {
-#pragma unroll
-            for (int i = 0; i < BITS; ++i) bw[i] = w[i];
-        }
-    }
-    // Code C of the unit as fp32.
-    template <int C> static __device__ __forceinline__ float code(const uint32_t (&bw)[NBW])
-    {
-        if constexpr (BITS == 8) {
-            return (float)((bw[C / 4] >> (8 * (C % 4))) & 0xFFu);
-        } else if constexpr (BITS == 4) {   // code 8 wi + 2 i + h: byte i of word 2 wi + h
-            return (float)((bw[2 * (C / 8) + (C % 2)] >> (8 * ((C % 8) / 2))) & 0xFFu);
-        } else if constexpr (BITS == 2) {   // code 16 wi + 4 i + h: byte i of word 4 wi + h
-            return (float)((bw[4 * (C / 16) + (C % 4)] >> (8 * ((C % 16) / 4))) & 0xFFu);
-        } else {
-            return (float)unit_code<BITS, C>(bw);
-        }
-    }
-};
-
 // Register budget per lane for THREADS-thread blocks (one block per CU).
 template <int THREADS> constexpr int mfma_vgpr_budget() { return THREADS > 512 ? 160 : 240; }
 

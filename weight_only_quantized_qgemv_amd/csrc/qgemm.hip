@@ -62,7 +62,6 @@ template <> struct MfmaTraits<DT_F16> {
 
 constexpr int BK = 64;          // k per step: two units of 32 codes
 constexpr int ROW_BYTES = 128;  // one LDS row of activations / weights: 64 x 16-bit
-constexpr int THREADS = 256;
 
 // Byte offset of 16-byte chunk c (0..7) of LDS row r: chunks are XOR-swizzled
 // by (r / 2) % 8. Two 128-byte rows fill one 256-byte sweep of the banks, so
@@ -90,14 +89,14 @@ template <int BITS> struct CodeLayout {
     static constexpr int CS = BITS == 3 ? 12 : 16;   // DMA chunk bytes
     static constexpr int CPR = RB / CS;              // chunks per row
     static constexpr int SLOT_ROW = 16 * CPR;        // LDS bytes per row
-    template <int BN> static constexpr int instr() { return (BN * CPR + 255) / 256; }
 };
-template <int BITS, int BN> struct CodeStage {
-    static constexpr int INSTR = CodeLayout<BITS>::template instr<BN>(); // per wave
-    static constexpr int STAGE = INSTR * 4 * 1024;                       // bytes
+template <int BITS, int BN, int WAVES> struct CodeStage {
+    static constexpr int INSTR =
+        (BN * CodeLayout<BITS>::CPR + 64 * WAVES - 1) / (64 * WAVES);       // per wave
+    static constexpr int STAGE = INSTR * WAVES * 1024;                        // bytes
 };
 
-template <int BITS, int DT, int BM, int BN>
+template <int BITS, int DT, int BM, int BN, int THREADS>
 __global__ __launch_bounds__(THREADS) void qgemm_kernel(const void* __restrict__ x,
                                                         const uint32_t* __restrict__ wq,
                                                         const void* __restrict__ scales,
@@ -108,13 +107,15 @@ __global__ __launch_bounds__(THREADS) void qgemm_kernel(const void* __restrict__
 {
     using T = MfmaTraits<DT>;
     using frag_t = typename T::frag_t;
-    struct CL : CodeLayout<BITS>, CodeStage<BITS, BN> {};
-    constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
+    constexpr int WAVES = THREADS / 64;
+    struct CL : CodeLayout<BITS>, CodeStage<BITS, BN, WAVES> {};
+    constexpr int WGN = WAVES / 2;               // waves: 2 along M x WGN along N
+    constexpr int WM = BM / 2, WN = BN / WGN;    // wave tile
     constexpr int FM = WM / 32, FN = WN / 32;    // 32 x 32 MFMA tiles per wave
     constexpr int UPT = 2 * BN / THREADS;        // weight units per thread per step
     static_assert(BN == THREADS || BN == THREADS / 2, "a weight row per one or two threads");
     constexpr int A_STAGE = BM * ROW_BYTES, B_STAGE = BN * ROW_BYTES;
-    constexpr int A_INSTR = A_STAGE / 1024 / 4;            // 1 KB DMA instructions per wave
+    constexpr int A_INSTR = A_STAGE / 1024 / WAVES;        // 1 KB DMA instructions per wave
     constexpr int C_INSTR = CL::INSTR;                      // per wave (64 chunks each)
     // Every DMA instruction writes 64 x 16 bytes, so a codes stage spans whole
     // 4 KB blocks (chunks past the tile read zeros into the spare slots).
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(THREADS) void qgemm_kernel(const void* __restrict__
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
 
     const uint32_t xrow_bytes = (uint32_t)K * 2;
     const uint32_t wrow_bytes = (uint32_t)K * BITS / 8;
@@ -202,14 +203,17 @@ __global__ __launch_bounds__(THREADS) void qgemm_kernel(const void* __restrict__
     // Codes of step kt (C stage kt % 2) -> activation-typed weights in B stage
     // kt % 2, in slices: slice `part` (0..3) writes 16-byte chunk `part` of each
     // of this thread's units, so the work can be spread over the MFMA phases.
-    uint32_t wcode[UPT][BITS];
+    using CB = CodeBytes<BITS>;
+    uint32_t wcode[UPT][CB::NBW];
     auto load_codes = [&](int stage) {
         const char* crow = c_st + stage * C_STAGE + b_r * CL::SLOT_ROW;
         static_for<UPT>([&](auto U) {
             const char* src = crow + (BITS == 3 ? (u0 + U) * 16 : (u0 + U) * 4 * BITS);
+            uint32_t w[BITS];
 #pragma unroll
             for (int i = 0; i < BITS; ++i)
-                wcode[U][i] = reinterpret_cast<const uint32_t*>(src)[i];
+                w[i] = reinterpret_cast<const uint32_t*>(src)[i];
+            CB::split(w, wcode[U]);
         });
     };
     auto dequant_part = [&](int stage, auto PART, const uint16_t (&sv)[UPT],
@@ -220,8 +224,8 @@ __global__ __launch_bounds__(THREADS) void qgemm_kernel(const void* __restrict__
             uint32_t packed[4];
             static_for<4>([&](auto P) {
                 constexpr int k0 = decltype(PART)::value * 8 + 2 * P;
-                const float w0 = __builtin_fmaf((float)unit_code<BITS, k0>(wcode[U]), s, b);
-                const float w1 = __builtin_fmaf((float)unit_code<BITS, k0 + 1>(wcode[U]), s, b);
+                const float w0 = __builtin_fmaf(CB::template code<k0>(wcode[U]), s, b);
+                const float w1 = __builtin_fmaf(CB::template code<k0 + 1>(wcode[U]), s, b);
                 packed[P] = T::pack2(w0, w1);
             });
             *reinterpret_cast<u32x4_t*>(brow + lds_off(b_r, (u0 + U) * 4 + decltype(PART)::value)) =
@@ -320,15 +324,15 @@ __global__ __launch_bounds__(THREADS) void qgemm_kernel(const void* __restrict__
         }
 }
 
-template <int BITS, int DT, int BM, int BN>
+template <int BITS, int DT, int BM, int BN, int NT>
 hipError_t run_gemm(const GemvArgs& a, hipStream_t st)
 {
-    constexpr int LDS = 2 * (BM + BN) * ROW_BYTES + 2 * CodeStage<BITS, BN>::STAGE;
+    constexpr int LDS = 2 * (BM + BN) * ROW_BYTES + 2 * CodeStage<BITS, BN, NT / 64>::STAGE;
     static_assert(LDS <= 160 * 1024, "LDS budget");
     static bool attr_set = false; // per instantiation; set before its first launch
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&qgemm_kernel<BITS, DT, BM, BN>),
+            reinterpret_cast<const void*>(&qgemm_kernel<BITS, DT, BM, BN, NT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
         if (e != hipSuccess)
             return e;
@@ -337,7 +341,7 @@ hipError_t run_gemm(const GemvArgs& a, hipStream_t st)
     const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
     const int tiles = tiles_m * tiles_n;
     const int per_xcd = (tiles + 7) / 8;
-    hipLaunchKernelGGL((qgemm_kernel<BITS, DT, BM, BN>), dim3(per_xcd * 8), dim3(THREADS), LDS, st,
+    hipLaunchKernelGGL((qgemm_kernel<BITS, DT, BM, BN, NT>), dim3(per_xcd * 8), dim3(NT), LDS, st,
                        a.x, a.wq, a.scales, a.biases, a.y, (int)a.M, (int)a.N, (int)a.K, a.gs,
                        tiles_n, tiles, per_xcd);
     return hipGetLastError();
@@ -346,14 +350,15 @@ hipError_t run_gemm(const GemvArgs& a, hipStream_t st)
 template <int DT>
 hipError_t run_gemm_dt(const GemvArgs& a, hipStream_t st)
 {
-    // Wide tiles when there are enough of them to fill the 256 CUs.
+    // Wide tiles (eight waves, two per SIMD) when there are enough of them to
+    // fill the 256 CUs; otherwise 256 x 128 tiles with four waves.
     const bool wide = ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 384;
     switch (a.bits) {
-    case 2: return wide ? run_gemm<2, DT, 256, 256>(a, st) : run_gemm<2, DT, 256, 128>(a, st);
-    case 3: return wide ? run_gemm<3, DT, 256, 256>(a, st) : run_gemm<3, DT, 256, 128>(a, st);
-    case 4: return wide ? run_gemm<4, DT, 256, 256>(a, st) : run_gemm<4, DT, 256, 128>(a, st);
-    case 6: return wide ? run_gemm<6, DT, 256, 256>(a, st) : run_gemm<6, DT, 256, 128>(a, st);
-    case 8: return wide ? run_gemm<8, DT, 256, 256>(a, st) : run_gemm<8, DT, 256, 128>(a, st);
+    case 2: return wide ? run_gemm<2, DT, 256, 256, 512>(a, st) : run_gemm<2, DT, 256, 128, 256>(a, st);
+    case 3: return wide ? run_gemm<3, DT, 256, 256, 512>(a, st) : run_gemm<3, DT, 256, 128, 256>(a, st);
+    case 4: return wide ? run_gemm<4, DT, 256, 256, 512>(a, st) : run_gemm<4, DT, 256, 128, 256>(a, st);
+    case 6: return wide ? run_gemm<6, DT, 256, 256, 512>(a, st) : run_gemm<6, DT, 256, 128, 256>(a, st);
+    case 8: return wide ? run_gemm<8, DT, 256, 256, 512>(a, st) : run_gemm<8, DT, 256, 128, 256>(a, st);
     }
     return hipErrorInvalidValue;
 }
