@@ -208,3 +208,58 @@ def test_moe_expert_with_many_pairs_spans_tiles():
     torch.cuda.synchronize()
     ref, S = qref.moe(a_s, BF16, ids, P, 1, C, 0, *h, BF16, E, R, C, bits, gs)
     assert_within(out, ref, S, BF16, "one expert")
+
+
+def skewed_ids(T):
+    """Token t picks expert 5 and expert 1 + t % 4 of six: expert 5 serves every
+    token (several 64-pair tiles), expert 0 none."""
+    return np.stack([np.full(T, 5), 1 + np.arange(T) % 4], axis=1).astype(np.int32).ravel()
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("T,top_k,E,R,C,gs,Rd", [
+    (96, 4, 8, 200, 320, 64, 192),    # 48 pairs per expert, ragged row blocks
+    (300, 2, 4, 96, 128, 32, 128),    # 150 per expert: three tiles each
+    (160, 2, 6, 72, 256, 128, 64),    # skewed: one expert on every token, one on none
+])
+def test_moe_routed_gemm_tiles(bits, dt, T, top_k, E, R, C, gs, Rd):
+    """Dozens of pairs per expert and K a multiple of 64 on both projections:
+    the routed matrix-core GEMM (tiles of up to 64 pairs of one expert)."""
+    log(f"moe routed gemm bits={bits} dt={dt} T={T} top_k={top_k} E={E} R={R} C={C} gs={gs}")
+    gate_h, gate_d = stack(E, R, C, bits, gs, dt, 161 + bits)
+    up_h, up_d = stack(E, R, C, bits, gs, dt, 162 + bits)
+    down_h, down_d = stack(E, C, Rd, bits, 32, dt, 163 + bits)
+    ids = skewed_ids(T) if E == 6 else synth.moe_ids(T, top_k, E, seed=165).ravel()
+    ids_d = torch.from_numpy(ids).to(dev())
+    a_s, a_d = activations((T, C), dt, 164)
+    out = qp.qgemv_moe_id_gate_up_silu(a_d, ids_d, T, top_k, C, 0, gate_d, up_d, bits, gs)
+    g = qp.qgemv_moe_id(a_d, ids_d, T, top_k, C, 0, *gate_d, bits, gs)
+    torch.cuda.synchronize()
+    ref = qref.moe_gate_up_silu(a_s, dt, ids, T, top_k, C, 0, gate_h, up_h, dt, E, R, C, bits, gs)
+    check_fused(out, ref, dt, "routed gate_up")
+    assert_within(g, ref["g"], ref["Sg"], dt, "routed plain")
+    # Down projection over the pairs' own rows (inner stride = row length).
+    h_s, h_d = activations((T * top_k, Rd), dt, 166)
+    out_d = qp.qgemv_moe_id(h_d, ids_d, T, top_k, top_k * Rd, Rd, *down_d, bits, 32)
+    torch.cuda.synchronize()
+    ref_d, S_d = qref.moe(h_s, dt, ids, T, top_k, top_k * Rd, Rd, *down_h, dt, E, C, Rd, bits, 32)
+    assert_within(out_d, ref_d, S_d, dt, "routed down")
+
+
+def test_moe_routed_gemm_pair_order_does_not_change_values():
+    """A pair's output does not depend on which tile slot it lands in: permuting
+    the pairs permutes the outputs bit for bit."""
+    E, R, C, bits, gs = 4, 136, 256, 4, 64
+    h, d = stack(E, R, C, bits, gs, BF16, 171)
+    P = 256
+    ids = synth.random_ints((P,), 0, E - 1, 172).astype(np.int32)
+    a_s, a_d = activations((P, C), BF16, 173)
+    out = qp.qgemv_moe_id(a_d, torch.from_numpy(ids).to(dev()), P, 1, C, 0, *d, bits, gs)
+    perm = synth.rng(174).permutation(P)
+    out_p = qp.qgemv_moe_id(a_d[torch.from_numpy(perm).to(dev())].contiguous(),
+                            torch.from_numpy(ids[perm]).to(dev()), P, 1, C, 0, *d, bits, gs)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out[torch.from_numpy(perm).to(dev())])
+    ref, S = qref.moe(a_s, BF16, ids, P, 1, C, 0, *h, BF16, E, R, C, bits, gs)
+    assert_within(out, ref, S, BF16, "routed")

@@ -50,6 +50,21 @@ template <> struct Elem<DT_BF16> {
     }
 };
 
+// Work description of one tile: `count` pairs (at most the tile height) of one expert, taken
+// from positions [start, start + count) of the pair list.
+struct TileDesc {
+    int expert;
+    int start;
+    int count;
+};
+
+// SiLU(z) = z * sigmoid(z), in fp32 (the activation of the fused gate / up
+// form; ferrum-kernels `gemv_moe_id_gate_up_silu` docs).
+__device__ __forceinline__ float silu_f32(float z)
+{
+    return z / (1.0f + expf(-z));
+}
+
 // Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so the body sees
 // I as a compile-time constant (table lookups fold, register arrays are
 // indexed statically).

@@ -195,14 +195,6 @@ template <int BITS, int DT> struct UnitX<BITS, DT, false> {
     }
 };
 
-// Work description of one tile: `count` (<= MT) pairs of one expert, taken
-// from positions [start, start + count) of the pair list.
-struct TileDesc {
-    int expert;
-    int start;
-    int count;
-};
-
 // Arguments of the streaming kernel. Element pointers are raw storage.
 struct GemvKernelArgs {
     const void* x;           // activations
@@ -220,11 +212,6 @@ struct GemvKernelArgs {
     void* out;               // [pairs, R]
     uint32_t out_bytes;      // size of `out` in bytes (< 2^31)
 };
-
-__device__ __forceinline__ float silu_f32(float z)
-{
-    return z / (1.0f + expf(-z));
-}
 
 // Buffer resource over `bytes` bytes at `p` (raw, untyped). Loads past the end
 // return zeros and stores past the end are dropped, which is what lets the

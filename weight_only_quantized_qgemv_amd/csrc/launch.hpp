@@ -73,6 +73,7 @@ struct MoeRouting {
     int mt;                 // tile height
     int64_t max_tiles;      // upper bound of the tile count
     int nb;                 // > 0: matrix-core tiles of 16 * nb pairs (mt == 16 * nb)
+    int gemm_bm;            // > 0: routed GEMM tiles of gemm_bm pairs (mt == gemm_bm)
 };
 hipError_t launch_moe_route(const MoeArgs& a, int mt, MoeRouting* r, hipStream_t stream);
 int moe_tile_height(int64_t n_pairs, int64_t num_experts, int bits, int dt);
@@ -80,6 +81,10 @@ int moe_tile_height(int64_t n_pairs, int64_t num_experts, int bits, int dt);
 // streaming kernel takes it (fp32 activations, few pairs per expert, or
 // operands the 16-byte / 32-bit-offset accesses cannot cover).
 int moe_mfma_nb(const MoeArgs& a);
+// Pairs per routed-GEMM tile for this call, or 0 when the GEMV kernels take
+// it (fp32 activations, few pairs per expert, K not a multiple of 64, or
+// operands the 16-byte / 32-bit-offset accesses cannot cover).
+int moe_gemm_bm(const MoeArgs& a);
 // LDS budget of the matrix-core tile kernels.
 constexpr unsigned kMfmaLdsBytes = 160 * 1024;
 #define QP_MOE_DECL(B)                                                                          \

@@ -178,6 +178,11 @@ hipError_t launch_moe_route(const MoeArgs& a, int mt, MoeRouting* r, hipStream_t
     return hipGetLastError();
 }
 
+#ifndef QP_MOE_GEMM_MIN_PAIRS
+#define QP_MOE_GEMM_MIN_PAIRS 16
+#endif
+constexpr int64_t kMoeGemmMinPairsPerExpert = QP_MOE_GEMM_MIN_PAIRS;
+
 int moe_mfma_nb(const MoeArgs& a)
 {
     if (a.dt == DT_F32)
@@ -207,16 +212,43 @@ int moe_mfma_nb(const MoeArgs& a)
     return nb;
 }
 
+int moe_gemm_bm(const MoeArgs& a)
+{
+    if (a.dt == DT_F32 || a.n_cols % 64 != 0)
+        return 0;
+    const int64_t P = a.n_tokens * a.top_k;
+    // The routed GEMM dequantizes each expert's weights once per 64-pair tile;
+    // it takes over from the GEMV tiles once experts see enough pairs each.
+    if (P < kMoeGemmMinPairsPerExpert * a.E)
+        return 0;
+    const int64_t es = 2;
+    const bool vec = reinterpret_cast<uintptr_t>(a.a) % 16 == 0 && (a.a_outer * es) % 16 == 0 &&
+                     (a.a_inner * es) % 16 == 0;
+    const int64_t x_span = ((a.n_tokens - 1) * a.a_outer + (a.top_k - 1) * a.a_inner + a.n_cols) * es;
+    // Scales / biases are read as aligned dwords over the whole stack.
+    const bool sb = reinterpret_cast<uintptr_t>(a.scales[0]) % 4 == 0 &&
+                    reinterpret_cast<uintptr_t>(a.biases[0]) % 4 == 0 &&
+                    (!a.fused_silu || (reinterpret_cast<uintptr_t>(a.scales[1]) % 4 == 0 &&
+                                       reinterpret_cast<uintptr_t>(a.biases[1]) % 4 == 0));
+    const bool small = x_span < (int64_t(1) << 31) &&
+                       a.n_rows * (a.n_cols * a.bits / 8) < (int64_t(1) << 31) &&
+                       a.E * a.n_rows * (a.n_cols / a.gs) * es < (int64_t(1) << 30) &&
+                       P * a.n_rows * es < (int64_t(1) << 31);
+    return vec && sb && small ? 64 : 0;
+}
+
 hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
 {
     MoeRouting r{};
     const int64_t P = a.n_tokens * a.top_k;
-    const int nb = moe_mfma_nb(a);
-    hipError_t e = launch_moe_route(a, nb > 0 ? 16 * nb : moe_tile_height(P, a.E, a.bits, a.dt),
-                                    &r, st);
+    const int bm = moe_gemm_bm(a);
+    const int nb = bm > 0 ? 0 : moe_mfma_nb(a);
+    const int mt = bm > 0 ? bm : nb > 0 ? 16 * nb : moe_tile_height(P, a.E, a.bits, a.dt);
+    hipError_t e = launch_moe_route(a, mt, &r, st);
     if (e != hipSuccess)
         return e;
     r.nb = nb;
+    r.gemm_bm = bm;
     const bool f = a.fused_silu;
     switch (a.bits) {
     case 2: return f ? launch_moe_b2_n2(a, r, st) : launch_moe_b2_n1(a, r, st);

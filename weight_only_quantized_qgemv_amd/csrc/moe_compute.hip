@@ -5,6 +5,7 @@
 // translation units.
 #include "gemv_core.hpp"
 #include "mfma_gemv.hpp"
+#include "gemm_core.hpp"
 #include "launch.hpp"
 
 #if !defined(QP_BITS) || !defined(QP_NMAT)
@@ -92,6 +93,69 @@ hipError_t run_mfma_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
     return hipGetLastError();
 }
 
+// Routed GEMM (gemm_core.hpp): tiles of BM pairs of one expert times BN / NMAT
+// rows of each of its NMAT matrices; grid x covers every (tile, row block) of
+// the largest possible tile list, XCD by XCD. Three activation stages and four
+// code / scale stages; at BN = 128 a block takes about 76 KB of LDS (4-bit),
+// so two blocks share a CU.
+#ifndef QP_MOE_GEMM_BN
+#define QP_MOE_GEMM_BN 128
+#endif
+#ifndef QP_MOE_GEMM_NA
+#define QP_MOE_GEMM_NA 3
+#endif
+#ifndef QP_MOE_GEMM_NC
+#define QP_MOE_GEMM_NC 4
+#endif
+constexpr int kMoeGemmBN = QP_MOE_GEMM_BN;
+constexpr int kMoeGemmThreads = 256;
+
+template <int BITS, int DT, int NMAT, int BM>
+hipError_t run_gemm_tiles(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
+{
+    constexpr int BN = kMoeGemmBN, NT = kMoeGemmThreads;
+    constexpr int NA = QP_MOE_GEMM_NA, NC = QP_MOE_GEMM_NC;
+    constexpr int LDS = gemm::lds_bytes<BITS, BM, BN, NT, NA, NC>();
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    const void* kern = reinterpret_cast<const void*>(
+        &gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, NMAT, true, NA, NC>);
+    static bool attr_set = false; // per instantiation; set before its first launch
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    const int64_t P = a.n_tokens * a.top_k;
+    GemmArgs g{};
+    g.x = a.a;
+    for (int t = 0; t < 2; ++t) {
+        const int src = NMAT == 2 ? t : 0;
+        g.wq[t] = a.wq[src];
+        g.scales[t] = a.scales[src];
+        g.biases[t] = a.biases[src];
+    }
+    g.y = a.out;
+    g.M = 0;
+    g.N = (int)a.n_rows;
+    g.K = (int)a.n_cols;
+    g.gs = a.gs;
+    g.x_bytes = (uint32_t)(((a.n_tokens - 1) * a.a_outer + (a.top_k - 1) * a.a_inner + a.n_cols) * 2);
+    g.y_bytes = (uint32_t)(P * a.n_rows * 2);
+    g.sb_bytes = (uint32_t)((a.E * a.n_rows * (a.n_cols / a.gs) * 2 + 3) & ~int64_t(3));
+    g.tiles_n = (int)((a.n_rows + BN / NMAT - 1) / (BN / NMAT));
+    g.perm = r.perm;
+    g.tdesc = static_cast<const TileDesc*>(r.tiles);
+    g.n_tiles = r.n_tiles;
+    g.top_k = (int)a.top_k;
+    g.outer_b = (uint32_t)(a.a_outer * 2);
+    g.inner_b = (uint32_t)(a.a_inner * 2);
+    const int64_t blocks = (r.max_tiles * g.tiles_n + 7) / 8 * 8;
+    hipLaunchKernelGGL((gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, NMAT, true, NA, NC>),
+                       dim3((unsigned)blocks), dim3(NT), LDS, st, g);
+    return hipGetLastError();
+}
+
 template <int BITS, int DT, int NMAT>
 hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
 {
@@ -127,6 +191,8 @@ hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     if constexpr (DT == DT_F32) {
         return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
     } else {
+        if (r.gemm_bm == 64)
+            return run_gemm_tiles<BITS, DT, NMAT, 64>(a, r, st);
         switch (r.nb) {
         case 1: return run_mfma_tiles<BITS, DT, 1, NMAT>(k, r.max_tiles, st);
         case 2: return run_mfma_tiles<BITS, DT, 2, NMAT>(k, r.max_tiles, st);
