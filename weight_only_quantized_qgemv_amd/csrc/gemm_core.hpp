@@ -8,19 +8,23 @@
 // a tile are the pairs one expert serves, gathered through the pair
 // permutation, and the weights are that expert's matrix of the stack.
 //  - block tile BM x BN x 64 (two 32-code units of every weight row per step),
-//    waves in 2 x (WAVES / 2), each wave a (BM/2) x (BN/(WAVES/2)) tile of
-//    v_mfma_f32_32x32x16 instructions accumulating in fp32;
-//  - each step, the block stages its activation tile [BM][64] and its weight
-//    tile [BN][64] in LDS: weight codes are unpacked (emily
-//    `dequantize_defn/1` layout) and dequantized in fp32 (q * s' + b') then
-//    rounded to the activation type, so every weight is dequantized once per
-//    block row;
-//  - two LDS stages: the next step's global loads are issued before the
-//    current step's MFMAs and written to the other stage interleaved with
-//    them (one barrier per step, no branch in the loop body);
-//  - LDS rows are 128 bytes (64 x 16-bit); 16-byte chunks are XOR-swizzled by
-//    (row / 2) % 8 so that the 16 rows one 16-lane phase of a fragment read
-//    touches at one chunk hit distinct banks;
+//    waves in WMW x (WAVES / WMW), each wave a (BM/WMW) x (BN/(WAVES/WMW))
+//    tile of v_mfma_f32_32x32x16 instructions accumulating in fp32;
+//  - each step, the block stages its activation tile [BM][64], the weight
+//    codes of its BN rows and their scales / biases in LDS by DMA; each lane
+//    then builds its MFMA B fragments in registers: it reads the 32 codes of
+//    one unit of its weight row (emily `dequantize_defn/1` layout), converts
+//    them with the byte-conversion instructions, applies q * s' + b' in fp32
+//    and rounds to the activation type. The contraction over the step's 64 k
+//    is taken in the order the units give: MFMA kk pairs k = 8 kk + i (lanes
+//    0-31) with k = 32 + 8 kk + i (lanes 32-63), and the activation fragments
+//    are read in the same order;
+//  - NA activation stages and NC code / scale stages: the DMA of later steps
+//    stays in flight across the per-step barrier;
+//  - LDS rows of activations are 128 bytes (64 x 16-bit); 16-byte chunks are
+//    XOR-swizzled by (row / 2) % 8, and the 16-byte code chunks of a row by a
+//    row-dependent XOR, so the rows one phase of a fragment read touches hit
+//    distinct banks;
 //  - all global accesses are raw buffer accesses: rows past the tile read
 //    zeros and their stores drop, so ragged shapes need no branches;
 //  - blocks are mapped to tiles XCD by XCD (block b runs on XCD b % 8), each
@@ -133,12 +137,26 @@ template <int BN> struct SbStage {
     static constexpr int INSTR = 2 * BN / 64;   // dword DMA instructions per block
 };
 
-// LDS bytes of one block: A[NA] | B[2] | C[NC] | SB[NC].
+// LDS bytes of one block: A[NA] | C[NC] | SB[NC].
 template <int BITS, int BM, int BN, int THREADS, int NA, int NC>
 constexpr int lds_bytes()
 {
-    return (NA * BM + 2 * BN) * ROW_BYTES + NC * (CodeStage<BITS, BN, THREADS / 64>::STAGE +
-                                                  SbStage<BN>::STAGE);
+    return NA * BM * ROW_BYTES + NC * (CodeStage<BITS, BN, THREADS / 64>::STAGE +
+                                       SbStage<BN>::STAGE);
+}
+
+// Logical 16-byte code chunk c of tile row r sits in slot r * CPR + (c ^
+// code_swz(r)): the rows one 16-lane phase of a unit read touches (16
+// consecutive rows, one chunk each) then cover all 16 bank groups.
+template <int BITS> __device__ __forceinline__ int code_swz(int r)
+{
+    constexpr int CPR = CodeLayout<BITS>::CPR;
+    if constexpr (CPR == 2)
+        return (r >> 3) & 1;
+    else if constexpr (CPR == 4)
+        return (r >> 2) & 3;
+    else
+        return 0;
 }
 
 // s_waitcnt immediate: at most `vm` vector-memory operations outstanding and
@@ -146,33 +164,32 @@ constexpr int lds_bytes()
 // lgkmcnt 11:8).
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
 
-// Pipeline (NA activation stages, NC code / scale stages, two dequantized
-// weight stages). Step kt issues the activation DMA of step kt + NA - 1 and
-// the code and scale DMA of step kt + NC, runs the MFMAs of step kt and
-// dequantizes step kt + 1 between them; it then waits only for what step
-// kt + 1 needs (activations of kt + 1, codes and scales of kt + 2), so code
-// loads get NC - 2 whole steps to arrive and the DMA of the newest steps stays
-// in flight across the barrier.
-template <int BITS, int DT, int BM, int BN, int THREADS, int NMAT, bool ROUTED, int NA, int NC>
+// Pipeline: step kt issues the activation DMA of step kt + NA - 1 and the code
+// and scale DMA of step kt + NC - 1, then runs the MFMAs of step kt; at its
+// end it waits only for what step kt + 1 needs (the activations and codes /
+// scales of kt + 1), so code loads get NC - 2 whole steps to arrive and the
+// DMA of the newest steps stays in flight across the barrier.
+template <int BITS, int DT, int BM, int BN, int THREADS, int WMW, int NMAT, bool ROUTED, int NA,
+          int NC>
 __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
 {
     using T = MfmaTraits<DT>;
     using frag_t = typename T::frag_t;
     using CL = CodeLayout<BITS>;
+    using CB = CodeBytes<BITS>;
     constexpr int WAVES = THREADS / 64;
-    constexpr int WGN = WAVES / 2;               // waves: 2 along M x WGN along N
-    constexpr int WM = BM / 2, WN = BN / WGN;    // wave tile
+    constexpr int WGN = WAVES / WMW;             // waves: WMW along M x WGN along N
+    constexpr int WM = BM / WMW, WN = BN / WGN;  // wave tile
     constexpr int FM = WM / 32, FN = WN / 32;    // 32 x 32 MFMA tiles per wave
-    constexpr int UPT = 2 * BN / THREADS;        // weight units per thread per step
     constexpr int BNO = BN / NMAT;               // output columns per tile
     constexpr int FNO = FN / NMAT;               // fragments per matrix per wave
-    static_assert(BN == THREADS || BN == THREADS / 2, "a weight row per one or two threads");
-    static_assert(FM >= 1 && FN >= NMAT && FN % NMAT == 0, "wave tile");
-    static_assert(!ROUTED || NMAT == 1 || (BNO % 64 == 0 && (BNO * CL::CPR) % 64 == 0),
-                  "each wave's rows and each DMA instruction within one matrix");
+    static_assert(WAVES % WMW == 0 && FM >= 1 && FM * 32 * WMW == BM, "wave rows");
+    static_assert(FN >= NMAT && FN % NMAT == 0 && FN * 32 * WGN == BN, "wave columns");
+    static_assert(NMAT == 1 || (BNO % 64 == 0 && (BNO * CL::CPR) % 64 == 0),
+                  "each DMA instruction within one matrix");
     static_assert(NMAT == 1 || ROUTED, "the fused form is routed");
     static_assert(NA >= 2 && NA <= 3 && NC >= 3, "pipeline depth");
-    constexpr int A_STAGE = BM * ROW_BYTES, B_STAGE = BN * ROW_BYTES;
+    constexpr int A_STAGE = BM * ROW_BYTES;
     constexpr int A_INSTR = A_STAGE / 1024 / WAVES;        // 1 KB DMA instructions per wave
     static_assert(A_INSTR * 1024 * WAVES == A_STAGE, "activation stage in whole DMA blocks");
     constexpr int C_INSTR = CodeStage<BITS, BN, WAVES>::INSTR;   // per wave (64 chunks each)
@@ -183,20 +200,17 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     constexpr int SB_INSTR = SbStage<BN>::INSTR / WAVES;   // per wave
     static_assert(SB_INSTR * WAVES == SbStage<BN>::INSTR, "scale DMA split over waves");
     // Vector-memory operations a wave issues per step, and how many of them
-    // may still be in flight when a step ends (the newest ones; everything
-    // older, up to the activations of the next step and the codes and scales
-    // of the one after, has landed).
+    // may still be in flight when a step ends. Step kt needs the activations
+    // and codes / scales of step kt + 1: the first DMA of step kt + 2 - NA and
+    // the last DMA of step kt + 2 - NC; what was issued after the later of the
+    // two may be in flight.
     constexpr int STEP_OPS = A_INSTR + C_INSTR + SB_INSTR;
-    // Step kt needs the activations of step kt + 1 (the first DMA of step
-    // kt + 2 - NA) and the codes / scales of step kt + 2 (the last DMA of step
-    // kt + 2 - NC); what was issued after the later of the two may be in flight.
     constexpr int IN_FLIGHT = NC > NA ? (C_INSTR + SB_INSTR) + (NA - 2) * STEP_OPS
                                       : (NC - 2) * STEP_OPS;
     static_assert(IN_FLIGHT < 64, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     char* const a_st = lds;
-    char* const b_st = a_st + NA * A_STAGE;
-    char* const c_st = b_st + 2 * B_STAGE;
+    char* const c_st = a_st + NA * A_STAGE;
     char* const sb_st = c_st + NC * C_STAGE;
 
     const int K = ga.K, N = ga.N;
@@ -232,12 +246,12 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         n0 = (tile % ga.tiles_n) * BN;
     }
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
 
     const __amdgpu_buffer_rsrc_t rx = rsrc(ga.x, ga.x_bytes);
-    // Weight operands of matrix t: this tile's expert in the stack.
+    // Weight codes of matrix t: this tile's expert in the stack.
     const size_t wmat_bytes = (size_t)N * wrow_bytes;
     auto rw_of = [&](int t) {
         return rsrc(reinterpret_cast<const char*>(ga.wq[t]) + (size_t)expert * wmat_bytes,
@@ -270,15 +284,16 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
             a_goff[i] = m0 + r < ga.M ? (uint32_t)(m0 + r) * xrow_bytes + c16 : OOB;
         }
     }
-    // Codes: flat chunk q = 64 * (wave * C_INSTR + i) + lane -> tile row
-    // q / CPR, part q % CPR; LDS slot q. Tile row r is row n0 + r % BNO of
-    // matrix r / BNO; one DMA instruction stays within one matrix.
+    // Codes: flat slot q = 64 * (wave * C_INSTR + i) + lane -> tile row
+    // r = q / CPR, physical part q % CPR, holding logical chunk
+    // (q % CPR) ^ code_swz(r). Tile row r is row n0 + r % BNO of matrix r / BNO;
+    // one DMA instruction stays within one matrix.
     uint32_t c_goff[C_INSTR];
     __amdgpu_buffer_rsrc_t rw[C_INSTR];
 #pragma unroll
     for (int i = 0; i < C_INSTR; ++i) {
         const int q = 64 * (wave * C_INSTR + i) + lane;
-        const int r = q / CL::CPR, part = q % CL::CPR;
+        const int r = q / CL::CPR, part = (q % CL::CPR) ^ code_swz<BITS>(r);
         const int row = n0 + r % BNO;
         c_goff[i] = (q < BN * CL::CPR && row < N)
             ? (uint32_t)row * wrow_bytes + part * CL::CS : OOB;
@@ -328,57 +343,77 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         }
     };
 
-    // Dequantization work of this thread: tile row b_r, units [u0, u0 + UPT).
-    const int b_r = tid % BN;
-    const int u0 = (tid / BN) * UPT;
-    const int b_row = n0 + b_r % BNO;
-    const uint32_t b_gbase = e_groups + (uint32_t)(b_row < N ? b_row : 0) * groups;
-    // Codes of step kt (C stage kt % NC) -> activation-typed weights in B stage
-    // kt % 2, in slices: slice `part` (0..3) writes 16-byte chunk `part` of each
-    // of this thread's units, so the work can be spread over the MFMA phases.
-    using CB = CodeBytes<BITS>;
-    uint32_t wcode[UPT][CB::NBW];
-    float s_u[UPT], b_u[UPT];
-    auto load_codes = [&](int kt, int stage) {
-        const char* crow = c_st + stage * C_STAGE + b_r * CL::SLOT_ROW;
-        static_for<UPT>([&](auto U) {
-            const char* src = crow + (BITS == 3 ? (u0 + U) * 16 : (u0 + U) * 4 * BITS);
-            uint32_t w[BITS];
+    // B fragments of this lane: column block j is tile row bt[j] (its weight
+    // row n0 + bt[j] % BNO of matrix bt[j] / BNO); the lane takes unit `half`
+    // (codes 32 half .. 32 half + 31 of the step) of that row.
+    int bt[FN];
+    uint32_t b_gbase[FN];
 #pragma unroll
-            for (int i = 0; i < BITS; ++i)
-                w[i] = reinterpret_cast<const uint32_t*>(src)[i];
-            CB::split(w, wcode[U]);
-        });
-        // The scale / bias dword holds elements (base & ~1) and (base & ~1) + 1
-        // of the array, base = this row's element of the step's first group:
-        // with 32-wide groups (base even) both groups of the step, else the
-        // step's one group in half base & 1.
-        const char* sbp = sb_st + stage * SB_STAGE + b_r * 4;
-        const uint32_t sd = *reinterpret_cast<const uint32_t*>(sbp);
-        const uint32_t bd = *reinterpret_cast<const uint32_t*>(sbp + 4 * BN);
-        const uint32_t base = b_gbase + (((uint32_t)kt * BK) >> gshift);
+    for (int j = 0; j < FN; ++j) {
+        if constexpr (NMAT == 1)
+            bt[j] = wn * WN + j * 32 + (lane & 31);
+        else
+            bt[j] = (j / FNO) * BNO + wn * (WN / 2) + (j % FNO) * 32 + (lane & 31);
+        const int row = n0 + bt[j] % BNO;
+        b_gbase[j] = e_groups + (uint32_t)(row < N ? row : 0) * groups;
+    }
+    uint32_t wcode[FN][CB::NBW];
+    float s_u[FN], b_u[FN];
+    // The unit's BITS words from C stage `stage`.
+    auto read_unit = [&](int stage, int r, uint32_t (&w)[BITS]) {
+        const char* row = c_st + stage * C_STAGE + r * CL::SLOT_ROW;
+        const int sw = code_swz<BITS>(r);
+        if constexpr (BITS == 4 || BITS == 3) {        // chunk `half` (16 or 12 bytes)
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + ((half ^ sw) << 4));
 #pragma unroll
-        for (int u = 0; u < UPT; ++u) {
-            const uint32_t g = b_gbase + (((uint32_t)kt * BK + (u0 + u) * 32) >> gshift);
-            const uint32_t sh = (g - (base & ~1u)) * 16;
-            s_u[u] = Elem<DT>::to_f32((uint16_t)(sd >> sh));
-            b_u[u] = Elem<DT>::to_f32((uint16_t)(bd >> sh));
+            for (int i = 0; i < BITS; ++i) w[i] = v[i];
+        } else if constexpr (BITS == 8) {               // chunks 2 half, 2 half + 1
+            const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(row + (((2 * half) ^ sw) << 4));
+            const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(row + (((2 * half + 1) ^ sw) << 4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { w[i] = v0[i]; w[4 + i] = v1[i]; }
+        } else {                                        // 2-bit: 8 bytes; 6-bit: 24 bytes
+#pragma unroll
+            for (int i = 0; i < BITS / 2; ++i) {
+                const u32x2_t v = *reinterpret_cast<const u32x2_t*>(row + half * 4 * BITS + 8 * i);
+                w[2 * i] = v[0];
+                w[2 * i + 1] = v[1];
+            }
         }
     };
-    auto dequant_part = [&](int stage, auto PART) {
-        char* brow = b_st + stage * B_STAGE;
-        static_for<UPT>([&](auto U) {
-            const float s = s_u[U], b = b_u[U];
-            uint32_t packed[4];
-            static_for<4>([&](auto P) {
-                constexpr int k0 = decltype(PART)::value * 8 + 2 * P;
-                const float w0 = __builtin_fmaf(CB::template code<k0>(wcode[U]), s, b);
-                const float w1 = __builtin_fmaf(CB::template code<k0 + 1>(wcode[U]), s, b);
-                packed[P] = T::pack2(w0, w1);
-            });
-            *reinterpret_cast<u32x4_t*>(brow + lds_off(b_r, (u0 + U) * 4 + decltype(PART)::value)) =
-                u32x4_t{packed[0], packed[1], packed[2], packed[3]};
+    // Codes and scale / bias of step kt (C / SB stage `stage`) for every
+    // column block. The scale / bias dword holds elements (base & ~1) and
+    // (base & ~1) + 1 of the array, base = the row's element of the step's
+    // first group: with 32-wide groups (base even) both groups of the step,
+    // else the step's one group in half base & 1.
+    auto load_units = [&](int kt, int stage) {
+        const uint32_t g0 = ((uint32_t)kt * BK) >> gshift;
+        const uint32_t gu = ((uint32_t)kt * BK + half * 32) >> gshift;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            uint32_t w[BITS];
+            read_unit(stage, bt[j], w);
+            CB::split(w, wcode[j]);
+            const char* sbp = sb_st + stage * SB_STAGE + bt[j] * 4;
+            const uint32_t sd = *reinterpret_cast<const uint32_t*>(sbp);
+            const uint32_t bd = *reinterpret_cast<const uint32_t*>(sbp + 4 * BN);
+            const uint32_t sh = ((b_gbase[j] + gu) - ((b_gbase[j] + g0) & ~1u)) * 16;
+            s_u[j] = Elem<DT>::to_f32((uint16_t)(sd >> sh));
+            b_u[j] = Elem<DT>::to_f32((uint16_t)(bd >> sh));
+        }
+    };
+    // B fragment of column block j for sub-step kk: codes 8 kk .. 8 kk + 7 of
+    // the lane's unit, dequantized.
+    auto make_bfrag = [&](auto J, auto KK) {
+        constexpr int j = decltype(J)::value, kk = decltype(KK)::value;
+        uint32_t packed[4];
+        static_for<4>([&](auto P) {
+            constexpr int c = 8 * kk + 2 * decltype(P)::value;
+            const float w0 = __builtin_fmaf(CB::template code<c>(wcode[j]), s_u[j], b_u[j]);
+            const float w1 = __builtin_fmaf(CB::template code<c + 1>(wcode[j]), s_u[j], b_u[j]);
+            packed[decltype(P)::value] = T::pack2(w0, w1);
         });
+        return __builtin_bit_cast(frag_t, u32x4_t{packed[0], packed[1], packed[2], packed[3]});
     };
     // End of a step: at most `vm` of this wave's DMAs in flight, its LDS
     // accesses done, then the block barrier. (A fence here would wait for
@@ -398,79 +433,59 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         for (int j = 0; j < FN; ++j)
             acc[i][j] = f32x16_t{};
 
-    // Tile row of B fragment j of this wave: NMAT = 1, WN consecutive rows;
-    // NMAT = 2, the wave's WN / 2 gate rows then the same up rows.
-    auto b_frag_row = [&](int j) {
-        if constexpr (NMAT == 1)
-            return wn * WN + j * 32;
-        else
-            return (j / FNO) * BNO + wn * (WN / 2) + (j % FNO) * 32;
-    };
-
-    // Prologue: the DMA of steps -NC .. -1 of the loop below (activations of
-    // steps 0 .. NA-2, codes / scales of steps 0 .. NC-1, in the loop's order,
-    // so the loop's in-flight counts hold from its first step), then B of
-    // step 0 from the first codes.
+    // Prologue: the DMA of steps 1 - NC .. -1 of the loop below (activations
+    // of steps 0 .. NA-2, codes / scales of steps 0 .. NC-2, in the loop's
+    // order, so the loop's in-flight counts hold from its first step).
     const int KT = K / BK;
 #pragma unroll
-    for (int s = -NC; s < 0; ++s) {
+    for (int s = 1 - NC; s < 0; ++s) {
         if (s + NA - 1 >= 0)
             dma_a(s + NA - 1, s + NA - 1);
-        dma_c(s + NC, s + NC);
+        dma_c(s + NC - 1, s + NC - 1);
     }
-    // Codes / scales of step 0 have landed: everything after them may not.
-    step_barrier(std::integral_constant<int, (NC - 1) * (C_INSTR + SB_INSTR) + (NA - 1) * A_INSTR>{});
-    load_codes(0, 0);
-    static_for<4>([&](auto PART) { dequant_part(0, PART); });
-    // Step 0 needs A(0) (the first DMA of step 1 - NA) and the codes / scales
-    // of step 1 (the last DMA of step 1 - NC).
-    constexpr int IN_FLIGHT0 = NC > NA ? (C_INSTR + SB_INSTR) + (NA - 2) * STEP_OPS
-                                       : (NC - 2) * STEP_OPS;
-    step_barrier(std::integral_constant<int, IN_FLIGHT0>{});
+    step_barrier(std::integral_constant<int, IN_FLIGHT>{});
 
-    int a_cur = 0, c_nxt = 1;          // A stage of step kt, C stage of step kt + 1
+    int a_cur = 0, c_cur = 0;          // A and C stages of step kt
     for (int kt = 0; kt < KT; ++kt) {
-        const int b_cur = kt & 1;
         // In flight during this step: activations of kt + NA - 1, codes and
-        // scales of kt + NC (reads past the last step are harmless: in-range
-        // bytes that are never used, or zeros).
-        const int a_new = a_cur + NA - 1 >= NA ? a_cur - 1 : a_cur + NA - 1;
-        const int c_new = c_nxt == 0 ? NC - 1 : c_nxt - 1;   // stage of step kt + NC
+        // scales of kt + NC - 1 (reads past the last step are harmless:
+        // in-range bytes that are never used, or zeros).
+        const int a_new = a_cur == 0 ? NA - 1 : a_cur - 1;
+        const int c_new = c_cur == 0 ? NC - 1 : c_cur - 1;
         dma_a(kt + NA - 1, a_new);
-        dma_c(kt + NC, c_new);
-        // MFMAs on A stage a_cur / B stage b_cur, fragments double-buffered
-        // across the four k16 sub-steps; after each sub-step's MFMAs, a quarter
-        // of the weights of step kt + 1 is dequantized.
+        dma_c(kt + NC - 1, c_new);
+        load_units(kt, c_cur);
+        // MFMAs on A stage a_cur; fragments double-buffered across the four
+        // k16 sub-steps, B fragments of the next sub-step built during the
+        // current one's MFMAs.
         const char* abase = a_st + a_cur * A_STAGE;
-        const char* bbase = b_st + b_cur * B_STAGE;
         frag_t af[2][FM], bfr[2][FN];
-        auto load_frags = [&](int kk, frag_t (&fa)[FM], frag_t (&fb)[FN]) {
-            const int chunk = 2 * kk + (lane >> 5);
+        auto load_afrags = [&](int kk, frag_t (&fa)[FM]) {
+            const int chunk = kk + 4 * half;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
                 fa[i] = *reinterpret_cast<const frag_t*>(
                     abase + lds_off(wm * WM + i * 32 + (lane & 31), chunk));
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                fb[j] = *reinterpret_cast<const frag_t*>(
-                    bbase + lds_off(b_frag_row(j) + (lane & 31), chunk));
         };
-        load_frags(0, af[0], bfr[0]);
-        load_codes(kt + 1, c_nxt);
+        load_afrags(0, af[0]);
+        static_for<FN>([&](auto J) { bfr[0][J] = make_bfrag(J, std::integral_constant<int, 0>{}); });
         static_for<BK / 16>([&](auto KK) {
             constexpr int kk = decltype(KK)::value;
             if constexpr (kk + 1 < BK / 16)
-                load_frags(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+                load_afrags(kk + 1, af[(kk + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = T::mfma(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
-            dequant_part(b_cur ^ 1, KK);
+            if constexpr (kk + 1 < BK / 16)
+                static_for<FN>([&](auto J) {
+                    bfr[(kk + 1) & 1][J] = make_bfrag(J, std::integral_constant<int, kk + 1>{});
+                });
         });
         step_barrier(std::integral_constant<int, IN_FLIGHT>{});
         a_cur = a_cur + 1 == NA ? 0 : a_cur + 1;
-        c_nxt = c_nxt + 1 == NC ? 0 : c_nxt + 1;
+        c_cur = c_cur + 1 == NC ? 0 : c_cur + 1;
     }
     // No DMA may still be writing this block's LDS when the block ends.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
@@ -484,7 +499,7 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         int orow[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int row = wm * WM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
             if constexpr (ROUTED)
                 orow[r] = row < count ? ga.perm[start + row] : -1;
             else

@@ -94,20 +94,18 @@ hipError_t run_mfma_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 }
 
 // Routed GEMM (gemm_core.hpp): tiles of BM pairs of one expert times BN / NMAT
-// rows of each of its NMAT matrices; grid x covers every (tile, row block) of
-// the largest possible tile list, XCD by XCD. Three activation stages and four
-// code / scale stages; at BN = 128 a block takes about 76 KB of LDS (4-bit),
-// so two blocks share a CU.
-#ifndef QP_MOE_GEMM_BN
-#define QP_MOE_GEMM_BN 128
-#endif
+// rows of each of its NMAT matrices, four waves side by side along the rows
+// (each weight fragment is built by one wave only); grid x covers every
+// (tile, row block) of the largest possible tile list, XCD by XCD. Three
+// activation stages and four code / scale stages: about 64 KB of LDS at
+// 4-bit, so two blocks share a CU.
 #ifndef QP_MOE_GEMM_NA
 #define QP_MOE_GEMM_NA 3
 #endif
 #ifndef QP_MOE_GEMM_NC
 #define QP_MOE_GEMM_NC 4
 #endif
-constexpr int kMoeGemmBN = QP_MOE_GEMM_BN;
+constexpr int kMoeGemmBN = 256;
 constexpr int kMoeGemmThreads = 256;
 
 template <int BITS, int DT, int NMAT, int BM>
@@ -118,7 +116,7 @@ hipError_t run_gemm_tiles(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     constexpr int LDS = gemm::lds_bytes<BITS, BM, BN, NT, NA, NC>();
     static_assert(LDS <= 160 * 1024, "LDS budget");
     const void* kern = reinterpret_cast<const void*>(
-        &gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, NMAT, true, NA, NC>);
+        &gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, 1, NMAT, true, NA, NC>);
     static bool attr_set = false; // per instantiation; set before its first launch
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
@@ -151,7 +149,7 @@ hipError_t run_gemm_tiles(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     g.outer_b = (uint32_t)(a.a_outer * 2);
     g.inner_b = (uint32_t)(a.a_inner * 2);
     const int64_t blocks = (r.max_tiles * g.tiles_n + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, NMAT, true, NA, NC>),
+    hipLaunchKernelGGL((gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, 1, NMAT, true, NA, NC>),
                        dim3((unsigned)blocks), dim3(NT), LDS, st, g);
     return hipGetLastError();
 }

@@ -11,18 +11,22 @@ namespace qp {
 
 namespace {
 
-// Pipeline depths: two activation stages, three code / scale stages (codes
-// and scales get two whole steps to arrive).
-constexpr int kStagesA = 2, kStagesC = 3;
+// Pipeline depths: four code / scale stages (codes and scales get two whole
+// steps to arrive), three activation stages where they fit the LDS, else two.
+template <int BITS, int BM, int BN, int NT>
+constexpr int stages_a()
+{
+    return gemm::lds_bytes<BITS, BM, BN, NT, 3, 4>() <= 160 * 1024 ? 3 : 2;
+}
 
 template <int BITS, int DT, int BM, int BN, int NT>
 hipError_t run_gemm(const GemvArgs& a, hipStream_t st)
 {
-    constexpr int NA = kStagesA, NC = kStagesC;
+    constexpr int NA = stages_a<BITS, BM, BN, NT>(), NC = 4;
     constexpr int LDS = gemm::lds_bytes<BITS, BM, BN, NT, NA, NC>();
     static_assert(LDS <= 160 * 1024, "LDS budget");
     const void* kern = reinterpret_cast<const void*>(
-        &gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, 1, false, NA, NC>);
+        &gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, 2, 1, false, NA, NC>);
     static bool attr_set = false; // per instantiation; set before its first launch
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
@@ -46,7 +50,7 @@ hipError_t run_gemm(const GemvArgs& a, hipStream_t st)
     g.tiles_n = (int)((a.N + BN - 1) / BN);
     g.tiles = (int)((a.M + BM - 1) / BM) * g.tiles_n;
     g.per_xcd = (g.tiles + 7) / 8;
-    hipLaunchKernelGGL((gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, 1, false, NA, NC>),
+    hipLaunchKernelGGL((gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, 2, 1, false, NA, NC>),
                        dim3(g.per_xcd * 8), dim3(NT), LDS, st, g);
     return hipGetLastError();
 }
@@ -55,15 +59,14 @@ template <int DT>
 hipError_t run_gemm_dt(const GemvArgs& a, hipStream_t st)
 {
     // Wide tiles (eight waves, two per SIMD) when there are enough of them to
-    // fill the 256 CUs and their three code stages fit the LDS (up to 4-bit
-    // codes); otherwise 256 x 128 tiles with four waves.
+    // fill the 256 CUs; otherwise 256 x 128 tiles with four waves.
     const bool wide = ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 384;
     switch (a.bits) {
     case 2: return wide ? run_gemm<2, DT, 256, 256, 512>(a, st) : run_gemm<2, DT, 256, 128, 256>(a, st);
     case 3: return wide ? run_gemm<3, DT, 256, 256, 512>(a, st) : run_gemm<3, DT, 256, 128, 256>(a, st);
     case 4: return wide ? run_gemm<4, DT, 256, 256, 512>(a, st) : run_gemm<4, DT, 256, 128, 256>(a, st);
-    case 6: return run_gemm<6, DT, 256, 128, 256>(a, st);
-    case 8: return run_gemm<8, DT, 256, 128, 256>(a, st);
+    case 6: return wide ? run_gemm<6, DT, 256, 256, 512>(a, st) : run_gemm<6, DT, 256, 128, 256>(a, st);
+    case 8: return wide ? run_gemm<8, DT, 256, 256, 512>(a, st) : run_gemm<8, DT, 256, 128, 256>(a, st);
     }
     return hipErrorInvalidValue;
 }
