@@ -200,8 +200,12 @@ struct GemvKernelArgs {
     const void* x;           // activations
     int64_t top_k, outer, inner; // pair p's row: x + (p/top_k)*outer + (p%top_k)*inner
     const int32_t* perm;     // pair list (nullptr: identity)
-    const TileDesc* tiles;   // tiles (nullptr: one tile of pairs 0..M-1, expert 0)
+    const TileDesc* tiles;   // tiles (nullptr: see `ids`)
     const int32_t* n_tiles;  // device tile count (with `tiles`)
+    const int32_t* ids;      // without `tiles`: tile t is pair t alone, of expert ids[t]
+                             // (ids outside [0, E) skip their pair); both null: one
+                             // tile of pairs 0..M-1, expert 0
+    int n_pairs, n_experts;  // with `ids`
     int M;                   // pairs of the single tile when tiles == nullptr
     const uint32_t* wq[2];   // [E, R, K*bits/32]
     const void* scales[2];   // [E, R, K/gs]
@@ -212,6 +216,34 @@ struct GemvKernelArgs {
     void* out;               // [pairs, R]
     uint32_t out_bytes;      // size of `out` in bytes (< 2^31)
 };
+
+// Tiles of a launch and tile t's expert, first pair slot and pair count;
+// false when tile t has nothing to compute (a pair with an invalid id).
+__device__ __forceinline__ int gemv_num_tiles(const GemvKernelArgs& a)
+{
+    return a.tiles != nullptr ? *a.n_tiles : a.ids != nullptr ? a.n_pairs : 1;
+}
+__device__ __forceinline__ bool gemv_tile(const GemvKernelArgs& a, int tile, int& expert,
+                                          int& start, int& count)
+{
+    if (a.tiles != nullptr) {
+        const TileDesc d = a.tiles[tile];
+        expert = d.expert;
+        start = d.start;
+        count = d.count;
+        return true;
+    }
+    if (a.ids != nullptr) {
+        expert = a.ids[tile];
+        start = tile;
+        count = 1;
+        return expert >= 0 && expert < a.n_experts;
+    }
+    expert = 0;
+    start = 0;
+    count = a.M;
+    return true;
+}
 
 // Buffer resource over `bytes` bytes at `p` (raw, untyped). Loads past the end
 // return zeros and stores past the end are dropped, which is what lets the
@@ -352,15 +384,11 @@ __global__ __launch_bounds__(MAXT) void qgemv_stream_kernel(GemvKernelArgs a)
         sboff[g] = (uint32_t)(((kl * U + g * UPG) * 32) / a.gs) * SB;
     const St* xs = static_cast<const St*>(a.x);
 
-    const int ntiles = a.tiles != nullptr ? *a.n_tiles : 1;
+    const int ntiles = gemv_num_tiles(a);
     for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
-        int expert = 0, start = 0, count = a.M;
-        if (a.tiles != nullptr) {
-            const TileDesc d = a.tiles[tile];
-            expert = d.expert;
-            start = d.start;
-            count = d.count;
-        }
+        int expert, start, count;
+        if (!gemv_tile(a, tile, expert, start, count))
+            continue;   // uniform over the block
         int64_t pair[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -556,15 +584,11 @@ __global__ __launch_bounds__(256) void qgemv_generic_kernel(GemvKernelArgs a)
 {
     using E = Elem<DT>;
     using St = typename E::storage;
-    const int ntiles = a.tiles != nullptr ? *a.n_tiles : 1;
+    const int ntiles = gemv_num_tiles(a);
     for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
-    int expert = 0, start = 0, count = a.M;
-    if (a.tiles != nullptr) {
-        const TileDesc d = a.tiles[tile];
-        expert = d.expert;
-        start = d.start;
-        count = d.count;
-    }
+    int expert, start, count;
+    if (!gemv_tile(a, tile, expert, start, count))
+        continue;   // uniform over the block
     const int lane = threadIdx.x & 63;
     const int64_t K = a.K, R = a.R;
     const int64_t units = K / 32, words_row = K * BITS / 32, groups_row = K / a.gs;

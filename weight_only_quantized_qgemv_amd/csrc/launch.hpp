@@ -67,7 +67,7 @@ size_t moe_workspace_bytes(int64_t n_pairs, int64_t num_experts);
 // Routing (moe.hip) and the per-(bits, fused) compute entry points
 // (moe_compute.hip, one translation unit each).
 struct MoeRouting {
-    const int32_t* n_tiles; // device tile count
+    const int32_t* n_tiles; // device tile count (null: pair t is tile t, see moe.hip)
     const int32_t* perm;    // pair indices in expert order
     const void* tiles;      // TileDesc list
     int mt;                 // tile height

@@ -132,15 +132,11 @@ __global__ __launch_bounds__(THREADS) void qgemv_mfma_kernel(GemvKernelArgs a, i
     const St* xs = static_cast<const St*>(a.x);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out, a.out_bytes);
 
-    const int ntiles = a.tiles != nullptr ? *a.n_tiles : 1;
+    const int ntiles = gemv_num_tiles(a);
     for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
-        int expert = 0, start = 0, count = a.M;
-        if (a.tiles != nullptr) {
-            const TileDesc d = a.tiles[tile];
-            expert = d.expert;
-            start = d.start;
-            count = d.count;
-        }
+        int expert, start, count;
+        if (!gemv_tile(a, tile, expert, start, count))
+            continue;   // uniform over the block
         const int rows = count < 16 * NB ? count : 16 * NB;
         __amdgpu_buffer_rsrc_t rw[NMAT], rs[NMAT], rbias[NMAT];
 #pragma unroll

@@ -9,10 +9,13 @@
 //  1. routing: one block counts pairs per expert (LDS atomics), scans the
 //     counts, writes a tile list (each tile: up to MT pairs of one expert) and
 //     scatters the pair indices into expert order, all in the workspace;
-//  2. compute: the streaming GEMV of gemv_core.hpp over the tile list; blocks
-//     past the device-written tile count exit at once. Each tile streams its
-//     expert's weights once, so an expert's weights are read once per launch
-//     when its pairs fit one tile.
+//  2. compute: over the tile list, one of the routed tile GEMM
+//     (gemm_core.hpp), the skinny matrix-core kernel (mfma_gemv.hpp) or the
+//     streaming GEMV (gemv_core.hpp); blocks past the device-written tile
+//     count exit at once. Each tile streams its expert's weights once, so an
+//     expert's weights are read once per launch when its pairs fit one tile.
+// With at most one pair per expert on average (tiles of one pair), the
+// routing launch is skipped: the compute launch takes pair t as tile t.
 // Each pair's accumulation order does not depend on its slot in a tile, so the
 // (unordered) scatter cannot change any output value.
 #include "gemv_core.hpp"
@@ -44,89 +47,100 @@ WsLayout ws_layout(int64_t P, int64_t E)
 
 } // namespace
 
-// Exclusive scan of one value per thread over a block of ROUTE_THREADS.
-__device__ int block_exclusive_scan(int v, int* s_tmp, int* total)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off, 64);
-        if (lane >= off)
-            incl += t;
-    }
-    if (lane == 63)
-        s_tmp[wave] = incl;
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int w = 0; w < ROUTE_THREADS / 64; ++w) {
-            const int t = s_tmp[w];
-            s_tmp[w] = run;
-            run += t;
-        }
-        s_tmp[ROUTE_THREADS / 64] = run;
-    }
-    __syncthreads();
-    const int excl = incl - v + s_tmp[wave];
-    *total = s_tmp[ROUTE_THREADS / 64];
-    __syncthreads();
-    return excl;
-}
-
 // hdr[0] = number of tiles, hdr[1] = number of pairs with an invalid id.
+// One block: the first ids are loaded before anything else (their latency
+// overlaps the clearing of the counts), the per-expert pair and tile counts
+// are scanned by the first wave alone (each lane owns a contiguous run of
+// experts; shuffles, no block barriers), so the block synchronises three
+// times in all.
 __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
     const int32_t* __restrict__ ids, int P, int E, int MT, int32_t* __restrict__ hdr,
     int32_t* __restrict__ perm, TileDesc* __restrict__ tiles)
 {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_cur[kMaxExperts];
-    __shared__ int s_tmp[ROUTE_THREADS / 64 + 1];
     __shared__ int s_invalid;
+    constexpr int PRE = 4;   // ids per thread loaded up front
     const int tid = threadIdx.x;
+    int pre[PRE];
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) {
+        const int p = tid + i * ROUTE_THREADS;
+        pre[i] = p < P ? ids[p] : -1;
+    }
     for (int e = tid; e < E; e += ROUTE_THREADS)
         s_cnt[e] = 0;
     if (tid == 0)
         s_invalid = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += ROUTE_THREADS) {
+    int invalid = 0;
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) {
+        const int e = pre[i];
+        if (e >= 0 && e < E)
+            atomicAdd(&s_cnt[e], 1);
+        else if (tid + i * ROUTE_THREADS < P)
+            ++invalid;
+    }
+    for (int p = tid + PRE * ROUTE_THREADS; p < P; p += ROUTE_THREADS) {
         const int e = ids[p];
         if (e >= 0 && e < E)
             atomicAdd(&s_cnt[e], 1);
         else
-            atomicAdd(&s_invalid, 1);
+            ++invalid;
     }
+    if (invalid)
+        atomicAdd(&s_invalid, invalid);
     __syncthreads();
 
-    // Each thread owns a contiguous run of experts; scan pair and tile counts.
-    const int ept = (E + ROUTE_THREADS - 1) / ROUTE_THREADS;
-    const int e0 = tid * ept;
-    int my_pairs = 0, my_tiles = 0;
-    for (int e = e0; e < e0 + ept && e < E; ++e) {
-        my_pairs += s_cnt[e];
-        my_tiles += (s_cnt[e] + MT - 1) / MT;
-    }
-    int tot_pairs, tot_tiles;
-    int pair_off = block_exclusive_scan(my_pairs, s_tmp, &tot_pairs);
-    int tile_off = block_exclusive_scan(my_tiles, s_tmp, &tot_tiles);
-    for (int e = e0; e < e0 + ept && e < E; ++e) {
-        const int c = s_cnt[e];
-        for (int j = 0; j * MT < c; ++j) {
-            TileDesc d;
-            d.expert = e;
-            d.start = pair_off + j * MT;
-            d.count = (c - j * MT) < MT ? (c - j * MT) : MT;
-            tiles[tile_off++] = d;
+    // Wave 0: lane l owns experts [l * ept, (l + 1) * ept); exclusive scans
+    // of the pair and tile counts across the lanes, then the tile list and
+    // the scatter cursors.
+    if (tid < 64) {
+        const int lane = tid;
+        const int ept = (E + 63) / 64;
+        const int e0 = lane * ept;
+        int my_pairs = 0, my_tiles = 0;
+        for (int e = e0; e < e0 + ept && e < E; ++e) {
+            my_pairs += s_cnt[e];
+            my_tiles += (s_cnt[e] + MT - 1) / MT;
         }
-        s_cur[e] = pair_off;
-        pair_off += c;
-    }
-    if (tid == 0) {
-        hdr[0] = tot_tiles;
-        hdr[1] = s_invalid;
+        int inc_p = my_pairs, inc_t = my_tiles;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int tp = __shfl_up(inc_p, off, 64);
+            const int tt = __shfl_up(inc_t, off, 64);
+            if (lane >= off) {
+                inc_p += tp;
+                inc_t += tt;
+            }
+        }
+        int pair_off = inc_p - my_pairs, tile_off = inc_t - my_tiles;
+        for (int e = e0; e < e0 + ept && e < E; ++e) {
+            const int c = s_cnt[e];
+            for (int j = 0; j * MT < c; ++j) {
+                TileDesc d;
+                d.expert = e;
+                d.start = pair_off + j * MT;
+                d.count = (c - j * MT) < MT ? (c - j * MT) : MT;
+                tiles[tile_off++] = d;
+            }
+            s_cur[e] = pair_off;
+            pair_off += c;
+        }
+        if (lane == 63) {
+            hdr[0] = inc_t;
+            hdr[1] = s_invalid;
+        }
     }
     __syncthreads();
-    for (int p = tid; p < P; p += ROUTE_THREADS) {
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) {
+        const int e = pre[i];
+        if (e >= 0 && e < E)
+            perm[atomicAdd(&s_cur[e], 1)] = tid + i * ROUTE_THREADS;
+    }
+    for (int p = tid + PRE * ROUTE_THREADS; p < P; p += ROUTE_THREADS) {
         const int e = ids[p];
         if (e >= 0 && e < E)
             perm[atomicAdd(&s_cur[e], 1)] = p;
@@ -219,7 +233,13 @@ int moe_gemm_bm(const MoeArgs& a)
     const int64_t P = a.n_tokens * a.top_k;
     // The routed GEMM dequantizes each expert's weights once per 64-pair tile;
     // it takes over from the GEMV tiles once experts see enough pairs each.
-    if (P < kMoeGemmMinPairsPerExpert * a.E)
+    // The skinny kernel refills its activation table for every 128 weight
+    // rows, which costs relatively more at short K: for the plain form with
+    // K <= 1024 (the down projection) the routed GEMM wins from 2 pairs per
+    // expert (measured 53 vs 60 us at 4, 47 vs 54 us at 2, [128, 2048, 768]).
+    const int64_t min_pairs =
+        (!a.fused_silu && a.n_cols <= 1024) ? 2 : kMoeGemmMinPairsPerExpert;
+    if (P < min_pairs * a.E)
         return 0;
     const int64_t es = 2;
     const bool vec = reinterpret_cast<uintptr_t>(a.a) % 16 == 0 && (a.a_outer * es) % 16 == 0 &&
@@ -244,9 +264,16 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
     const int bm = moe_gemm_bm(a);
     const int nb = bm > 0 ? 0 : moe_mfma_nb(a);
     const int mt = bm > 0 ? bm : nb > 0 ? 16 * nb : moe_tile_height(P, a.E, a.bits, a.dt);
-    hipError_t e = launch_moe_route(a, mt, &r, st);
-    if (e != hipSuccess)
-        return e;
+    if (mt == 1) {
+        // One pair per tile: tile t is pair t itself, read straight from ids by
+        // the compute launch, and the routing launch is skipped.
+        r.mt = 1;
+        r.max_tiles = P;
+    } else {
+        hipError_t e = launch_moe_route(a, mt, &r, st);
+        if (e != hipSuccess)
+            return e;
+    }
     r.nb = nb;
     r.gemm_bm = bm;
     const bool f = a.fused_silu;

@@ -165,6 +165,11 @@ hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     k.perm = r.perm;
     k.tiles = static_cast<const TileDesc*>(r.tiles);
     k.n_tiles = r.n_tiles;
+    if (r.tiles == nullptr) {   // no routing launch: pair t is tile t
+        k.ids = a.ids;
+        k.n_pairs = (int)(a.n_tokens * a.top_k);
+        k.n_experts = (int)a.E;
+    }
     k.M = 0;
     for (int t = 0; t < 2; ++t) {
         const int src = NMAT == 2 ? t : 0;
