@@ -263,3 +263,29 @@ def test_moe_routed_gemm_pair_order_does_not_change_values():
     assert torch.equal(out_p, out[torch.from_numpy(perm).to(dev())])
     ref, S = qref.moe(a_s, BF16, ids, P, 1, C, 0, *h, BF16, E, R, C, bits, gs)
     assert_within(out, ref, S, BF16, "routed")
+
+
+def test_moe_routed_scales_not_dword_aligned():
+    """64 pairs per expert (the routed GEMM's range) with the stack's scales and
+    biases at an address that is 2 mod 4: the call takes the matrix-core GEMV
+    tiles instead, with the same results."""
+    E, R, C, bits, gs = 4, 136, 256, 4, 64
+    h, d = stack(E, R, C, bits, gs, BF16, 181)
+    wq, s, b = d
+    buf_s = torch.empty(s.numel() + 1, dtype=s.dtype, device=s.device)
+    buf_b = torch.empty(b.numel() + 1, dtype=b.dtype, device=b.device)
+    s2 = buf_s[1:].view(s.shape)
+    b2 = buf_b[1:].view(b.shape)
+    s2.copy_(s)
+    b2.copy_(b)
+    assert s2.data_ptr() % 4 == 2
+    P = 256
+    ids = synth.random_ints((P,), 0, E - 1, 182).astype(np.int32)
+    a_s, a_d = activations((P, C), BF16, 183)
+    ids_d = torch.from_numpy(ids).to(dev())
+    out = qp.qgemv_moe_id(a_d, ids_d, P, 1, C, 0, wq, s2, b2, bits, gs)
+    out_al = qp.qgemv_moe_id(a_d, ids_d, P, 1, C, 0, wq, s, b, bits, gs)
+    torch.cuda.synchronize()
+    ref, S = qref.moe(a_s, BF16, ids, P, 1, C, 0, *h, BF16, E, R, C, bits, gs)
+    assert_within(out, ref, S, BF16, "scales 2 mod 4")
+    assert_within(out_al, ref, S, BF16, "scales aligned")

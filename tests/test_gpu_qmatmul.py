@@ -256,3 +256,32 @@ def test_qmatmul_dtype_mismatch_raises():
     _, (gq, gs_, gb) = quantize_both(w, 4, 64, BF16)
     with pytest.raises(qp.QpackError, match="DTYPE_MISMATCH"):
         qp.qmatmul(torch.zeros((1, 64), dtype=torch.float16, device=dev()), gq, gs_, gb, 4, 64)
+
+
+def shifted_copy(t: torch.Tensor) -> torch.Tensor:
+    """A contiguous copy of t placed one element into a fresh buffer (for
+    16-bit elements: an address that is 2 mod 4)."""
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("m", [40, 300])
+def test_qmatmul_prefill_scales_not_dword_aligned(m):
+    """Scales and biases at an address that is 2 mod 4: the tile GEMM reads
+    them as aligned dwords, so such a call takes the 16-row skinny launches;
+    both must match the oracle."""
+    n, k, bits, gs, dt = 150, 256, 4, 64, BF16
+    log(f"prefill unaligned scales m={m}")
+    w = synth.normal_f32((n, k), 0.02, 3700 + m)
+    (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, bits, gs, dt)
+    s2, b2 = shifted_copy(gs_), shifted_copy(gb)
+    assert s2.data_ptr() % 4 == 2 and b2.data_ptr() % 4 == 2
+    xs, xt = activations((m, k), dt, 3800 + m)
+    y_shift = qp.qmatmul(xt, gq, s2, b2, bits, gs)
+    y_al = qp.qmatmul(xt, gq, gs_, gb, bits, gs)
+    torch.cuda.synchronize()
+    y_ref, S = qref.qmatmul(xs, dt, rq, rs, rb, dt, k, bits, gs)
+    assert_within(y_shift, y_ref, S, dt, "scales 2 mod 4")
+    assert_within(y_al, y_ref, S, dt, "scales aligned")

@@ -257,7 +257,10 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         return rsrc(reinterpret_cast<const char*>(ga.wq[t]) + (size_t)expert * wmat_bytes,
                     (uint32_t)wmat_bytes);
     };
-    // Scales / biases: the whole array (all experts), read as aligned dwords.
+    // Scales / biases: the whole array (all experts), read as aligned dwords
+    // (the array is 4-byte aligned; with an odd element count the last dword
+    // reaches 2 bytes past its end, inside the same aligned word and so the
+    // same page, and those bytes are never used).
     auto rsb_of = [&](int t, bool bias) {
         return rsrc(bias ? ga.biases[t] : ga.scales[t], ga.sb_bytes);
     };
