@@ -92,9 +92,12 @@ qp_status qpack_quantize(const float* w, int64_t n, int64_t k, int32_t bits,
  *   scales, biases  device, sb_dtype [n, k/group_size]; sb_dtype must equal
  *           x_dtype (QP_ERR_DTYPE_MISMATCH otherwise)
  *   y       device, x_dtype [m, n] (output)
- * fp32 accumulation. m <= 16 runs the decode GEMV (VALU, weights streamed
- * once); m > 16 with 16-bit activations runs the MFMA prefill GEMM. k == 0
- * writes zeros; m == 0 or n == 0 is a no-op.
+ * fp32 accumulation. m <= 16 runs the decode GEMV, weights streamed once
+ * (dot products for m <= 2 and fp32; from 3 rows of 16-bit activations the
+ * codes feed the matrix cores). m > 16 with 16-bit activations runs the MFMA
+ * tile GEMM when k is a multiple of 64 and scales / biases are 4-byte
+ * aligned, else the matrix-core GEMV once per 16 rows. k == 0 writes zeros;
+ * m == 0 or n == 0 is a no-op.
  */
 qp_status qmatmul(const void* x, qp_dtype x_dtype, int64_t m, int64_t k,
                   const uint32_t* wq, const void* scales, const void* biases,
@@ -122,8 +125,10 @@ size_t qgemv_moe_workspace_bytes(int64_t n_pairs, int64_t num_experts);
  * The single-token form of the page is n_tokens = 1, top_k = n_selected,
  * a_outer_stride = 0, a_inner_stride = src1_stride; its offset form is
  * pointer arithmetic on `a` and `ids`. Pairs are sorted by expert on the
- * device, so each expert's weights are streamed once per launch. A pair whose
- * id is out of range is skipped (its output row is left unwritten).
+ * device and grouped into tiles of one expert, so each expert's weights are
+ * streamed once per tile (with at most one pair per expert on average every
+ * pair is its own tile and the sort is skipped). A pair whose id is out of
+ * range is skipped (its output row is left unwritten).
  */
 qp_status qgemv_moe_id(const void* a, qp_dtype a_dtype, const int32_t* ids,
                        int64_t n_tokens, int64_t top_k, int64_t a_outer_stride,
