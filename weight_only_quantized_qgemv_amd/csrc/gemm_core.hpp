@@ -20,7 +20,8 @@
 //    0-31) with k = 32 + 8 kk + i (lanes 32-63), and the activation fragments
 //    are read in the same order;
 //  - NA activation stages and NC code / scale stages: the DMA of later steps
-//    stays in flight across the per-step barrier;
+//    stays in flight across the per-step barrier, and each step's first
+//    fragments (activations and B) are prepared during the step before;
 //  - LDS rows of activations are 128 bytes (64 x 16-bit); 16-byte chunks are
 //    XOR-swizzled by (row / 2) % 8, and the 16-byte code chunks of a row by a
 //    row-dependent XOR, so the rows one phase of a fragment read touches hit
@@ -165,10 +166,13 @@ template <int BITS> __device__ __forceinline__ int code_swz(int r)
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
 
 // Pipeline: step kt issues the activation DMA of step kt + NA - 1 and the code
-// and scale DMA of step kt + NC - 1, then runs the MFMAs of step kt; at its
-// end it waits only for what step kt + 1 needs (the activations and codes /
-// scales of kt + 1), so code loads get NC - 2 whole steps to arrive and the
-// DMA of the newest steps stays in flight across the barrier.
+// and scale DMA of step kt + NC - 1, then runs the MFMAs of step kt; during
+// its last two sub-steps it reads the codes, scales and first activation
+// fragments of step kt + 1 and builds that step's first B fragments, so the
+// next step's MFMAs can start right after the barrier. At its end it waits
+// only for what step kt + 1 reads early (the activations and codes / scales
+// of kt + 2): activation loads get one step to arrive and code loads NC - 2,
+// and the newest code DMA stays in flight across the barrier.
 template <int BITS, int DT, int BM, int BN, int THREADS, int WMW, int NMAT, bool ROUTED, int NA,
           int NC>
 __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
@@ -200,13 +204,13 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     constexpr int SB_INSTR = SbStage<BN>::INSTR / WAVES;   // per wave
     static_assert(SB_INSTR * WAVES == SbStage<BN>::INSTR, "scale DMA split over waves");
     // Vector-memory operations a wave issues per step, and how many of them
-    // may still be in flight when a step ends. Step kt needs the activations
-    // and codes / scales of step kt + 1: the first DMA of step kt + 2 - NA and
-    // the last DMA of step kt + 2 - NC; what was issued after the later of the
-    // two may be in flight.
+    // may still be in flight when a step ends. Step kt + 1 reads the
+    // activations and codes / scales of step kt + 2: the first DMA of step
+    // kt + 3 - NA (this step, for NA = 3) and the last DMA of the earlier step
+    // kt + 3 - NC; what was issued after the activations may be in flight.
     constexpr int STEP_OPS = A_INSTR + C_INSTR + SB_INSTR;
-    constexpr int IN_FLIGHT = NC > NA ? (C_INSTR + SB_INSTR) + (NA - 2) * STEP_OPS
-                                      : (NC - 2) * STEP_OPS;
+    static_assert(NA >= 3 && NC > NA, "prefetch pipeline depth");
+    constexpr int IN_FLIGHT = (C_INSTR + SB_INSTR) + (NA - 3) * STEP_OPS;
     static_assert(IN_FLIGHT < 64, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     char* const a_st = lds;
@@ -448,47 +452,53 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     }
     step_barrier(std::integral_constant<int, IN_FLIGHT>{});
 
+    frag_t af[2][FM], bfr[2][FN];
+    auto load_afrags = [&](int stage, int kk, frag_t (&fa)[FM]) {
+        const char* abase = a_st + stage * A_STAGE;
+        const int chunk = kk + 4 * half;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            fa[i] = *reinterpret_cast<const frag_t*>(
+                abase + lds_off(wm * WM + i * 32 + (lane & 31), chunk));
+    };
+    load_units(0, 0);
+    load_afrags(0, 0, af[0]);
+    static_for<FN>([&](auto J) { bfr[0][J] = make_bfrag(J, std::integral_constant<int, 0>{}); });
+
     int a_cur = 0, c_cur = 0;          // A and C stages of step kt
     for (int kt = 0; kt < KT; ++kt) {
-        // In flight during this step: activations of kt + NA - 1, codes and
-        // scales of kt + NC - 1 (reads past the last step are harmless:
-        // in-range bytes that are never used, or zeros).
         const int a_new = a_cur == 0 ? NA - 1 : a_cur - 1;
         const int c_new = c_cur == 0 ? NC - 1 : c_cur - 1;
+        const int a_nxt = a_cur + 1 == NA ? 0 : a_cur + 1;
+        const int c_nxt = c_cur + 1 == NC ? 0 : c_cur + 1;
         dma_a(kt + NA - 1, a_new);
         dma_c(kt + NC - 1, c_new);
-        load_units(kt, c_cur);
-        // MFMAs on A stage a_cur; fragments double-buffered across the four
-        // k16 sub-steps, B fragments of the next sub-step built during the
-        // current one's MFMAs.
-        const char* abase = a_st + a_cur * A_STAGE;
-        frag_t af[2][FM], bfr[2][FN];
-        auto load_afrags = [&](int kk, frag_t (&fa)[FM]) {
-            const int chunk = kk + 4 * half;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[i] = *reinterpret_cast<const frag_t*>(
-                    abase + lds_off(wm * WM + i * 32 + (lane & 31), chunk));
-        };
-        load_afrags(0, af[0]);
-        static_for<FN>([&](auto J) { bfr[0][J] = make_bfrag(J, std::integral_constant<int, 0>{}); });
         static_for<BK / 16>([&](auto KK) {
             constexpr int kk = decltype(KK)::value;
             if constexpr (kk + 1 < BK / 16)
-                load_afrags(kk + 1, af[(kk + 1) & 1]);
+                load_afrags(a_cur, kk + 1, af[(kk + 1) & 1]);
+            else
+                load_afrags(a_nxt, 0, af[0]);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = T::mfma(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
-            if constexpr (kk + 1 < BK / 16)
+            if constexpr (kk + 1 < BK / 16) {
                 static_for<FN>([&](auto J) {
                     bfr[(kk + 1) & 1][J] = make_bfrag(J, std::integral_constant<int, kk + 1>{});
                 });
+                if constexpr (kk + 2 == BK / 16)
+                    load_units(kt + 1, c_nxt);
+            } else {
+                static_for<FN>([&](auto J) {
+                    bfr[0][J] = make_bfrag(J, std::integral_constant<int, 0>{});
+                });
+            }
         });
         step_barrier(std::integral_constant<int, IN_FLIGHT>{});
-        a_cur = a_cur + 1 == NA ? 0 : a_cur + 1;
-        c_cur = c_cur + 1 == NC ? 0 : c_cur + 1;
+        a_cur = a_nxt;
+        c_cur = c_nxt;
     }
     // No DMA may still be writing this block's LDS when the block ends.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));

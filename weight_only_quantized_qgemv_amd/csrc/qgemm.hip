@@ -11,18 +11,11 @@ namespace qp {
 
 namespace {
 
-// Pipeline depths: four code / scale stages (codes and scales get two whole
-// steps to arrive), three activation stages where they fit the LDS, else two.
-template <int BITS, int BM, int BN, int NT>
-constexpr int stages_a()
-{
-    return gemm::lds_bytes<BITS, BM, BN, NT, 3, 4>() <= 160 * 1024 ? 3 : 2;
-}
-
+// Pipeline depths: three activation stages and four code / scale stages.
 template <int BITS, int DT, int BM, int BN, int NT>
 hipError_t run_gemm(const GemvArgs& a, hipStream_t st)
 {
-    constexpr int NA = stages_a<BITS, BM, BN, NT>(), NC = 4;
+    constexpr int NA = 3, NC = 4;
     constexpr int LDS = gemm::lds_bytes<BITS, BM, BN, NT, NA, NC>();
     static_assert(LDS <= 160 * 1024, "LDS budget");
     const void* kern = reinterpret_cast<const void*>(
@@ -59,14 +52,15 @@ template <int DT>
 hipError_t run_gemm_dt(const GemvArgs& a, hipStream_t st)
 {
     // Wide tiles (eight waves, two per SIMD) when there are enough of them to
-    // fill the 256 CUs; otherwise 256 x 128 tiles with four waves.
+    // fill the 256 CUs and their stages fit the LDS (up to 4-bit codes);
+    // otherwise 256 x 128 tiles with four waves.
     const bool wide = ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 384;
     switch (a.bits) {
     case 2: return wide ? run_gemm<2, DT, 256, 256, 512>(a, st) : run_gemm<2, DT, 256, 128, 256>(a, st);
     case 3: return wide ? run_gemm<3, DT, 256, 256, 512>(a, st) : run_gemm<3, DT, 256, 128, 256>(a, st);
     case 4: return wide ? run_gemm<4, DT, 256, 256, 512>(a, st) : run_gemm<4, DT, 256, 128, 256>(a, st);
-    case 6: return wide ? run_gemm<6, DT, 256, 256, 512>(a, st) : run_gemm<6, DT, 256, 128, 256>(a, st);
-    case 8: return wide ? run_gemm<8, DT, 256, 256, 512>(a, st) : run_gemm<8, DT, 256, 128, 256>(a, st);
+    case 6: return run_gemm<6, DT, 256, 128, 256>(a, st);
+    case 8: return run_gemm<8, DT, 256, 128, 256>(a, st);
     }
     return hipErrorInvalidValue;
 }
