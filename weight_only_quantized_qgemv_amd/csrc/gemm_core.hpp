@@ -192,8 +192,7 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     static_assert(NMAT == 1 || (BNO % 64 == 0 && (BNO * CL::CPR) % 64 == 0),
                   "each DMA instruction within one matrix");
     static_assert(NMAT == 1 || ROUTED, "the fused form is routed");
-    static_assert(NA >= 2 && NA <= 3 && NC >= 3, "pipeline depth");
-    constexpr int A_STAGE = BM * ROW_BYTES;
+        constexpr int A_STAGE = BM * ROW_BYTES;
     constexpr int A_INSTR = A_STAGE / 1024 / WAVES;        // 1 KB DMA instructions per wave
     static_assert(A_INSTR * 1024 * WAVES == A_STAGE, "activation stage in whole DMA blocks");
     constexpr int C_INSTR = CodeStage<BITS, BN, WAVES>::INSTR;   // per wave (64 chunks each)
@@ -206,11 +205,12 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     // Vector-memory operations a wave issues per step, and how many of them
     // may still be in flight when a step ends. Step kt + 1 reads the
     // activations and codes / scales of step kt + 2: the first DMA of step
-    // kt + 3 - NA (this step, for NA = 3) and the last DMA of the earlier step
-    // kt + 3 - NC; what was issued after the activations may be in flight.
+    // kt + 3 - NA and the last DMA of step kt + 3 - NC; what was issued after
+    // the later of the two may be in flight.
     constexpr int STEP_OPS = A_INSTR + C_INSTR + SB_INSTR;
-    static_assert(NA >= 3 && NC > NA, "prefetch pipeline depth");
-    constexpr int IN_FLIGHT = (C_INSTR + SB_INSTR) + (NA - 3) * STEP_OPS;
+    static_assert(NA >= 3 && NC >= 4, "prefetch pipeline depth");
+    constexpr int IN_FLIGHT = NC > NA ? (C_INSTR + SB_INSTR) + (NA - 3) * STEP_OPS
+                                      : (NC - 3) * STEP_OPS;
     static_assert(IN_FLIGHT < 64, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     char* const a_st = lds;

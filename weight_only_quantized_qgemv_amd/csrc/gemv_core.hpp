@@ -215,6 +215,8 @@ struct GemvKernelArgs {
     int KL;                  // lanes per row
     void* out;               // [pairs, R]
     uint32_t out_bytes;      // size of `out` in bytes (< 2^31)
+    uint32_t x_bytes;        // bytes of activations reachable from `x` (< 2^31; read
+                             // by the matrix-core kernel's table DMA)
 };
 
 // Tiles of a launch and tile t's expert, first pair slot and pair count;

@@ -16,7 +16,7 @@
 //    rounded to the activation type, giving four 8-element A fragments; the
 //    weights are therefore rounded once to bf16/fp16, like the prefill GEMM;
 //  - v_mfma_f32_16x16x32 contracts them with B fragments from an LDS table of
-//    the tile's activation rows, stored fragment-major: B lane (m, g) of
+//    the tile's activation rows (filled by LDS DMA), stored fragment-major: B lane (m, g) of
 //    fragment i of quad j holds x[m][32 (4j + g) + 8 i .. + 7] (the k's of
 //    the A lane (r, g) fragment i, so both sides agree on the k order), and
 //    the 64 lanes of one fragment read one contiguous kilobyte;
@@ -129,7 +129,6 @@ __global__ __launch_bounds__(THREADS) void qgemv_mfma_kernel(GemvKernelArgs a, i
     const int units = (int)(a.K / 32);
     const int NGW = kpad / KS / a.gs;        // groups per wave's K range
     char* const sbw = red + (uint32_t)wave * (uint32_t)(NMAT * 16 * NGW * 4); // this wave's pairs
-    const St* xs = static_cast<const St*>(a.x);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out, a.out_bytes);
 
     const int ntiles = gemv_num_tiles(a);
@@ -200,56 +199,44 @@ __global__ __launch_bounds__(THREADS) void qgemv_mfma_kernel(GemvKernelArgs a, i
             }
         }
 
-        // Activation table (overlaps the first ring loads): for each column
-        // block, wave w fills the 4 KB quad blocks q = w, w + WAVES, ..., three
-        // at a time; lane (m, g) moves the 64 bytes of row 16 nb + m, unit
-        // 4 q + g, into fragments i = 0..3. Rows past the tile and units past K
-        // are zeros. Each lane resolves its rows' activation offsets once.
+        // Activation table (overlaps the first ring loads), filled by LDS DMA:
+        // the 1 KB fragment block (nb, q, i) is one DMA instruction whose lane
+        // (m, g) brings x[row 16 nb + m][32 (4 q + g) + 8 i .. + 7]. Rows past
+        // the tile and units past K read zeros (offsets past the end). Each
+        // lane resolves its rows' activation offsets once.
         {
-            int64_t xoff[NB];
+            const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+            uint32_t xb[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const int row = nb * 16 + r16;
-                xoff[nb] = -1;
+                xb[nb] = OOB;
                 if (row < rows) {
                     const uint32_t p = a.perm != nullptr ? (uint32_t)a.perm[start + row]
                                                          : (uint32_t)(start + row);
                     const uint32_t tk = (uint32_t)a.top_k;
-                    xoff[nb] = (int64_t)(p / tk) * a.outer + (int64_t)(p % tk) * a.inner;
+                    xb[nb] = ((p / tk) * (uint32_t)a.outer + (p % tk) * (uint32_t)a.inner) * SB;
                 }
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                for (int q0 = wave; q0 < NQ; q0 += 3 * WAVES) {
-                    u32x4_t v[3][4];
-                    static_for<3>([&](auto B) {
-                        const int q = q0 + (int)B * WAVES, unit = 4 * q + g4;
-                        const bool live = q < NQ && xoff[nb] >= 0 && unit < units;
-                        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
-                            xs + (live ? xoff[nb] + (int64_t)unit * 32 : 0));
+                for (int q = wave; q < NQ; q += WAVES) {
+                    const int unit = 4 * q + g4;
+                    const uint32_t src = (xb[nb] != OOB && unit < units)
+                        ? xb[nb] + (uint32_t)unit * 32u * SB : OOB;
+                    char* dst = table + ((uint32_t)nb * (uint32_t)NQ + (uint32_t)q) * 4096u;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const u32x4_t t = src[i];
-                            v[B][i] = live ? t : u32x4_t{0u, 0u, 0u, 0u};
-                        }
-                    });
-                    static_for<3>([&](auto B) {
-                        const int q = q0 + (int)B * WAVES;
-                        if (q < NQ) {
-                            char* dst = table + ((uint32_t)nb * (uint32_t)NQ + (uint32_t)q) * 4096u +
-                                        (uint32_t)lane * 16u;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                *reinterpret_cast<u32x4_t*>(dst + (uint32_t)i * 1024u) = v[B][i];
-                        }
-                    });
+                    for (int i = 0; i < 4; ++i)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rx, (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                            16, src == OOB ? OOB : src + (uint32_t)(i * 8 * SB), 0, 0, 0);
                 }
             }
         }
-        // All of this lane's loads have landed: the table loads were issued
-        // after the ring's, so this costs no ring overlap, and no load is left
-        // pending into the main loop (where it would make every later write
-        // of a reused register wait for all memory traffic).
+        // All of this lane's loads and DMA have landed: the table DMA was
+        // issued after the ring's loads, so this costs no ring overlap, and no
+        // load is left pending into the main loop (where it would make every
+        // later write of a reused register wait for all memory traffic).
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 

@@ -208,7 +208,9 @@ int moe_mfma_nb(const MoeArgs& a)
     const int64_t es = 2;
     const bool vec = reinterpret_cast<uintptr_t>(a.a) % 16 == 0 && (a.a_outer * es) % 16 == 0 &&
                      (a.a_inner * es) % 16 == 0;
-    const bool small = a.n_rows * (a.n_cols * a.bits / 8) < (int64_t(1) << 31) &&
+    const int64_t x_span = ((a.n_tokens - 1) * a.a_outer + (a.top_k - 1) * a.a_inner + a.n_cols) * es;
+    const bool small = x_span < (int64_t(1) << 31) &&
+                       a.n_rows * (a.n_cols * a.bits / 8) < (int64_t(1) << 31) &&
                        a.n_rows * (a.n_cols / a.gs) * es < (int64_t(1) << 31) &&
                        P * a.n_rows * es < (int64_t(1) << 31);
     if (!vec || !small)

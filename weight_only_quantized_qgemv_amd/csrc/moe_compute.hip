@@ -97,8 +97,8 @@ hipError_t run_mfma_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 // rows of each of its NMAT matrices, four waves side by side along the rows
 // (each weight fragment is built by one wave only); grid x covers every
 // (tile, row block) of the largest possible tile list, XCD by XCD. Three
-// activation stages and four code / scale stages: about 64 KB of LDS at
-// 4-bit, so two blocks share a CU.
+// activation stages and four code / scale stages: 64 KB of LDS at 4-bit, so
+// two blocks share a CU (four activation stages measured the same).
 #ifndef QP_MOE_GEMM_NA
 #define QP_MOE_GEMM_NA 3
 #endif
@@ -191,6 +191,8 @@ hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
                        a.n_rows * (a.n_cols / a.gs) * es < (int64_t(1) << 31) &&
                        P * a.n_rows * es < (int64_t(1) << 31);
     k.out_bytes = (uint32_t)(x_vec ? P * a.n_rows * es : 0);
+    const int64_t x_span = ((a.n_tokens - 1) * a.a_outer + (a.top_k - 1) * a.a_inner + a.n_cols) * es;
+    k.x_bytes = (uint32_t)(x_span < (int64_t(1) << 31) ? x_span : 0);
     if constexpr (DT == DT_F32) {
         return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
     } else {

@@ -47,6 +47,7 @@ GemvKernelArgs dense_args(const GemvArgs& a, int64_t m0, int mc, int elem_size, 
     k.KL = KL;
     k.out = static_cast<char*>(a.y) + m0 * a.N * elem_size;
     k.out_bytes = (uint32_t)(mc * a.N * elem_size);
+    k.x_bytes = (uint32_t)(mc * a.K * elem_size);
     return k;
 }
 
