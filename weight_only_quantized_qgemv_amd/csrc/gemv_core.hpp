@@ -261,9 +261,11 @@ constexpr uint32_t OOB = 0x80000000u;
 
 // Cache policy for weight codes read once per launch (sc0 | nt): the loads
 // skip the L1 and stream through the L2 without displacing reused lines
-// (activations, scales). Measured on the 4-bit 14336 x 4096 decode shape:
-// about 3% faster with one activation row (and with the matrix-core tiles),
-// about 5% slower with two, which keep the default policy.
+// (activations, scales). Taken where it measured faster: the one-row stream
+// at 2, 3, 4 and 6 bits (4-bit 14336 x 4096: 10.05 -> 9.84 us; 2-bit:
+// 10.1 -> 9.8 us; cross-word 4096 x 4096: 7.6 -> 7.1 us). The 8-bit one-row
+// stream (14.5 -> 20.1 us), two rows and the matrix-core tiles were slower
+// with it and keep the default policy.
 constexpr int kStreamPolicy = 3;
 
 template <int NW, int POLICY = 0>
@@ -454,7 +456,8 @@ __global__ __launch_bounds__(MAXT) void qgemv_stream_kernel(GemvKernelArgs a)
             const uint32_t r = (uint32_t)(p * RPW + sub);
 #pragma unroll
             for (int t = 0; t < NMAT; ++t) {
-                buffer_words<NW, MT == 1 ? kStreamPolicy : 0>(rw[t], r * row_bytes + lane_off, dw[t]);
+                buffer_words<NW, (MT == 1 && BITS != 8) ? kStreamPolicy : 0>(
+                    rw[t], r * row_bytes + lane_off, dw[t]);
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     ds[t][g] = buffer_elem<DT>(rs[t], r * groups_row * SB + sboff[g]);

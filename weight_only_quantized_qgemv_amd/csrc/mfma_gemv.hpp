@@ -163,7 +163,7 @@ __global__ __launch_bounds__(THREADS) void qgemv_mfma_kernel(GemvKernelArgs a, i
             const uint32_t woff = row_off + u * (uint32_t)(4 * NW);
 #pragma unroll
             for (int t = 0; t < NMAT; ++t)
-                buffer_words<NW, kStreamPolicy>(rw[t], woff, dw[t]);
+                buffer_words<NW>(rw[t], woff, dw[t]);
         };
         static_for<D>([&](auto J) { fetch(J < UQ ? (int)J : UQ - 1, w[J]); });
 
