@@ -171,8 +171,8 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // fragments of step kt + 1 and builds that step's first B fragments, so the
 // next step's MFMAs can start right after the barrier. At its end it waits
 // only for what step kt + 1 reads early (the activations and codes / scales
-// of kt + 2): activation loads get one step to arrive and code loads NC - 2,
-// and the newest code DMA stays in flight across the barrier.
+// of kt + 2): activation loads get NA - 2 steps to arrive and code loads
+// NC - 2, and the newest DMA stays in flight across the barrier.
 template <int BITS, int DT, int BM, int BN, int THREADS, int WMW, int NMAT, bool ROUTED, int NA,
           int NC>
 __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     static_assert(NMAT == 1 || (BNO % 64 == 0 && (BNO * CL::CPR) % 64 == 0),
                   "each DMA instruction within one matrix");
     static_assert(NMAT == 1 || ROUTED, "the fused form is routed");
-        constexpr int A_STAGE = BM * ROW_BYTES;
+    constexpr int A_STAGE = BM * ROW_BYTES;
     constexpr int A_INSTR = A_STAGE / 1024 / WAVES;        // 1 KB DMA instructions per wave
     static_assert(A_INSTR * 1024 * WAVES == A_STAGE, "activation stage in whole DMA blocks");
     constexpr int C_INSTR = CodeStage<BITS, BN, WAVES>::INSTR;   // per wave (64 chunks each)
