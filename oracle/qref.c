@@ -32,7 +32,9 @@
  *
  * Arithmetic: fp32 for quantize and dequantize (compiled with
  * -ffp-contract=off, so a*b+c is a multiply then an add), fp64 for every
- * product sum. Each output's sum runs sequentially in k order, so the OpenMP
+ * product sum. The dense weight in the scales' own type (the pages'
+ * `dequantize_impl`, which casts the codes to the scales' type) rounds the
+ * product and then the sum to that type, each exactly once. Each output's sum runs sequentially in k order, so the OpenMP
  * loops over outputs give the same bits at any thread count.
  */
 #include "qref.h"
@@ -76,15 +78,15 @@ struct fmt16 { int mant_bits, exp_bits, bias; };
 static const struct fmt16 FMT_BF16 = {7, 8, 127};
 static const struct fmt16 FMT_F16 = {10, 5, 15};
 
-static uint16_t encode_rne(float f, struct fmt16 F)
+/* x (an fp64 value) rounded to format F, nearest with ties to even. */
+static uint16_t encode_rne_d(double x, struct fmt16 F)
 {
-    uint32_t u = f32_bits(f);
-    uint16_t sign = (uint16_t)((u >> 31) << 15);
+    uint16_t sign = (uint16_t)(signbit(x) ? 0x8000u : 0u);
     uint16_t exp_all_ones = (uint16_t)(((1u << F.exp_bits) - 1u) << F.mant_bits);
-    if (isnan(f))
+    if (isnan(x))
         return (uint16_t)(sign | exp_all_ones | (1u << (F.mant_bits - 1)));
-    double a = fabs((double)f);
-    if (isinf(f))
+    double a = fabs(x);
+    if (isinf(x))
         return (uint16_t)(sign | exp_all_ones);
     if (a == 0.0)
         return sign;
@@ -108,6 +110,8 @@ static uint16_t encode_rne(float f, struct fmt16 F)
     uint32_t mant = (uint32_t)((v / ldexp(1.0, e) - 1.0) * ldexp(1.0, F.mant_bits));
     return (uint16_t)(sign | ((uint32_t)(e + F.bias) << F.mant_bits) | mant);
 }
+
+static uint16_t encode_rne(float f, struct fmt16 F) { return encode_rne_d((double)f, F); }
 
 uint16_t qref_f32_to_bf16(float f) { return encode_rne(f, FMT_BF16); }
 uint16_t qref_f32_to_f16(float f) { return encode_rne(f, FMT_F16); }
@@ -332,6 +336,60 @@ int qref_dequantize(const uint32_t* wq, const void* scales, const void* biases,
         for (int64_t i = 0; i < k; ++i)
             w_out[r * k + i] = dequant_elem(wq + r * words, words, scales, biases, sb_dtype,
                                             r * groups, i, bits, group_size);
+    return 0;
+}
+
+/* v rounded to nearest, ties to even, in element type `dtype`; the rounded
+ * value is returned and, when `out` is non-null, stored at out[idx]. */
+static double round_to_type(double v, int dtype, void* out, int64_t idx)
+{
+    switch (dtype) {
+    case QREF_F32: {
+        float f = (float)v; /* C's double -> float conversion rounds to nearest even */
+        if (out)
+            ((float*)out)[idx] = f;
+        return f;
+    }
+    case QREF_F16: {
+        uint16_t h = encode_rne_d(v, FMT_F16);
+        if (out)
+            ((uint16_t*)out)[idx] = h;
+        return qref_f16_to_f32(h);
+    }
+    case QREF_BF16: {
+        uint16_t h = encode_rne_d(v, FMT_BF16);
+        if (out)
+            ((uint16_t*)out)[idx] = h;
+        return qref_bf16_to_f32(h);
+    }
+    }
+    abort();
+}
+
+/* The dense weight in the scales' own type T (emily `dequantize_impl`: the
+ * unpacked codes are cast to the scales' type, then multiplied by the scale
+ * and added to the bias as two operations of that type). Each operation is
+ * taken exactly in fp64 and rounded once to T: q < 2^8 times a scale of at
+ * most 24 significant bits is exact in fp64, and so is the sum of two values
+ * of T unless their exponents lie more than 29 apart, where the one fp64
+ * rounding cannot change the nearest value of T (53 >= 2 * 24 + 2). */
+int qref_dequantize_typed(const uint32_t* wq, const void* scales, const void* biases,
+                          int sb_dtype, int64_t n, int64_t k, int bits, int group_size,
+                          void* w_out)
+{
+    if (!args_ok(n, k, bits, group_size, sb_dtype))
+        return -1;
+    int64_t groups = k / group_size, words = words_per_row(k, bits);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t i = 0; i < k; ++i) {
+            double q = (double)unpack_lane(wq + r * words, words, i, bits);
+            int64_t g = r * groups + i / group_size;
+            double s = (double)load_elem(scales, sb_dtype, g);
+            double b = (double)load_elem(biases, sb_dtype, g);
+            double prod = round_to_type(q * s, sb_dtype, NULL, 0);
+            round_to_type(prod + b, sb_dtype, w_out, r * k + i);
+        }
     return 0;
 }
 

@@ -55,6 +55,14 @@ int qref_dequantize(const uint32_t* wq, const void* scales, const void* biases,
                     int sb_dtype, int64_t n, int64_t k, int bits, int group_size,
                     float* w_out);
 
+/* Dense weight in the scales' own element type sb_dtype (w_out: [n,k] of that
+ * type): cast the code to that type, then multiply by the scale and add the
+ * bias, each operation rounded to nearest even in that type. For fp32 scales
+ * this equals qref_dequantize. */
+int qref_dequantize_typed(const uint32_t* wq, const void* scales, const void* biases,
+                          int sb_dtype, int64_t n, int64_t k, int bits, int group_size,
+                          void* w_out);
+
 /* y[m,n] = sum_k x[m,k] * w'[n,k] in fp64, in k order, plus
  * S[m,n] = sum_k |x[m,k]| * |w'[n,k]| (the scale of the error bound).
  * x: [m,k] of element type x_dtype. y, S: [m,n] fp64. */

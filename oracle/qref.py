@@ -59,6 +59,7 @@ def lib():
         L.qref_unpack.argtypes = [P, I64, I64, I, P]
         L.qref_quantize.argtypes = [P, I64, I64, I, I, I, P, P, P]
         L.qref_dequantize.argtypes = [P, P, P, I, I64, I64, I, I, P]
+        L.qref_dequantize_typed.argtypes = [P, P, P, I, I64, I64, I, I, P]
         L.qref_qmatmul.argtypes = [P, I, I64, I64, P, P, P, I, I64, I, I, P, P]
         L.qref_qmatmul_sampled.argtypes = [P, I, I64, I64, P, P, P, I, I64, I, I, P, P, I64,
                                            P, P]
@@ -150,6 +151,18 @@ def dequantize(wq, s, b, sb_dtype, k, bits, group_size):
     out = np.empty((n, k), dtype=np.float32)
     _check(lib().qref_dequantize(_p(wq), _p(np.ascontiguousarray(s)), _p(np.ascontiguousarray(b)),
                                  sb_dtype, n, k, bits, group_size, _p(out)), "dequantize")
+    return out
+
+
+def dequantize_typed(wq, s, b, sb_dtype, k, bits, group_size):
+    """Dense weight in the scales' type: fp32 array, or uint16 bit patterns for
+    fp16 / bf16 scales."""
+    wq = np.ascontiguousarray(wq, dtype=np.uint32)
+    n = wq.shape[0]
+    out = _sb_empty((n, k), sb_dtype)
+    _check(lib().qref_dequantize_typed(_p(wq), _p(np.ascontiguousarray(s)),
+                                       _p(np.ascontiguousarray(b)), sb_dtype, n, k, bits,
+                                       group_size, _p(out)), "dequantize_typed")
     return out
 
 

@@ -40,6 +40,8 @@ MUTANTS = [
     ("silu_sign", "static double silu(double z) { return z / (1.0 + exp(-z)); }",
      "static double silu(double z) { return z / (1.0 + exp(z)); }", FAST),
     ("product_operand", "mag += fabs(xv) * fabs(wv);", "mag += fabs(xv) + fabs(wv);", FAST),
+    ("typed_dequant_single_rounding", "double prod = round_to_type(q * s, sb_dtype, NULL, 0);",
+     "double prod = q * s;", FAST),
     ("rne_ties_up", "r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "r = lo + 1.0;", "rne"),
     ("f16_decode_exponent", "v = ldexp((double)(1024 + m), e - 25);",
      "v = ldexp((double)(1024 + m), e - 24);", "f16 or decoders"),

@@ -317,6 +317,68 @@ def test_quantize_clamps_codes_to_range():
         assert qref.unpack(wq, 32, 8)[0, idx] == clamped
 
 
+# ---------------------------------------------------------------- dense weight in the scales' type
+
+def _typed_case(n, k, bits, gs, dt, seed):
+    """Random codes with scales and biases of full mantissa in type dt."""
+    codes = synth.random_codes((n, k), bits, seed)
+    wq = np.array([bigint_pack(codes[r], bits) for r in range(n)], dtype=np.uint32)
+    s = store(np.abs(synth.normal_f32((n, k // gs), 0.02, seed + 1)) + 1e-3, dt)
+    b = store(synth.normal_f32((n, k // gs), 0.3, seed + 2), dt)
+    return codes, wq, s, b
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("gs", [32, 128])
+def test_dequantize_typed_f16_matches_numpy_half_arithmetic(bits, gs):
+    """numpy's float16 multiply and add each round to nearest-even fp16."""
+    codes, wq, s, b = _typed_case(24, 512, bits, gs, F16, 900 + bits)
+    s16 = np.repeat(s.view(np.float16), gs, axis=1)
+    b16 = np.repeat(b.view(np.float16), gs, axis=1)
+    expect = (codes.astype(np.float16) * s16 + b16).view(np.uint16)
+    got = qref.dequantize_typed(wq, s, b, F16, 512, bits, gs)
+    assert got.dtype == np.uint16
+    assert np.array_equal(got, expect)
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("gs", [32, 128])
+def test_dequantize_typed_bf16_matches_torch_bf16_arithmetic(bits, gs):
+    """torch's CPU bfloat16 multiply and add each round to nearest-even bf16."""
+    codes, wq, s, b = _typed_case(24, 512, bits, gs, BF16, 950 + bits)
+    st = torch.from_numpy(s.view(np.int16).copy()).view(torch.bfloat16).repeat_interleave(gs, 1)
+    bt = torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).repeat_interleave(gs, 1)
+    prod = torch.from_numpy(codes.astype(np.int32)).to(torch.bfloat16) * st
+    expect = (prod + bt).view(torch.int16).numpy().view(np.uint16)
+    got = qref.dequantize_typed(wq, s, b, BF16, 512, bits, gs)
+    assert np.array_equal(got, expect)
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+def test_dequantize_typed_f32_is_the_fp32_form(bits):
+    codes, wq, s, b = _typed_case(8, 256, bits, 64, F32, 990 + bits)
+    expect = (codes.astype(np.float32) * np.repeat(s, 64, axis=1)) + np.repeat(b, 64, axis=1)
+    assert np.array_equal(qref.dequantize_typed(wq, s, b, F32, 256, bits, 64), expect)
+    assert np.array_equal(qref.dequantize(wq, s, b, F32, 256, bits, 64), expect)
+
+
+def test_dequantize_typed_rounds_product_then_sum():
+    """Worked by hand in bf16 (8 significant bits; spacing 2^-6 on [2, 4)):
+    q = 3, s = 1 + 2^-7, b = -2^-7. The product 3 + 3*2^-7 lies halfway
+    between 3 + 2^-6 and 3 + 2^-5 and rounds to the even one, 3 + 2^-5; adding
+    b gives 3 + 3*2^-7, again a tie, which rounds to 3 + 2^-5. Rounding only
+    once would give 3 + 2^-6 (q*s + b = 3 + 2^-6 exactly)."""
+    codes = np.zeros((1, 32), dtype=np.int64)
+    codes[0, 0] = 3
+    wq = np.array([bigint_pack(codes[0], 4)], dtype=np.uint32)
+    s = store(np.array([[1.0 + 2.0 ** -7]], np.float32), BF16)
+    b = store(np.array([[-(2.0 ** -7)]], np.float32), BF16)
+    got = values(qref.dequantize_typed(wq, s, b, BF16, 32, 4, 32), BF16)
+    assert got[0, 0] == 3.0 + 2.0 ** -5
+    assert got[0, 1] == -(2.0 ** -7)     # code 0: the bias itself
+    assert qref.dequantize(wq, s, b, BF16, 32, 4, 32)[0, 0] == 3.0 + 2.0 ** -6
+
+
 # ---------------------------------------------------------------- products
 
 def test_qmatmul_iota_example():
