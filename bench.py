@@ -11,8 +11,10 @@ region cycles through >= 512 MB of distinct weight copies (more than twice the
 
 Every other row of the hot path is measured too, in `rows`: decode at 2/4/8
 bits and M = 1/4/16, the cross-word 3/6-bit layouts over three group sizes,
-both prefill GEMM shapes against the bf16 MFMA peak, and the MoE gate+up+SiLU
-and down calls at T = 1/64/512 tokens.
+both prefill GEMM shapes against the bf16 MFMA peak, the MoE gate+up+SiLU
+and down calls at T = 1/64/512 tokens, and the unfused two-kernel form
+(qpack_dequantize to a dense bf16 weight, then torch.matmul) at M = 1 and
+2048 beside the fused call.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
@@ -113,6 +115,36 @@ def bench_dense(N, K, M, bits, gs, dt, steps, warmup, stream, dev, seed=21):
     del sets
     torch.cuda.empty_cache()
     return ms, wb, copies
+
+
+def bench_unfused(N, K, M, bits, gs, dt, steps, warmup, stream, dev, seed=21):
+    """The two-kernel form the fused product replaces: qpack_dequantize to a
+    dense [N, K] weight in the scales' type, then a dense torch.matmul. Returns
+    (ms of the dequantize alone, ms of both, weight bytes)."""
+    import torch
+    import weight_only_quantized_qgemv_amd as qp
+    from weight_only_quantized_qgemv_amd import synth
+    es = torch.finfo(dt).bits // 8
+    wb = weight_bytes(N, K, bits, gs, es)
+    copies = copies_for(wb)
+    sets = make_weights(N, K, bits, gs, dt, copies, seed, dev)
+    x = torch.from_numpy(synth.normal_f32((M, K), 1.0, seed + 1)).to(dt).to(dev)
+    y = torch.empty((M, N), dtype=dt, device=dev)
+    wd = torch.empty((N, K), dtype=dt, device=dev)
+
+    def deq(i):
+        wq, s, b = sets[i % copies]
+        qp.qpack_dequantize(wq, s, b, bits, gs, out=wd)
+
+    def both(i):
+        deq(i)
+        torch.matmul(x, wd.t(), out=y)
+
+    ms_deq = time_calls(deq, steps, warmup, stream)
+    ms_both = time_calls(both, steps, warmup, stream)
+    del sets, wd
+    torch.cuda.empty_cache()
+    return ms_deq, ms_both, wb
 
 
 def bench_moe(T, steps, warmup, stream, dev):
@@ -281,6 +313,18 @@ def main():
                 "us": round(ms_r * 1e3, 2), "tflops": round(tf, 1),
                 "frac_bf16_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                 "tokens_per_s": round(2048 / (ms_r * 1e-3), 1)}
+        # Unfused rows: dequantize to a dense bf16 weight, then torch.matmul, on
+        # the decode and prefill shapes, beside the fused call measured above.
+        for M, fused_key in ((1, "decode_b4_m1"), (2048, "prefill_m2048_n14336_k4096")):
+            st = del_steps if M == 1 else 20
+            ms_deq, ms_both, wb_r = bench_unfused(N, K, M, 4, 64, bf16, st, 3, stream, dev)
+            fused_us = rows[fused_key]["us"]
+            rows[f"unfused_b4_m{M}"] = {
+                "dequantize_us": round(ms_deq * 1e3, 3),
+                "dequantize_GBps": round((wb_r + N * K * 2) / (ms_deq * 1e-3) / 1e9, 1),
+                "dequantize_then_matmul_us": round(ms_both * 1e3, 3),
+                "fused_us": fused_us,
+                "fused_speedup": round(ms_both * 1e3 / fused_us, 2)}
         # MoE rows: 128 experts, top-8, 4-bit gs64 bf16.
         for T in (1, 64, 512):
             ms_gu, ms_d, touched, per_expert = bench_moe(T, del_steps, 5, stream, dev)

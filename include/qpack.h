@@ -85,6 +85,27 @@ qp_status qpack_quantize(const float* w, int64_t n, int64_t k, int32_t bits,
                          void* scales, void* biases, hipStream_t stream);
 
 /*
+ * Dense weight (emily "Defn-native dequantize": `dequantize_defn/1` and its
+ * affine `dequantize_impl`, the math of `QuantizedWeight.to_dense/1`):
+ *   w[r, i] = q[r, i] * s'[r, i/gs] + b'[r, i/gs],  q = bits [i*bits, i*bits + bits)
+ *   of row r's u32 stream
+ *   wq      device, u32 [n, k*bits/32]
+ *   scales, biases  device, sb_dtype [n, k/group_size]
+ *   out     device, out_dtype [n, k] (output)
+ * out_dtype QP_F32: fp32(q) * s' + b', a multiply and then an add in fp32
+ * (the weight qmatmul's product is defined on). out_dtype == sb_dtype (16-bit):
+ * the code cast to that type, then the product and the sum each rounded to
+ * nearest-even in that type, as the pages' affine step computes in the
+ * scales' type. Any other out_dtype is QP_ERR_DTYPE_MISMATCH; k above 2^33 is
+ * QP_ERR_UNSUPPORTED. Deterministic
+ * and exact to these definitions on any launch. n == 0 or k == 0 is a no-op.
+ */
+qp_status qpack_dequantize(const uint32_t* wq, const void* scales, const void* biases,
+                           qp_dtype sb_dtype, int64_t n, int64_t k, int32_t bits,
+                           int32_t group_size, qp_dtype out_dtype, void* out,
+                           hipStream_t stream);
+
+/*
  * Quantized linear (emily `quantized_matmul/2`, transpose = true):
  *   y[m, n] = sum_k x[m, k] * (q[n, k] * s'[n, k/gs] + b'[n, k/gs])
  *   x       device, x_dtype [m, k]

@@ -92,6 +92,28 @@ def test_quantize_empty_is_a_noop():
     assert quantize(k=0, w=None) == OK
 
 
+def dequantize(wq=A, s=A, b=A, sdt=BF16, n=4, k=64, bits=4, gs=64, odt=BF16, out=A):
+    return qp.lib().qpack_dequantize(wq, s, b, sdt, n, k, bits, gs, odt, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=7), UNSUPPORTED), (dict(gs=48), UNSUPPORTED), (dict(k=96), SHAPE),
+    (dict(n=-1), INVALID), (dict(sdt=3), INVALID), (dict(odt=3), INVALID),
+    (dict(odt=F16), MISMATCH), (dict(sdt=F32, odt=BF16), MISMATCH), (dict(wq=None), INVALID),
+    (dict(out=None), INVALID), (dict(wq=P(0x10002)), ALIGN), (dict(s=ODD), ALIGN),
+    (dict(odt=F32, out=P(0x10002)), ALIGN), (dict(k=(1 << 33) + 64), UNSUPPORTED),
+])
+def test_dequantize_argument_errors(kw, status):
+    assert dequantize(**kw) == status
+    assert qp.last_error() != ""
+
+
+def test_dequantize_empty_is_a_noop():
+    assert dequantize(n=0, wq=None, out=None) == OK
+    assert dequantize(k=0, wq=None, out=None) == OK
+    assert dequantize(sdt=F16, odt=F32, n=0) == OK
+
+
 def moe(fused=False, a=A, dt=BF16, ids=A, T=2, top_k=2, outer=64, inner=0, sdt=BF16, E=4, R=8,
         C=64, bits=4, gs=64, out=A, ws=A, ws_bytes=None):
     L = qp.lib()

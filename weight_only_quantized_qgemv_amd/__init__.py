@@ -27,7 +27,7 @@ STATUS = {0: "QP_OK", 1: "QP_ERR_INVALID_ARG", 2: "QP_ERR_UNSUPPORTED",
           6: "QP_ERR_WORKSPACE", 7: "QP_ERR_HIP"}
 
 # Every symbol include/qpack.h declares.
-EXPORTS = ("qpack_quantize", "qmatmul", "qgemv_moe_workspace_bytes", "qgemv_moe_id",
+EXPORTS = ("qpack_quantize", "qpack_dequantize", "qmatmul", "qgemv_moe_workspace_bytes", "qgemv_moe_id",
            "qgemv_moe_id_gate_up_silu", "qpack_last_error", "qpack_version")
 
 
@@ -51,6 +51,9 @@ def lib() -> ctypes.CDLL:
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
         L.qpack_quantize.argtypes = [P, I64, I64, I32, I32, ctypes.c_int, P, P, P, P]
         L.qpack_quantize.restype = ctypes.c_int
+        L.qpack_dequantize.argtypes = [P, P, P, ctypes.c_int, I64, I64, I32, I32, ctypes.c_int,
+                                       P, P]
+        L.qpack_dequantize.restype = ctypes.c_int
         L.qmatmul.argtypes = [P, ctypes.c_int, I64, I64, P, P, P, ctypes.c_int, I64, I32, I32, P,
                               P]
         L.qmatmul.restype = ctypes.c_int
@@ -127,6 +130,26 @@ def qpack_quantize(w, bits: int, group_size: int, sb_dtype=None, wq=None, scales
     check(lib().qpack_quantize(_ptr(w), n, k, bits, group_size, dtype_code(sb_dtype), _ptr(wq),
                                _ptr(scales), _ptr(biases), _stream(w)))
     return wq, scales, biases
+
+
+def qpack_dequantize(wq, scales, biases, bits: int, group_size: int, out_dtype=None,
+                     out=None):
+    """Dense weight [n, k] from packed codes: fp32, or (the default) the scales' own
+    dtype, with the product and sum rounded to that dtype."""
+    import torch
+    for t, nm in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _dev(t, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    n = wq.shape[0]
+    k = wq.shape[1] * 32 // bits if bits else 0
+    out_dtype = out_dtype or scales.dtype
+    if out is None:
+        out = torch.empty((n, k), dtype=out_dtype, device=wq.device)
+    check(lib().qpack_dequantize(_ptr(wq), _ptr(scales), _ptr(biases), dtype_code(scales.dtype),
+                                 n, k, bits, group_size, dtype_code(out.dtype), _ptr(out),
+                                 _stream(wq)))
+    return out
 
 
 def qmatmul(x, wq, scales, biases, bits: int, group_size: int, out=None):

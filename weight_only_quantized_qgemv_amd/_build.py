@@ -21,7 +21,8 @@ BITS = (2, 3, 4, 6, 8)
 # (source, object name, defines): kernels with many template instantiations are
 # compiled once per bit width (and MoE form) so the work spreads over cores.
 UNITS = ([("api.cpp", "api", {}), ("quantize.hip", "quantize", {}), ("moe.hip", "moe", {}),
-          ("qgemm.hip", "qgemm", {})]
+          ("qgemm.hip", "qgemm", {}),
+          ("dequantize.hip", "dequantize", {})]
          + [("qgemv.hip", f"qgemv_b{b}", {"QP_BITS": b}) for b in BITS]
          + [("moe_compute.hip", f"moe_b{b}_n{n}", {"QP_BITS": b, "QP_NMAT": n})
             for b in BITS for n in (1, 2)])

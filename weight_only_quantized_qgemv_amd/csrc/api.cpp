@@ -103,6 +103,38 @@ qp_status qpack_quantize(const float* w, int64_t n, int64_t k, int32_t bits, int
     return hip_result(qp::launch_quantize(a, stream), "qpack_quantize");
 }
 
+qp_status qpack_dequantize(const uint32_t* wq, const void* scales, const void* biases,
+                           qp_dtype sb_dtype, int64_t n, int64_t k, int32_t bits,
+                           int32_t group_size, qp_dtype out_dtype, void* out, hipStream_t stream)
+{
+    if (n < 0 || k < 0)
+        return fail(QP_ERR_INVALID_ARG, "negative size (n=%lld, k=%lld)", (long long)n,
+                    (long long)k);
+    if (!dtype_ok(sb_dtype) || !dtype_ok(out_dtype))
+        return fail(QP_ERR_INVALID_ARG, "unknown dtype (scales=%d, out=%d)", (int)sb_dtype,
+                    (int)out_dtype);
+    if (qp_status s = check_layout(k, bits, group_size); s != QP_OK)
+        return s;
+    if (k > (int64_t(1) << 33))
+        return fail(QP_ERR_UNSUPPORTED, "k=%lld above 2^33", (long long)k);
+    if (out_dtype != QP_F32 && out_dtype != sb_dtype)
+        return fail(QP_ERR_DTYPE_MISMATCH,
+                    "output dtype %d must be fp32 or the scales dtype %d", (int)out_dtype,
+                    (int)sb_dtype);
+    if (!mul_ok(n, k))
+        return fail(QP_ERR_INVALID_ARG, "n*k overflows");
+    if (n == 0 || k == 0)
+        return ok();
+    if (!wq || !scales || !biases || !out)
+        return fail(QP_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(wq, 4) || !aligned(scales, esize(sb_dtype)) || !aligned(biases, esize(sb_dtype)) ||
+        !aligned(out, esize(out_dtype)))
+        return fail(QP_ERR_ALIGN, "pointer not aligned to its element size");
+    qp::DequantArgs a{wq, scales, biases, (int)sb_dtype, (int)out_dtype, n, k, bits, group_size,
+                      out};
+    return hip_result(qp::launch_dequantize(a, stream), "qpack_dequantize");
+}
+
 qp_status qmatmul(const void* x, qp_dtype x_dtype, int64_t m, int64_t k, const uint32_t* wq,
                   const void* scales, const void* biases, qp_dtype sb_dtype, int64_t n,
                   int32_t bits, int32_t group_size, void* y, hipStream_t stream)

@@ -48,6 +48,17 @@ struct QuantizeArgs {
 };
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
 
+struct DequantArgs {
+    const uint32_t* wq;     // [N, K*bits/32]
+    const void* scales;     // [N, K/gs] of sdt
+    const void* biases;
+    int sdt, odt;           // scales' type; output type (DT_F32, or sdt)
+    int64_t N, K;
+    int bits, gs;
+    void* out;              // [N, K] of odt
+};
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
+
 struct MoeArgs {
     const void* a;          // activations
     int dt;
