@@ -29,6 +29,8 @@
  *    (p%top_k)*inner] and expert ids[p]), and the CPU fallback in the module
  *    docs (per-expert Linear calls): here, one dot product per pair and row.
  *    `gemv_moe_id_gate_up_silu` docs: SiLU(gate) * up.
+ *  - Microscaled modes: emily `dequantize_defn/1` docs and its mxfp4 / mxfp8
+ *    / nvfp4 implementations (lane and scale formats below).
  *
  * Arithmetic: fp32 for quantize and dequantize (compiled with
  * -ffp-contract=off, so a*b+c is a multiply then an add), fp64 for every
@@ -501,6 +503,113 @@ int qref_moe_gate_up_silu(const void* a, int a_dtype, const int32_t* ids, int64_
     int64_t total = n_tokens * top_k * n_rows;
     for (int64_t i = 0; i < total; ++i)
         silu_out[i] = silu(g[i]) * u[i];
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Microscaled modes                                                   */
+/* ------------------------------------------------------------------ */
+/* emily lib/emily/quantization.ex, `dequantize_mxfp4_impl`,
+ * `dequantize_mxfp8_impl`, `dequantize_nvfp4_impl`: no biases; each group of
+ * gs lanes along a row shares one scale byte; w = lane_value * scale_value.
+ *   mxfp4: 4-bit lanes, FP4-E2M1; gs 32; E8M0 scales.
+ *   mxfp8: 8-bit lanes, FP8-E4M3 as MLX decodes it; gs 32; E8M0 scales.
+ *   nvfp4: 4-bit lanes, FP4-E2M1; gs 16; FP8-E4M3 scales (MLX decode).
+ * Group sizes: ollama x/create/client/quantize.go `quantizeParams` (nvfp4
+ * 16, mxfp8 32) and the mxfp4 docs (one scale per 32 lanes). */
+
+int qref_mx_params(int mode, int* bits, int* group_size)
+{
+    switch (mode) {
+    case QREF_MXFP4: *bits = 4; *group_size = 32; return 0;
+    case QREF_MXFP8: *bits = 8; *group_size = 32; return 0;
+    case QREF_NVFP4: *bits = 4; *group_size = 16; return 0;
+    }
+    return -1;
+}
+
+/* FP4-E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; an
+ * exponent field of 0 is subnormal (value = mantissa * 2^-1). */
+double qref_fp4_e2m1(uint32_t c)
+{
+    double sign = (c & 8u) ? -1.0 : 1.0;
+    int e = (int)((c >> 1) & 3u), m = (int)(c & 1u);
+    double mag = e == 0 ? m * 0.5 : (1.0 + m / 2.0) * ldexp(1.0, e - 1);
+    return sign * mag;
+}
+
+/* FP8-E4M3 as MLX decodes it (the pages' `fp8_e4m3_lut`): sign bit 7,
+ * exponent bits 6..3 (bias 7), mantissa bits 2..0; an exponent field of 0 is
+ * subnormal (mantissa * 2^-9). No code is NaN: 0x7F / 0xFF are +-480. */
+double qref_fp8_e4m3(uint32_t b)
+{
+    double sign = (b & 0x80u) ? -1.0 : 1.0;
+    int e = (int)((b >> 3) & 15u), m = (int)(b & 7u);
+    double mag = e == 0 ? m * ldexp(1.0, -9) : (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+    return sign * mag;
+}
+
+/* FP8-E8M0: 2^(s - 127) (the pages' `e8m0_lut`; s = 255 gives 2^128). */
+double qref_e8m0(uint32_t s) { return ldexp(1.0, (int)s - 127); }
+
+/* Element i of row r's dense weight, exactly (fp64 holds every product). */
+static double mx_weight(const uint32_t* row_wq, int64_t words, const uint8_t* row_scales, int mode,
+                        int bits, int group_size, int64_t i)
+{
+    uint32_t q = unpack_lane(row_wq, words, i, bits);
+    uint32_t sb = row_scales[i / group_size];
+    double lane = mode == QREF_MXFP8 ? qref_fp8_e4m3(q) : qref_fp4_e2m1(q);
+    double scale = mode == QREF_NVFP4 ? qref_fp8_e4m3(sb) : qref_e8m0(sb);
+    return lane * scale;
+}
+
+static int mx_args_ok(int mode, int64_t n, int64_t k, int* bits, int* group_size)
+{
+    if (qref_mx_params(mode, bits, group_size) != 0 || n < 0 || k < 0)
+        return 0;
+    return k % *group_size == 0 && (k * *bits) % 32 == 0;
+}
+
+int qref_mx_dequantize(const uint32_t* wq, const uint8_t* scales, int mode, int64_t n, int64_t k,
+                       int out_dtype, void* w_out)
+{
+    int bits, gs;
+    if (!mx_args_ok(mode, n, k, &bits, &gs))
+        return -1;
+    if (out_dtype != QREF_F32 && out_dtype != QREF_F16 && out_dtype != QREF_BF16)
+        return -1;
+    int64_t words = words_per_row(k, bits), groups = k / gs;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t i = 0; i < k; ++i)
+            round_to_type(mx_weight(wq + r * words, words, scales + r * groups, mode, bits, gs, i),
+                          out_dtype, w_out, r * k + i);
+    return 0;
+}
+
+int qref_mx_qmatmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint32_t* wq,
+                    const uint8_t* scales, int mode, int64_t n, double* y, double* S)
+{
+    int bits, gs;
+    if (!mx_args_ok(mode, n, k, &bits, &gs) || m < 0)
+        return -1;
+    if (x_dtype != QREF_F32 && x_dtype != QREF_F16 && x_dtype != QREF_BF16)
+        return -1;
+    int64_t words = words_per_row(k, bits), groups = k / gs;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t mi = 0; mi < m; ++mi)
+        for (int64_t ni = 0; ni < n; ++ni) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t i = 0; i < k; ++i) {
+                double xv = (double)load_elem(x, x_dtype, mi * k + i);
+                double wv = mx_weight(wq + ni * words, words, scales + ni * groups, mode, bits,
+                                      gs, i);
+                acc += xv * wv;
+                mag += fabs(xv) * fabs(wv);
+            }
+            y[mi * n + ni] = acc;
+            S[mi * n + ni] = mag;
+        }
     return 0;
 }
 

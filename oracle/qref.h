@@ -100,6 +100,24 @@ int qref_moe_gate_up_silu(const void* a, int a_dtype, const int32_t* ids,
                           int64_t n_cols, int bits, int group_size,
                           double* silu_out, double* g, double* u, double* Sg, double* Su);
 
+/* Microscaled modes: no biases, one scale byte per group of lanes.
+ *   mode 1 = mxfp4 (4-bit FP4-E2M1 lanes, gs 32, E8M0 scales),
+ *   mode 2 = mxfp8 (8-bit FP8-E4M3 lanes as MLX decodes them, gs 32, E8M0),
+ *   mode 3 = nvfp4 (4-bit FP4-E2M1 lanes, gs 16, FP8-E4M3 scales).
+ * wq: [n, k*bits/32] packed as above; scales: [n, k/gs] u8. */
+enum { QREF_MXFP4 = 1, QREF_MXFP8 = 2, QREF_NVFP4 = 3 };
+int qref_mx_params(int mode, int* bits, int* group_size);
+double qref_fp4_e2m1(uint32_t code);
+double qref_fp8_e4m3(uint32_t byte);
+double qref_e8m0(uint32_t byte);
+/* Dense weight lane * scale (exact in fp64), rounded to nearest even in
+ * out_dtype (0/1/2 as above); w_out: [n, k]. */
+int qref_mx_dequantize(const uint32_t* wq, const uint8_t* scales, int mode, int64_t n,
+                       int64_t k, int out_dtype, void* w_out);
+/* y[m,n] = sum_k x[m,k] * w[n,k] in fp64 in k order, and S = sum |x||w|. */
+int qref_mx_qmatmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint32_t* wq,
+                    const uint8_t* scales, int mode, int64_t n, double* y, double* S);
+
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int qref_num_threads(void);
 

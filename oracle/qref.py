@@ -67,6 +67,12 @@ def lib():
                                P, P]
         L.qref_moe_gate_up_silu.argtypes = [P, I, P, I64, I64, I64, I64, P, P, P, P, P, P, I,
                                             I64, I64, I64, I, I, P, P, P, P, P]
+        L.qref_mx_params.argtypes = [I, P, P]
+        for f in ("qref_fp4_e2m1", "qref_fp8_e4m3", "qref_e8m0"):
+            getattr(L, f).restype = ctypes.c_double
+            getattr(L, f).argtypes = [ctypes.c_uint32]
+        L.qref_mx_dequantize.argtypes = [P, P, I, I64, I64, I, P]
+        L.qref_mx_qmatmul.argtypes = [P, I, I64, I64, P, P, I, I64, P, P]
         L.qref_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -224,3 +230,49 @@ def moe_gate_up_silu(a, a_dtype, ids, n_tokens, top_k, a_outer, a_inner, gate, u
         _p(res["silu_out"]), _p(res["g"]), _p(res["u"]), _p(res["Sg"]), _p(res["Su"])),
         "moe_gate_up_silu")
     return res
+
+
+MXFP4, MXFP8, NVFP4 = 1, 2, 3
+
+
+def mx_params(mode):
+    """(bits, group_size) of a microscaled mode."""
+    bits, gs = ctypes.c_int(), ctypes.c_int()
+    _check(lib().qref_mx_params(mode, ctypes.byref(bits), ctypes.byref(gs)), "mx_params")
+    return bits.value, gs.value
+
+
+def fp4_e2m1(code):
+    return lib().qref_fp4_e2m1(code)
+
+
+def fp8_e4m3(byte):
+    return lib().qref_fp8_e4m3(byte)
+
+
+def e8m0(byte):
+    return lib().qref_e8m0(byte)
+
+
+def mx_dequantize(wq, scales, mode, k, out_dtype=F32):
+    """Dense weight [n, k]: fp32 values, or uint16 bit patterns for fp16/bf16."""
+    wq = np.ascontiguousarray(wq, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    n = wq.shape[0]
+    out = _sb_empty((n, k), out_dtype)
+    _check(lib().qref_mx_dequantize(_p(wq), _p(scales), mode, n, k, out_dtype, _p(out)),
+           "mx_dequantize")
+    return out
+
+
+def mx_qmatmul(x, x_dtype, wq, scales, mode, k):
+    """x: [m,k] fp32 values or uint16 bit patterns. Returns (y, S) fp64 [m, n]."""
+    x = np.ascontiguousarray(x)
+    wq = np.ascontiguousarray(wq, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    m, n = x.shape[0], wq.shape[0]
+    y = np.empty((m, n), dtype=np.float64)
+    S = np.empty((m, n), dtype=np.float64)
+    _check(lib().qref_mx_qmatmul(_p(x), x_dtype, m, k, _p(wq), _p(scales), mode, n, _p(y), _p(S)),
+           "mx_qmatmul")
+    return y, S

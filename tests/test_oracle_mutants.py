@@ -42,6 +42,14 @@ MUTANTS = [
     ("product_operand", "mag += fabs(xv) * fabs(wv);", "mag += fabs(xv) + fabs(wv);", FAST),
     ("typed_dequant_single_rounding", "double prod = round_to_type(q * s, sb_dtype, NULL, 0);",
      "double prod = q * s;", FAST),
+    ("fp4_exponent_bias", "(1.0 + m / 2.0) * ldexp(1.0, e - 1);", "(1.0 + m / 2.0) * ldexp(1.0, e - 2);",
+     FAST),
+    ("e4m3_subnormal_scale", "m * ldexp(1.0, -9)", "m * ldexp(1.0, -10)", FAST),
+    ("e8m0_bias", "return ldexp(1.0, (int)s - 127);", "return ldexp(1.0, (int)s - 126);", FAST),
+    ("nvfp4_scale_format", "double scale = mode == QREF_NVFP4 ? qref_fp8_e4m3(sb) : qref_e8m0(sb);",
+     "double scale = qref_e8m0(sb);", FAST),
+    ("mx_group_index", "uint32_t sb = row_scales[i / group_size];",
+     "uint32_t sb = row_scales[i / 32];", FAST),
     ("rne_ties_up", "r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "r = lo + 1.0;", "rne"),
     ("f16_decode_exponent", "v = ldexp((double)(1024 + m), e - 25);",
      "v = ldexp((double)(1024 + m), e - 24);", "f16 or decoders"),

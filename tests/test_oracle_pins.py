@@ -379,6 +379,121 @@ def test_dequantize_typed_rounds_product_then_sum():
     assert qref.dequantize(wq, s, b, BF16, 32, 4, 32)[0, 0] == 3.0 + 2.0 ** -6
 
 
+# ---------------------------------------------------------------- microscaled modes
+
+def load_mx_luts():
+    d = {}
+    with open(os.path.join(GOLDEN, "mx_luts.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            key, val = (t.strip() for t in line.split("|"))
+            d[key] = val.split()
+    return d
+
+
+def test_fp4_e2m1_matches_the_printed_table():
+    lut = [float(v) for v in load_mx_luts()["fp4"]]
+    got = [qref.fp4_e2m1(c) for c in range(16)]
+    assert got == lut
+    assert [math.copysign(1.0, g) for g in got] == [math.copysign(1.0, v) for v in lut]
+
+
+def test_fp8_e4m3_matches_torch_and_the_printed_quirk():
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ref = ref.to(torch.float64).numpy()
+    quirk = dict((int(a, 16), float(b)) for a, b in
+                 (t.split(":") for t in load_mx_luts()["e4m3_quirk"]))
+    for byte in range(256):
+        got = qref.fp8_e4m3(byte)
+        if byte in quirk:
+            assert got == quirk[byte]
+        else:
+            assert got == ref[byte] and math.copysign(1, got) == math.copysign(1, ref[byte]), byte
+
+
+def test_e8m0_matches_torch_and_the_printed_formula():
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu)
+    ref = ref.to(torch.float64).numpy()
+    for s in range(255):
+        assert qref.e8m0(s) == ref[s] == 2.0 ** (s - 127)
+    assert qref.e8m0(255) == 2.0 ** 128      # torch: NaN; the page's formula: 2^128
+    for t in load_mx_luts()["e8m0"]:
+        a, b = t.split(":")
+        assert qref.e8m0(int(a)) == float(b)
+
+
+def test_mx_params_follow_the_pages():
+    assert qref.mx_params(qref.MXFP4) == (4, 32)
+    assert qref.mx_params(qref.MXFP8) == (8, 32)
+    assert qref.mx_params(qref.NVFP4) == (4, 16)
+
+
+def _lut_dense(codes, sbytes, mode):
+    """Dense weight from the printed tables (fp4) and torch's decoders (fp8 /
+    e8m0, with the printed 0x7F / 0xFF quirk), independent of the oracle."""
+    luts = load_mx_luts()
+    fp4 = np.array([float(v) for v in luts["fp4"]])
+    e4m3 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    e4m3 = e4m3.to(torch.float64).numpy().copy()
+    e4m3[0x7F], e4m3[0xFF] = 480.0, -480.0
+    e8m0 = np.array([2.0 ** (s - 127) for s in range(256)])
+    lanes = e4m3[codes] if mode == qref.MXFP8 else fp4[codes]
+    scales = e4m3[sbytes] if mode == qref.NVFP4 else e8m0[sbytes]
+    gs = qref.mx_params(mode)[1]
+    return lanes * np.repeat(scales, gs, axis=1)
+
+
+def _mx_case(n, k, mode, seed, lo=110, hi=140):
+    bits, gs = qref.mx_params(mode)
+    codes = synth.random_codes((n, k), bits, seed)
+    wq = np.array([bigint_pack(codes[r], bits) for r in range(n)], dtype=np.uint32)
+    if mode == qref.NVFP4:   # E4M3 scale bytes of both signs, all exponents
+        sbytes = synth.random_ints((n, k // gs), 0, 256, seed + 1)
+    else:
+        sbytes = synth.random_ints((n, k // gs), lo, hi, seed + 1)
+    return codes, wq, sbytes.astype(np.uint8)
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3], ids=["mxfp4", "mxfp8", "nvfp4"])
+def test_mx_dequantize_matches_table_decode(mode):
+    codes, wq, sb = _mx_case(16, 256, mode, 1600 + mode)
+    dense = _lut_dense(codes, sb, mode)
+    assert np.array_equal(qref.mx_dequantize(wq, sb, mode, 256, F32), dense.astype(np.float32))
+    assert np.array_equal(qref.mx_dequantize(wq, sb, mode, 256, BF16),
+                          to_bits16(dense.astype(np.float32), BF16))
+
+
+def test_mx_dequantize_extreme_scales_round_to_the_output_type():
+    """E8M0 255 is 2^128: lanes +-1 overflow to +-inf in fp32 and bf16, lane
+    0.5 gives 2^127. E8M0 0 with lane 0.5 is 2^-128, an fp32 subnormal."""
+    codes = np.zeros((1, 32), dtype=np.int64)
+    codes[0, 0], codes[0, 1], codes[0, 2] = 2, 10, 1     # +1.0, -1.0, +0.5
+    wq = np.array([bigint_pack(codes[0], 4)], dtype=np.uint32)
+    big = qref.mx_dequantize(wq, np.array([[255]], np.uint8), qref.MXFP4, 32, F32)
+    assert big[0, 0] == np.inf and big[0, 1] == -np.inf
+    assert big[0, 2] == np.float32(2.0 ** 127) and big[0, 3] == 0.0
+    big16 = values(qref.mx_dequantize(wq, np.array([[255]], np.uint8), qref.MXFP4, 32, BF16), BF16)
+    assert big16[0, 0] == np.inf and big16[0, 2] == 2.0 ** 127
+    tiny = qref.mx_dequantize(wq, np.array([[0]], np.uint8), qref.MXFP4, 32, F32)
+    assert tiny[0, 2] == np.float32(2.0 ** -128) and tiny[0, 0] == np.float32(2.0 ** -127)
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3], ids=["mxfp4", "mxfp8", "nvfp4"])
+def test_mx_qmatmul_exact_integer_case(mode):
+    """Integer activations and scales 2^(s-127) with s in [124, 130]: every
+    product and partial sum is a short dyadic number, exact in fp64 in any
+    order, so the oracle must equal numpy's matmul of the table-decoded weight."""
+    codes, wq, sb = _mx_case(12, 128, mode, 1700 + mode, 124, 131)
+    if mode == qref.NVFP4:
+        sb = synth.random_ints(sb.shape, 0x30, 0x48, 1710).astype(np.uint8)   # 2^-1 .. 2^2
+    x = synth.random_ints((5, 128), -8, 9, 1720 + mode).astype(np.float32)
+    y, S = qref.mx_qmatmul(x, F32, wq, sb, mode, 128)
+    dense = _lut_dense(codes, sb, mode)
+    assert np.array_equal(y, x.astype(np.float64) @ dense.T)
+    assert np.array_equal(S, np.abs(x.astype(np.float64)) @ np.abs(dense).T)
+
+
 # ---------------------------------------------------------------- products
 
 def test_qmatmul_iota_example():
