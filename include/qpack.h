@@ -65,6 +65,16 @@ typedef enum qp_status {
 
 typedef enum qp_dtype { QP_F32 = 0, QP_F16 = 1, QP_BF16 = 2 } qp_dtype;
 
+/* Microscaled modes (emily "Defn-native dequantize", the mxfp4 / mxfp8 /
+ * nvfp4 implementations; group sizes as in ollama quantize.go
+ * `quantizeParams`): no biases, one scale byte per group of lanes.
+ *   QP_MXFP4: 4-bit FP4-E2M1 lanes, groups of 32, FP8-E8M0 scales 2^(s-127);
+ *   QP_MXFP8: 8-bit FP8-E4M3 lanes, groups of 32, FP8-E8M0 scales;
+ *   QP_NVFP4: 4-bit FP4-E2M1 lanes, groups of 16, FP8-E4M3 scales.
+ * FP8-E4M3 is decoded as MLX decodes it: bias 7, subnormals, and no NaN
+ * (0x7F / 0xFF are +-480). Lanes are packed as in the affine mode. */
+typedef enum qp_mode { QP_MXFP4 = 1, QP_MXFP8 = 2, QP_NVFP4 = 3 } qp_mode;
+
 /*
  * Affine group quantization (ollama quantize.go `loadAndQuantizeArray`,
  * emily `QuantizedWeight.from_dense/2`), computed on the device.
@@ -104,6 +114,40 @@ qp_status qpack_dequantize(const uint32_t* wq, const void* scales, const void* b
                            qp_dtype sb_dtype, int64_t n, int64_t k, int32_t bits,
                            int32_t group_size, qp_dtype out_dtype, void* out,
                            hipStream_t stream);
+
+/*
+ * Dense weight of a microscaled mode: w[r, i] = lane(q[r, i]) * scale(s[r, i/gs]),
+ * exact in fp32 (every lane times every scale up to 2^127 is an fp32 value;
+ * E8M0 byte 255 is 2^128 and gives +-inf, or 0 for a zero lane), rounded to
+ * nearest even in out_dtype (QP_F32, QP_F16 or QP_BF16; the pages' output is
+ * bf16).
+ *   wq      device, u32 [n, k*bits/32]
+ *   scales  device, u8 [n, k/gs]
+ *   out     device, out_dtype [n, k] (output)
+ * k must be a multiple of the mode's group size (QP_ERR_SHAPE). n == 0 or
+ * k == 0 is a no-op.
+ */
+qp_status qpack_dequantize_mx(const uint32_t* wq, const uint8_t* scales, qp_mode mode,
+                              int64_t n, int64_t k, qp_dtype out_dtype, void* out,
+                              hipStream_t stream);
+
+/*
+ * Quantized linear in a microscaled mode (emily `quantized_matmul/2` with
+ * mode mxfp4 / mxfp8 / nvfp4, transpose = true):
+ *   y[m, n] = sum_k x[m, k] * lane(q[n, k]) * scale(s[n, k/gs])
+ *   x       device, x_dtype [m, k] (any of QP_F32, QP_F16, QP_BF16)
+ *   wq      device, u32 [n, k*bits/32];  scales  device, u8 [n, k/gs]
+ *   y       device, x_dtype [m, n] (output)
+ * fp32 accumulation; every dense weight must be finite in fp32. 16-bit x
+ * with k a multiple of 32 up to 16384 and x 16-byte aligned runs the stream
+ * kernel (codes converted by the gfx950 FP4 / FP8 instructions, dot2
+ * products), one or two activation rows per pass over the weights; every
+ * other call runs the generic kernel (one wave per output). k == 0 writes
+ * zeros; m == 0 or n == 0 is a no-op.
+ */
+qp_status qmatmul_mx(const void* x, qp_dtype x_dtype, int64_t m, int64_t k,
+                     const uint32_t* wq, const uint8_t* scales, qp_mode mode, int64_t n,
+                     void* y, hipStream_t stream);
 
 /*
  * Quantized linear (emily `quantized_matmul/2`, transpose = true):

@@ -114,6 +114,46 @@ def test_dequantize_empty_is_a_noop():
     assert dequantize(sdt=F16, odt=F32, n=0) == OK
 
 
+def dequantize_mx(wq=A, s=A, mode=1, n=4, k=64, odt=BF16, out=A):
+    return qp.lib().qpack_dequantize_mx(wq, s, mode, n, k, odt, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mode=0), UNSUPPORTED), (dict(mode=4), UNSUPPORTED), (dict(k=48), SHAPE),
+    (dict(mode=3, k=40), SHAPE), (dict(n=-1), INVALID), (dict(odt=3), INVALID),
+    (dict(wq=None), INVALID), (dict(s=None), INVALID), (dict(out=None), INVALID),
+    (dict(wq=P(0x10002)), ALIGN), (dict(odt=F32, out=P(0x10002)), ALIGN),
+])
+def test_dequantize_mx_argument_errors(kw, status):
+    assert dequantize_mx(**kw) == status
+    assert qp.last_error() != ""
+
+
+def test_dequantize_mx_accepts_nvfp4_group_multiples_and_empty():
+    assert dequantize_mx(n=0, mode=3, k=48, wq=None, out=None) == OK
+    assert dequantize_mx(k=0, wq=None, out=None) == OK
+
+
+def qmatmul_mx(x=A, xdt=BF16, m=2, k=64, wq=A, s=A, mode=1, n=4, y=A):
+    return qp.lib().qmatmul_mx(x, xdt, m, k, wq, s, mode, n, y, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mode=5), UNSUPPORTED), (dict(k=80), SHAPE), (dict(mode=2, k=16), SHAPE),
+    (dict(m=-1), INVALID), (dict(xdt=3), INVALID), (dict(x=None), INVALID),
+    (dict(wq=None), INVALID), (dict(s=None), INVALID), (dict(y=None), INVALID),
+    (dict(y=ODD), ALIGN), (dict(x=ODD), ALIGN), (dict(wq=P(0x10002)), ALIGN),
+    (dict(k=1 << 31), INVALID),
+])
+def test_qmatmul_mx_argument_errors(kw, status):
+    assert qmatmul_mx(**kw) == status
+
+
+def test_qmatmul_mx_empty_is_a_noop():
+    assert qmatmul_mx(m=0, x=None, y=None) == OK
+    assert qmatmul_mx(n=0, x=None, y=None) == OK
+
+
 def moe(fused=False, a=A, dt=BF16, ids=A, T=2, top_k=2, outer=64, inner=0, sdt=BF16, E=4, R=8,
         C=64, bits=4, gs=64, out=A, ws=A, ws_bytes=None):
     L = qp.lib()

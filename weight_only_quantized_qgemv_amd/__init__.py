@@ -27,7 +27,7 @@ STATUS = {0: "QP_OK", 1: "QP_ERR_INVALID_ARG", 2: "QP_ERR_UNSUPPORTED",
           6: "QP_ERR_WORKSPACE", 7: "QP_ERR_HIP"}
 
 # Every symbol include/qpack.h declares.
-EXPORTS = ("qpack_quantize", "qpack_dequantize", "qmatmul", "qgemv_moe_workspace_bytes", "qgemv_moe_id",
+EXPORTS = ("qpack_quantize", "qpack_dequantize", "qpack_dequantize_mx", "qmatmul", "qmatmul_mx", "qgemv_moe_workspace_bytes", "qgemv_moe_id",
            "qgemv_moe_id_gate_up_silu", "qpack_last_error", "qpack_version")
 
 
@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.qpack_dequantize.argtypes = [P, P, P, ctypes.c_int, I64, I64, I32, I32, ctypes.c_int,
                                        P, P]
         L.qpack_dequantize.restype = ctypes.c_int
+        L.qpack_dequantize_mx.argtypes = [P, P, ctypes.c_int, I64, I64, ctypes.c_int, P, P]
+        L.qpack_dequantize_mx.restype = ctypes.c_int
+        L.qmatmul_mx.argtypes = [P, ctypes.c_int, I64, I64, P, P, ctypes.c_int, I64, P, P]
+        L.qmatmul_mx.restype = ctypes.c_int
         L.qmatmul.argtypes = [P, ctypes.c_int, I64, I64, P, P, P, ctypes.c_int, I64, I32, I32, P,
                               P]
         L.qmatmul.restype = ctypes.c_int
@@ -149,6 +153,47 @@ def qpack_dequantize(wq, scales, biases, bits: int, group_size: int, out_dtype=N
     check(lib().qpack_dequantize(_ptr(wq), _ptr(scales), _ptr(biases), dtype_code(scales.dtype),
                                  n, k, bits, group_size, dtype_code(out.dtype), _ptr(out),
                                  _stream(wq)))
+    return out
+
+
+MXFP4, MXFP8, NVFP4 = 1, 2, 3
+MX_LAYOUT = {MXFP4: (4, 32), MXFP8: (8, 32), NVFP4: (4, 16)}   # mode -> (bits, group size)
+
+
+def qpack_dequantize_mx(wq, scales, mode: int, out_dtype=None, out=None):
+    """Dense weight [n, k] of a microscaled mode (scales: uint8 [n, k/gs]); bf16 by
+    default, as the pages return it."""
+    import torch
+    for t, nm in ((wq, "wq"), (scales, "scales")):
+        _dev(t, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if mode not in MX_LAYOUT:
+        raise ValueError(f"unknown microscaled mode {mode}")
+    n, k = wq.shape[0], wq.shape[1] * 32 // MX_LAYOUT[mode][0]
+    if out is None:
+        out = torch.empty((n, k), dtype=out_dtype or torch.bfloat16, device=wq.device)
+    check(lib().qpack_dequantize_mx(_ptr(wq), _ptr(scales), mode, n, k, dtype_code(out.dtype),
+                                    _ptr(out), _stream(wq)))
+    return out
+
+
+def qmatmul_mx(x, wq, scales, mode: int, out=None):
+    """y = x @ dequant(W)^T for a microscaled W; x [m, k] fp32/fp16/bf16, y in x's dtype."""
+    import torch
+    _dev(x, "x")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [m, k] tensor")
+    for t, nm in ((wq, "wq"), (scales, "scales")):
+        _dev(t, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    m, k = x.shape
+    n = wq.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    check(lib().qmatmul_mx(_ptr(x), dtype_code(x.dtype), m, k, _ptr(wq), _ptr(scales), mode, n,
+                           _ptr(out), _stream(x)))
     return out
 
 

@@ -135,6 +135,77 @@ qp_status qpack_dequantize(const uint32_t* wq, const void* scales, const void* b
     return hip_result(qp::launch_dequantize(a, stream), "qpack_dequantize");
 }
 
+static qp_status mx_layout(int mode, int64_t k, int* bits, int* gs)
+{
+    switch (mode) {
+    case QP_MXFP4: *bits = 4; *gs = 32; break;
+    case QP_MXFP8: *bits = 8; *gs = 32; break;
+    case QP_NVFP4: *bits = 4; *gs = 16; break;
+    default: return fail(QP_ERR_UNSUPPORTED, "mode=%d not supported (1 mxfp4, 2 mxfp8, 3 nvfp4)",
+                         mode);
+    }
+    if (k % *gs != 0)
+        return fail(QP_ERR_SHAPE, "K=%lld is not a multiple of the mode's group size %d",
+                    (long long)k, *gs);
+    return QP_OK;
+}
+
+qp_status qpack_dequantize_mx(const uint32_t* wq, const uint8_t* scales, qp_mode mode, int64_t n,
+                              int64_t k, qp_dtype out_dtype, void* out, hipStream_t stream)
+{
+    if (n < 0 || k < 0)
+        return fail(QP_ERR_INVALID_ARG, "negative size (n=%lld, k=%lld)", (long long)n,
+                    (long long)k);
+    if (!dtype_ok(out_dtype))
+        return fail(QP_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dtype);
+    int bits, gs;
+    if (qp_status s = mx_layout(mode, k, &bits, &gs); s != QP_OK)
+        return s;
+    if (k > (int64_t(1) << 33))
+        return fail(QP_ERR_UNSUPPORTED, "k=%lld above 2^33", (long long)k);
+    if (!mul_ok(n, k))
+        return fail(QP_ERR_INVALID_ARG, "n*k overflows");
+    if (n == 0 || k == 0)
+        return ok();
+    if (!wq || !scales || !out)
+        return fail(QP_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(wq, 4) || !aligned(out, esize(out_dtype)))
+        return fail(QP_ERR_ALIGN, "pointer not aligned to its element size");
+    qp::DequantMxArgs a{wq, scales, (int)mode, (int)out_dtype, n, k, out};
+    return hip_result(qp::launch_dequantize_mx(a, stream), "qpack_dequantize_mx");
+}
+
+qp_status qmatmul_mx(const void* x, qp_dtype x_dtype, int64_t m, int64_t k, const uint32_t* wq,
+                     const uint8_t* scales, qp_mode mode, int64_t n, void* y, hipStream_t stream)
+{
+    if (m < 0 || k < 0 || n < 0)
+        return fail(QP_ERR_INVALID_ARG, "negative size (m=%lld, k=%lld, n=%lld)", (long long)m,
+                    (long long)k, (long long)n);
+    if (!dtype_ok(x_dtype))
+        return fail(QP_ERR_INVALID_ARG, "unknown dtype %d", (int)x_dtype);
+    int bits, gs;
+    if (qp_status s = mx_layout(mode, k, &bits, &gs); s != QP_OK)
+        return s;
+    if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n) || k >= (int64_t(1) << 31) ||
+        n >= (int64_t(1) << 31) || m >= (int64_t(1) << 31))
+        return fail(QP_ERR_INVALID_ARG, "size too large");
+    if (m == 0 || n == 0)
+        return ok();
+    if (!y)
+        return fail(QP_ERR_INVALID_ARG, "null output pointer");
+    const size_t es = esize(x_dtype);
+    if (!aligned(y, es))
+        return fail(QP_ERR_ALIGN, "y not aligned to its element size");
+    if (k == 0)
+        return hip_result(qp::launch_fill_zero(y, (int)x_dtype, m * n, stream), "qmatmul_mx");
+    if (!x || !wq || !scales)
+        return fail(QP_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(x, es) || !aligned(wq, 4))
+        return fail(QP_ERR_ALIGN, "pointer not aligned to its element size");
+    qp::GemvMxArgs a{x, (int)x_dtype, (int)mode, m, k, n, wq, scales, y};
+    return hip_result(qp::launch_qmatmul_mx(a, stream), "qmatmul_mx");
+}
+
 qp_status qmatmul(const void* x, qp_dtype x_dtype, int64_t m, int64_t k, const uint32_t* wq,
                   const void* scales, const void* biases, qp_dtype sb_dtype, int64_t n,
                   int32_t bits, int32_t group_size, void* y, hipStream_t stream)

@@ -21,6 +21,7 @@
 // stores are both contiguous across the wave.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mx.hpp"
 
 namespace qp {
 
@@ -165,7 +166,129 @@ hipError_t run_dequantize_bits(const DequantArgs& a, hipStream_t st)
     return hipErrorInvalidValue;
 }
 
+// Microscaled modes: w = lane * scale, exact in fp32 (at most 4 significant
+// bits from the lane and a power of two or 4 bits from the scale, down to
+// 2^-136), then rounded once to the output type. A run is 8 lanes: one word
+// of 4-bit lanes, two of 8-bit lanes, all inside one group.
+template <int MODE, int ODT, bool VEC>
+__global__ __launch_bounds__(kThreads) void dequantize_mx_kernel(
+    const uint32_t* __restrict__ wq, const uint8_t* __restrict__ scales, uint32_t runs,
+    uint32_t runs_row, uint32_t words_row, uint32_t groups_row,
+    typename Elem<ODT>::storage* __restrict__ out)
+{
+    using F = MxFmt<MODE>;
+    using OE = Elem<ODT>;
+    constexpr int U = kRunsPerThread;
+    constexpr int WPR = F::BITS / 4;          // words per run
+    constexpr int RPG = F::GS / 8;            // runs per group
+    const uint32_t first = blockIdx.x * (uint32_t)(kThreads * U) + threadIdx.x;
+
+    uint32_t w[U][WPR], sb[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        uint32_t r = first + (uint32_t)(j * kThreads);
+        r = r < runs ? r : runs - 1u;       // in bounds; past-the-end runs store nothing
+        const uint32_t row = r / runs_row, rc = r - row * runs_row;
+        const uint32_t* p = wq + (size_t)row * words_row + (size_t)rc * WPR;
+#pragma unroll
+        for (int i = 0; i < WPR; ++i)
+            w[j][i] = __builtin_nontemporal_load(p + i);
+        sb[j] = scales[(size_t)row * groups_row + rc / RPG];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const uint32_t r = first + (uint32_t)(j * kThreads);
+        if (r >= runs)
+            continue;
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t code = (w[j][(i * F::BITS) / 32] >> ((i * F::BITS) % 32)) &
+                                  ((1u << F::BITS) - 1u);
+            v[i] = mx_scaled<MODE>(mx_lane<MODE>(code), sb[j]);
+        }
+        typename OE::storage* o = out + (size_t)r * 8;
+        if constexpr (ODT == DT_F32) {
+            if constexpr (VEC) {
+                reinterpret_cast<float4*>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+                reinterpret_cast<float4*>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    o[i] = v[i];
+            }
+        } else {
+            uint16_t h[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                h[i] = OE::from_f32(v[i]);
+            if constexpr (VEC) {
+                u32x4_t q;
+                q.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                q.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                q.z = (uint32_t)h[4] | ((uint32_t)h[5] << 16);
+                q.w = (uint32_t)h[6] | ((uint32_t)h[7] << 16);
+                *reinterpret_cast<u32x4_t*>(o) = q;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    o[i] = h[i];
+            }
+        }
+    }
+}
+
+template <int MODE, int ODT>
+hipError_t run_dequantize_mx(const DequantMxArgs& a, hipStream_t st)
+{
+    using F = MxFmt<MODE>;
+    using O = typename Elem<ODT>::storage;
+    const int64_t runs_row = a.K / 8, words_row = a.K * F::BITS / 32, groups_row = a.K / F::GS;
+    const bool vec = reinterpret_cast<uintptr_t>(a.out) % 16 == 0;
+    const int64_t rows_per_launch = ((int64_t)1 << 30) / runs_row;
+    for (int64_t r0 = 0; r0 < a.N; r0 += rows_per_launch) {
+        const int64_t rows = a.N - r0 < rows_per_launch ? a.N - r0 : rows_per_launch;
+        const uint32_t runs = (uint32_t)(rows * runs_row);
+        const uint32_t blocks = (runs + kThreads * kRunsPerThread - 1) / (kThreads * kRunsPerThread);
+        const uint32_t* wq = a.wq + r0 * words_row;
+        const uint8_t* sc = a.scales + r0 * groups_row;
+        O* out = static_cast<O*>(a.out) + r0 * a.K;
+        if (vec)
+            hipLaunchKernelGGL((dequantize_mx_kernel<MODE, ODT, true>), dim3(blocks),
+                               dim3(kThreads), 0, st, wq, sc, runs, (uint32_t)runs_row,
+                               (uint32_t)words_row, (uint32_t)groups_row, out);
+        else
+            hipLaunchKernelGGL((dequantize_mx_kernel<MODE, ODT, false>), dim3(blocks),
+                               dim3(kThreads), 0, st, wq, sc, runs, (uint32_t)runs_row,
+                               (uint32_t)words_row, (uint32_t)groups_row, out);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+template <int MODE>
+hipError_t run_dequantize_mx_mode(const DequantMxArgs& a, hipStream_t st)
+{
+    switch (a.odt) {
+    case DT_F32: return run_dequantize_mx<MODE, DT_F32>(a, st);
+    case DT_F16: return run_dequantize_mx<MODE, DT_F16>(a, st);
+    case DT_BF16: return run_dequantize_mx<MODE, DT_BF16>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 } // namespace
+
+hipError_t launch_dequantize_mx(const DequantMxArgs& a, hipStream_t st)
+{
+    switch (a.mode) {
+    case MODE_MXFP4: return run_dequantize_mx_mode<MODE_MXFP4>(a, st);
+    case MODE_MXFP8: return run_dequantize_mx_mode<MODE_MXFP8>(a, st);
+    case MODE_NVFP4: return run_dequantize_mx_mode<MODE_NVFP4>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st)
 {

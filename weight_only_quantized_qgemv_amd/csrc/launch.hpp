@@ -59,6 +59,26 @@ struct DequantArgs {
 };
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 
+// Microscaled modes (mode 1 mxfp4, 2 mxfp8, 3 nvfp4; see mx.hpp).
+struct DequantMxArgs {
+    const uint32_t* wq;     // [N, K*bits/32]
+    const uint8_t* scales;  // [N, K/gs]
+    int mode, odt;
+    int64_t N, K;
+    void* out;              // [N, K] of odt
+};
+hipError_t launch_dequantize_mx(const DequantMxArgs& a, hipStream_t stream);
+
+struct GemvMxArgs {
+    const void* x;          // [M, K] of dt
+    int dt, mode;
+    int64_t M, K, N;
+    const uint32_t* wq;     // [N, K*bits/32]
+    const uint8_t* scales;  // [N, K/gs]
+    void* y;                // [M, N] of dt
+};
+hipError_t launch_qmatmul_mx(const GemvMxArgs& a, hipStream_t stream);
+
 struct MoeArgs {
     const void* a;          // activations
     int dt;
