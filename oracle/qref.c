@@ -604,8 +604,9 @@ int qref_mx_qmatmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint
                 double xv = (double)load_elem(x, x_dtype, mi * k + i);
                 double wv = mx_weight(wq + ni * words, words, scales + ni * groups, mode, bits,
                                       gs, i);
-                acc += xv * wv;
-                mag += fabs(xv) * fabs(wv);
+                double term = xv * wv;
+                acc += term;
+                mag += fabs(term);
             }
             y[mi * n + ni] = acc;
             S[mi * n + ni] = mag;

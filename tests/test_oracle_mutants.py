@@ -50,6 +50,7 @@ MUTANTS = [
      "double scale = qref_e8m0(sb);", FAST),
     ("mx_group_index", "uint32_t sb = row_scales[i / group_size];",
      "uint32_t sb = row_scales[i / 32];", FAST),
+    ("mx_magnitude_sum", "mag += fabs(term);", "mag += term;", FAST),
     ("rne_ties_up", "r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "r = lo + 1.0;", "rne"),
     ("f16_decode_exponent", "v = ldexp((double)(1024 + m), e - 25);",
      "v = ldexp((double)(1024 + m), e - 24);", "f16 or decoders"),
