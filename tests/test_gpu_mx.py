@@ -200,3 +200,62 @@ def test_mx_qmatmul_k0_and_rejections():
     with pytest.raises(qp.QpackError) as e:
         qp.qmatmul_mx(x, wq, sb, 7)
     assert e.value.status == 2
+
+
+# ------------------------------------------------------------------ prefill tiles (M > 16)
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("dt", [BF16, F16])
+def test_mx_qmatmul_prefill_tiles(mode, dt):
+    # 300 activation rows (two 256-row tiles, the second ragged), 520 weight
+    # rows (ragged 128- or 256-wide tiles), K = 1024: 16 k steps.
+    run_mx(300, 520, 1024, mode, dt, 3000 + 10 * mode + dt, "prefill tiles")
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_mx_qmatmul_prefill_exact_integer_case(mode):
+    """The exact case of the stream kernel on the matrix-core tiles: y must be
+    the oracle's exact result rounded once."""
+    n, k, m = 96, 512, 40
+    wq, sb = mx_weights(n, k, mode, 3100 + mode, 125, 129)
+    if mode == qref.NVFP4:
+        sb = synth.random_ints(sb.shape, 0x30, 0x47, 3110).astype(np.uint8)
+    if mode == qref.MXFP8:
+        e = synth.random_ints((n, k), 6, 9, 3111)
+        mant = synth.random_ints((n, k), 0, 7, 3112)
+        sign = synth.random_ints((n, k), 0, 1, 3113)
+        codes = (sign << 7 | e << 3 | mant).astype(np.uint8)
+        codes[::7, ::5] = 0x7F      # +480 * scale: the patched conversion
+        codes[3::7, 1::5] = 0xFF
+        wq = qref.pack(codes, 8)
+    x = synth.random_ints((m, k), -2, 2, 3120 + mode).astype(np.float32)
+    xt = torch.from_numpy(x).to(torch.bfloat16).to(dev())
+    y = qp.qmatmul_mx(xt, to_device(wq, F32), dev_u8(sb), mode)
+    torch.cuda.synchronize()
+    yr, _ = qref.mx_qmatmul(x, F32, wq, sb, mode, k)
+    expect = torch.from_numpy(yr.astype(np.float32)).to(torch.bfloat16)
+    assert torch.equal(y.cpu(), expect)
+
+
+def test_mx_qmatmul_prefill_k_not_multiple_of_64():
+    """nvfp4 K = 96: not whole 64-wide tile steps, so the stream kernel runs
+    two activation rows at a time."""
+    run_mx(20, 70, 96, qref.NVFP4, BF16, 3200, "prefill k=96")
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_mx_qmatmul_prefill_full_size_sampled(mode):
+    """x bf16 [2048, 4096] times W [14336, 4096] in the launch configuration of
+    the benchmark; a 16 x 64 block of outputs (rows and columns spread over
+    the tiles) against the oracle."""
+    M, N, K = 2048, 14336, 4096
+    wq, sb = mx_weights(N, K, mode, 3300 + mode)
+    x_st, _ = activations((M, K), BF16, 3310 + mode)
+    log(f"full-size prefill: mode={mode}")
+    y = qp.qmatmul_mx(to_device(x_st, BF16), to_device(wq, F32), dev_u8(sb), mode)
+    torch.cuda.synchronize()
+    mi = np.linspace(0, M - 1, 16).astype(np.int64)
+    ni = np.linspace(0, N - 1, 64).astype(np.int64)
+    yr, S = qref.mx_qmatmul(x_st[mi], BF16, wq[ni], sb[ni], mode, K)
+    block = y.cpu()[torch.from_numpy(mi)][:, torch.from_numpy(ni)]
+    assert_within(block, yr, S, BF16, "full-size prefill")

@@ -203,6 +203,8 @@ qp_status qmatmul_mx(const void* x, qp_dtype x_dtype, int64_t m, int64_t k, cons
     if (!aligned(x, es) || !aligned(wq, 4))
         return fail(QP_ERR_ALIGN, "pointer not aligned to its element size");
     qp::GemvMxArgs a{x, (int)x_dtype, (int)mode, m, k, n, wq, scales, y};
+    if (m > 16 && qp::qgemm_mx_fits(a))
+        return hip_result(qp::launch_qgemm_mx(a, stream), "qmatmul_mx");
     return hip_result(qp::launch_qmatmul_mx(a, stream), "qmatmul_mx");
 }
 

@@ -37,6 +37,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "mx.hpp"
 
 namespace qp {
 
@@ -132,18 +133,25 @@ template <int BITS, int BN, int WAVES> struct CodeStage {
 
 // Scales / biases of one step: one dword per tile row for the scales, then
 // one per row for the biases (the aligned dword holding the row's first
-// group of the step; with 32-wide groups, both groups of the step).
-template <int BN> struct SbStage {
-    static constexpr int STAGE = 8 * BN;        // bytes
-    static constexpr int INSTR = 2 * BN / 64;   // dword DMA instructions per block
+// group of the step; with 32-wide groups, both groups of the step). The
+// microscaled modes (MODE > 0) have no biases, and their one-byte scales of a
+// step (two of 32-wide groups, four of 16-wide) share one aligned dword.
+// Every wave issues the same number of these DMAs (its wait counts assume
+// it), so with fewer instructions than waves the spare waves load zeros into
+// spare slots.
+template <int BN, int WAVES, int MODE = 0> struct SbStage {
+    static constexpr int ARRAYS = MODE == 0 ? 2 : 1;
+    static constexpr int INSTR = ARRAYS * BN / 64;                  // useful dword DMAs per block
+    static constexpr int PER_WAVE = (INSTR + WAVES - 1) / WAVES;    // issued by every wave
+    static constexpr int STAGE = PER_WAVE * WAVES * 256;            // bytes
 };
 
 // LDS bytes of one block: A[NA] | C[NC] | SB[NC].
-template <int BITS, int BM, int BN, int THREADS, int NA, int NC>
+template <int BITS, int BM, int BN, int THREADS, int NA, int NC, int MODE = 0>
 constexpr int lds_bytes()
 {
     return NA * BM * ROW_BYTES + NC * (CodeStage<BITS, BN, THREADS / 64>::STAGE +
-                                       SbStage<BN>::STAGE);
+                                       SbStage<BN, THREADS / 64, MODE>::STAGE);
 }
 
 // Logical 16-byte code chunk c of tile row r sits in slot r * CPR + (c ^
@@ -174,9 +182,11 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // of kt + 2): activation loads get NA - 2 steps to arrive and code loads
 // NC - 2, and the newest DMA stays in flight across the barrier.
 template <int BITS, int DT, int BM, int BN, int THREADS, int WMW, int NMAT, bool ROUTED, int NA,
-          int NC>
+          int NC, int MODE = 0>
 __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
 {
+    static_assert(MODE == 0 || (MxFmt<MODE>::BITS == BITS && NMAT == 1 && !ROUTED),
+                  "microscaled modes: dense single-matrix tiles");
     using T = MfmaTraits<DT>;
     using frag_t = typename T::frag_t;
     using CL = CodeLayout<BITS>;
@@ -199,9 +209,9 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     // Every DMA instruction writes 64 x 16 bytes, so a codes stage spans whole
     // 1 KB blocks (chunks past the tile read zeros into the spare slots).
     constexpr int C_STAGE = CodeStage<BITS, BN, WAVES>::STAGE;
-    constexpr int SB_STAGE = SbStage<BN>::STAGE;
-    constexpr int SB_INSTR = SbStage<BN>::INSTR / WAVES;   // per wave
-    static_assert(SB_INSTR * WAVES == SbStage<BN>::INSTR, "scale DMA split over waves");
+    using SBS = SbStage<BN, WAVES, MODE>;
+    constexpr int SB_STAGE = SBS::STAGE;
+    constexpr int SB_INSTR = SBS::PER_WAVE;        // per wave
     // Vector-memory operations a wave issues per step, and how many of them
     // may still be in flight when a step ends. Step kt + 1 reads the
     // activations and codes / scales of step kt + 2: the first DMA of step
@@ -309,7 +319,8 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         rw[i] = rw_of(t);
     }
     // Scales / biases: instruction j = wave * SB_INSTR + i moves the dwords of
-    // tile rows 64 (j % (BN / 64)) + lane, scales for j < BN / 64, else biases.
+    // tile rows 64 (j % (BN / 64)) + lane, scales for j < BN / 64, else biases;
+    // instructions j >= SBS::INSTR read zeros into spare slots.
     uint32_t sb_row[SB_INSTR];
     __amdgpu_buffer_rsrc_t rsb[SB_INSTR];
 #pragma unroll
@@ -317,8 +328,8 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         const int j = wave * SB_INSTR + i;
         const int r = 64 * (j % (BN / 64)) + lane;
         const int row = n0 + r % BNO;
-        sb_row[i] = row < N ? e_groups + (uint32_t)row * groups : 0x40000000u;
-        rsb[i] = rsb_of(NMAT == 1 ? 0 : (r / BNO), j >= BN / 64);
+        sb_row[i] = row < N && j < SBS::INSTR ? e_groups + (uint32_t)row * groups : 0x40000000u;
+        rsb[i] = rsb_of(NMAT == 1 ? 0 : (r / BNO), MODE == 0 && j >= BN / 64);
     }
     const uint32_t gshift = (uint32_t)__builtin_ctz((unsigned)ga.gs);
     auto dma_a = [&](int kt, int stage) {
@@ -341,7 +352,8 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
 #pragma unroll
         for (int i = 0; i < SB_INSTR; ++i) {
             // Rows past N: an offset past the end (reads zeros).
-            const uint32_t off = sb_row[i] < 0x40000000u ? ((sb_row[i] + g0) * 2) & ~3u : OOB;
+            constexpr uint32_t ES = MODE == 0 ? 2 : 1;   // bytes per scale
+            const uint32_t off = sb_row[i] < 0x40000000u ? ((sb_row[i] + g0) * ES) & ~3u : OOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsb[i],
                 (__attribute__((address_space(3))) void*)(sb_st + stage * SB_STAGE +
@@ -366,6 +378,11 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     }
     uint32_t wcode[FN][CB::NBW];
     float s_u[FN], b_u[FN];
+    // Microscaled modes: the unit's raw code words, and its scale bytes (one,
+    // or two for 16-wide groups).
+    constexpr int MX_SPU = MODE == 0 ? 1 : 32 / MxFmt<MODE == 0 ? 1 : MODE>::GS;
+    uint32_t mx_w[FN][BITS];
+    uint32_t mx_sb[FN][MX_SPU];
     // The unit's BITS words from C stage `stage`.
     auto read_unit = [&](int stage, int r, uint32_t (&w)[BITS]) {
         const char* row = c_st + stage * C_STAGE + r * CL::SLOT_ROW;
@@ -396,6 +413,22 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     auto load_units = [&](int kt, int stage) {
         const uint32_t g0 = ((uint32_t)kt * BK) >> gshift;
         const uint32_t gu = ((uint32_t)kt * BK + half * 32) >> gshift;
+        if constexpr (MODE != 0) {
+            // The row's scale bytes of the step sit in one aligned dword, from
+            // byte (b_gbase + g0) & 3 on; the lane's unit takes byte gu - g0
+            // (and the next, for 16-wide groups) of the step's.
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                read_unit(stage, bt[j], mx_w[j]);
+                const uint32_t sd = *reinterpret_cast<const uint32_t*>(sb_st + stage * SB_STAGE +
+                                                                       bt[j] * 4);
+                const uint32_t sh = ((b_gbase[j] + g0) & 3u) * 8 + (gu - g0) * 8;
+#pragma unroll
+                for (int g = 0; g < MX_SPU; ++g)
+                    mx_sb[j][g] = (sd >> (sh + 8 * g)) & 0xFFu;
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             uint32_t w[BITS];
@@ -414,6 +447,43 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     auto make_bfrag = [&](auto J, auto KK) {
         constexpr int j = decltype(J)::value, kk = decltype(KK)::value;
         uint32_t packed[4];
+        if constexpr (MODE != 0) {
+            // Codes 8 kk .. 8 kk + 7 of the unit, converted exactly to fp32,
+            // scaled by their group's scale (exact), rounded to the
+            // activation type.
+            constexpr int MXG = MODE == 0 ? 1 : MxFmt<MODE == 0 ? 1 : MODE>::GS;
+            const uint32_t sbyte = mx_sb[j][(8 * kk) / MXG];
+            float v[8];
+            if constexpr (BITS == 4) {
+                const uint32_t w = mx_w[j][kk];
+                static_for<4>([&](auto B) {
+                    constexpr int b = decltype(B)::value;
+                    const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, b);
+                    v[2 * b] = p.x;
+                    v[2 * b + 1] = p.y;
+                });
+            } else {
+                static_for<2>([&](auto H) {
+                    constexpr int h = decltype(H)::value;
+                    const uint32_t w = mx_w[j][2 * kk + h];
+                    const f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+                    const f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+                    v[4 * h] = lo.x; v[4 * h + 1] = lo.y; v[4 * h + 2] = hi.x; v[4 * h + 3] = hi.y;
+                    // 0x7F / 0xFF convert to NaN; the pages' E4M3 reads +-480.
+                    if (__builtin_expect((((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) != 0u, 0)) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            v[4 * h + c] = mx_e4m3((w >> (8 * c)) & 0xFFu);
+                    }
+                });
+            }
+            static_for<4>([&](auto P) {
+                constexpr int p = decltype(P)::value;
+                packed[p] = T::pack2(mx_scaled<MODE == 0 ? 1 : MODE>(v[2 * p], sbyte),
+                                     mx_scaled<MODE == 0 ? 1 : MODE>(v[2 * p + 1], sbyte));
+            });
+            return __builtin_bit_cast(frag_t, u32x4_t{packed[0], packed[1], packed[2], packed[3]});
+        }
         static_for<4>([&](auto P) {
             constexpr int c = 8 * kk + 2 * decltype(P)::value;
             const float w0 = __builtin_fmaf(CB::template code<c>(wcode[j]), s_u[j], b_u[j]);

@@ -78,6 +78,10 @@ struct GemvMxArgs {
     void* y;                // [M, N] of dt
 };
 hipError_t launch_qmatmul_mx(const GemvMxArgs& a, hipStream_t stream);
+// Prefill tiles for the microscaled modes (qgemm.hip): 16-bit activations,
+// K a multiple of 64, 4-byte aligned scales, operands below 2 GB.
+bool qgemm_mx_fits(const GemvMxArgs& a);
+hipError_t launch_qgemm_mx(const GemvMxArgs& a, hipStream_t stream);
 
 struct MoeArgs {
     const void* a;          // activations
