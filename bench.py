@@ -12,9 +12,10 @@ region cycles through >= 512 MB of distinct weight copies (more than twice the
 Every other row of the hot path is measured too, in `rows`: decode at 2/4/8
 bits and M = 1/4/16, the cross-word 3/6-bit layouts over three group sizes,
 both prefill GEMM shapes against the bf16 MFMA peak, the MoE gate+up+SiLU
-and down calls at T = 1/64/512 tokens, and the unfused two-kernel form
+and down calls at T = 1/64/512 tokens, the unfused two-kernel form
 (qpack_dequantize to a dense bf16 weight, then torch.matmul) at M = 1 and
-2048 beside the fused call.
+2048 beside the fused call, and the microscaled modes (mxfp4, nvfp4, mxfp8)
+at decode, prefill and dense-weight shapes.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
@@ -145,6 +146,47 @@ def bench_unfused(N, K, M, bits, gs, dt, steps, warmup, stream, dev, seed=21):
     del sets, wd
     torch.cuda.empty_cache()
     return ms_deq, ms_both, wb
+
+
+def bench_mx(mode, M, steps, warmup, stream, dev, no_nan_codes=False, what="matmul"):
+    """Microscaled W[14336, 4096] (mode 1 mxfp4, 2 mxfp8, 3 nvfp4): seeded
+    uniform random codes (mxfp8: optionally without the 0x7F / 0xFF codes) and
+    scale bytes (E8M0 118..133; nvfp4 E4M3 0x20..0x5F), x bf16 [M, 4096].
+    Returns (ms, weight bytes)."""
+    import torch
+    import weight_only_quantized_qgemv_amd as qp
+    from weight_only_quantized_qgemv_amd import synth
+    N, K = 14336, 4096
+    bits, gs = qp.MX_LAYOUT[mode]
+    wb = N * K * bits // 8 + N * (K // gs)
+    copies = copies_for(wb)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(61 + mode)
+    sets = []
+    for _ in range(copies):
+        codes = torch.randint(0, 256, (N, K * bits // 8), dtype=torch.uint8, device=dev,
+                              generator=gen)
+        if no_nan_codes:
+            codes[(codes & 0x7F) == 0x7F] -= 1          # 0x7F -> 0x7E, 0xFF -> 0xFE
+        lo, hi = (0x20, 0x5F) if mode == qp.NVFP4 else (118, 133)
+        sb = torch.randint(lo, hi + 1, (N, K // gs), dtype=torch.uint8, device=dev,
+                           generator=gen)
+        sets.append((codes.view(torch.int32), sb))
+    x = torch.from_numpy(synth.normal_f32((M, K), 1.0, 62)).to(torch.bfloat16).to(dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        wq, sb = sets[i % copies]
+        if what == "dequantize":
+            qp.qpack_dequantize_mx(wq, sb, mode, out=w)
+        else:
+            qp.qmatmul_mx(x, wq, sb, mode, out=y)
+
+    ms = time_calls(step, steps, warmup, stream)
+    del sets
+    torch.cuda.empty_cache()
+    return ms, wb
 
 
 def bench_moe(T, steps, warmup, stream, dev):
@@ -325,6 +367,24 @@ def main():
                 "dequantize_then_matmul_us": round(ms_both * 1e3, 3),
                 "fused_us": fused_us,
                 "fused_speedup": round(ms_both * 1e3 / fused_us, 2)}
+        # Microscaled rows: decode M = 1, prefill M = 2048, dense weight.
+        for mode, name in ((1, "mxfp4"), (3, "nvfp4"), (2, "mxfp8")):
+            for variant in ((False, True) if mode == 2 else (False,)):
+                tag = name + ("_no480" if variant else "")
+                ms_r, wb_r = bench_mx(mode, 1, del_steps, 5, stream, dev, no_nan_codes=variant)
+                g = wb_r / (ms_r * 1e-3) / 1e9
+                rows[f"mx_decode_{tag}_m1"] = {"us": round(ms_r * 1e3, 3), "weight_GBps": round(g, 1),
+                                               "frac_hbm": round(g / HBM_PEAK_GBS, 4)}
+                ms_r, _ = bench_mx(mode, 2048, 20, 3, stream, dev, no_nan_codes=variant)
+                tf = 2.0 * 2048 * N * K / (ms_r * 1e-3) / 1e12
+                rows[f"mx_prefill_{tag}_m2048"] = {
+                    "us": round(ms_r * 1e3, 2), "tflops": round(tf, 1),
+                    "frac_bf16_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+            ms_r, wb_r = bench_mx(mode, 1, 50, 5, stream, dev, what="dequantize")
+            moved = wb_r + N * K * 2
+            rows[f"mx_dequantize_{name}"] = {
+                "us": round(ms_r * 1e3, 3), "GBps": round(moved / (ms_r * 1e-3) / 1e9, 1),
+                "frac_hbm": round(moved / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # MoE rows: 128 experts, top-8, 4-bit gs64 bf16.
         for T in (1, 64, 512):
             ms_gu, ms_d, touched, per_expert = bench_moe(T, del_steps, 5, stream, dev)

@@ -469,11 +469,14 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
                     const f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
                     const f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
                     v[4 * h] = lo.x; v[4 * h + 1] = lo.y; v[4 * h + 2] = hi.x; v[4 * h + 3] = hi.y;
-                    // 0x7F / 0xFF convert to NaN; the pages' E4M3 reads +-480.
+                    // 0x7F / 0xFF convert to NaN; the pages' E4M3 reads +-480
+                    // (fp32 0x43F00000, with the code's sign).
                     if (__builtin_expect((((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) != 0u, 0)) {
 #pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            v[4 * h + c] = mx_e4m3((w >> (8 * c)) & 0xFFu);
+                        for (int c = 0; c < 4; ++c) {
+                            const float fix = __uint_as_float(0x43F00000u | ((w << (24 - 8 * c)) & 0x80000000u));
+                            v[4 * h + c] = v[4 * h + c] != v[4 * h + c] ? fix : v[4 * h + c];
+                        }
                     }
                 });
             }

@@ -13,10 +13,10 @@
 // activation type (every FP4-E2M1 and FP8-E4M3 value is exact in bf16 and
 // fp16), v_dot2 forms the unit's partial sum in fp32, and the group scale is
 // applied to that sum. The conversions read FP8 0x7F / 0xFF as NaN where the
-// pages' E4M3 has +-480: a unit holding such a code (found with integer ops
-// on its code words) is summed with the exact decode instead. D rows are
-// loaded before any is reduced, and each wave's partial sums meet in a DPP
-// reduction.
+// pages' E4M3 has +-480: in a unit holding such a code (found with integer
+// ops on its code words) those halves of the converted pairs are replaced by
+// +-480 before the products. D rows are loaded before any is reduced, and
+// each wave's partial sums meet in a DPP reduction.
 //
 // Generic kernel (fp32 activations and every other shape): one wave per
 // (activation row, weight row), lanes over the groups of the row, exact
@@ -39,6 +39,22 @@ struct MxKArgs {
     uint32_t row_bytes, groups_row, units_row;
 };
 
+// Pair `hi` (bytes 2, 3, else 0, 1) of FP8 word w converted to 16-bit `pair`,
+// with the halves whose code is 0x7F / 0xFF (NaN to the conversion, +-480 on
+// the pages) replaced by +-480 (`m480`: 480 in the 16-bit type). Bit 7 of a
+// byte of f flags such a code; v_perm replicates a flag into the half's mask
+// (selector 8 / 9: bit 15 / 31 of the low source, 10 / 11: of the high one),
+// and the half's sign comes from its code's bit 7 the same way.
+__device__ __forceinline__ uint32_t fp8_fix_nan(uint32_t pair, uint32_t w, bool hi, uint32_t m480)
+{
+    const uint32_t f = ((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    const uint32_t sel = hi ? 0x0B0B0909u : 0x0A0A0808u;
+    const uint32_t mask = __builtin_amdgcn_perm(f, f << 8, sel);
+    const uint32_t sign = __builtin_amdgcn_perm(w, w << 8, sel) & 0x80008000u;
+    const uint32_t repl = m480 | (m480 << 16) | sign;
+    return (repl & mask) | (pair & ~mask);
+}
+
 template <int DT> struct MxPair;
 template <> struct MxPair<DT_BF16> {
     using pair_t = bf16x2_t;
@@ -55,6 +71,11 @@ template <> struct MxPair<DT_BF16> {
     {
         return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
                   : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    }
+    static __device__ __forceinline__ pair_t fp8_fixed(uint32_t w, bool hi)
+    {
+        const uint32_t p = __builtin_bit_cast(uint32_t, fp8(w, hi));
+        return __builtin_bit_cast(pair_t, fp8_fix_nan(p, w, hi, 0x43F0u));   // bf16 480
     }
     static __device__ __forceinline__ float dot(pair_t a, uint32_t x, float acc)
     {
@@ -76,6 +97,11 @@ template <> struct MxPair<DT_F16> {
     {
         return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
                   : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    }
+    static __device__ __forceinline__ pair_t fp8_fixed(uint32_t w, bool hi)
+    {
+        const uint32_t p = __builtin_bit_cast(uint32_t, fp8(w, hi));
+        return __builtin_bit_cast(pair_t, fp8_fix_nan(p, w, hi, 0x5F80u));   // fp16 480
     }
     static __device__ __forceinline__ float dot(pair_t a, uint32_t x, float acc)
     {
@@ -193,11 +219,14 @@ __global__ __launch_bounds__(256) void qgemv_mx_stream_kernel(MxKArgs a)
                                                   part[0]);
                             }
                         } else {
-                            // A 0x7F / 0xFF code: the exact decode, in k order.
-                            for (int c = 0; c < 32; ++c) {
-                                const uint32_t code = (w[d][j][c >> 2] >> (8 * (c & 3))) & 0xFFu;
-                                part[0] = __builtin_fmaf(mx_e4m3(code),
-                                                         pair_elem<DT>(xr[m][j][c >> 1], c), part[0]);
+                            // A 0x7F / 0xFF code: its half of the converted pair
+                            // is replaced by +-480 before the product.
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                const uint32_t wi = w[d][j][i];
+                                part[0] = PX::dot(PX::fp8_fixed(wi, false), xr[m][j][2 * i], part[0]);
+                                part[0] = PX::dot(PX::fp8_fixed(wi, true), xr[m][j][2 * i + 1],
+                                                  part[0]);
                             }
                         }
                     }
