@@ -507,6 +507,65 @@ int qref_moe_gate_up_silu(const void* a, int a_dtype, const int32_t* ids, int64_
 }
 
 /* ------------------------------------------------------------------ */
+/* MoE feed-forward block                                              */
+/* ------------------------------------------------------------------ */
+/* One MoE FFN block over stacked experts, as the ferrum-kernels MoE calls
+ * chain (`gemv_moe_id_gate_up_silu` into `gemv_moe_id_batched`, each storing
+ * its output in the activation type), closed by the weighted sum over each
+ * token's top_k slots, which the pages leave to the caller:
+ *   h[p]   = RNE_dt(SiLU(a_t Wg[e]^T) * (a_t Wu[e]^T)),   p = t*top_k + j, e = ids[p]
+ *   o[p]   = RNE_dt(h[p] Wd[e]^T)
+ *   out[t] = sum_j rw[t*top_k + j] * o[t*top_k + j]       (fp64, j in order)
+ * a: [n_tokens, d_model]; gate / up: [E, d_ff, d_model*bits/32]; down:
+ * [E, d_model, d_ff*bits/32]. h_out [P, d_ff] and o_out [P, d_model] receive
+ * the rounded intermediates (storage of a_dtype); out is [n_tokens, d_model]. */
+int qref_moe_ffn(const void* a, int a_dtype, const int32_t* ids, const float* rw,
+                 int64_t n_tokens, int64_t top_k, const uint32_t* gate_wq, const void* gate_s,
+                 const void* gate_b, const uint32_t* up_wq, const void* up_s, const void* up_b,
+                 const uint32_t* down_wq, const void* down_s, const void* down_b, int sb_dtype,
+                 int64_t num_experts, int64_t d_model, int64_t d_ff, int bits, int group_size,
+                 double* out, void* h_out, void* o_out)
+{
+    int64_t P = n_tokens * top_k;
+    size_t nh = (size_t)(P * d_ff > 0 ? P * d_ff : 1), no = (size_t)(P * d_model > 0 ? P * d_model : 1);
+    double* silu_v = (double*)malloc(nh * sizeof(double));
+    double* g = (double*)malloc(nh * sizeof(double));
+    double* u = (double*)malloc(nh * sizeof(double));
+    double* Sg = (double*)malloc(nh * sizeof(double));
+    double* Su = (double*)malloc(nh * sizeof(double));
+    double* o = (double*)malloc(no * sizeof(double));
+    double* So = (double*)malloc(no * sizeof(double));
+    int rc = -1;
+    if (!silu_v || !g || !u || !Sg || !Su || !o || !So)
+        goto done;
+    rc = qref_moe_gate_up_silu(a, a_dtype, ids, n_tokens, top_k, d_model, 0, gate_wq, gate_s,
+                               gate_b, up_wq, up_s, up_b, sb_dtype, num_experts, d_ff, d_model,
+                               bits, group_size, silu_v, g, u, Sg, Su);
+    if (rc)
+        goto done;
+    for (int64_t i = 0; i < P * d_ff; ++i)
+        round_to_type(silu_v[i], a_dtype, h_out, i);
+    rc = qref_moe(h_out, a_dtype, ids, n_tokens, top_k, top_k * d_ff, d_ff, down_wq, down_s,
+                  down_b, sb_dtype, num_experts, d_model, d_ff, bits, group_size, o, So);
+    if (rc)
+        goto done;
+    for (int64_t i = 0; i < P * d_model; ++i)
+        round_to_type(o[i], a_dtype, o_out, i);
+    for (int64_t t = 0; t < n_tokens; ++t)
+        for (int64_t d = 0; d < d_model; ++d) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < top_k; ++j) {
+                int64_t p = t * top_k + j;
+                acc += (double)rw[p] * (double)load_elem(o_out, a_dtype, p * d_model + d);
+            }
+            out[t * d_model + d] = acc;
+        }
+done:
+    free(silu_v); free(g); free(u); free(Sg); free(Su); free(o); free(So);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
 /* Microscaled modes                                                   */
 /* ------------------------------------------------------------------ */
 /* emily lib/emily/quantization.ex, `dequantize_mxfp4_impl`,

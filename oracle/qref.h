@@ -100,6 +100,16 @@ int qref_moe_gate_up_silu(const void* a, int a_dtype, const int32_t* ids,
                           int64_t n_cols, int bits, int group_size,
                           double* silu_out, double* g, double* u, double* Sg, double* Su);
 
+/* MoE FFN block: gate+up+SiLU, down, then out[t] = sum_j rw[t*top_k+j] *
+ * o[t*top_k+j] in fp64, with the intermediates h [P, d_ff] and o [P, d_model]
+ * rounded to a_dtype (returned in h_out / o_out). out: [n_tokens, d_model]. */
+int qref_moe_ffn(const void* a, int a_dtype, const int32_t* ids, const float* rw,
+                 int64_t n_tokens, int64_t top_k, const uint32_t* gate_wq, const void* gate_s,
+                 const void* gate_b, const uint32_t* up_wq, const void* up_s, const void* up_b,
+                 const uint32_t* down_wq, const void* down_s, const void* down_b, int sb_dtype,
+                 int64_t num_experts, int64_t d_model, int64_t d_ff, int bits, int group_size,
+                 double* out, void* h_out, void* o_out);
+
 /* Microscaled modes: no biases, one scale byte per group of lanes.
  *   mode 1 = mxfp4 (4-bit FP4-E2M1 lanes, gs 32, E8M0 scales),
  *   mode 2 = mxfp8 (8-bit FP8-E4M3 lanes as MLX decodes them, gs 32, E8M0),

@@ -68,6 +68,7 @@ def lib():
         L.qref_moe_gate_up_silu.argtypes = [P, I, P, I64, I64, I64, I64, P, P, P, P, P, P, I,
                                             I64, I64, I64, I, I, P, P, P, P, P]
         L.qref_mx_params.argtypes = [I, P, P]
+        L.qref_moe_ffn.argtypes = [P, I, P, P, I64, I64] + [P] * 9 + [I, I64, I64, I64, I, I, P, P, P]
         for f in ("qref_fp4_e2m1", "qref_fp8_e4m3", "qref_e8m0"):
             getattr(L, f).restype = ctypes.c_double
             getattr(L, f).argtypes = [ctypes.c_uint32]
@@ -230,6 +231,24 @@ def moe_gate_up_silu(a, a_dtype, ids, n_tokens, top_k, a_outer, a_inner, gate, u
         _p(res["silu_out"]), _p(res["g"]), _p(res["u"]), _p(res["Sg"]), _p(res["Su"])),
         "moe_gate_up_silu")
     return res
+
+
+def moe_ffn(a, a_dtype, ids, rw, n_tokens, top_k, gate, up, down, sb_dtype, num_experts,
+            d_model, d_ff, bits, group_size):
+    """gate, up, down: (wq, s, b). Returns (out fp64 [T, d_model], h, o) with h
+    [P, d_ff] and o [P, d_model] the intermediates in a_dtype storage."""
+    a = np.ascontiguousarray(a)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    rw = np.ascontiguousarray(rw, dtype=np.float32)
+    P = n_tokens * top_k
+    out = np.empty((n_tokens, d_model), dtype=np.float64)
+    h = _sb_empty((P, d_ff), a_dtype)
+    o = _sb_empty((P, d_model), a_dtype)
+    ws = [np.ascontiguousarray(x) for trio in (gate, up, down) for x in trio]
+    _check(lib().qref_moe_ffn(_p(a), a_dtype, _p(ids), _p(rw), n_tokens, top_k,
+                              *[_p(x) for x in ws], sb_dtype, num_experts, d_model, d_ff, bits,
+                              group_size, _p(out), _p(h), _p(o)), "moe_ffn")
+    return out, h, o
 
 
 MXFP4, MXFP8, NVFP4 = 1, 2, 3

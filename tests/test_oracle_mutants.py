@@ -51,6 +51,11 @@ MUTANTS = [
     ("mx_group_index", "uint32_t sb = row_scales[i / group_size];",
      "uint32_t sb = row_scales[i / 32];", FAST),
     ("mx_magnitude_sum", "mag += fabs(term);", "mag += term;", FAST),
+    ("ffn_slot_row", "acc += (double)rw[p] * (double)load_elem(o_out, a_dtype, p * d_model + d);",
+     "acc += (double)rw[p] * (double)load_elem(o_out, a_dtype, (t + j * n_tokens) * d_model + d);",
+     FAST),
+    ("ffn_h_unrounded", "round_to_type(silu_v[i], a_dtype, h_out, i);",
+     "round_to_type(silu_v[i] * 1.001, a_dtype, h_out, i);", FAST),
     ("rne_ties_up", "r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "r = lo + 1.0;", "rne"),
     ("f16_decode_exponent", "v = ldexp((double)(1024 + m), e - 25);",
      "v = ldexp((double)(1024 + m), e - 24);", "f16 or decoders"),

@@ -379,6 +379,61 @@ def test_dequantize_typed_rounds_product_then_sum():
     assert qref.dequantize(wq, s, b, BF16, 32, 4, 32)[0, 0] == 3.0 + 2.0 ** -6
 
 
+# ---------------------------------------------------------------- MoE FFN block
+
+def _ffn_case(T=5, top_k=3, E=6, D=64, F=96, bits=4, gs=32, dt=BF16, seed=1900):
+    def stack(rows, cols, s):
+        w = synth.normal_f32((E * rows, cols), 0.05, s)
+        wq, sc, bi = qref.quantize(w, bits, gs, dt)
+        return wq.reshape(E, rows, -1), sc.reshape(E, rows, -1), bi.reshape(E, rows, -1)
+    gate, up, down = stack(F, D, seed), stack(F, D, seed + 1), stack(D, F, seed + 2)
+    a = store(synth.normal_f32((T, D), 1.0, seed + 3), dt)
+    ids = np.stack([synth.rng(seed + 4 + t).permutation(E)[:top_k] for t in range(T)]).ravel()
+    rw = synth.normal_f32((T * top_k,), 0.5, seed + 5)
+    return dict(a=a, ids=ids.astype(np.int32), rw=rw, T=T, top_k=top_k, E=E, D=D, F=F,
+                bits=bits, gs=gs, dt=dt, gate=gate, up=up, down=down)
+
+
+def _ffn(c, ids=None, rw=None):
+    return qref.moe_ffn(c["a"], c["dt"], c["ids"] if ids is None else ids,
+                        c["rw"] if rw is None else rw, c["T"], c["top_k"], c["gate"], c["up"],
+                        c["down"], c["dt"], c["E"], c["D"], c["F"], c["bits"], c["gs"])
+
+
+def test_moe_ffn_composes_the_pinned_moe_products():
+    """Gate+up+SiLU, rounded to bf16 by torch, then down, rounded by torch, then
+    the slot sum in numpy: the block's definition rebuilt from the pinned MoE
+    products and library roundings."""
+    c = _ffn_case()
+    out, h, o = _ffn(c)
+    r = qref.moe_gate_up_silu(c["a"], c["dt"], c["ids"], c["T"], c["top_k"], c["D"], 0,
+                              c["gate"], c["up"], c["dt"], c["E"], c["F"], c["D"], c["bits"], c["gs"])
+    h_ref = to_bits16(r["silu_out"].astype(np.float32), BF16)
+    assert np.array_equal(h, h_ref)
+    y, _ = qref.moe(h_ref, BF16, c["ids"], c["T"], c["top_k"], c["top_k"] * c["F"], c["F"],
+                    *c["down"], c["dt"], c["E"], c["D"], c["F"], c["bits"], c["gs"])
+    o_ref = to_bits16(y.astype(np.float32), BF16)
+    assert np.array_equal(o, o_ref)
+    ov = values(o_ref, BF16).astype(np.float64).reshape(c["T"], c["top_k"], c["D"])
+    expect = (c["rw"].astype(np.float64).reshape(c["T"], c["top_k"], 1) * ov).sum(axis=1)
+    assert np.allclose(out, expect, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_ffn_slot_order_and_linearity():
+    c = _ffn_case(seed=1950)
+    out, _, _ = _ffn(c)
+    perm = np.concatenate([t * c["top_k"] + synth.rng(1960 + t).permutation(c["top_k"])
+                           for t in range(c["T"])])
+    out_p, _, _ = _ffn(c, ids=c["ids"][perm], rw=c["rw"][perm])
+    assert np.allclose(out_p, out, rtol=1e-12, atol=1e-12)
+    rw2 = synth.normal_f32(c["rw"].shape, 0.5, 1970)
+    out2, _, _ = _ffn(c, rw=rw2)
+    out12, _, _ = _ffn(c, rw=(c["rw"].astype(np.float64) + rw2).astype(np.float32))
+    assert np.allclose(out12, out + out2, rtol=1e-6, atol=1e-6)
+    zero, _, _ = _ffn(c, rw=np.zeros_like(c["rw"]))
+    assert not zero.any()
+
+
 # ---------------------------------------------------------------- microscaled modes
 
 def load_mx_luts():
