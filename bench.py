@@ -222,13 +222,23 @@ def bench_moe(T, steps, warmup, stream, dev):
         _, _, d = wsets[i % 2]
         qp.qgemv_moe_id(h, ids, T, top_k, top_k * F, F, *d, bits, gs, out=o, workspace=ws)
 
+    rw = torch.from_numpy(synth.normal_f32((P,), 0.4, 56)).to(dev)
+    out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    ffn_ws = torch.empty(qp.qgemv_moe_ffn_workspace_bytes(T, top_k, E, D, F, torch.bfloat16),
+                         dtype=torch.uint8, device=dev)
+
+    def ffn(i):
+        g, u, d = wsets[i % 2]
+        qp.qgemv_moe_ffn(a, ids, rw, top_k, g, u, d, bits, gs, out=out, workspace=ffn_ws)
+
     ms_gu = time_calls(gate_up, steps, warmup, stream)
     ms_d = time_calls(down, steps, warmup, stream)
+    ms_ffn = time_calls(ffn, steps, warmup, stream)
     touched = len(np.unique(ids_np))
     per_expert = weight_bytes(F, D, bits, gs, 2)   # one [768, 2048] matrix
     del wsets
     torch.cuda.empty_cache()
-    return ms_gu, ms_d, touched, per_expert
+    return ms_gu, ms_d, ms_ffn, touched, per_expert
 
 
 def cpu_baseline(n, k, bits, gs, budget_s=12.0):
@@ -387,7 +397,7 @@ def main():
                 "frac_hbm": round(moved / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # MoE rows: 128 experts, top-8, 4-bit gs64 bf16.
         for T in (1, 64, 512):
-            ms_gu, ms_d, touched, per_expert = bench_moe(T, del_steps, 5, stream, dev)
+            ms_gu, ms_d, ms_ffn, touched, per_expert = bench_moe(T, del_steps, 5, stream, dev)
             gu_bytes, d_bytes = 2 * touched * per_expert, touched * per_expert
             rows[f"moe_t{T}"] = {
                 "experts_touched": touched,
@@ -396,7 +406,9 @@ def main():
                 "down_us": round(ms_d * 1e3, 3),
                 "down_weight_GBps": round(d_bytes / (ms_d * 1e-3) / 1e9, 1),
                 "tflops_total": round(2.0 * T * 8 * 3 * 768 * 2048 / ((ms_gu + ms_d) * 1e-3)
-                                      / 1e12, 2)}
+                                      / 1e12, 2),
+                "ffn_block_us": round(ms_ffn * 1e3, 3),
+                "ffn_block_weight_GBps": round(3 * touched * per_expert / (ms_ffn * 1e-3) / 1e9, 1)}
         result["rows"] = rows
 
     if not args.no_cpu_baseline:

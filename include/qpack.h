@@ -230,6 +230,43 @@ const char* qpack_last_error(void);
 /* Library version string. */
 const char* qpack_version(void);
 
+/*
+ * Workspace (bytes) of qgemv_moe_ffn: the routing tables of n_tokens*top_k
+ * pairs, then the intermediates h [P, d_ff] and o [P, d_model] in `dtype`.
+ * 0 for invalid sizes.
+ */
+size_t qgemv_moe_ffn_workspace_bytes(int64_t n_tokens, int64_t top_k, int64_t num_experts,
+                                     int64_t d_model, int64_t d_ff, qp_dtype dtype);
+
+/*
+ * One MoE feed-forward block over stacked experts, on the device with no
+ * host round trip (ferrum-kernels stacked_expert.rs: the fused gate/up call
+ * `gemv_moe_id_gate_up_silu`, then the down call `gemv_moe_id_batched` on its
+ * output; the weighted sum over a token's slots, which the pages leave to
+ * the caller, closes it):
+ *   h[p] = SiLU(a_t Wg[e]^T) * (a_t Wu[e]^T),  o[p] = h[p] Wd[e]^T,
+ *   out[t] = sum_j route_weights[t*top_k + j] * o[t*top_k + j],
+ *   p = t*top_k + j, e = ids[p]; h and o are stored in a_dtype.
+ *   a              device, a_dtype [n_tokens, d_model] (contiguous)
+ *   ids            device, int32 [n_tokens*top_k]
+ *   route_weights  device, fp32 [n_tokens*top_k]
+ *   gate_*, up_*   device, expert stacks [E, d_ff, d_model*bits/32], s/b [E, d_ff, d_model/gs]
+ *   down_*         device, expert stack [E, d_model, d_ff*bits/32], s/b [E, d_model, d_ff/gs]
+ *   out            device, a_dtype [n_tokens, d_model] (output)
+ *   workspace      device, >= qgemv_moe_ffn_workspace_bytes(...), 16-byte aligned
+ * The slot sum is taken in fp32 in slot order; a slot whose id is outside
+ * [0, E) adds nothing. Errors as for the MoE calls above. n_tokens == 0 or
+ * d_model == 0 is a no-op; top_k == 0 or d_ff == 0 writes zeros.
+ */
+qp_status qgemv_moe_ffn(const void* a, qp_dtype a_dtype, const int32_t* ids,
+                        const float* route_weights, int64_t n_tokens, int64_t top_k,
+                        const uint32_t* gate_wq, const void* gate_scales, const void* gate_biases,
+                        const uint32_t* up_wq, const void* up_scales, const void* up_biases,
+                        const uint32_t* down_wq, const void* down_scales, const void* down_biases,
+                        qp_dtype sb_dtype, int64_t num_experts, int64_t d_model, int64_t d_ff,
+                        int32_t bits, int32_t group_size, void* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -154,6 +154,35 @@ def test_qmatmul_mx_empty_is_a_noop():
     assert qmatmul_mx(n=0, x=None, y=None) == OK
 
 
+def ffn(a=A, dt=BF16, ids=A, rw=A, T=2, top_k=2, sdt=BF16, E=4, D=64, F=64, bits=4, gs=64,
+        out=A, ws=A, ws_bytes=None):
+    L = qp.lib()
+    if ws_bytes is None:
+        ws_bytes = L.qgemv_moe_ffn_workspace_bytes(T, top_k, E, D, F, dt)
+    return L.qgemv_moe_ffn(a, dt, ids, rw, T, top_k, *([A] * 9), sdt, E, D, F, bits, gs, out, ws,
+                           ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=5), UNSUPPORTED), (dict(F=96), SHAPE), (dict(D=96), SHAPE), (dict(dt=F16), MISMATCH),
+    (dict(T=-1), INVALID), (dict(out=None), INVALID), (dict(ws=None), INVALID),
+    (dict(rw=None), INVALID), (dict(ids=None), INVALID), (dict(ws_bytes=64), WORKSPACE),
+    (dict(out=ODD), ALIGN), (dict(rw=P(0x10002)), ALIGN), (dict(E=5000), UNSUPPORTED),
+])
+def test_moe_ffn_argument_errors(kw, status):
+    assert ffn(**kw) == status
+
+
+def test_moe_ffn_empty_and_workspace_size():
+    assert ffn(T=0, a=None, out=None, ws=None) == OK
+    assert ffn(D=0, a=None, out=None, ws=None) == OK
+    L = qp.lib()
+    small = L.qgemv_moe_ffn_workspace_bytes(4, 8, 128, 2048, 768, BF16)
+    big = L.qgemv_moe_ffn_workspace_bytes(64, 8, 128, 2048, 768, BF16)
+    assert small >= 4 * 8 * (2048 + 768) * 2 and big > small
+    assert L.qgemv_moe_ffn_workspace_bytes(-1, 8, 128, 2048, 768, BF16) == 0
+
+
 def moe(fused=False, a=A, dt=BF16, ids=A, T=2, top_k=2, outer=64, inner=0, sdt=BF16, E=4, R=8,
         C=64, bits=4, gs=64, out=A, ws=A, ws_bytes=None):
     L = qp.lib()

@@ -27,8 +27,9 @@ STATUS = {0: "QP_OK", 1: "QP_ERR_INVALID_ARG", 2: "QP_ERR_UNSUPPORTED",
           6: "QP_ERR_WORKSPACE", 7: "QP_ERR_HIP"}
 
 # Every symbol include/qpack.h declares.
-EXPORTS = ("qpack_quantize", "qpack_dequantize", "qpack_dequantize_mx", "qmatmul", "qmatmul_mx", "qgemv_moe_workspace_bytes", "qgemv_moe_id",
-           "qgemv_moe_id_gate_up_silu", "qpack_last_error", "qpack_version")
+EXPORTS = ("qpack_quantize", "qpack_dequantize", "qpack_dequantize_mx", "qmatmul", "qmatmul_mx",
+           "qgemv_moe_workspace_bytes", "qgemv_moe_id", "qgemv_moe_id_gate_up_silu",
+           "qgemv_moe_ffn_workspace_bytes", "qgemv_moe_ffn", "qpack_last_error", "qpack_version")
 
 
 class QpackError(RuntimeError):
@@ -70,6 +71,11 @@ def lib() -> ctypes.CDLL:
                                                 P, P, P, ctypes.c_int, I64, I64, I64, I32, I32,
                                                 P, P, SZ, P]
         L.qgemv_moe_id_gate_up_silu.restype = ctypes.c_int
+        L.qgemv_moe_ffn_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, ctypes.c_int]
+        L.qgemv_moe_ffn_workspace_bytes.restype = SZ
+        L.qgemv_moe_ffn.argtypes = ([P, ctypes.c_int, P, P, I64, I64] + [P] * 9 +
+                                    [ctypes.c_int, I64, I64, I64, I32, I32, P, P, SZ, P])
+        L.qgemv_moe_ffn.restype = ctypes.c_int
         L.qpack_last_error.restype = ctypes.c_char_p
         L.qpack_version.restype = ctypes.c_char_p
         _lib = L
@@ -266,4 +272,34 @@ def qgemv_moe_id_gate_up_silu(a, ids, n_tokens: int, top_k: int, a_outer: int, a
         _ptr(a), dtype_code(a.dtype), _ptr(ids), n_tokens, top_k, a_outer, a_inner, _ptr(gwq),
         _ptr(gs_), _ptr(gb), _ptr(uwq), _ptr(us), _ptr(ub), dtype_code(gs_.dtype), E, n_rows,
         n_cols, bits, group_size, _ptr(out), _ptr(workspace), workspace.numel(), _stream(a)))
+    return out
+
+
+def qgemv_moe_ffn_workspace_bytes(n_tokens: int, top_k: int, num_experts: int, d_model: int,
+                                  d_ff: int, dtype) -> int:
+    return int(lib().qgemv_moe_ffn_workspace_bytes(n_tokens, top_k, num_experts, d_model, d_ff,
+                                                   dtype_code(dtype)))
+
+
+def qgemv_moe_ffn(a, ids, route_weights, top_k: int, gate, up, down, bits: int, group_size: int,
+                  out=None, workspace=None):
+    """One MoE FFN block: a [T, d_model], ids int32 [T*top_k], route_weights fp32
+    [T*top_k]; gate / up / down = (wq, scales, biases) expert stacks. Returns
+    out [T, d_model] in a's dtype."""
+    import torch
+    for t, nm in ((a, "a"), (ids, "ids"), (route_weights, "route_weights")):
+        _dev(t, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    T, D = a.shape
+    E, F = gate[0].shape[0], gate[0].shape[1]
+    if workspace is None:
+        nbytes = qgemv_moe_ffn_workspace_bytes(T, top_k, E, D, F, a.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=a.device)
+    if out is None:
+        out = torch.empty((T, D), dtype=a.dtype, device=a.device)
+    ptrs = [_ptr(x) for trio in (gate, up, down) for x in trio]
+    check(lib().qgemv_moe_ffn(_ptr(a), dtype_code(a.dtype), _ptr(ids), _ptr(route_weights), T,
+                              top_k, *ptrs, dtype_code(gate[1].dtype), E, D, F, bits, group_size,
+                              _ptr(out), _ptr(workspace), workspace.numel(), _stream(a)))
     return out

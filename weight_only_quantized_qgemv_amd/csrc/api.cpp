@@ -352,6 +352,95 @@ qp_status qgemv_moe_id_gate_up_silu(const void* a, qp_dtype a_dtype, const int32
     return hip_result(qp::launch_moe(m, stream), "qgemv_moe_id_gate_up_silu");
 }
 
+static size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t qgemv_moe_ffn_workspace_bytes(int64_t n_tokens, int64_t top_k, int64_t num_experts,
+                                     int64_t d_model, int64_t d_ff, qp_dtype dtype)
+{
+    if (n_tokens < 0 || top_k < 0 || num_experts < 0 || d_model < 0 || d_ff < 0 ||
+        !dtype_ok(dtype) || !mul_ok(n_tokens, top_k))
+        return 0;
+    const int64_t P = n_tokens * top_k;
+    if (!mul_ok(P, d_ff) || !mul_ok(P, d_model))
+        return 0;
+    const size_t es = esize(dtype);
+    return round256(qp::moe_workspace_bytes(P, num_experts)) + round256((size_t)(P * d_ff) * es) +
+           (size_t)(P * d_model) * es;
+}
+
+qp_status qgemv_moe_ffn(const void* a, qp_dtype a_dtype, const int32_t* ids,
+                        const float* route_weights, int64_t n_tokens, int64_t top_k,
+                        const uint32_t* gate_wq, const void* gate_scales, const void* gate_biases,
+                        const uint32_t* up_wq, const void* up_scales, const void* up_biases,
+                        const uint32_t* down_wq, const void* down_scales, const void* down_biases,
+                        qp_dtype sb_dtype, int64_t num_experts, int64_t d_model, int64_t d_ff,
+                        int32_t bits, int32_t group_size, void* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream)
+{
+    const char* what = "qgemv_moe_ffn";
+    if (dtype_ok(a_dtype) && dtype_ok(sb_dtype) && a_dtype != sb_dtype)
+        return fail(QP_ERR_DTYPE_MISMATCH, "%s: input dtype must match scales dtype", what);
+    if (n_tokens < 0 || top_k < 0 || num_experts < 0 || d_model < 0 || d_ff < 0)
+        return fail(QP_ERR_INVALID_ARG, "%s: negative size", what);
+    if (!dtype_ok(a_dtype))
+        return fail(QP_ERR_INVALID_ARG, "%s: unknown dtype", what);
+    if (qp_status s = check_layout(d_model, bits, group_size); s != QP_OK)
+        return s;
+    if (qp_status s = check_layout(d_ff, bits, group_size); s != QP_OK)
+        return s;
+    if (!mul_ok(n_tokens, top_k) || n_tokens * top_k > (int64_t)INT32_MAX / 2 ||
+        !mul_ok(n_tokens, d_model))
+        return fail(QP_ERR_INVALID_ARG, "%s: too many pairs", what);
+    const int64_t P = n_tokens * top_k;
+    if (n_tokens == 0 || d_model == 0)
+        return ok();
+    if (!out)
+        return fail(QP_ERR_INVALID_ARG, "%s: null output pointer", what);
+    if (!aligned(out, esize(a_dtype)))
+        return fail(QP_ERR_ALIGN, "%s: output not aligned", what);
+    if (P == 0 || d_ff == 0) // empty slot sums, or h = 0 and so o = 0
+        return hip_result(qp::launch_fill_zero(out, (int)a_dtype, n_tokens * d_model, stream), what);
+    const size_t need = qgemv_moe_ffn_workspace_bytes(n_tokens, top_k, num_experts, d_model, d_ff,
+                                                      a_dtype);
+    if (!workspace || !route_weights)
+        return fail(QP_ERR_INVALID_ARG, "%s: null pointer", what);
+    if (workspace_bytes < need)
+        return fail(QP_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", what,
+                    workspace_bytes, need);
+    if (!aligned(route_weights, 4))
+        return fail(QP_ERR_ALIGN, "%s: router weights not aligned", what);
+    const size_t es = esize(a_dtype);
+    const size_t route_bytes = round256(qp::moe_workspace_bytes(P, num_experts));
+    char* h = static_cast<char*>(workspace) + route_bytes;
+    char* o = h + round256((size_t)(P * d_ff) * es);
+
+    qp::MoeArgs gu{};
+    gu.a = a; gu.dt = (int)a_dtype; gu.ids = ids;
+    gu.n_tokens = n_tokens; gu.top_k = top_k; gu.a_outer = d_model; gu.a_inner = 0;
+    gu.wq[0] = gate_wq; gu.scales[0] = gate_scales; gu.biases[0] = gate_biases;
+    gu.wq[1] = up_wq; gu.scales[1] = up_scales; gu.biases[1] = up_biases;
+    gu.E = num_experts; gu.n_rows = d_ff; gu.n_cols = d_model; gu.bits = bits; gu.gs = group_size;
+    gu.fused_silu = true; gu.out = h; gu.workspace = workspace; gu.ws_bytes = route_bytes;
+    qp::MoeArgs dn{};
+    dn.a = h; dn.dt = (int)a_dtype; dn.ids = ids;
+    dn.n_tokens = n_tokens; dn.top_k = top_k; dn.a_outer = top_k * d_ff; dn.a_inner = d_ff;
+    dn.wq[0] = dn.wq[1] = down_wq; dn.scales[0] = dn.scales[1] = down_scales;
+    dn.biases[0] = dn.biases[1] = down_biases;
+    dn.E = num_experts; dn.n_rows = d_model; dn.n_cols = d_ff; dn.bits = bits; dn.gs = group_size;
+    dn.fused_silu = false; dn.out = o; dn.workspace = workspace; dn.ws_bytes = route_bytes;
+    if (qp_status s = moe_common(gu, what); s != QP_OK)
+        return s;
+    if (qp_status s = moe_common(dn, what); s != QP_OK)
+        return s;
+    if (hipError_t e = qp::launch_moe(gu, stream); e != hipSuccess)
+        return hip_result(e, what);
+    if (hipError_t e = qp::launch_moe(dn, stream); e != hipSuccess)
+        return hip_result(e, what);
+    qp::MoeCombineArgs c{o, ids, route_weights, n_tokens, top_k, d_model, num_experts,
+                         (int)a_dtype, out};
+    return hip_result(qp::launch_moe_combine(c, stream), what);
+}
+
 } // extern "C"
 
 namespace qp {

@@ -133,4 +133,15 @@ QP_MOE_DECL(8)
 #undef QP_MOE_DECL
 hipError_t launch_moe(const MoeArgs& a, hipStream_t stream);
 
+// Weighted slot sum closing an MoE FFN block (moe_ffn.hip).
+struct MoeCombineArgs {
+    const void* o;          // [n_tokens * top_k, d_model] of dt
+    const int32_t* ids;     // [n_tokens * top_k]
+    const float* rw;        // [n_tokens * top_k] router weights
+    int64_t n_tokens, top_k, d_model, E;
+    int dt;
+    void* out;              // [n_tokens, d_model] of dt
+};
+hipError_t launch_moe_combine(const MoeCombineArgs& a, hipStream_t stream);
+
 } // namespace qp
