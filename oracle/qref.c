@@ -29,6 +29,8 @@
  *    (p%top_k)*inner] and expert ids[p]), and the CPU fallback in the module
  *    docs (per-expert Linear calls): here, one dot product per pair and row.
  *    `gemv_moe_id_gate_up_silu` docs: SiLU(gate) * up.
+ *  - Per-tensor dynamic-range int8: mlex src/quant.rs (`quantize_dynamic_int8`,
+ *    `dequantize_dynamic_int8`).
  *  - Microscaled modes: emily `dequantize_defn/1` docs and its mxfp4 / mxfp8
  *    / nvfp4 implementations (lane and scale formats below).
  *
@@ -503,6 +505,80 @@ int qref_moe_gate_up_silu(const void* a, int a_dtype, const int32_t* ids, int64_
     int64_t total = n_tokens * top_k * n_rows;
     for (int64_t i = 0; i < total; ++i)
         silu_out[i] = silu(g[i]) * u[i];
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-tensor dynamic-range int8                                       */
+/* ------------------------------------------------------------------ */
+/* mlex src/quant.rs, `quantize_dynamic_int8` / `dequantize_dynamic_int8`:
+ * one output range [lo, hi] for the whole tensor; the signed int8 code q maps
+ * affinely onto it, w = (q + 128) * ((hi - lo) / 255) + lo, each step an fp32
+ * operation (cast, add, multiply, add). The quantizer takes lo / hi as the
+ * tensor's min / max, floors its step at FLT_EPSILON, and codes
+ * q = clamp(round((w - lo) / step) - 128, -128, 127), round half away. */
+int qref_quantize_int8_tensor(const float* w, int64_t count, int8_t* q, float* range)
+{
+    if (count < 0)
+        return -1;
+    float lo = INFINITY, hi = -INFINITY;
+    for (int64_t i = 0; i < count; ++i) {
+        lo = fminf(lo, w[i]);
+        hi = fmaxf(hi, w[i]);
+    }
+    float step = (hi - lo) / 255.0f;
+    if (!(step >= FLT_EPSILON))
+        step = FLT_EPSILON;
+    for (int64_t i = 0; i < count; ++i) {
+        float t = roundf((w[i] - lo) / step) - 128.0f;
+        if (t < -128.0f) t = -128.0f;
+        if (t > 127.0f) t = 127.0f;
+        q[i] = (int8_t)t;
+    }
+    range[0] = lo;
+    range[1] = hi;
+    return 0;
+}
+
+static float int8_tensor_weight(int8_t q, float step, float lo)
+{
+    float shifted = (float)q + 128.0f;
+    float scaled = shifted * step;
+    return scaled + lo;
+}
+
+int qref_dequantize_int8_tensor(const int8_t* q, int64_t count, const float* range, float* w)
+{
+    if (count < 0)
+        return -1;
+    float step = (range[1] - range[0]) / 255.0f;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        w[i] = int8_tensor_weight(q[i], step, range[0]);
+    return 0;
+}
+
+/* y[m,n] = sum_k x[m,k] * w[n,k] (fp64, k order) with w the dequantized
+ * int8 weight [n, k]; S = sum |x||w|. */
+int qref_qmatmul_int8_tensor(const void* x, int x_dtype, int64_t m, int64_t k, const int8_t* q,
+                             const float* range, int64_t n, double* y, double* S)
+{
+    if (m < 0 || k < 0 || n < 0)
+        return -1;
+    float step = (range[1] - range[0]) / 255.0f;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t mi = 0; mi < m; ++mi)
+        for (int64_t ni = 0; ni < n; ++ni) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t i = 0; i < k; ++i) {
+                double xv = (double)load_elem(x, x_dtype, mi * k + i);
+                double wv = (double)int8_tensor_weight(q[ni * k + i], step, range[0]);
+                acc += xv * wv;
+                mag += fabs(xv * wv);
+            }
+            y[mi * n + ni] = acc;
+            S[mi * n + ni] = mag;
+        }
     return 0;
 }
 

@@ -100,6 +100,14 @@ int qref_moe_gate_up_silu(const void* a, int a_dtype, const int32_t* ids,
                           int64_t n_cols, int bits, int group_size,
                           double* silu_out, double* g, double* u, double* Sg, double* Su);
 
+/* Per-tensor dynamic-range int8 (one range [lo, hi] = range[0..1] for the
+ * whole tensor): w = (q + 128) * ((hi - lo) / 255) + lo in fp32 steps. The
+ * quantizer sets the range to the tensor's min / max. */
+int qref_quantize_int8_tensor(const float* w, int64_t count, int8_t* q, float* range);
+int qref_dequantize_int8_tensor(const int8_t* q, int64_t count, const float* range, float* w);
+int qref_qmatmul_int8_tensor(const void* x, int x_dtype, int64_t m, int64_t k, const int8_t* q,
+                             const float* range, int64_t n, double* y, double* S);
+
 /* MoE FFN block: gate+up+SiLU, down, then out[t] = sum_j rw[t*top_k+j] *
  * o[t*top_k+j] in fp64, with the intermediates h [P, d_ff] and o [P, d_model]
  * rounded to a_dtype (returned in h_out / o_out). out: [n_tokens, d_model]. */

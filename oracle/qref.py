@@ -68,6 +68,9 @@ def lib():
         L.qref_moe_gate_up_silu.argtypes = [P, I, P, I64, I64, I64, I64, P, P, P, P, P, P, I,
                                             I64, I64, I64, I, I, P, P, P, P, P]
         L.qref_mx_params.argtypes = [I, P, P]
+        L.qref_quantize_int8_tensor.argtypes = [P, I64, P, P]
+        L.qref_dequantize_int8_tensor.argtypes = [P, I64, P, P]
+        L.qref_qmatmul_int8_tensor.argtypes = [P, I, I64, I64, P, P, I64, P, P]
         L.qref_moe_ffn.argtypes = [P, I, P, P, I64, I64] + [P] * 9 + [I, I64, I64, I64, I, I, P, P, P]
         for f in ("qref_fp4_e2m1", "qref_fp8_e4m3", "qref_e8m0"):
             getattr(L, f).restype = ctypes.c_double
@@ -294,4 +297,35 @@ def mx_qmatmul(x, x_dtype, wq, scales, mode, k):
     S = np.empty((m, n), dtype=np.float64)
     _check(lib().qref_mx_qmatmul(_p(x), x_dtype, m, k, _p(wq), _p(scales), mode, n, _p(y), _p(S)),
            "mx_qmatmul")
+    return y, S
+
+
+def quantize_int8_tensor(w):
+    """fp32 array -> (int8 codes of the same shape, float32 range [lo, hi])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    q = np.empty(w.shape, dtype=np.int8)
+    rng_ = np.empty(2, dtype=np.float32)
+    _check(lib().qref_quantize_int8_tensor(_p(w), w.size, _p(q), _p(rng_)), "quantize_int8_tensor")
+    return q, rng_
+
+
+def dequantize_int8_tensor(q, rng_):
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    rng_ = np.ascontiguousarray(rng_, dtype=np.float32)
+    w = np.empty(q.shape, dtype=np.float32)
+    _check(lib().qref_dequantize_int8_tensor(_p(q), q.size, _p(rng_), _p(w)), "dequantize_int8_tensor")
+    return w
+
+
+def qmatmul_int8_tensor(x, x_dtype, q, rng_):
+    """x: [m, k] fp32 values or uint16 bits; q: int8 [n, k]. Returns (y, S) fp64."""
+    x = np.ascontiguousarray(x)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    rng_ = np.ascontiguousarray(rng_, dtype=np.float32)
+    m, k = x.shape
+    n = q.shape[0]
+    y = np.empty((m, n), dtype=np.float64)
+    S = np.empty((m, n), dtype=np.float64)
+    _check(lib().qref_qmatmul_int8_tensor(_p(x), x_dtype, m, k, _p(q), _p(rng_), n, _p(y), _p(S)),
+           "qmatmul_int8_tensor")
     return y, S

@@ -56,6 +56,11 @@ MUTANTS = [
      FAST),
     ("ffn_h_unrounded", "round_to_type(silu_v[i], a_dtype, h_out, i);",
      "round_to_type(silu_v[i] * 1.001, a_dtype, h_out, i);", FAST),
+    ("int8_offset", "float shifted = (float)q + 128.0f;", "float shifted = (float)q + 127.0f;", FAST),
+    ("int8_step", "float step = (range[1] - range[0]) / 255.0f;\n#pragma omp parallel for schedule(static)\n    for (int64_t i = 0; i < count; ++i)",
+     "float step = (range[1] - range[0]) / 256.0f;\n#pragma omp parallel for schedule(static)\n    for (int64_t i = 0; i < count; ++i)", FAST),
+    ("int8_quant_offset", "float t = roundf((w[i] - lo) / step) - 128.0f;",
+     "float t = roundf((w[i] - lo) / step) - 127.0f;", FAST),
     ("rne_ties_up", "r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "r = lo + 1.0;", "rne"),
     ("f16_decode_exponent", "v = ldexp((double)(1024 + m), e - 25);",
      "v = ldexp((double)(1024 + m), e - 24);", "f16 or decoders"),

@@ -379,6 +379,64 @@ def test_dequantize_typed_rounds_product_then_sum():
     assert qref.dequantize(wq, s, b, BF16, 32, 4, 32)[0, 0] == 3.0 + 2.0 ** -6
 
 
+# ---------------------------------------------------------------- per-tensor int8
+
+def load_int8_example():
+    d = {}
+    with open(os.path.join(GOLDEN, "int8_tensor_example.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            key, val = (t.strip() for t in line.split("|"))
+            d[key] = [float(v) for v in val.split()]
+    return d
+
+
+def test_int8_tensor_printed_round_trip():
+    g = load_int8_example()
+    w = np.array(g["input"], dtype=np.float32)
+    q, rng_ = qref.quantize_int8_tensor(w)
+    assert rng_.tolist() == g["range"]
+    assert q.tolist() == [int(v) for v in g["codes"]]
+    back = qref.dequantize_int8_tensor(q, rng_)
+    tol = (rng_[1] - rng_[0]) / 255.0 + 1e-4        # the page's own check
+    assert np.all(np.abs(back - w) <= tol)
+
+
+def test_int8_tensor_dequantize_matches_numpy_fp32_steps():
+    q = synth.random_ints((300,), -128, 127, 2050).astype(np.int8)
+    rng_ = np.array([-0.37, 0.91], dtype=np.float32)
+    step = np.float32((rng_[1] - rng_[0]) / np.float32(255.0))
+    expect = (q.astype(np.float32) + np.float32(128.0)) * step + rng_[0]
+    assert np.array_equal(qref.dequantize_int8_tensor(q, rng_), expect)
+
+
+def test_int8_tensor_round_trip_bound_and_constant_tensor():
+    w = synth.normal_f32((64, 96), 0.05, 2060)
+    q, rng_ = qref.quantize_int8_tensor(w)
+    back = qref.dequantize_int8_tensor(q, rng_)
+    step = (float(rng_[1]) - float(rng_[0])) / 255.0
+    slack = 2.0 ** -21 * (np.abs(w) + abs(float(rng_[0])) + 255 * step)
+    assert np.all(np.abs(back.astype(np.float64) - w) <= step / 2 + slack)
+    assert q.min() == -128 and q.max() == 127
+    c = np.full((5, 7), 0.25, dtype=np.float32)
+    qc, rc = qref.quantize_int8_tensor(c)
+    assert (qc == -128).all() and rc.tolist() == [0.25, 0.25]
+    assert (qref.dequantize_int8_tensor(qc, rc) == 0.25).all()
+
+
+def test_int8_tensor_qmatmul_exact_case():
+    """Range [-8, 7.9375]: step 1/16, every weight (q + 128)/16 - 8 and every
+    product with an integer activation exact, so the oracle equals numpy's."""
+    q = synth.random_ints((9, 128), -128, 127, 2070).astype(np.int8)
+    rng_ = np.array([-8.0, 7.9375], dtype=np.float32)
+    x = synth.random_ints((4, 128), -9, 9, 2071).astype(np.float32)
+    y, S = qref.qmatmul_int8_tensor(x, F32, q, rng_)
+    w = (q.astype(np.float64) + 128.0) / 16.0 - 8.0
+    assert np.array_equal(y, x.astype(np.float64) @ w.T)
+    assert np.array_equal(S, np.abs(x.astype(np.float64)) @ np.abs(w).T)
+
+
 # ---------------------------------------------------------------- MoE FFN block
 
 def _ffn_case(T=5, top_k=3, E=6, D=64, F=96, bits=4, gs=32, dt=BF16, seed=1900):
