@@ -300,6 +300,8 @@ def main():
         return
 
     import torch
+    import weight_only_quantized_qgemv_amd as qp
+    from weight_only_quantized_qgemv_amd.synth import normal_f32 as synth_normal
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -395,6 +397,24 @@ def main():
             rows[f"mx_dequantize_{name}"] = {
                 "us": round(ms_r * 1e3, 3), "GBps": round(moved / (ms_r * 1e-3) / 1e9, 1),
                 "frac_hbm": round(moved / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # Per-tensor dynamic-range int8 W[14336, 4096], seeded random codes.
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(71)
+        wb_i8 = N * K
+        i8_copies = copies_for(wb_i8)
+        i8_sets = [torch.randint(-128, 128, (N, K), dtype=torch.int8, device=dev, generator=gen)
+                   for _ in range(i8_copies)]
+        i8_rng = torch.tensor([-0.1, 0.1], dtype=torch.float32, device=dev)
+        for M in (1, 2):
+            x_i8 = torch.from_numpy(synth_normal((M, K), 1.0, 72)).to(bf16).to(dev)
+            y_i8 = torch.empty((M, N), dtype=bf16, device=dev)
+            ms_r = time_calls(lambda i: qp.qmatmul_int8_tensor(x_i8, i8_sets[i % i8_copies], i8_rng,
+                                                               out=y_i8), del_steps, 5, stream)
+            g = wb_i8 / (ms_r * 1e-3) / 1e9
+            rows[f"int8_tensor_decode_m{M}"] = {"us": round(ms_r * 1e3, 3), "weight_GBps": round(g, 1),
+                                                "frac_hbm": round(g / HBM_PEAK_GBS, 4)}
+        del i8_sets
+        torch.cuda.empty_cache()
         # MoE rows: 128 experts, top-8, 4-bit gs64 bf16.
         for T in (1, 64, 512):
             ms_gu, ms_d, ms_ffn, touched, per_expert = bench_moe(T, del_steps, 5, stream, dev)

@@ -231,6 +231,39 @@ const char* qpack_last_error(void);
 const char* qpack_version(void);
 
 /*
+ * Per-tensor dynamic-range int8 (mlex src/quant.rs, `quantize_dynamic_int8`
+ * and `dequantize_dynamic_int8`): one output range [lo, hi] for the whole
+ * weight, held on the device as range[0] = lo, range[1] = hi (fp32), and
+ *   w = (q + 128) * ((hi - lo) / 255) + lo     (fp32: add, multiply, add)
+ * for the signed code q. The input range the page also records is not needed
+ * for weight-only products and is not kept.
+ *
+ * qpack_quantize_int8_tensor: w device fp32 [count] -> q device int8 [count]
+ * and range; lo / hi are the tensor's min / max, the step (hi - lo) / 255 is
+ * floored at FLT_EPSILON, q = clamp(round_half_away((w - lo) / step) - 128,
+ * -128, 127). Finite inputs; deterministic on any launch.
+ */
+qp_status qpack_quantize_int8_tensor(const float* w, int64_t count, int8_t* q, float* range,
+                                     hipStream_t stream);
+
+/* qpack_dequantize_int8_tensor: q device int8 [count], range device fp32 [2]
+ * -> out device out_dtype [count] (w rounded to nearest even). */
+qp_status qpack_dequantize_int8_tensor(const int8_t* q, int64_t count, const float* range,
+                                       qp_dtype out_dtype, void* out, hipStream_t stream);
+
+/*
+ * y[m, n] = sum_k x[m, k] * w[n, k] for a per-tensor int8 weight q [n, k]
+ * (row-major) and its device range. x: x_dtype [m, k]; y: x_dtype [m, n];
+ * fp32 accumulation (computed as step * sum x (q + 128) + lo * sum x). 16-bit
+ * x with k a multiple of 32 up to 16384 (16-byte aligned) runs the stream
+ * kernel, one or two activation rows per pass; everything else the generic
+ * kernel. k == 0 writes zeros; m == 0 or n == 0 is a no-op.
+ */
+qp_status qmatmul_int8_tensor(const void* x, qp_dtype x_dtype, int64_t m, int64_t k,
+                              const int8_t* q, const float* range, int64_t n, void* y,
+                              hipStream_t stream);
+
+/*
  * Workspace (bytes) of qgemv_moe_ffn: the routing tables of n_tokens*top_k
  * pairs, then the intermediates h [P, d_ff] and o [P, d_model] in `dtype`.
  * 0 for invalid sizes.

@@ -183,6 +183,23 @@ def test_moe_ffn_empty_and_workspace_size():
     assert L.qgemv_moe_ffn_workspace_bytes(-1, 8, 128, 2048, 768, BF16) == 0
 
 
+def test_int8_tensor_argument_errors():
+    L = qp.lib()
+    assert L.qpack_quantize_int8_tensor(A, -1, A, A, None) == INVALID
+    assert L.qpack_quantize_int8_tensor(None, 8, A, A, None) == INVALID
+    assert L.qpack_quantize_int8_tensor(P(0x10002), 8, A, A, None) == ALIGN
+    assert L.qpack_quantize_int8_tensor(None, 0, None, None, None) == OK
+    assert L.qpack_dequantize_int8_tensor(A, 8, A, 3, A, None) == INVALID
+    assert L.qpack_dequantize_int8_tensor(A, 8, None, BF16, A, None) == INVALID
+    assert L.qpack_dequantize_int8_tensor(A, 8, A, F32, P(0x10002), None) == ALIGN
+    assert L.qmatmul_int8_tensor(A, BF16, -1, 64, A, A, 4, A, None) == INVALID
+    assert L.qmatmul_int8_tensor(A, 3, 2, 64, A, A, 4, A, None) == INVALID
+    assert L.qmatmul_int8_tensor(A, BF16, 2, 64, None, A, 4, A, None) == INVALID
+    assert L.qmatmul_int8_tensor(A, BF16, 2, 64, A, None, 4, A, None) == INVALID
+    assert L.qmatmul_int8_tensor(ODD, BF16, 2, 64, A, A, 4, A, None) == ALIGN
+    assert L.qmatmul_int8_tensor(None, BF16, 0, 64, None, None, 4, None, None) == OK
+
+
 def moe(fused=False, a=A, dt=BF16, ids=A, T=2, top_k=2, outer=64, inner=0, sdt=BF16, E=4, R=8,
         C=64, bits=4, gs=64, out=A, ws=A, ws_bytes=None):
     L = qp.lib()

@@ -29,7 +29,9 @@ STATUS = {0: "QP_OK", 1: "QP_ERR_INVALID_ARG", 2: "QP_ERR_UNSUPPORTED",
 # Every symbol include/qpack.h declares.
 EXPORTS = ("qpack_quantize", "qpack_dequantize", "qpack_dequantize_mx", "qmatmul", "qmatmul_mx",
            "qgemv_moe_workspace_bytes", "qgemv_moe_id", "qgemv_moe_id_gate_up_silu",
-           "qgemv_moe_ffn_workspace_bytes", "qgemv_moe_ffn", "qpack_last_error", "qpack_version")
+           "qgemv_moe_ffn_workspace_bytes", "qgemv_moe_ffn", "qpack_quantize_int8_tensor",
+           "qpack_dequantize_int8_tensor", "qmatmul_int8_tensor", "qpack_last_error",
+           "qpack_version")
 
 
 class QpackError(RuntimeError):
@@ -76,6 +78,12 @@ def lib() -> ctypes.CDLL:
         L.qgemv_moe_ffn.argtypes = ([P, ctypes.c_int, P, P, I64, I64] + [P] * 9 +
                                     [ctypes.c_int, I64, I64, I64, I32, I32, P, P, SZ, P])
         L.qgemv_moe_ffn.restype = ctypes.c_int
+        L.qpack_quantize_int8_tensor.argtypes = [P, I64, P, P, P]
+        L.qpack_quantize_int8_tensor.restype = ctypes.c_int
+        L.qpack_dequantize_int8_tensor.argtypes = [P, I64, P, ctypes.c_int, P, P]
+        L.qpack_dequantize_int8_tensor.restype = ctypes.c_int
+        L.qmatmul_int8_tensor.argtypes = [P, ctypes.c_int, I64, I64, P, P, I64, P, P]
+        L.qmatmul_int8_tensor.restype = ctypes.c_int
         L.qpack_last_error.restype = ctypes.c_char_p
         L.qpack_version.restype = ctypes.c_char_p
         _lib = L
@@ -302,4 +310,43 @@ def qgemv_moe_ffn(a, ids, route_weights, top_k: int, gate, up, down, bits: int, 
     check(lib().qgemv_moe_ffn(_ptr(a), dtype_code(a.dtype), _ptr(ids), _ptr(route_weights), T,
                               top_k, *ptrs, dtype_code(gate[1].dtype), E, D, F, bits, group_size,
                               _ptr(out), _ptr(workspace), workspace.numel(), _stream(a)))
+    return out
+
+
+def qpack_quantize_int8_tensor(w, q=None, rng=None):
+    """Per-tensor dynamic-range int8 of fp32 w: (int8 codes shaped like w, fp32 range [lo, hi])."""
+    import torch
+    _dev(w, "w")
+    if w.dtype != torch.float32 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous fp32 tensor")
+    q = torch.empty(w.shape, dtype=torch.int8, device=w.device) if q is None else q
+    rng = torch.empty(2, dtype=torch.float32, device=w.device) if rng is None else rng
+    check(lib().qpack_quantize_int8_tensor(_ptr(w), w.numel(), _ptr(q), _ptr(rng), _stream(w)))
+    return q, rng
+
+
+def qpack_dequantize_int8_tensor(q, rng, out_dtype=None, out=None):
+    import torch
+    _dev(q, "q")
+    _dev(rng, "range")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    check(lib().qpack_dequantize_int8_tensor(_ptr(q), q.numel(), _ptr(rng), dtype_code(out.dtype),
+                                             _ptr(out), _stream(q)))
+    return out
+
+
+def qmatmul_int8_tensor(x, q, rng, out=None):
+    """y = x @ W^T for a per-tensor int8 weight q [n, k] with device range [lo, hi]."""
+    import torch
+    for t, nm in ((x, "x"), (q, "q"), (rng, "range")):
+        _dev(t, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    m, k = x.shape
+    n = q.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    check(lib().qmatmul_int8_tensor(_ptr(x), dtype_code(x.dtype), m, k, _ptr(q), _ptr(rng), n,
+                                    _ptr(out), _stream(x)))
     return out

@@ -352,6 +352,69 @@ qp_status qgemv_moe_id_gate_up_silu(const void* a, qp_dtype a_dtype, const int32
     return hip_result(qp::launch_moe(m, stream), "qgemv_moe_id_gate_up_silu");
 }
 
+qp_status qpack_quantize_int8_tensor(const float* w, int64_t count, int8_t* q, float* range,
+                                     hipStream_t stream)
+{
+    if (count < 0)
+        return fail(QP_ERR_INVALID_ARG, "negative size %lld", (long long)count);
+    if (count == 0)
+        return ok();
+    if (!w || !q || !range)
+        return fail(QP_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(w, 4) || !aligned(range, 4))
+        return fail(QP_ERR_ALIGN, "pointer not aligned to its element size");
+    return hip_result(qp::launch_quantize_int8_tensor(w, count, q, range, stream),
+                      "qpack_quantize_int8_tensor");
+}
+
+qp_status qpack_dequantize_int8_tensor(const int8_t* q, int64_t count, const float* range,
+                                       qp_dtype out_dtype, void* out, hipStream_t stream)
+{
+    if (count < 0)
+        return fail(QP_ERR_INVALID_ARG, "negative size %lld", (long long)count);
+    if (!dtype_ok(out_dtype))
+        return fail(QP_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dtype);
+    if (count == 0)
+        return ok();
+    if (!q || !range || !out)
+        return fail(QP_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(range, 4) || !aligned(out, esize(out_dtype)))
+        return fail(QP_ERR_ALIGN, "pointer not aligned to its element size");
+    return hip_result(qp::launch_dequantize_int8_tensor(q, count, range, (int)out_dtype, out,
+                                                        stream),
+                      "qpack_dequantize_int8_tensor");
+}
+
+qp_status qmatmul_int8_tensor(const void* x, qp_dtype x_dtype, int64_t m, int64_t k,
+                              const int8_t* q, const float* range, int64_t n, void* y,
+                              hipStream_t stream)
+{
+    if (m < 0 || k < 0 || n < 0)
+        return fail(QP_ERR_INVALID_ARG, "negative size (m=%lld, k=%lld, n=%lld)", (long long)m,
+                    (long long)k, (long long)n);
+    if (!dtype_ok(x_dtype))
+        return fail(QP_ERR_INVALID_ARG, "unknown dtype %d", (int)x_dtype);
+    if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n) || k >= (int64_t(1) << 31) ||
+        n >= (int64_t(1) << 31) || m >= (int64_t(1) << 31))
+        return fail(QP_ERR_INVALID_ARG, "size too large");
+    if (m == 0 || n == 0)
+        return ok();
+    if (!y)
+        return fail(QP_ERR_INVALID_ARG, "null output pointer");
+    const size_t es = esize(x_dtype);
+    if (!aligned(y, es))
+        return fail(QP_ERR_ALIGN, "y not aligned to its element size");
+    if (k == 0)
+        return hip_result(qp::launch_fill_zero(y, (int)x_dtype, m * n, stream),
+                          "qmatmul_int8_tensor");
+    if (!x || !q || !range)
+        return fail(QP_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(x, es) || !aligned(range, 4))
+        return fail(QP_ERR_ALIGN, "pointer not aligned to its element size");
+    qp::Int8TensorArgs a{x, (int)x_dtype, m, k, n, q, range, y};
+    return hip_result(qp::launch_qmatmul_int8_tensor(a, stream), "qmatmul_int8_tensor");
+}
+
 static size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 size_t qgemv_moe_ffn_workspace_bytes(int64_t n_tokens, int64_t top_k, int64_t num_experts,

@@ -133,6 +133,22 @@ QP_MOE_DECL(8)
 #undef QP_MOE_DECL
 hipError_t launch_moe(const MoeArgs& a, hipStream_t stream);
 
+// Per-tensor dynamic-range int8 (int8_tensor.hip). `range` is the device
+// pair [lo, hi]; the quantizer uses it as scratch for its reduction keys.
+hipError_t launch_quantize_int8_tensor(const float* w, int64_t count, int8_t* q, float* range,
+                                       hipStream_t stream);
+hipError_t launch_dequantize_int8_tensor(const int8_t* q, int64_t count, const float* range,
+                                         int odt, void* out, hipStream_t stream);
+struct Int8TensorArgs {
+    const void* x;          // [M, K] of dt
+    int dt;
+    int64_t M, K, N;
+    const int8_t* q;        // [N, K]
+    const float* range;     // [2] device
+    void* y;                // [M, N] of dt
+};
+hipError_t launch_qmatmul_int8_tensor(const Int8TensorArgs& a, hipStream_t stream);
+
 // Weighted slot sum closing an MoE FFN block (moe_ffn.hip).
 struct MoeCombineArgs {
     const void* o;          // [n_tokens * top_k, d_model] of dt
