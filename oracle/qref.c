@@ -509,6 +509,39 @@ int qref_moe_gate_up_silu(const void* a, int a_dtype, const int32_t* ids, int64_
 }
 
 /* ------------------------------------------------------------------ */
+/* The transpose = false layout                                        */
+/* ------------------------------------------------------------------ */
+/* emily `quantized_matmul/2` with transpose = false (the AWQ convention):
+ * the packed weight is W [k, n], quantized along its last axis, so row i
+ * holds n lanes with n / group_size groups, and y = x @ W':
+ *   y[m, j] = sum_i x[m, i] * w'[i, j],  w'[i, j] = q[i, j] * s'[i, j/gs] + b'[i, j/gs]
+ * with w' the fp32 dequantized weight of qref_dequantize (row i, lane j). */
+int qref_qmatmul_t(const void* x, int x_dtype, int64_t m, int64_t k, const uint32_t* wq,
+                   const void* scales, const void* biases, int sb_dtype, int64_t n, int bits,
+                   int group_size, double* y, double* S)
+{
+    if (!args_ok(k, n, bits, group_size, sb_dtype) || m < 0)
+        return -1;
+    int64_t groups = n / group_size, words = words_per_row(n, bits);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t mi = 0; mi < m; ++mi)
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t i = 0; i < k; ++i) {
+                double xv = (double)load_elem(x, x_dtype, mi * k + i);
+                double wv = (double)dequant_elem(wq + i * words, words, scales, biases, sb_dtype,
+                                                 i * groups, j, bits, group_size);
+                double term = xv * wv;
+                acc += term;
+                mag += fabs(term);
+            }
+            y[mi * n + j] = acc;
+            S[mi * n + j] = mag;
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Per-tensor dynamic-range int8                                       */
 /* ------------------------------------------------------------------ */
 /* mlex src/quant.rs, `quantize_dynamic_int8` / `dequantize_dynamic_int8`:

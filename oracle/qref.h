@@ -100,6 +100,13 @@ int qref_moe_gate_up_silu(const void* a, int a_dtype, const int32_t* ids,
                           int64_t n_cols, int bits, int group_size,
                           double* silu_out, double* g, double* u, double* Sg, double* Su);
 
+/* transpose = false: wq packs W [k, n] along n (wq: [k, n*bits/32], scales /
+ * biases: [k, n/gs]); y[m, j] = sum_i x[m, i] * w'[i, j] in fp64, in i order,
+ * and S = sum |x||w'|. */
+int qref_qmatmul_t(const void* x, int x_dtype, int64_t m, int64_t k, const uint32_t* wq,
+                   const void* scales, const void* biases, int sb_dtype, int64_t n, int bits,
+                   int group_size, double* y, double* S);
+
 /* Per-tensor dynamic-range int8 (one range [lo, hi] = range[0..1] for the
  * whole tensor): w = (q + 128) * ((hi - lo) / 255) + lo in fp32 steps. The
  * quantizer sets the range to the tensor's min / max. */

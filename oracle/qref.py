@@ -68,6 +68,7 @@ def lib():
         L.qref_moe_gate_up_silu.argtypes = [P, I, P, I64, I64, I64, I64, P, P, P, P, P, P, I,
                                             I64, I64, I64, I, I, P, P, P, P, P]
         L.qref_mx_params.argtypes = [I, P, P]
+        L.qref_qmatmul_t.argtypes = [P, I, I64, I64, P, P, P, I, I64, I, I, P, P]
         L.qref_quantize_int8_tensor.argtypes = [P, I64, P, P]
         L.qref_dequantize_int8_tensor.argtypes = [P, I64, P, P]
         L.qref_qmatmul_int8_tensor.argtypes = [P, I, I64, I64, P, P, I64, P, P]
@@ -328,4 +329,17 @@ def qmatmul_int8_tensor(x, x_dtype, q, rng_):
     S = np.empty((m, n), dtype=np.float64)
     _check(lib().qref_qmatmul_int8_tensor(_p(x), x_dtype, m, k, _p(q), _p(rng_), n, _p(y), _p(S)),
            "qmatmul_int8_tensor")
+    return y, S
+
+
+def qmatmul_t(x, x_dtype, wq, s, b, sb_dtype, n, bits, group_size):
+    """transpose = false: wq packs W [k, n] along n. Returns (y, S) fp64 [m, n]."""
+    x = np.ascontiguousarray(x)
+    wq = np.ascontiguousarray(wq, dtype=np.uint32)
+    m, k = x.shape
+    y = np.empty((m, n), dtype=np.float64)
+    S = np.empty((m, n), dtype=np.float64)
+    _check(lib().qref_qmatmul_t(_p(x), x_dtype, m, k, _p(wq), _p(np.ascontiguousarray(s)),
+                                _p(np.ascontiguousarray(b)), sb_dtype, n, bits, group_size,
+                                _p(y), _p(S)), "qmatmul_t")
     return y, S

@@ -61,6 +61,8 @@ MUTANTS = [
      "float step = (range[1] - range[0]) / 256.0f;\n#pragma omp parallel for schedule(static)\n    for (int64_t i = 0; i < count; ++i)", FAST),
     ("int8_quant_offset", "float t = roundf((w[i] - lo) / step) - 128.0f;",
      "float t = roundf((w[i] - lo) / step) - 127.0f;", FAST),
+    ("qmatmul_t_row_index", "double wv = (double)dequant_elem(wq + i * words, words, scales, biases, sb_dtype,\n                                                 i * groups, j, bits, group_size);",
+     "double wv = (double)dequant_elem(wq + i * words, words, scales, biases, sb_dtype,\n                                                 i * groups, j % k, bits, group_size);", FAST),
     ("rne_ties_up", "r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "r = lo + 1.0;", "rne"),
     ("f16_decode_exponent", "v = ldexp((double)(1024 + m), e - 25);",
      "v = ldexp((double)(1024 + m), e - 24);", "f16 or decoders"),

@@ -379,6 +379,26 @@ def test_dequantize_typed_rounds_product_then_sum():
     assert qref.dequantize(wq, s, b, BF16, 32, 4, 32)[0, 0] == 3.0 + 2.0 ** -6
 
 
+# ---------------------------------------------------------------- transpose = false
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("dt", [F32, BF16])
+def test_qmatmul_t_brute_force_dyadic(bits, dt):
+    """W [k, n] built from dyadic codes, scales and biases along n: x @ W is
+    exact in fp64 in any order, so the oracle equals numpy's product of the
+    dequantized weight (and of its transpose, read with transpose = true)."""
+    k, n, gs = 96, 128, 32
+    wq, s, b, dense = _dyadic_weights(k, n, bits, gs, dt, 2100 + bits)   # dense: [k, n]
+    xs, xv = _activation(5, k, dt, 2110 + bits, sigma=1.0)
+    if dt == F32:
+        xs = np.round(xs * 8).astype(np.float32) / 8
+        xv = xs.astype(np.float64)
+    y, S = qref.qmatmul_t(xs, dt, wq, s, b, dt, n, bits, gs)
+    assert np.array_equal(y, xv @ dense) or np.allclose(y, xv @ dense, rtol=1e-12, atol=1e-12)
+    assert np.allclose(S, np.abs(xv) @ np.abs(dense), rtol=1e-12)
+    assert np.array_equal(dense, qref.dequantize(wq, s, b, dt, n, bits, gs).astype(np.float64))
+
+
 # ---------------------------------------------------------------- per-tensor int8
 
 def load_int8_example():
