@@ -415,6 +415,20 @@ def main():
                                                 "frac_hbm": round(g / HBM_PEAK_GBS, 4)}
         del i8_sets
         torch.cuda.empty_cache()
+        # transpose = false: W [4096, 14336] stored [k, n], 4-bit gs64 bf16, M = 1.
+        wb_t = weight_bytes(K, N, 4, 64, 2)
+        t_copies = copies_for(wb_t)
+        t_sets = make_weights(K, N, 4, 64, bf16, t_copies, 81, dev)
+        x_t = torch.from_numpy(synth_normal((1, K), 1.0, 82)).to(bf16).to(dev)
+        y_t = torch.empty((1, N), dtype=bf16, device=dev)
+        ws_t = torch.empty(qp.qmatmul_t_workspace_bytes(1, K, N, 4), dtype=torch.uint8, device=dev)
+        ms_r = time_calls(lambda i: qp.qmatmul_t(x_t, *t_sets[i % t_copies], 4, 64, out=y_t,
+                                                 workspace=ws_t), del_steps, 5, stream)
+        g = wb_t / (ms_r * 1e-3) / 1e9
+        rows["transpose_false_b4_m1"] = {"us": round(ms_r * 1e3, 3), "weight_GBps": round(g, 1),
+                                         "frac_hbm": round(g / HBM_PEAK_GBS, 4)}
+        del t_sets
+        torch.cuda.empty_cache()
         # MoE rows: 128 experts, top-8, 4-bit gs64 bf16.
         for T in (1, 64, 512):
             ms_gu, ms_d, ms_ffn, touched, per_expert = bench_moe(T, del_steps, 5, stream, dev)

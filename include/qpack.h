@@ -231,6 +231,28 @@ const char* qpack_last_error(void);
 const char* qpack_version(void);
 
 /*
+ * Quantized linear with transpose = false (emily `quantized_matmul/2`: the
+ * packed weight read as already transposed, the AWQ convention):
+ *   y[m, j] = sum_i x[m, i] * (q[i, j] * s'[i, j/gs] + b'[i, j/gs])
+ *   x       device, x_dtype [m, k]
+ *   wq      device, u32 [k, n*bits/32]   (W stored [k, n], packed along n)
+ *   scales, biases  device, sb_dtype [k, n/group_size] (sb_dtype == x_dtype)
+ *   y       device, x_dtype [m, n] (output)
+ *   workspace device, >= qmatmul_t_workspace_bytes(m, k, n, bits), 4-byte
+ *           aligned: fp32 partial sums of the k splits.
+ * n must be a multiple of group_size and n*bits of 32. A lane owns a slice of
+ * output columns and walks down the rows; blocks split k, and a second
+ * kernel adds the splits in order (deterministic), rounding to x_dtype. Up to
+ * 4 activation rows (2 at 3 and 6 bits) per pass over the weights. k == 0
+ * writes zeros; m == 0 or n == 0 is a no-op.
+ */
+size_t qmatmul_t_workspace_bytes(int64_t m, int64_t k, int64_t n, int32_t bits);
+qp_status qmatmul_t(const void* x, qp_dtype x_dtype, int64_t m, int64_t k, const uint32_t* wq,
+                    const void* scales, const void* biases, qp_dtype sb_dtype, int64_t n,
+                    int32_t bits, int32_t group_size, void* y, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Per-tensor dynamic-range int8 (mlex src/quant.rs, `quantize_dynamic_int8`
  * and `dequantize_dynamic_int8`): one output range [lo, hi] for the whole
  * weight, held on the device as range[0] = lo, range[1] = hi (fp32), and

@@ -200,6 +200,29 @@ def test_int8_tensor_argument_errors():
     assert L.qmatmul_int8_tensor(None, BF16, 0, 64, None, None, 4, None, None) == OK
 
 
+def qmatmul_t(x=A, xdt=BF16, m=2, k=64, wq=A, s=A, b=A, sdt=BF16, n=128, bits=4, gs=64, y=A,
+              ws=A, ws_bytes=1 << 20):
+    return qp.lib().qmatmul_t(x, xdt, m, k, wq, s, b, sdt, n, bits, gs, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=7), UNSUPPORTED), (dict(gs=48), UNSUPPORTED), (dict(n=96), SHAPE),
+    (dict(xdt=F16), MISMATCH), (dict(m=-1), INVALID), (dict(y=None), INVALID),
+    (dict(x=None), INVALID), (dict(ws=None), INVALID), (dict(ws_bytes=8), WORKSPACE),
+    (dict(y=ODD), ALIGN), (dict(wq=P(0x10002)), ALIGN), (dict(ws=P(0x10002)), ALIGN),
+])
+def test_qmatmul_t_argument_errors(kw, status):
+    assert qmatmul_t(**kw) == status
+
+
+def test_qmatmul_t_empty_and_workspace_size():
+    assert qmatmul_t(m=0, x=None, y=None, ws=None) == OK
+    L = qp.lib()
+    assert L.qmatmul_t_workspace_bytes(1, 4096, 14336, 4) >= 14336 * 4
+    assert L.qmatmul_t_workspace_bytes(16, 4096, 14336, 4) > L.qmatmul_t_workspace_bytes(1, 4096, 14336, 4)
+    assert L.qmatmul_t_workspace_bytes(0, 4096, 14336, 4) == 0
+
+
 def moe(fused=False, a=A, dt=BF16, ids=A, T=2, top_k=2, outer=64, inner=0, sdt=BF16, E=4, R=8,
         C=64, bits=4, gs=64, out=A, ws=A, ws_bytes=None):
     L = qp.lib()

@@ -30,7 +30,8 @@ STATUS = {0: "QP_OK", 1: "QP_ERR_INVALID_ARG", 2: "QP_ERR_UNSUPPORTED",
 EXPORTS = ("qpack_quantize", "qpack_dequantize", "qpack_dequantize_mx", "qmatmul", "qmatmul_mx",
            "qgemv_moe_workspace_bytes", "qgemv_moe_id", "qgemv_moe_id_gate_up_silu",
            "qgemv_moe_ffn_workspace_bytes", "qgemv_moe_ffn", "qpack_quantize_int8_tensor",
-           "qpack_dequantize_int8_tensor", "qmatmul_int8_tensor", "qpack_last_error",
+           "qpack_dequantize_int8_tensor", "qmatmul_int8_tensor", "qmatmul_t_workspace_bytes",
+           "qmatmul_t", "qpack_last_error",
            "qpack_version")
 
 
@@ -84,6 +85,11 @@ def lib() -> ctypes.CDLL:
         L.qpack_dequantize_int8_tensor.restype = ctypes.c_int
         L.qmatmul_int8_tensor.argtypes = [P, ctypes.c_int, I64, I64, P, P, I64, P, P]
         L.qmatmul_int8_tensor.restype = ctypes.c_int
+        L.qmatmul_t_workspace_bytes.argtypes = [I64, I64, I64, I32]
+        L.qmatmul_t_workspace_bytes.restype = SZ
+        L.qmatmul_t.argtypes = [P, ctypes.c_int, I64, I64, P, P, P, ctypes.c_int, I64, I32, I32, P,
+                                P, SZ, P]
+        L.qmatmul_t.restype = ctypes.c_int
         L.qpack_last_error.restype = ctypes.c_char_p
         L.qpack_version.restype = ctypes.c_char_p
         _lib = L
@@ -349,4 +355,32 @@ def qmatmul_int8_tensor(x, q, rng, out=None):
         out = torch.empty((m, n), dtype=x.dtype, device=x.device)
     check(lib().qmatmul_int8_tensor(_ptr(x), dtype_code(x.dtype), m, k, _ptr(q), _ptr(rng), n,
                                     _ptr(out), _stream(x)))
+    return out
+
+
+def qmatmul_t_workspace_bytes(m: int, k: int, n: int, bits: int) -> int:
+    return int(lib().qmatmul_t_workspace_bytes(m, k, n, bits))
+
+
+def qmatmul_t(x, wq, scales, biases, bits: int, group_size: int, out=None, workspace=None):
+    """transpose = false: y = x @ dequant(W) with W stored [k, n] (wq [k, n*bits/32],
+    scales / biases [k, n/gs], groups along n)."""
+    import torch
+    _dev(x, "x")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [m, k] tensor")
+    for t, nm in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _dev(t, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    m, k = x.shape
+    n = wq.shape[1] * 32 // bits
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        nbytes = qmatmul_t_workspace_bytes(m, k, n, bits)
+        workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=x.device)
+    check(lib().qmatmul_t(_ptr(x), dtype_code(x.dtype), m, k, _ptr(wq), _ptr(scales), _ptr(biases),
+                          dtype_code(scales.dtype), n, bits, group_size, _ptr(out), _ptr(workspace),
+                          workspace.numel(), _stream(x)))
     return out

@@ -23,7 +23,8 @@ BITS = (2, 3, 4, 6, 8)
 UNITS = ([("api.cpp", "api", {}), ("quantize.hip", "quantize", {}), ("moe.hip", "moe", {}),
           ("qgemm.hip", "qgemm", {}),
           ("dequantize.hip", "dequantize", {}), ("mx_gemv.hip", "mx_gemv", {}),
-          ("moe_ffn.hip", "moe_ffn", {}), ("int8_tensor.hip", "int8_tensor", {})]
+          ("moe_ffn.hip", "moe_ffn", {}), ("int8_tensor.hip", "int8_tensor", {}),
+          ("qgemv_t.hip", "qgemv_t", {})]
          + [("qgemv.hip", f"qgemv_b{b}", {"QP_BITS": b}) for b in BITS]
          + [("moe_compute.hip", f"moe_b{b}_n{n}", {"QP_BITS": b, "QP_NMAT": n})
             for b in BITS for n in (1, 2)])

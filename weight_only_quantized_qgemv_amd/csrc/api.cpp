@@ -415,6 +415,53 @@ qp_status qmatmul_int8_tensor(const void* x, qp_dtype x_dtype, int64_t m, int64_
     return hip_result(qp::launch_qmatmul_int8_tensor(a, stream), "qmatmul_int8_tensor");
 }
 
+size_t qmatmul_t_workspace_bytes(int64_t m, int64_t k, int64_t n, int32_t bits)
+{
+    if (m <= 0 || k <= 0 || n <= 0 || !bits_ok(bits) || !mul_ok(m, n) || !mul_ok(k, n))
+        return 0;
+    return qp::qgemv_t_plan(m, k, n, bits).workspace_bytes;
+}
+
+qp_status qmatmul_t(const void* x, qp_dtype x_dtype, int64_t m, int64_t k, const uint32_t* wq,
+                    const void* scales, const void* biases, qp_dtype sb_dtype, int64_t n,
+                    int32_t bits, int32_t group_size, void* y, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream)
+{
+    const char* what = "qmatmul_t";
+    if (m < 0 || k < 0 || n < 0)
+        return fail(QP_ERR_INVALID_ARG, "%s: negative size", what);
+    if (!dtype_ok(x_dtype) || !dtype_ok(sb_dtype))
+        return fail(QP_ERR_INVALID_ARG, "%s: unknown dtype", what);
+    if (qp_status s = check_layout(n, bits, group_size); s != QP_OK)   // groups run along n
+        return s;
+    if (x_dtype != sb_dtype)
+        return fail(QP_ERR_DTYPE_MISMATCH, "%s: input dtype must match scales dtype", what);
+    if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n) || k >= (int64_t(1) << 31) ||
+        n >= (int64_t(1) << 31))
+        return fail(QP_ERR_INVALID_ARG, "%s: size too large", what);
+    if (m == 0 || n == 0)
+        return ok();
+    if (!y)
+        return fail(QP_ERR_INVALID_ARG, "%s: null output pointer", what);
+    const size_t es = esize(x_dtype);
+    if (!aligned(y, es))
+        return fail(QP_ERR_ALIGN, "%s: y not aligned", what);
+    if (k == 0)
+        return hip_result(qp::launch_fill_zero(y, (int)x_dtype, m * n, stream), what);
+    if (!x || !wq || !scales || !biases || !workspace)
+        return fail(QP_ERR_INVALID_ARG, "%s: null pointer", what);
+    const size_t need = qmatmul_t_workspace_bytes(m, k, n, bits);
+    if (workspace_bytes < need)
+        return fail(QP_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", what,
+                    workspace_bytes, need);
+    if (!aligned(x, es) || !aligned(wq, 4) || !aligned(scales, es) || !aligned(biases, es) ||
+        !aligned(workspace, 4))
+        return fail(QP_ERR_ALIGN, "%s: pointer not aligned", what);
+    qp::QgemvTArgs a{x, (int)x_dtype, m, k, n, wq, scales, biases, bits, group_size, y,
+                     static_cast<float*>(workspace)};
+    return hip_result(qp::launch_qgemv_t(a, stream), what);
+}
+
 static size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 size_t qgemv_moe_ffn_workspace_bytes(int64_t n_tokens, int64_t top_k, int64_t num_experts,

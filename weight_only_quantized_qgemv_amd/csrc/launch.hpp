@@ -133,6 +133,29 @@ QP_MOE_DECL(8)
 #undef QP_MOE_DECL
 hipError_t launch_moe(const MoeArgs& a, hipStream_t stream);
 
+// The transpose = false product (qgemv_t.hip): W stored [K, N], grouped along
+// N; fp32 partial sums of the K splits in `workspace`.
+struct QgemvTArgs {
+    const void* x;          // [M, K] of dt
+    int dt;
+    int64_t M, K, N;
+    const uint32_t* wq;     // [K, N*bits/32]
+    const void* scales;     // [K, N/gs] of dt
+    const void* biases;
+    int bits, gs;
+    void* y;                // [M, N] of dt
+    float* workspace;       // >= qgemv_t_plan(...).workspace_bytes
+};
+struct QgemvTPlan {
+    int splits, rows_per_split;
+    size_t workspace_bytes;
+};
+// Activation rows per pass over the weights (the LDS of the split reduction
+// holds 3 x rows x columns-per-lane x 64 floats).
+constexpr int qgemv_t_rows(int bits) { return (bits == 3 || bits == 6) ? 2 : 4; }
+QgemvTPlan qgemv_t_plan(int64_t m, int64_t k, int64_t n, int bits);
+hipError_t launch_qgemv_t(const QgemvTArgs& a, hipStream_t stream);
+
 // Per-tensor dynamic-range int8 (int8_tensor.hip). `range` is the device
 // pair [lo, hi]; the quantizer uses it as scratch for its reduction keys.
 hipError_t launch_quantize_int8_tensor(const float* w, int64_t count, int8_t* q, float* range,
