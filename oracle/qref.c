@@ -531,9 +531,9 @@ int qref_qmatmul_t(const void* x, int x_dtype, int64_t m, int64_t k, const uint3
                 double xv = (double)load_elem(x, x_dtype, mi * k + i);
                 double wv = (double)dequant_elem(wq + i * words, words, scales, biases, sb_dtype,
                                                  i * groups, j, bits, group_size);
-                double term = xv * wv;
-                acc += term;
-                mag += fabs(term);
+                double t_ij = xv * wv;
+                acc += t_ij;
+                mag += fabs(t_ij);
             }
             y[mi * n + j] = acc;
             S[mi * n + j] = mag;

@@ -63,6 +63,7 @@ MUTANTS = [
      "float t = roundf((w[i] - lo) / step) - 127.0f;", FAST),
     ("qmatmul_t_row_index", "double wv = (double)dequant_elem(wq + i * words, words, scales, biases, sb_dtype,\n                                                 i * groups, j, bits, group_size);",
      "double wv = (double)dequant_elem(wq + i * words, words, scales, biases, sb_dtype,\n                                                 i * groups, j % k, bits, group_size);", FAST),
+    ("qmatmul_t_magnitude", "mag += fabs(t_ij);", "mag += t_ij;", FAST),
     ("rne_ties_up", "r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "r = lo + 1.0;", "rne"),
     ("f16_decode_exponent", "v = ldexp((double)(1024 + m), e - 25);",
      "v = ldexp((double)(1024 + m), e - 24);", "f16 or decoders"),
