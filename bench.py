@@ -44,7 +44,7 @@ CSRC = os.path.join(ROOT, "weight_only_quantized_qgemv_amd", "csrc")
 # (FETCH_SIZE, WRITE_SIZE) of `bench.py --steps 20 --warmup 2 --no-rows
 # --no-cpu-baseline`, each scaled by the same counter on a plain 1 GiB copy.
 # It holds only while the decode kernel's sources are the ones it was taken on.
-TRAFFIC = {"src_sha": "2e32667874abdf8e", "fetch_bytes": 33226466, "write_bytes": 68800,
+TRAFFIC = {"src_sha": "a5c6b3a48e42db96", "fetch_bytes": 33225952, "write_bytes": 68800,
            "fetch_scale": 2.0, "write_scale": 1.0}
 DECODE_SOURCES = ("gemv_core.hpp", "common.hpp", "unpack_plan.hpp", "qgemv.hip")
 
