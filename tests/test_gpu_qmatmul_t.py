@@ -68,6 +68,21 @@ def test_qmatmul_t_exact_case():
     assert torch.equal(y.cpu(), torch.from_numpy(yr.astype(np.float32)).to(torch.bfloat16))
 
 
+def test_qmatmul_t_codes_not_16_byte_aligned():
+    """Codes one word into their buffer take the word-load form."""
+    k, n, bits, gs = 64, 256, 4, 64
+    w = synth.normal_f32((k, n), 0.02, 6400)
+    wq, s, b = qref.quantize(w, bits, gs, BF16)
+    buf = torch.zeros(wq.size + 1, dtype=torch.int32, device=dev())
+    buf[1:] = to_device(wq, BF16).reshape(-1)
+    wq_d = buf[1:].view(k, -1)
+    x_st, _ = activations((2, k), BF16, 6401)
+    y = qp.qmatmul_t(to_device(x_st, BF16), wq_d, to_device(s, BF16), to_device(b, BF16), bits, gs)
+    torch.cuda.synchronize()
+    yr, S = qref.qmatmul_t(x_st, BF16, wq, s, b, BF16, n, bits, gs)
+    assert_within(y, yr, S, BF16, "unaligned codes")
+
+
 def test_qmatmul_t_k0_and_workspace_check():
     x = torch.zeros((2, 0), dtype=torch.bfloat16, device=dev())
     wq = torch.zeros((0, 64), dtype=torch.int32, device=dev())

@@ -5,12 +5,14 @@
 //   y[m, j] = sum_i x[m, i] * (q[i, j] * s[i, j/gs] + b[i, j/gs]).
 //
 // A row of W is contiguous along the output index, so a lane owns a fixed
-// slice of output columns (one packed word at 2/4/8 bits, one 32-code unit at
-// 3/6 bits) and walks down the rows, folding the affine map into
-// q * (x s) + x b. A block's four waves take interleaved rows of its K range
-// and meet in LDS; blocks split K further and write fp32 partial sums to the
-// caller's workspace, which a second kernel adds in split order (so results
-// do not depend on scheduling) and rounds to the activation type.
+// slice of 32 output columns (one 32-code unit, one group) and walks down
+// every fourth row of its wave's share, folding the affine map into
+// q * (x s) + x b; 16 lanes cover a row's 512 columns of the block's tile.
+// A block's four waves take interleaved rows of its K range; row groups meet
+// by shuffles and waves in LDS. Blocks split K further and write fp32
+// partial sums to the caller's workspace, which a second kernel adds in split
+// order (so results do not depend on scheduling) and rounds to the
+// activation type.
 #include "common.hpp"
 #include "gemv_core.hpp"
 #include "launch.hpp"
@@ -19,19 +21,21 @@ namespace qp {
 
 namespace {
 
-// A lane's chunk of a row: one packed word at 2/4/8 bits, one 32-code unit
-// at 3/6 bits; either lies in one group.
+// A lane's chunk of a row: one 32-code unit (BITS words, one group). Lanes
+// 16 r .. 16 r + 15 of a wave take row group r (rows i with i % 4 == r of
+// the wave's rows), so one load instruction covers 4 rows x 16 units and a
+// wave tile is 512 columns at every width.
 template <int BITS> struct TChunk {
-    static constexpr bool CROSS = BITS == 3 || BITS == 6;
-    static constexpr int WORDS = CROSS ? BITS : 1;              // words per lane chunk
-    static constexpr int CODES = WORDS * 32 / BITS;             // columns per lane
+    static constexpr int WORDS = BITS;
+    static constexpr int CODES = 32;
     static constexpr int MT_MAX = qgemv_t_rows(BITS);           // activation rows per pass
 };
 
 constexpr int kRowsInFlight = 4;
 constexpr int kWaves = 4;                                       // waves per block
+constexpr int kTileCols = 512;                                  // columns per block
 
-template <int BITS, int DT, int MT>
+template <int BITS, int DT, int MT, bool VEC>
 __global__ __launch_bounds__(64 * kWaves) void qgemv_t_partial_kernel(QgemvTArgs a, int splits,
                                                                       int rows_per_split,
                                                                       float* __restrict__ partial)
@@ -41,15 +45,17 @@ __global__ __launch_bounds__(64 * kWaves) void qgemv_t_partial_kernel(QgemvTArgs
     using St = typename E::storage;
     constexpr int U = kRowsInFlight;
     constexpr uint32_t mask = (1u << BITS) - 1u;
-    __shared__ float red[kWaves - 1][MT][C::CODES][64];
+    constexpr int RS = 4 * kWaves;                              // row streams per block
+    __shared__ float red[kWaves - 1][MT][C::CODES][16];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rg = lane >> 4, cl = lane & 15;
     const int split = (int)blockIdx.x % splits, tile = (int)blockIdx.x / splits;
-    const int64_t chunks_row = a.N / C::CODES;
-    const int64_t chunk = (int64_t)tile * 64 + lane;
-    const bool live = chunk < chunks_row;
+    const int64_t units_row = a.N / 32;
+    const int64_t unit = (int64_t)tile * 16 + cl;
+    const bool live = unit < units_row;
     const int64_t words_row = a.N * BITS / 32, groups_row = a.N / a.gs;
-    const int64_t g = live ? (chunk * C::CODES) / a.gs : 0;
+    const int64_t g = live ? (unit * 32) / a.gs : 0;
     const int k0 = split * rows_per_split;
     const int k1 = k0 + rows_per_split < a.K ? k0 + rows_per_split : a.K;
 
@@ -64,31 +70,42 @@ __global__ __launch_bounds__(64 * kWaves) void qgemv_t_partial_kernel(QgemvTArgs
         for (int c = 0; c < C::CODES; ++c)
             acc[m][c] = 0.0f;
     }
-    for (int i0 = k0 + wave; i0 < k1; i0 += kWaves * U) {
+    for (int i0 = k0 + wave * 4 + rg; i0 < k1; i0 += RS * U) {
         uint32_t w[U][C::WORDS];
         St s_raw[U], b_raw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int i = i0 + kWaves * u;
+            const int i = i0 + RS * u;
             const bool ok = live && i < k1;
             const int ii = ok ? i : k0;   // an in-bounds row; its terms are not used
-            const uint32_t* p = a.wq + (size_t)ii * words_row + (live ? chunk : 0) * C::WORDS;
+            const uint32_t* p = a.wq + (size_t)ii * words_row + (live ? unit : 0) * C::WORDS;
+            if constexpr (VEC && C::WORDS % 4 == 0) {   // 16-byte aligned units
 #pragma unroll
-            for (int v = 0; v < C::WORDS; ++v)
-                w[u][v] = __builtin_nontemporal_load(p + v);
+                for (int v = 0; v < C::WORDS; v += 4) {
+                    const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + v));
+                    w[u][v] = q.x; w[u][v + 1] = q.y; w[u][v + 2] = q.z; w[u][v + 3] = q.w;
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < C::WORDS; ++v)
+                    w[u][v] = __builtin_nontemporal_load(p + v);
+            }
             s_raw[u] = sc[(size_t)ii * groups_row + g];
             b_raw[u] = bi[(size_t)ii * groups_row + g];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int i = i0 + kWaves * u;
+            const int i = i0 + RS * u;
             if (!(live && i < k1))
                 continue;
             const float s = E::to_f32(s_raw[u]), b = E::to_f32(b_raw[u]);
-            float xv[MT];
+            float xsv[MT];
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-                xv[m] = m < a.M ? E::to_f32(xs[(int64_t)m * a.K + i]) : 0.0f;
+            for (int m = 0; m < MT; ++m) {
+                const float xv = m < a.M ? E::to_f32(xs[(int64_t)m * a.K + i]) : 0.0f;
+                xsv[m] = xv * s;
+                accb[m] = __builtin_fmaf(xv, b, accb[m]);
+            }
 #pragma unroll
             for (int c = 0; c < C::CODES; ++c) {
                 const int bit = c * BITS, wi = bit / 32, sh = bit % 32;
@@ -100,34 +117,42 @@ __global__ __launch_bounds__(64 * kWaves) void qgemv_t_partial_kernel(QgemvTArgs
                 const float q = (float)qc;
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-                    acc[m][c] = __builtin_fmaf(q, xv[m] * s, acc[m][c]);
+                    acc[m][c] = __builtin_fmaf(q, xsv[m], acc[m][c]);
             }
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                accb[m] = __builtin_fmaf(xv[m], b, accb[m]);
         }
     }
-    // The waves' partials meet in LDS; wave 0 adds them in wave order.
-    if (wave > 0) {
+    // Row groups of a wave, then the waves of the block, are added in a fixed
+    // order: lanes cl, cl + 16, cl + 32, cl + 48 by two xor shuffles; waves
+    // 1..3 through LDS into wave 0.
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int c = 0; c < C::CODES; ++c) {
+            float v = acc[m][c] + accb[m];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc[m][c] = v;
+        }
+    if (wave > 0 && rg == 0) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int c = 0; c < C::CODES; ++c)
-                red[wave - 1][m][c][lane] = acc[m][c] + accb[m];
+                red[wave - 1][m][c][cl] = acc[m][c];
     }
     __syncthreads();
-    if (wave == 0 && live) {
+    if (wave == 0 && rg == 0 && live) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m >= a.M)
                 continue;
-            float* out = partial + ((size_t)split * a.M + m) * a.N + chunk * C::CODES;
+            float* out = partial + ((size_t)split * a.M + m) * a.N + unit * 32;
 #pragma unroll
             for (int c = 0; c < C::CODES; ++c) {
-                float v = acc[m][c] + accb[m];
+                float v = acc[m][c];
 #pragma unroll
                 for (int wv = 0; wv < kWaves - 1; ++wv)
-                    v += red[wv][m][c][lane];
+                    v += red[wv][m][c][cl];
                 out[c] = v;
             }
         }
@@ -141,8 +166,19 @@ __global__ __launch_bounds__(256) void qgemv_t_reduce_kernel(const float* __rest
 {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn;
          i += (int64_t)gridDim.x * blockDim.x) {
+        // Splits added in order; eight loads in flight at a time.
         float v = 0.0f;
-        for (int s = 0; s < splits; ++s)
+        int s = 0;
+        for (; s + 8 <= splits; s += 8) {
+            float t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                t[j] = partial[(size_t)(s + j) * mn + i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v += t[j];
+        }
+        for (; s < splits; ++s)
             v += partial[(size_t)s * mn + i];
         y[i] = Elem<DT>::from_f32(v);
     }
@@ -150,7 +186,7 @@ __global__ __launch_bounds__(256) void qgemv_t_reduce_kernel(const float* __rest
 
 constexpr int kTargetBlocks = 1024;
 
-template <int BITS, int MT>
+template <int BITS, int MT, bool VEC>
 hipError_t run_t_mt(const QgemvTArgs& a, int64_t mc, const void* x, void* y, float* partial,
                     int splits, int rows_per_split, hipStream_t st)
 {
@@ -158,19 +194,20 @@ hipError_t run_t_mt(const QgemvTArgs& a, int64_t mc, const void* x, void* y, flo
     QgemvTArgs k = a;
     k.x = x;
     k.M = mc;
-    const int64_t tiles = (a.N / C::CODES + 63) / 64;
+    (void)sizeof(C);
+    const int64_t tiles = (a.N + kTileCols - 1) / kTileCols;
     const dim3 grid((unsigned)(tiles * splits));
     switch (a.dt) {
     case DT_F32:
-        hipLaunchKernelGGL((qgemv_t_partial_kernel<BITS, DT_F32, MT>), grid, dim3(64 * kWaves), 0, st, k,
+        hipLaunchKernelGGL((qgemv_t_partial_kernel<BITS, DT_F32, MT, VEC>), grid, dim3(64 * kWaves), 0, st, k,
                            splits, rows_per_split, partial);
         break;
     case DT_F16:
-        hipLaunchKernelGGL((qgemv_t_partial_kernel<BITS, DT_F16, MT>), grid, dim3(64 * kWaves), 0, st, k,
+        hipLaunchKernelGGL((qgemv_t_partial_kernel<BITS, DT_F16, MT, VEC>), grid, dim3(64 * kWaves), 0, st, k,
                            splits, rows_per_split, partial);
         break;
     case DT_BF16:
-        hipLaunchKernelGGL((qgemv_t_partial_kernel<BITS, DT_BF16, MT>), grid, dim3(64 * kWaves), 0, st, k,
+        hipLaunchKernelGGL((qgemv_t_partial_kernel<BITS, DT_BF16, MT, VEC>), grid, dim3(64 * kWaves), 0, st, k,
                            splits, rows_per_split, partial);
         break;
     default:
@@ -204,17 +241,20 @@ hipError_t run_t_bits(const QgemvTArgs& a, hipStream_t st)
     const QgemvTPlan p = qgemv_t_plan(a.M, a.K, a.N, a.bits);
     const int es = a.dt == DT_F32 ? 4 : 2;
     constexpr int MTX = TChunk<BITS>::MT_MAX;
+    const bool vec = reinterpret_cast<uintptr_t>(a.wq) % 16 == 0;
     for (int64_t m0 = 0; m0 < a.M; m0 += MTX) {
         const int64_t mc = a.M - m0 < MTX ? a.M - m0 : MTX;
         const void* x = static_cast<const char*>(a.x) + m0 * a.K * es;
         void* y = static_cast<char*>(a.y) + m0 * a.N * es;
         hipError_t e;
-        if (mc == 1)
-            e = run_t_mt<BITS, 1>(a, mc, x, y, a.workspace, p.splits, p.rows_per_split, st);
-        else if (mc == 2)
-            e = run_t_mt<BITS, 2>(a, mc, x, y, a.workspace, p.splits, p.rows_per_split, st);
+        if (vec)
+            e = mc == 1   ? run_t_mt<BITS, 1, true>(a, mc, x, y, a.workspace, p.splits, p.rows_per_split, st)
+                : mc == 2 ? run_t_mt<BITS, 2, true>(a, mc, x, y, a.workspace, p.splits, p.rows_per_split, st)
+                          : run_t_mt<BITS, MTX, true>(a, mc, x, y, a.workspace, p.splits, p.rows_per_split, st);
         else
-            e = run_t_mt<BITS, MTX>(a, mc, x, y, a.workspace, p.splits, p.rows_per_split, st);
+            e = mc == 1   ? run_t_mt<BITS, 1, false>(a, mc, x, y, a.workspace, p.splits, p.rows_per_split, st)
+                : mc == 2 ? run_t_mt<BITS, 2, false>(a, mc, x, y, a.workspace, p.splits, p.rows_per_split, st)
+                          : run_t_mt<BITS, MTX, false>(a, mc, x, y, a.workspace, p.splits, p.rows_per_split, st);
         if (e != hipSuccess)
             return e;
     }
@@ -225,8 +265,8 @@ hipError_t run_t_bits(const QgemvTArgs& a, hipStream_t st)
 
 QgemvTPlan qgemv_t_plan(int64_t m, int64_t k, int64_t n, int bits)
 {
-    const int codes = (bits == 3 || bits == 6) ? 32 : 32 / bits;
-    const int64_t tiles = (n / codes + 63) / 64;
+    (void)bits;
+    const int64_t tiles = (n + kTileCols - 1) / kTileCols;
     int64_t splits = tiles > 0 ? (kTargetBlocks + tiles - 1) / tiles : 1;
     const int64_t max_splits = k / 16 > 1 ? k / 16 : 1;   // at least 16 rows per block
     splits = splits < max_splits ? splits : max_splits;
