@@ -44,9 +44,9 @@ CSRC = os.path.join(ROOT, "weight_only_quantized_qgemv_amd", "csrc")
 # (FETCH_SIZE, WRITE_SIZE) of `bench.py --steps 20 --warmup 2 --no-rows
 # --no-cpu-baseline`, each scaled by the same counter on a plain 1 GiB copy.
 # It holds only while the decode kernel's sources are the ones it was taken on.
-TRAFFIC = {"src_sha": "a5c6b3a48e42db96", "fetch_bytes": 33225952, "write_bytes": 68800,
+TRAFFIC = {"src_sha": "d6e3909dcf4569c5", "fetch_bytes": 33207532, "write_bytes": 28672,
            "fetch_scale": 2.0, "write_scale": 1.0}
-DECODE_SOURCES = ("gemv_core.hpp", "common.hpp", "unpack_plan.hpp", "qgemv.hip")
+DECODE_SOURCES = ("rowstream.hpp", "gemv_core.hpp", "common.hpp", "qgemv.hip")
 
 
 def decode_src_sha() -> str:
@@ -332,7 +332,7 @@ def main():
                    "rotation_bytes": wb * copies},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "qgemv_stream_kernel<4, bf16, MT=1, U=2, G=1, KL=64, NMAT=1>",
+                     "kernel": "qgemv_rowstream_kernel<BITS=4, bf16, MT=1, UPL=2>",
                      "us_per_launch": round(ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": wb},
     }
@@ -349,6 +349,11 @@ def main():
                     "us": round(ms_r * 1e3, 3), "weight_GBps": round(g, 1),
                     "frac_hbm": round(g / HBM_PEAK_GBS, 4),
                     "tokens_per_s": round(M / (ms_r * 1e-3), 1)}
+        # The down-projection shape, W[4096,14336], 4-bit gs64 bf16, M = 1.
+        ms_r, wb_r, _ = bench_dense(4096, 14336, 1, 4, 64, bf16, del_steps, 5, stream, dev, seed=23)
+        g = wb_r / (ms_r * 1e-3) / 1e9
+        rows["decode_b4_k14336_m1"] = {"us": round(ms_r * 1e3, 3), "weight_GBps": round(g, 1),
+                                       "frac_hbm": round(g / HBM_PEAK_GBS, 4)}
         # Cross-word rows: W[4096,4096] fp16 at 3/6 bits over gs 32/64/128, M = 1/8.
         for bits in (3, 6):
             for gs in (32, 64, 128):

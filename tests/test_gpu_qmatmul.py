@@ -101,6 +101,20 @@ def test_qmatmul_parity_small(bits, dt, k, m):
     assert_within(y, y_ref, S, dt, f"qmatmul b{bits} dt{dt} k{k} m{m}")
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("k,m,gs", [(14336, 1, 64), (11008, 1, 128), (8192, 2, 32), (6144, 2, 64),
+                                    (2080, 1, 32), (16384, 2, 64), (12288, 1, 32)])
+def test_qmatmul_row_stream_units_per_lane(bits, dt, k, m, gs):
+    """2/4/8-bit decode on the row-per-wave kernel: 1 to 8 units of 32 codes
+    per lane, ragged unit counts (11008 = 344 units, 2080 = 65 units), two
+    rows per pass up to K = 8192 and one beyond."""
+    n = 300
+    log(f"row stream bits={bits} dt={dt} n={n} k={k} m={m} gs={gs}")
+    y, y_ref, S = run_case(n, k, m, bits, gs, dt, seed=7000 + k + m + gs + bits)
+    assert_within(y, y_ref, S, dt, f"row stream b{bits} k{k} m{m}")
+
+
 @pytest.mark.parametrize("bits", [4, 3])
 @pytest.mark.parametrize("dt", [F16, BF16])
 @pytest.mark.parametrize("n,k,m,gs", [(301, 14336, 16, 128), (50, 14336, 7, 64),

@@ -7,6 +7,7 @@
 
 #include "gemv_core.hpp"
 #include "mfma_gemv.hpp"
+#include "rowstream.hpp"
 #include "launch.hpp"
 
 namespace qp {
@@ -199,6 +200,43 @@ hipError_t run_mfma(const GemvArgs& a, hipStream_t st, bool* done)
     return hipSuccess;
 }
 
+// 2-, 4- and 8-bit codes, one or two 16-bit activation rows: the row-per-wave
+// stream kernel (rowstream.hpp), for K a multiple of 32 up to 16384 (at most
+// 8 units per lane).
+template <int BITS, int DT, int MT, int UPL>
+hipError_t run_rowstream(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
+{
+    constexpr int D = rowstream_depth<BITS, UPL>();
+    RowStreamArgs k{};
+    k.x = static_cast<const char*>(a.x) + m0 * a.K * 2;
+    k.wq = a.wq;
+    k.scales = a.scales;
+    k.biases = a.biases;
+    k.y = static_cast<char*>(a.y) + m0 * a.N * 2;
+    k.M = mc;
+    k.N = (int)a.N;
+    k.K = (int)a.K;
+    k.gs = a.gs;
+    k.units_row = (uint32_t)(a.K / 32);
+    int64_t blocks = (a.N + 4 * D - 1) / (4 * D);
+    blocks = blocks < kMaxBlocks ? blocks : kMaxBlocks;
+    hipLaunchKernelGGL((qgemv_rowstream_kernel<BITS, DT, MT, UPL>), dim3((int)blocks), dim3(256), 0,
+                       st, k);
+    return hipGetLastError();
+}
+
+template <int BITS, int DT, int MT>
+hipError_t run_rowstream_upl(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
+{
+    const int64_t upl = (a.K / 32 + 63) / 64;
+    if (upl <= 1) return run_rowstream<BITS, DT, MT, 1>(a, m0, mc, st);
+    if (upl <= 2) return run_rowstream<BITS, DT, MT, 2>(a, m0, mc, st);
+    if (upl <= 4) return run_rowstream<BITS, DT, MT, 4>(a, m0, mc, st);
+    if constexpr (MT == 1)
+        return run_rowstream<BITS, DT, MT, 8>(a, m0, mc, st);
+    return hipErrorInvalidValue;   // two rows only up to four units per lane
+}
+
 template <int BITS, int DT>
 hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
 {
@@ -226,6 +264,24 @@ hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
             hipError_t e = run_mfma<BITS, DT>(a, st, &done);
             if (e != hipSuccess || done)
                 return e;
+        }
+    }
+    if constexpr ((BITS == 2 || BITS == 4 || BITS == 8) && DT != DT_F32) {
+        // 8-bit codes keep the slice kernel on the K it has a shape for
+        // (measured 14.5 against 15.2 us at 14336 x 4096).
+        const bool slice_shape = BITS == 8 && (a.K == 4096 || a.K == 2048 || a.K == 768 ||
+                                               (a.K == 1024 && a.M <= 2) || (a.K == 8192 && a.M == 1));
+        if (a.M <= 2 && a.K % 32 == 0 && a.K <= 8 * 64 * 32 && !slice_shape) {
+            // Two activation rows per pass up to four units per lane, else one.
+            const int rows = a.K <= 4 * 64 * 32 ? 2 : 1;
+            for (int64_t m0 = 0; m0 < a.M; m0 += rows) {
+                const int mc = (int)((a.M - m0) < rows ? (a.M - m0) : rows);
+                hipError_t e = mc == 2 ? run_rowstream_upl<BITS, DT, 2>(a, m0, mc, st)
+                                       : run_rowstream_upl<BITS, DT, 1>(a, m0, mc, st);
+                if (e != hipSuccess)
+                    return e;
+            }
+            return hipSuccess;
         }
     }
     for (int64_t m0 = 0; m0 < a.M;) {
