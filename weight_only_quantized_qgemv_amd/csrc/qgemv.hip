@@ -218,11 +218,31 @@ hipError_t run_rowstream(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
     k.K = (int)a.K;
     k.gs = a.gs;
     k.units_row = (uint32_t)(a.K / 32);
-    int64_t blocks = (a.N + 4 * D - 1) / (4 * D);
-    blocks = blocks < kMaxBlocks ? blocks : kMaxBlocks;
-    hipLaunchKernelGGL((qgemv_rowstream_kernel<BITS, DT, MT, UPL>), dim3((int)blocks), dim3(256), 0,
-                       st, k);
-    return hipGetLastError();
+    auto launch = [&](auto wpb) {
+        constexpr int WPB = decltype(wpb)::value;
+        int64_t blocks = (a.N + WPB * D - 1) / (WPB * D);
+        blocks = blocks < kMaxBlocks ? blocks : kMaxBlocks;
+        // Scales and biases as whole dword-aligned rows when a row has an
+        // even number of groups.
+        if ((a.K / a.gs) % 2 == 0)
+            hipLaunchKernelGGL((qgemv_rowstream_kernel<BITS, DT, MT, UPL, WPB, true>),
+                               dim3((int)blocks), dim3(64 * WPB), 0, st, k);
+        else
+            hipLaunchKernelGGL((qgemv_rowstream_kernel<BITS, DT, MT, UPL, WPB, false>),
+                               dim3((int)blocks), dim3(64 * WPB), 0, st, k);
+        return hipGetLastError();
+    };
+#ifdef QP_TUNING
+    switch (tuning_env("QP_RS_WPB", 4)) {
+    case 2: return launch(std::integral_constant<int, 2>{});
+    case 7: return launch(std::integral_constant<int, 7>{});
+    case 8: return launch(std::integral_constant<int, 8>{});
+    case 14: return launch(std::integral_constant<int, 14>{});
+    case 16: return launch(std::integral_constant<int, 16>{});
+    default: break;
+    }
+#endif
+    return launch(std::integral_constant<int, 4>{});
 }
 
 template <int BITS, int DT, int MT>

@@ -14,6 +14,13 @@
 // sum x (OFFSET + q) per unit, the unit's activation sum removes the offset,
 // and the group's scale and bias are applied once per unit. D rows are
 // loaded before any is reduced.
+//
+// Every wave of a block needs the same activation slices, so the block
+// prepares them once: its threads load the raw activation units, permute
+// them and form their sums into LDS, and each wave then copies its slices
+// from there. The first row batch's loads are issued before that set-up (and
+// after the raw activation loads, which are waited for first), so the set-up
+// runs under the weight stream's latency.
 #pragma once
 
 #include "common.hpp"
@@ -57,8 +64,8 @@ template <int BITS, int UPL> constexpr int rowstream_depth()
     return 32 / (BITS * UPL) < 1 ? 1 : (32 / (BITS * UPL) > 4 ? 4 : 32 / (BITS * UPL));
 }
 
-template <int BITS, int DT, int MT, int UPL>
-__global__ __launch_bounds__(256) void qgemv_rowstream_kernel(RowStreamArgs a)
+template <int BITS, int DT, int MT, int UPL, int WPB, bool WIDE>
+__global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs a)
 {
     using PX = RowStreamPair<DT>;
     using E = Elem<DT>;
@@ -72,61 +79,65 @@ __global__ __launch_bounds__(256) void qgemv_rowstream_kernel(RowStreamArgs a)
     constexpr uint32_t M1 = (1u << BITS) - 1u;
     constexpr uint32_t MASK = M1 | (M1 << 16);
     const int lane = threadIdx.x & 63;
-    const int gw = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    const int GW = (int)gridDim.x * 4;
+    const int gw = (int)blockIdx.x * WPB + (int)(threadIdx.x >> 6);
+    const int GW = (int)gridDim.x * WPB;
 
-    // Activation pairs of the lane's units, permuted: pair HALF i + t of a
-    // unit holds x[CPW i + t] (low) and x[CPW i + t + HALF] (high); and each
-    // unit's sum.
-    uint32_t xr[MT][UPL][16];
-    float xs[MT][UPL];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-            const int u = lane + 64 * j;
-            xs[m][j] = 0.0f;
-            if (u < (int)a.units_row && m < a.M) {
-                const St* p = static_cast<const St*>(a.x) + (int64_t)m * a.K + 32 * u;
-                uint32_t raw[16];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const u32x4_t q = reinterpret_cast<const u32x4_t*>(p)[v];
-                    raw[4 * v] = q.x; raw[4 * v + 1] = q.y; raw[4 * v + 2] = q.z; raw[4 * v + 3] = q.w;
-                }
-                // raw[k / 2] holds x[k] (low) and x[k + 1] (high).
-#pragma unroll
-                for (int i = 0; i < BITS; ++i)
-#pragma unroll
-                    for (int t = 0; t < HALF; ++t) {
-                        const int k0 = CPW * i + t, k1 = k0 + HALF;
-                        const uint32_t lo = (raw[k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
-                        const uint32_t hi = (raw[k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
-                        xr[m][j][HALF * i + t] = lo | (hi << 16);
-                    }
-#pragma unroll
-                for (int k = 0; k < 32; ++k)
-                    xs[m][j] += E::to_f32((uint16_t)(raw[k / 2] >> (16 * (k & 1))));
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) xr[m][j][i] = 0u;
-            }
-        }
+    constexpr int UNITS = 64 * UPL;                  // unit slots of one activation row
+    constexpr int ENTRIES = MT * UNITS;              // (row, unit) slices set up per block
+    constexpr int EPT = (ENTRIES + 64 * WPB - 1) / (64 * WPB);   // slices per thread
+    // Permuted pairs of slice (m, u) as four 4-word vectors xl[m][q][u], and
+    // its sum: consecutive lanes touch consecutive vectors.
+    __shared__ u32x4_t xl[MT][4][UNITS];
+    __shared__ float sl[MT][UNITS];
 
     const uint32_t row_bytes = (uint32_t)a.K * BITS / 8;
     const uint32_t groups_row = (uint32_t)(a.K / a.gs);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wq, (uint32_t)a.N * row_bytes);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)a.N * groups_row * 2);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.biases, (uint32_t)a.N * groups_row * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.K * 2);
     St* y = static_cast<St*>(a.y);
     uint32_t gofs[UPL];
 #pragma unroll
     for (int j = 0; j < UPL; ++j)
         gofs[j] = (uint32_t)((32 * (lane + 64 * j)) / a.gs) * 2;
 
-    for (int r0 = gw * D; r0 < a.N; r0 += GW * D) {
-        uint32_t w[D][UPL][BITS];
-        St sv[D][UPL], bv[D][UPL];
+    // Raw activation slices of this thread: raw[e][k / 2] holds x[k] (low)
+    // and x[k + 1] (high) of the 32 activations of its slice (zeros past the
+    // row or the activation rows).
+    uint32_t raw[EPT][16];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int idx = (int)threadIdx.x + 64 * WPB * e, m = idx / UNITS, u = idx % UNITS;
+        const bool live = idx < ENTRIES && m < a.M && u < (int)a.units_row;
+        buffer_words<16>(rx, live ? ((uint32_t)m * (uint32_t)a.K + 32u * (uint32_t)u) * 2 : OOB,
+                         raw[e]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // WIDE (an even number of groups per row): a batch's scales and biases
+    // are D whole rows, contiguous and dword-aligned, read as lane-contiguous
+    // dwords (NV loads per array instead of D * UPL) and handed to the lanes
+    // that need them through the wave's own LDS slots.
+    constexpr int SBD = 32 * D * UPL;                // dwords of one batch's scales, gs >= 32
+    constexpr int NV = (SBD + 63) / 64;
+    __shared__ uint32_t sbl[WPB][2][WIDE ? SBD : 1];
+    const int wv = (int)(threadIdx.x >> 6);
+    const uint32_t nd = (uint32_t)D * groups_row / 2;
+    uint32_t sw[NV], bw[NV];
+    uint32_t w[D][UPL][BITS];
+    St sv[D][UPL], bv[D][UPL];
+    auto load = [&](int r0) {
+        if constexpr (WIDE) {
+            const uint32_t base = (uint32_t)r0 * groups_row * 2;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const uint32_t i = (uint32_t)(lane + 64 * v);
+                const uint32_t off = i < nd ? base + 4 * i : OOB;
+                sw[v] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+                bw[v] = __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0);
+            }
+        }
 #pragma unroll
         for (int d = 0; d < D; ++d)
 #pragma unroll
@@ -135,10 +146,92 @@ __global__ __launch_bounds__(256) void qgemv_rowstream_kernel(RowStreamArgs a)
                 const bool live = u < (int)a.units_row && r < a.N;
                 buffer_words<BITS, BITS == 8 ? 0 : kStreamPolicy>(
                     rw, live ? (uint32_t)r * row_bytes + (uint32_t)u * (4 * BITS) : OOB, w[d][j]);
-                const uint32_t so = live ? (uint32_t)r * groups_row * 2 + gofs[j] : OOB;
-                sv[d][j] = buffer_elem<DT>(rs, so);
-                bv[d][j] = buffer_elem<DT>(rb, so);
+                if constexpr (!WIDE) {
+                    const uint32_t so = live ? (uint32_t)r * groups_row * 2 + gofs[j] : OOB;
+                    sv[d][j] = buffer_elem<DT>(rs, so);
+                    bv[d][j] = buffer_elem<DT>(rb, so);
+                }
             }
+    };
+    // Units past the row take zero scale and bias, as the per-lane loads
+    // give them (their codes and activations are zero as well).
+    auto exchange = [&]() {
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const uint32_t i = (uint32_t)(lane + 64 * v);
+                if (i < nd) {
+                    sbl[wv][0][i] = sw[v];
+                    sbl[wv][1][i] = bw[v];
+                }
+            }
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+#pragma unroll
+                for (int j = 0; j < UPL; ++j) {
+                    const bool live = lane + 64 * j < (int)a.units_row;
+                    // Element e = d * groups + g of the batch sits in half
+                    // e % 2 of slot e / 2 (little-endian); e / 2 < SBD for
+                    // every lane, live or not. Read as the slots' own type.
+                    const uint32_t e = (uint32_t)d * groups_row + gofs[j] / 2;
+                    const uint32_t ds = sbl[wv][0][e >> 1], db = sbl[wv][1][e >> 1];
+                    const uint32_t sh = 16 * (e & 1);
+                    sv[d][j] = live ? St(ds >> sh) : St(0);
+                    bv[d][j] = live ? St(db >> sh) : St(0);
+                }
+        }
+    };
+    int r0 = gw * D;
+    load(r0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Pair HALF i + t of a slice holds x[CPW i + t] (low) and
+    // x[CPW i + t + HALF] (high).
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int idx = (int)threadIdx.x + 64 * WPB * e, m = idx / UNITS, u = idx % UNITS;
+        if (idx < ENTRIES) {
+            uint32_t p[16];
+#pragma unroll
+            for (int i = 0; i < BITS; ++i)
+#pragma unroll
+                for (int t = 0; t < HALF; ++t) {
+                    const int k0 = CPW * i + t, k1 = k0 + HALF;
+                    const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
+                    const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
+                    p[HALF * i + t] = lo | (hi << 16);
+                }
+            float sum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                sum += E::to_f32((uint16_t)(raw[e][k / 2] >> (16 * (k & 1))));
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xl[m][q][u] = u32x4_t{p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]};
+            sl[m][u] = sum;
+        }
+    }
+    __syncthreads();
+    uint32_t xr[MT][UPL][16];
+    float xs[MT][UPL];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+            const int u = lane + 64 * j;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4_t v = xl[m][q][u];
+                xr[m][j][4 * q] = v.x; xr[m][j][4 * q + 1] = v.y;
+                xr[m][j][4 * q + 2] = v.z; xr[m][j][4 * q + 3] = v.w;
+            }
+            xs[m][j] = sl[m][u];
+        }
+
+    for (bool first = true; r0 < a.N; r0 += GW * D, first = false) {
+        if (!first)
+            load(r0);
+        exchange();
         float acc[D * MT];
 #pragma unroll
         for (int d = 0; d < D; ++d)
