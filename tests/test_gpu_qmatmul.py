@@ -105,11 +105,14 @@ def test_qmatmul_parity_small(bits, dt, k, m):
 @pytest.mark.parametrize("dt", [F16, BF16])
 @pytest.mark.parametrize("k,m,gs", [(14336, 1, 64), (11008, 1, 128), (8192, 2, 32), (6144, 2, 64),
                                     (2080, 1, 32), (16384, 2, 64), (12288, 1, 32), (2176, 2, 64),
-                                    (2176, 1, 32), (2112, 2, 64), (128, 2, 64), (96, 1, 32)])
+                                    (2176, 1, 32), (2112, 2, 64), (128, 2, 64), (96, 1, 32),
+                                    (4096, 4, 64), (2176, 3, 64), (2112, 4, 64), (96, 3, 32),
+                                    (1024, 4, 128)])
 def test_qmatmul_row_stream_units_per_lane(bits, dt, k, m, gs):
     """2/4/8-bit decode on the row-per-wave kernel: 1 to 8 units of 32 codes
     per lane, ragged unit counts (11008 = 344 units, 2176 = 68, 2080 = 65,
-    96 = 3), two rows per pass up to K = 8192 and one beyond; rows with an
+    96 = 3), two rows per pass up to K = 8192 and one beyond, three and four
+    rows (activation slices read from LDS) up to K = 4096; rows with an
     even number of groups (scales read as whole rows) and with an odd one
     (2080 / 32 = 65, 2112 / 64 = 33, 96 / 32 = 3)."""
     n = 300

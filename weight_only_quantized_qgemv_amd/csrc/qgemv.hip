@@ -257,6 +257,16 @@ hipError_t run_rowstream_upl(const GemvArgs& a, int64_t m0, int mc, hipStream_t 
     return hipErrorInvalidValue;   // two rows only up to four units per lane
 }
 
+// Three or four activation rows in one pass (their slices read from LDS),
+// up to two units per lane: the LDS of four rows' slices stays under 64 KB.
+template <int BITS, int DT>
+hipError_t run_rowstream_m4(const GemvArgs& a, hipStream_t st)
+{
+    const int64_t upl = (a.K / 32 + 63) / 64;
+    if (upl <= 1) return run_rowstream<BITS, DT, 4, 1>(a, 0, (int)a.M, st);
+    return run_rowstream<BITS, DT, 4, 2>(a, 0, (int)a.M, st);
+}
+
 template <int BITS, int DT>
 hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
 {
@@ -279,6 +289,15 @@ hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
         // on the 14336 x 4096 decode shape); three and more go to the matrix cores.
         constexpr int min_m = 3;
 #endif
+#ifdef QP_TUNING
+        const bool m4_rows = tuning_env("QP_RS_M4", 1) != 0;
+#else
+        constexpr bool m4_rows = true;
+#endif
+        if constexpr (BITS == 2 || BITS == 4 || BITS == 8) {
+            if (m4_rows && (a.M == 3 || a.M == 4) && a.K % 32 == 0 && a.K <= 2 * 64 * 32)
+                return run_rowstream_m4<BITS, DT>(a, st);
+        }
         if (a.M >= min_m) {
             bool done = false;
             hipError_t e = run_mfma<BITS, DT>(a, st, &done);

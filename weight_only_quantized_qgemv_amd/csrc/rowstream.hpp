@@ -212,55 +212,105 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
         }
     }
     __syncthreads();
-    uint32_t xr[MT][UPL][16];
-    float xs[MT][UPL];
+    // Up to two activation rows keep their slices in registers; more rows
+    // read them from LDS as the dot products go (four pairs at a time), which
+    // keeps the register count of four rows near that of one.
+    constexpr bool XREG = MT <= 2;
+    uint32_t xr[XREG ? MT : 1][UPL][16];
+    float xs[XREG ? MT : 1][UPL];
+    if constexpr (XREG) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-            const int u = lane + 64 * j;
+            for (int j = 0; j < UPL; ++j) {
+                const int u = lane + 64 * j;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4_t v = xl[m][q][u];
-                xr[m][j][4 * q] = v.x; xr[m][j][4 * q + 1] = v.y;
-                xr[m][j][4 * q + 2] = v.z; xr[m][j][4 * q + 3] = v.w;
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4_t v = xl[m][q][u];
+                    xr[m][j][4 * q] = v.x; xr[m][j][4 * q + 1] = v.y;
+                    xr[m][j][4 * q + 2] = v.z; xr[m][j][4 * q + 3] = v.w;
+                }
+                xs[m][j] = sl[m][u];
             }
-            xs[m][j] = sl[m][u];
-        }
+    }
 
     for (bool first = true; r0 < a.N; r0 += GW * D, first = false) {
         if (!first)
             load(r0);
         exchange();
         float acc[D * MT];
+        // Code pair p = HALF i + t of a unit: codes t and t + HALF of word i,
+        // as a 16-bit pair (OFFSET + q, or q converted).
+        auto code_pair = [&](int d, int j, int p) -> uint32_t {
+            const uint32_t codes = (w[d][j][p / HALF] >> (BITS * (p % HALF))) & MASK;
+            if constexpr (CONVERT)
+                return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)(float)(codes & 0xFFu),
+                                                             (__bf16)(float)(codes >> 16)});
+            else
+                return codes | PX::MAGIC;
+        };
+        if constexpr (XREG) {
 #pragma unroll
-        for (int d = 0; d < D; ++d)
+            for (int d = 0; d < D; ++d)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                float total = 0.0f;
+                for (int m = 0; m < MT; ++m) {
+                    float total = 0.0f;
 #pragma unroll
-                for (int j = 0; j < UPL; ++j) {
-                    float part = 0.0f;
+                    for (int j = 0; j < UPL; ++j) {
+                        float part = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < BITS; ++i)
-#pragma unroll
-                        for (int t = 0; t < HALF; ++t) {
-                            const uint32_t codes = (w[d][j][i] >> (BITS * t)) & MASK;
-                            uint32_t pair;
-                            if constexpr (CONVERT)
-                                pair = __builtin_bit_cast(
-                                    uint32_t, bf16x2_t{(__bf16)(float)(codes & 0xFFu),
-                                                       (__bf16)(float)(codes >> 16)});
-                            else
-                                pair = codes | PX::MAGIC;
-                            part = PX::dot(pair, xr[m][j][HALF * i + t], part);
-                        }
-                    const float s = E::to_f32(sv[d][j]), b = E::to_f32(bv[d][j]);
-                    const float qx = part - OFFSET * xs[m][j];
-                    total = __builtin_fmaf(s, qx, __builtin_fmaf(b, xs[m][j], total));
+                        for (int p = 0; p < 16; ++p)
+                            part = PX::dot(code_pair(d, j, p), xr[m][j][p], part);
+                        const float s = E::to_f32(sv[d][j]), b = E::to_f32(bv[d][j]);
+                        const float qx = part - OFFSET * xs[m][j];
+                        total = __builtin_fmaf(s, qx, __builtin_fmaf(b, xs[m][j], total));
+                    }
+                    acc[d * MT + m] = total;
                 }
-                acc[d * MT + m] = total;
+        } else {
+#pragma unroll
+            for (int i = 0; i < D * MT; ++i)
+                acc[i] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < UPL; ++j) {
+                const int u = lane + 64 * j;
+                float part[D][MT];
+#pragma unroll
+                for (int d = 0; d < D; ++d)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        part[d][m] = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u32x4_t xv[MT];
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        xv[m] = xl[m][q][u];
+#pragma unroll
+                    for (int d = 0; d < D; ++d)
+#pragma unroll
+                        for (int pp = 0; pp < 4; ++pp) {
+                            const uint32_t pair = code_pair(d, j, 4 * q + pp);
+#pragma unroll
+                            for (int m = 0; m < MT; ++m)
+                                part[d][m] = PX::dot(pair, xv[m][pp], part[d][m]);
+                        }
+                    // One step's activation vectors live at a time.
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const float xsum = sl[m][u];
+#pragma unroll
+                    for (int d = 0; d < D; ++d) {
+                        const float s = E::to_f32(sv[d][j]), b = E::to_f32(bv[d][j]);
+                        const float qx = part[d][m] - OFFSET * xsum;
+                        acc[d * MT + m] =
+                            __builtin_fmaf(s, qx, __builtin_fmaf(b, xsum, acc[d * MT + m]));
+                    }
+                }
             }
+        }
         reduce_slots<D * MT, 64>(acc);
         if (lane == 63) {
 #pragma unroll
