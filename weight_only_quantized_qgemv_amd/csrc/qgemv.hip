@@ -257,14 +257,42 @@ hipError_t run_rowstream_upl(const GemvArgs& a, int64_t m0, int mc, hipStream_t 
     return hipErrorInvalidValue;   // two rows only up to four units per lane
 }
 
-// Three or four activation rows in one pass (their slices read from LDS),
-// up to two units per lane: the LDS of four rows' slices stays under 64 KB.
-template <int BITS, int DT>
-hipError_t run_rowstream_m4(const GemvArgs& a, hipStream_t st)
+// Three or four activation rows with the products on the 4x4x4 matrix
+// instruction: a wave per four weight rows, R rounds of 16 units (up to
+// K = 4096: the LDS of four rows' activation slices stays under 64 KB).
+template <int BITS, int DT, int R>
+hipError_t run_rowmfma_r(const GemvArgs& a, hipStream_t st)
 {
-    const int64_t upl = (a.K / 32 + 63) / 64;
-    if (upl <= 1) return run_rowstream<BITS, DT, 4, 1>(a, 0, (int)a.M, st);
-    return run_rowstream<BITS, DT, 4, 2>(a, 0, (int)a.M, st);
+    RowStreamArgs k{};
+    k.x = a.x;
+    k.wq = a.wq;
+    k.scales = a.scales;
+    k.biases = a.biases;
+    k.y = a.y;
+    k.M = (int)a.M;
+    k.N = (int)a.N;
+    k.K = (int)a.K;
+    k.gs = a.gs;
+    k.units_row = (uint32_t)(a.K / 32);
+    int64_t blocks = (a.N + 15) / 16;
+    blocks = blocks < kMaxBlocks ? blocks : kMaxBlocks;
+    if ((a.K / a.gs) % 2 == 0)
+        hipLaunchKernelGGL((qgemv_rowmfma_kernel<BITS, DT, R, true>), dim3((int)blocks), dim3(256), 0,
+                           st, k);
+    else
+        hipLaunchKernelGGL((qgemv_rowmfma_kernel<BITS, DT, R, false>), dim3((int)blocks), dim3(256),
+                           0, st, k);
+    return hipGetLastError();
+}
+
+template <int BITS, int DT>
+hipError_t run_rowmfma(const GemvArgs& a, hipStream_t st)
+{
+    const int64_t rounds = (a.K / 32 + 15) / 16;
+    if (rounds <= 1) return run_rowmfma_r<BITS, DT, 1>(a, st);
+    if (rounds <= 2) return run_rowmfma_r<BITS, DT, 2>(a, st);
+    if (rounds <= 4) return run_rowmfma_r<BITS, DT, 4>(a, st);
+    return run_rowmfma_r<BITS, DT, 8>(a, st);
 }
 
 template <int BITS, int DT>
@@ -289,14 +317,13 @@ hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
         // on the 14336 x 4096 decode shape); three and more go to the matrix cores.
         constexpr int min_m = 3;
 #endif
-#ifdef QP_TUNING
-        const bool m4_rows = tuning_env("QP_RS_M4", 1) != 0;
-#else
-        constexpr bool m4_rows = true;
-#endif
+        // Three and four rows: measured 12.0 us at 4 bits on 14336 x 4096
+        // (15.5 on the tile path below, 14.6 with dot products on four
+        // activation rows); one and two rows stay on the dot-product stream
+        // (9.0 against 11.3 us at one row).
         if constexpr (BITS == 2 || BITS == 4 || BITS == 8) {
-            if (m4_rows && (a.M == 3 || a.M == 4) && a.K % 32 == 0 && a.K <= 2 * 64 * 32)
-                return run_rowstream_m4<BITS, DT>(a, st);
+            if ((a.M == 3 || a.M == 4) && a.K % 32 == 0 && a.K <= 2 * 64 * 32)
+                return run_rowmfma<BITS, DT>(a, st);
         }
         if (a.M >= min_m) {
             bool done = false;

@@ -212,27 +212,22 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
         }
     }
     __syncthreads();
-    // Up to two activation rows keep their slices in registers; more rows
-    // read them from LDS as the dot products go (four pairs at a time), which
-    // keeps the register count of four rows near that of one.
-    constexpr bool XREG = MT <= 2;
-    uint32_t xr[XREG ? MT : 1][UPL][16];
-    float xs[XREG ? MT : 1][UPL];
-    if constexpr (XREG) {
+    static_assert(MT <= 2, "three and more activation rows use the matrix-core kernel");
+    uint32_t xr[MT][UPL][16];
+    float xs[MT][UPL];
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int j = 0; j < UPL; ++j) {
-                const int u = lane + 64 * j;
+        for (int j = 0; j < UPL; ++j) {
+            const int u = lane + 64 * j;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const u32x4_t v = xl[m][q][u];
-                    xr[m][j][4 * q] = v.x; xr[m][j][4 * q + 1] = v.y;
-                    xr[m][j][4 * q + 2] = v.z; xr[m][j][4 * q + 3] = v.w;
-                }
-                xs[m][j] = sl[m][u];
+            for (int q = 0; q < 4; ++q) {
+                const u32x4_t v = xl[m][q][u];
+                xr[m][j][4 * q] = v.x; xr[m][j][4 * q + 1] = v.y;
+                xr[m][j][4 * q + 2] = v.z; xr[m][j][4 * q + 3] = v.w;
             }
-    }
+            xs[m][j] = sl[m][u];
+        }
 
     for (bool first = true; r0 < a.N; r0 += GW * D, first = false) {
         if (!first)
@@ -249,68 +244,23 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
             else
                 return codes | PX::MAGIC;
         };
-        if constexpr (XREG) {
 #pragma unroll
-            for (int d = 0; d < D; ++d)
+        for (int d = 0; d < D; ++d)
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    float total = 0.0f;
+            for (int m = 0; m < MT; ++m) {
+                float total = 0.0f;
 #pragma unroll
-                    for (int j = 0; j < UPL; ++j) {
-                        float part = 0.0f;
+                for (int j = 0; j < UPL; ++j) {
+                    float part = 0.0f;
 #pragma unroll
-                        for (int p = 0; p < 16; ++p)
-                            part = PX::dot(code_pair(d, j, p), xr[m][j][p], part);
-                        const float s = E::to_f32(sv[d][j]), b = E::to_f32(bv[d][j]);
-                        const float qx = part - OFFSET * xs[m][j];
-                        total = __builtin_fmaf(s, qx, __builtin_fmaf(b, xs[m][j], total));
-                    }
-                    acc[d * MT + m] = total;
+                    for (int p = 0; p < 16; ++p)
+                        part = PX::dot(code_pair(d, j, p), xr[m][j][p], part);
+                    const float s = E::to_f32(sv[d][j]), b = E::to_f32(bv[d][j]);
+                    const float qx = part - OFFSET * xs[m][j];
+                    total = __builtin_fmaf(s, qx, __builtin_fmaf(b, xs[m][j], total));
                 }
-        } else {
-#pragma unroll
-            for (int i = 0; i < D * MT; ++i)
-                acc[i] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < UPL; ++j) {
-                const int u = lane + 64 * j;
-                float part[D][MT];
-#pragma unroll
-                for (int d = 0; d < D; ++d)
-#pragma unroll
-                    for (int m = 0; m < MT; ++m)
-                        part[d][m] = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    u32x4_t xv[MT];
-#pragma unroll
-                    for (int m = 0; m < MT; ++m)
-                        xv[m] = xl[m][q][u];
-#pragma unroll
-                    for (int d = 0; d < D; ++d)
-#pragma unroll
-                        for (int pp = 0; pp < 4; ++pp) {
-                            const uint32_t pair = code_pair(d, j, 4 * q + pp);
-#pragma unroll
-                            for (int m = 0; m < MT; ++m)
-                                part[d][m] = PX::dot(pair, xv[m][pp], part[d][m]);
-                        }
-                    // One step's activation vectors live at a time.
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const float xsum = sl[m][u];
-#pragma unroll
-                    for (int d = 0; d < D; ++d) {
-                        const float s = E::to_f32(sv[d][j]), b = E::to_f32(bv[d][j]);
-                        const float qx = part[d][m] - OFFSET * xsum;
-                        acc[d * MT + m] =
-                            __builtin_fmaf(s, qx, __builtin_fmaf(b, xsum, acc[d * MT + m]));
-                    }
-                }
+                acc[d * MT + m] = total;
             }
-        }
         reduce_slots<D * MT, 64>(acc);
         if (lane == 63) {
 #pragma unroll
@@ -319,6 +269,237 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
                 for (int m = 0; m < MT; ++m)
                     if (r0 + d < a.N && m < a.M)
                         y[(int64_t)m * a.N + r0 + d] = E::from_f32(acc[d * MT + m]);
+        }
+    }
+}
+
+// Three or four activation rows on the matrix cores: the 4x4x4 instruction
+// holds sixteen independent 4 x 4 blocks per wave, and here block b of a wave
+// is unit 16 rho + b of the wave's four weight rows at round rho. Lane 4 b + c
+// holds, for its block, activation row c (operand A, four activations of the
+// unit) and weight row r0 + c (operand B, the same four positions as OFFSET + q
+// pairs), and ends with the sums for weight row r0 + c over activation rows
+// 0..3 (one per accumulator register). A unit takes eight instructions; its
+// group's scale and bias are then applied per lane, and the sixteen blocks are
+// summed at the end. Per code this is the same extraction work as one
+// activation row on the dot-product path, while the products of all four
+// activation rows go to the matrix cores.
+template <int DT> struct RowMfma;
+template <> struct RowMfma<DT_BF16> {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    static __device__ __forceinline__ f32x4_t mma(u32x2_t a, u32x2_t b, f32x4_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                      __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+    }
+};
+template <> struct RowMfma<DT_F16> {
+    typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+    static __device__ __forceinline__ f32x4_t mma(u32x2_t a, u32x2_t b, f32x4_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(f16x4_t, a),
+                                                  __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+    }
+};
+
+template <int BITS, int DT, int R, bool WIDE>
+__global__ __launch_bounds__(256) void qgemv_rowmfma_kernel(RowStreamArgs a)
+{
+    using PX = RowStreamPair<DT>;
+    using E = Elem<DT>;
+    using St = typename E::storage;
+    static_assert(BITS == 2 || BITS == 4 || BITS == 8, "codes in whole 16-bit halves");
+    constexpr int CPW = 32 / BITS;                   // codes per word
+    constexpr int HALF = CPW / 2;                    // pairs per word
+    constexpr bool CONVERT = BITS == 8 && DT == DT_BF16;
+    constexpr float OFFSET = CONVERT ? 0.0f : PX::OFFSET;
+    constexpr uint32_t M1 = (1u << BITS) - 1u;
+    constexpr uint32_t MASK = M1 | (M1 << 16);
+    constexpr int UNITS = 16 * R;                    // unit slots of a row
+    constexpr int ENTRIES = 4 * UNITS;               // (activation row, unit) slices
+    constexpr int EPT = (ENTRIES + 255) / 256;
+    // Permuted activation pairs of slice (m, u), four 4-word vectors, and the
+    // slice sums of unit u for the four activation rows.
+    __shared__ u32x4_t xl[4][4][UNITS];
+    __shared__ float sl[UNITS][4];
+    constexpr int SBD = 2 * UNITS;                   // dwords of four rows' scales at most
+    constexpr int NV = (SBD + 63) / 64;
+    __shared__ uint32_t sbl[4][2][WIDE ? SBD : 1];
+
+    const int lane = threadIdx.x & 63, blk = lane >> 2, col = lane & 3;
+    const int wv = (int)(threadIdx.x >> 6);
+    const int gw = (int)blockIdx.x * 4 + wv;
+    const int GW = (int)gridDim.x * 4;
+    const uint32_t row_bytes = (uint32_t)a.K * BITS / 8;
+    const uint32_t groups_row = (uint32_t)(a.K / a.gs);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wq, (uint32_t)a.N * row_bytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)a.N * groups_row * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.biases, (uint32_t)a.N * groups_row * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.K * 2);
+    St* y = static_cast<St*>(a.y);
+    uint32_t gofs[R];                                // byte offset of unit 16 rho + blk's group
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho)
+        gofs[rho] = (uint32_t)((32 * (16 * rho + blk)) / a.gs) * 2;
+
+    uint32_t raw[EPT][16];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int idx = (int)threadIdx.x + 256 * e, m = idx / UNITS, u = idx % UNITS;
+        const bool live = idx < ENTRIES && m < a.M && u < (int)a.units_row;
+        buffer_words<16>(rx, live ? ((uint32_t)m * (uint32_t)a.K + 32u * (uint32_t)u) * 2 : OOB,
+                         raw[e]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    const uint32_t nd = 2 * groups_row;              // dwords of four rows' scales
+    uint32_t sw[NV], bw[NV];
+    uint32_t w[R][BITS];
+    St sv[R], bv[R];
+    auto load = [&](int r0) {
+        if constexpr (WIDE) {
+            const uint32_t base = (uint32_t)r0 * groups_row * 2;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const uint32_t i = (uint32_t)(lane + 64 * v);
+                const uint32_t off = i < nd ? base + 4 * i : OOB;
+                sw[v] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+                bw[v] = __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int rho = 0; rho < R; ++rho) {
+            const int u = 16 * rho + blk, r = r0 + col;
+            const bool live = u < (int)a.units_row && r < a.N;
+            buffer_words<BITS, BITS == 8 ? 0 : kStreamPolicy>(
+                rw, live ? (uint32_t)r * row_bytes + (uint32_t)u * (4 * BITS) : OOB, w[rho]);
+            if constexpr (!WIDE) {
+                const uint32_t so = live ? (uint32_t)r * groups_row * 2 + gofs[rho] : OOB;
+                sv[rho] = buffer_elem<DT>(rs, so);
+                bv[rho] = buffer_elem<DT>(rb, so);
+            }
+        }
+    };
+    auto exchange = [&]() {
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const uint32_t i = (uint32_t)(lane + 64 * v);
+                if (i < nd) {
+                    sbl[wv][0][i] = sw[v];
+                    sbl[wv][1][i] = bw[v];
+                }
+            }
+#pragma unroll
+            for (int rho = 0; rho < R; ++rho) {
+                const bool live = 16 * rho + blk < (int)a.units_row;
+                // Element e = c * groups + g sits in half e % 2 of slot e / 2;
+                // e / 2 < SBD for every lane.
+                const uint32_t e = (uint32_t)col * groups_row + gofs[rho] / 2;
+                const uint32_t ds = sbl[wv][0][e >> 1], db = sbl[wv][1][e >> 1];
+                const uint32_t sh = 16 * (e & 1);
+                sv[rho] = live ? St(ds >> sh) : St(0);
+                bv[rho] = live ? St(db >> sh) : St(0);
+            }
+        }
+    };
+    int r0 = gw * 4;
+    load(r0);
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int idx = (int)threadIdx.x + 256 * e, m = idx / UNITS, u = idx % UNITS;
+        if (idx < ENTRIES) {
+            uint32_t p[16];
+#pragma unroll
+            for (int i = 0; i < BITS; ++i)
+#pragma unroll
+                for (int t = 0; t < HALF; ++t) {
+                    const int k0 = CPW * i + t, k1 = k0 + HALF;
+                    const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
+                    const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
+                    p[HALF * i + t] = lo | (hi << 16);
+                }
+            float sum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                sum += E::to_f32((uint16_t)(raw[e][k / 2] >> (16 * (k & 1))));
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xl[m][q][u] = u32x4_t{p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]};
+            sl[u][m] = sum;
+        }
+    }
+    __syncthreads();
+
+    for (bool first = true; r0 < a.N; r0 += GW * 4, first = false) {
+        if (!first)
+            load(r0);
+        exchange();
+        auto code_pair = [&](int rho, int p) -> uint32_t {
+            const uint32_t codes = (w[rho][p / HALF] >> (BITS * (p % HALF))) & MASK;
+            if constexpr (CONVERT)
+                return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)(float)(codes & 0xFFu),
+                                                             (__bf16)(float)(codes >> 16)});
+            else
+                return codes | PX::MAGIC;
+        };
+        // Two rounds at a time, their instruction chains interleaved.
+        constexpr int RP = R >= 2 ? 2 : 1;
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int r2 = 0; r2 < R; r2 += RP) {
+            f32x4_t c[RP];
+#pragma unroll
+            for (int h = 0; h < RP; ++h)
+                c[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x4_t xv[RP];
+#pragma unroll
+                for (int h = 0; h < RP; ++h)
+                    xv[h] = xl[col][q][16 * (r2 + h) + blk];
+#pragma unroll
+                for (int h = 0; h < RP; ++h)
+                    c[h] = RowMfma<DT>::mma(
+                        u32x2_t{xv[h].x, xv[h].y},
+                        u32x2_t{code_pair(r2 + h, 4 * q), code_pair(r2 + h, 4 * q + 1)}, c[h]);
+#pragma unroll
+                for (int h = 0; h < RP; ++h)
+                    c[h] = RowMfma<DT>::mma(
+                        u32x2_t{xv[h].z, xv[h].w},
+                        u32x2_t{code_pair(r2 + h, 4 * q + 2), code_pair(r2 + h, 4 * q + 3)}, c[h]);
+            }
+#pragma unroll
+            for (int h = 0; h < RP; ++h) {
+                const int u = 16 * (r2 + h) + blk;
+                const float s = E::to_f32(sv[r2 + h]), b = E::to_f32(bv[r2 + h]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float xs = sl[u][i];
+                    acc[i] = __builtin_fmaf(s, c[h][i] - OFFSET * xs, __builtin_fmaf(b, xs, acc[i]));
+                }
+            }
+            // Two rounds' activation vectors live at a time.
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Sum over the sixteen blocks: rotations by 4 and 8 within each row of
+        // 16 lanes, then across the rows.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = acc[i];
+            v += dpp_f32<0x124>(v);
+            v += dpp_f32<0x128>(v);
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc[i] = v;
+        }
+        if (lane < 4 && r0 + lane < a.N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < a.M)
+                    y[(int64_t)i * a.N + r0 + lane] = E::from_f32(acc[i]);
         }
     }
 }
