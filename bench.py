@@ -44,8 +44,8 @@ CSRC = os.path.join(ROOT, "weight_only_quantized_qgemv_amd", "csrc")
 # (FETCH_SIZE, WRITE_SIZE) of `bench.py --steps 20 --warmup 2 --no-rows
 # --no-cpu-baseline`, each scaled by the same counter on a plain 1 GiB copy.
 # It holds only while the decode kernel's sources are the ones it was taken on.
-TRAFFIC = {"src_sha": "d6e3909dcf4569c5", "fetch_bytes": 33207532, "write_bytes": 28672,
-           "fetch_scale": 2.0, "write_scale": 1.0}
+TRAFFIC = {"src_sha": "c717d3eb4d5290bb", "fetch_bytes": 33222897, "write_bytes": 28672,
+           "fetch_scale": 1.9999, "write_scale": 1.0}
 DECODE_SOURCES = ("rowstream.hpp", "gemv_core.hpp", "common.hpp", "qgemv.hip")
 
 
@@ -332,7 +332,7 @@ def main():
                    "rotation_bytes": wb * copies},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "qgemv_rowstream_kernel<BITS=4, bf16, MT=1, UPL=2>",
+                     "kernel": "qgemv_rowstream_kernel<BITS=4, bf16, MT=1, UPL=2, WPB=4, WIDE=true>",
                      "us_per_launch": round(ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": wb},
     }
