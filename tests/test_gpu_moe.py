@@ -120,6 +120,33 @@ def moe_config(T, seed_ids=55):
     return E, top_k, ids, a_s, a_d, (gate_h, gate_d), (up_h, up_d), (down_h, down_d)
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("T,top_k,E,R,C,gs,skew", [
+    (24, 4, 32, 130, 2048, 64, False),   # 3 pairs per expert, K = 2048, ragged rows
+    (12, 8, 24, 72, 96, 32, False),      # 4 per expert, 3 units per row, odd group count
+    (10, 4, 16, 64, 512, 128, True),     # expert 0 in every token: 10 pairs, two tiles
+])
+def test_moe_fused_few_pairs_per_expert(bits, dt, T, top_k, E, R, C, gs, skew):
+    """The fused form at two to four pairs per expert, where tiles of up to 8
+    pairs go to the four-row matrix-instruction kernel: ragged row counts,
+    partial unit rounds, and an expert whose pairs span two tiles."""
+    log(f"moe few pairs bits={bits} dt={dt} T={T} top_k={top_k} E={E} R={R} C={C} skew={skew}")
+    gate_h, gate_d = stack(E, R, C, bits, gs, dt, 71 + bits)
+    up_h, up_d = stack(E, R, C, bits, gs, dt, 72 + bits)
+    if skew:
+        ids = np.array([[0] + [1 + (t + j) % (E - 1) for j in range(top_k - 1)] for t in range(T)],
+                       dtype=np.int32).ravel()
+    else:
+        ids = synth.moe_ids(T, top_k, E, seed=75).ravel()
+    ids_d = torch.from_numpy(ids).to(dev())
+    a_s, a_d = activations((T, C), dt, 74)
+    out = qp.qgemv_moe_id_gate_up_silu(a_d, ids_d, T, top_k, C, 0, gate_d, up_d, bits, gs)
+    torch.cuda.synchronize()
+    ref = qref.moe_gate_up_silu(a_s, dt, ids, T, top_k, C, 0, gate_h, up_h, dt, E, R, C, bits, gs)
+    check_fused(out, ref, dt, "few pairs gate_up")
+
+
 @pytest.mark.parametrize("T", [1, 64, 512])
 def test_moe_config_sampled(T):
     """128 experts, top-8, gate/up [128, 768, 2048], down [128, 2048, 768], 4-bit

@@ -154,6 +154,15 @@ size_t moe_workspace_bytes(int64_t n_pairs, int64_t num_experts)
 
 namespace {
 
+#ifdef QP_TUNING
+// Path override for tuning builds only (never defined in the library).
+int tuning_env_moe(const char* name, int dflt)
+{
+    const char* v = getenv(name);
+    return v ? atoi(v) : dflt;
+}
+#endif
+
 int pick_mt(int64_t P, int64_t E, int mtmax)
 {
     int mt = 1;
@@ -228,6 +237,38 @@ int moe_mfma_nb(const MoeArgs& a)
     return nb;
 }
 
+int moe_rowmfma_mt(const MoeArgs& a)
+{
+    if (a.dt == DT_F32 || !(a.bits == 2 || a.bits == 4 || a.bits == 8) || a.n_cols % 32 != 0 ||
+        a.n_cols > 2048)
+        return 0;
+    const int64_t P = a.n_tokens * a.top_k;
+    // The fused gate + up form at two to four pairs per expert: measured 59.4
+    // against 72.6 us at 256 pairs and 68.4 against 75.3 us at 512 pairs over
+    // 128 experts ([768, 2048] matrices, 4-bit), where the 16-pair
+    // matrix-core tiles took it. At 128 and 1024 pairs, and for the plain
+    // down projection (against the routed GEMM), it was slower.
+#ifdef QP_TUNING
+    const int force = tuning_env_moe("QP_MOE_ROW", -1);
+    if (force == 0)
+        return 0;
+    const bool dense_enough = force == 1 || (a.fused_silu && P >= 2 * a.E && P <= 4 * a.E);
+#else
+    const bool dense_enough = a.fused_silu && P >= 2 * a.E && P <= 4 * a.E;
+#endif
+    if (!dense_enough)
+        return 0;
+    const int64_t es = 2;
+    const bool vec = reinterpret_cast<uintptr_t>(a.a) % 16 == 0 && (a.a_outer * es) % 16 == 0 &&
+                     (a.a_inner * es) % 16 == 0;
+    const int64_t x_span = ((a.n_tokens - 1) * a.a_outer + (a.top_k - 1) * a.a_inner + a.n_cols) * es;
+    const bool small = x_span < (int64_t(1) << 31) &&
+                       a.n_rows * (a.n_cols * a.bits / 8) < (int64_t(1) << 31) &&
+                       a.n_rows * (a.n_cols / a.gs) * es < (int64_t(1) << 31) &&
+                       P * a.n_rows * es < (int64_t(1) << 31);
+    return vec && small ? 8 : 0;
+}
+
 int moe_gemm_bm(const MoeArgs& a)
 {
     if (a.dt == DT_F32 || a.n_cols % 64 != 0)
@@ -263,9 +304,11 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
 {
     MoeRouting r{};
     const int64_t P = a.n_tokens * a.top_k;
-    const int bm = moe_gemm_bm(a);
-    const int nb = bm > 0 ? 0 : moe_mfma_nb(a);
-    const int mt = bm > 0 ? bm : nb > 0 ? 16 * nb : moe_tile_height(P, a.E, a.bits, a.dt);
+    const int rm = moe_rowmfma_mt(a);
+    const int bm = rm > 0 ? 0 : moe_gemm_bm(a);
+    const int nb = rm > 0 || bm > 0 ? 0 : moe_mfma_nb(a);
+    const int mt = rm > 0 ? rm : bm > 0 ? bm : nb > 0 ? 16 * nb
+                                                       : moe_tile_height(P, a.E, a.bits, a.dt);
     if (mt == 1) {
         // One pair per tile: tile t is pair t itself, read straight from ids by
         // the compute launch, and the routing launch is skipped.
@@ -278,6 +321,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
     }
     r.nb = nb;
     r.gemm_bm = bm;
+    r.rowmfma = rm;
     const bool f = a.fused_silu;
     switch (a.bits) {
     case 2: return f ? launch_moe_b2_n2(a, r, st) : launch_moe_b2_n1(a, r, st);

@@ -6,6 +6,7 @@
 #include "gemv_core.hpp"
 #include "mfma_gemv.hpp"
 #include "gemm_core.hpp"
+#include "moe_rowmfma.hpp"
 #include "launch.hpp"
 
 #if !defined(QP_BITS) || !defined(QP_NMAT)
@@ -154,6 +155,33 @@ hipError_t run_gemm_tiles(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     return hipGetLastError();
 }
 
+// Four-row matrix-instruction tiles of up to 8 pairs (moe_rowmfma.hpp): grid x
+// covers the expert's rows 64 at a time, y strides over the tiles.
+template <int BITS, int DT, int NMAT>
+hipError_t run_rowmfma_tiles(const GemvKernelArgs& k, int64_t max_tiles, hipStream_t st)
+{
+    if constexpr ((BITS == 2 || BITS == 4 || BITS == 8) && DT != DT_F32) {
+        int64_t gy = max_tiles < 65535 ? max_tiles : 65535;
+        gy = gy < 1 ? 1 : gy;
+        constexpr int rows = 4 * kMoeRowWaves * kMoeRowQuads;
+        const dim3 grid((unsigned)((k.R + rows - 1) / rows), (unsigned)gy);
+        const dim3 block(64 * kMoeRowWaves);
+        const int64_t rounds = (k.K / 32 + 15) / 16;
+        if (rounds <= 1)
+            hipLaunchKernelGGL((qgemv_moe_rowmfma_kernel<BITS, DT, 1, NMAT, 2>), grid, block, 0, st, k);
+        else if (rounds <= 2)
+            hipLaunchKernelGGL((qgemv_moe_rowmfma_kernel<BITS, DT, 2, NMAT, 2>), grid, block, 0, st, k);
+        else if (rounds <= 4)
+            hipLaunchKernelGGL((qgemv_moe_rowmfma_kernel<BITS, DT, 4, NMAT, 2>), grid, block, 0, st, k);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    } else {
+        (void)k; (void)max_tiles; (void)st;
+        return hipErrorInvalidValue;
+    }
+}
+
 template <int BITS, int DT, int NMAT>
 hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
 {
@@ -196,6 +224,8 @@ hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     if constexpr (DT == DT_F32) {
         return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
     } else {
+        if (r.rowmfma > 0)
+            return run_rowmfma_tiles<BITS, DT, NMAT>(k, r.max_tiles, st);
         if (r.gemm_bm == 64)
             return run_gemm_tiles<BITS, DT, NMAT, 64>(a, r, st);
         switch (r.nb) {

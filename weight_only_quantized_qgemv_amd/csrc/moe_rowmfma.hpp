@@ -1,0 +1,251 @@
+// moe_rowmfma.hpp — routed MoE tiles of up to 8 pairs on the 4x4x4 matrix
+// instruction (ferrum-kernels src/stacked_expert.rs, `gemv_moe_id_batched` and
+// `gemv_moe_id_gate_up_silu`: every pair of a tile shares its expert's
+// weights, which are read once per tile).
+//
+// The dense four-row kernel (rowstream.hpp, `qgemv_rowmfma_kernel`) applied to
+// a routed tile: the tile's pair rows are gathered into the block's LDS as the
+// same permuted activation slices, and each wave owns four rows of the
+// expert's matrix (or of both matrices of the fused form). Block b of a wave
+// is unit 16 rho + b at round rho; lane 4 b + c holds activation row c of each
+// 4-row chunk (A) and weight row r0 + c (B, OFFSET + q pairs). Per unit the
+// group's scale and bias are applied per lane; the sixteen blocks are summed at
+// the end, and lanes 0..3 store their row for every pair of the tile, through
+// SiLU(gate) * up in the fused form.
+//
+// A block of 4 waves covers 64 weight rows, each wave 4 row quads in turn, so
+// that the gather (up to 8 activation rows of K elements from L2) is shared by
+// 64 rows while several blocks still share a CU and hide each other's
+// latency.
+#pragma once
+
+#include "gemv_core.hpp"
+#include "rowstream.hpp"
+
+namespace qp {
+
+constexpr int kMoeRowWaves = 4;
+constexpr int kMoeRowQuads = 4;                      // row quads per wave and tile
+
+template <int BITS, int DT, int R, int NMAT, int MC>
+__global__ __launch_bounds__(64 * kMoeRowWaves) void qgemv_moe_rowmfma_kernel(GemvKernelArgs a)
+{
+    using PX = RowStreamPair<DT>;
+    using E = Elem<DT>;
+    using St = typename E::storage;
+    static_assert(BITS == 2 || BITS == 4 || BITS == 8, "codes in whole 16-bit halves");
+    constexpr int CPW = 32 / BITS;
+    constexpr int HALF = CPW / 2;
+    constexpr bool CONVERT = BITS == 8 && DT == DT_BF16;
+    constexpr float OFFSET = CONVERT ? 0.0f : PX::OFFSET;
+    constexpr uint32_t M1 = (1u << BITS) - 1u;
+    constexpr uint32_t MASK = M1 | (M1 << 16);
+    constexpr int MT = 4 * MC;                       // pairs per tile at most
+    constexpr int UNITS = 16 * R;                    // unit slots of a row
+    constexpr int ENTRIES = MT * UNITS;              // (pair, unit) slices
+    constexpr int THREADS = 64 * kMoeRowWaves;
+    constexpr int EPT = (ENTRIES + THREADS - 1) / THREADS;
+    constexpr int SB = (int)sizeof(St);
+    __shared__ u32x4_t xl[MT][4][UNITS];
+    __shared__ float sl[UNITS][MT];
+
+    const int lane = threadIdx.x & 63, blk = lane >> 2, col = lane & 3;
+    const int wv = (int)(threadIdx.x >> 6);
+    const int Rr = (int)a.R;
+    const uint32_t units_row = (uint32_t)(a.K / 32);
+    const uint32_t row_bytes = (uint32_t)a.K * BITS / 8;
+    const uint32_t groups_row = (uint32_t)(a.K / a.gs);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out, a.out_bytes);
+    uint32_t gofs[R];
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho)
+        gofs[rho] = (uint32_t)((32 * (16 * rho + blk)) / a.gs) * SB;
+
+    const int ntiles = gemv_num_tiles(a);
+    for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
+        int expert, start, count;
+        if (!gemv_tile(a, tile, expert, start, count))
+            continue;
+        // Gather: raw activation units of the tile's pairs (zeros past the
+        // tile or the row).
+        uint32_t raw[EPT][16];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int idx = (int)threadIdx.x + THREADS * e, m = idx / UNITS, u = idx % UNITS;
+            uint32_t off = OOB;
+            if (idx < ENTRIES && m < count && u < (int)units_row) {
+                const uint32_t p = a.perm != nullptr ? (uint32_t)a.perm[start + m]
+                                                     : (uint32_t)(start + m);
+                const uint32_t tk = (uint32_t)a.top_k;
+                off = ((p / tk) * (uint32_t)a.outer + (p % tk) * (uint32_t)a.inner +
+                       32u * (uint32_t)u) * (uint32_t)SB;
+            }
+            buffer_words<16>(rx, off, raw[e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // The codes and scales of the expert's rows r0 .. r0 + 3 of this
+        // wave's quad j.
+        const int64_t erow = (int64_t)expert * a.R;
+        uint32_t w[NMAT][R][BITS];
+        St sv[NMAT][R], bv[NMAT][R];
+        auto load = [&](int r0) {
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t) {
+                const __amdgpu_buffer_rsrc_t rw =
+                    make_rsrc(reinterpret_cast<const char*>(a.wq[t]) + erow * row_bytes,
+                              (uint32_t)a.R * row_bytes);
+                const __amdgpu_buffer_rsrc_t rs =
+                    make_rsrc(static_cast<const char*>(a.scales[t]) + erow * groups_row * SB,
+                              (uint32_t)a.R * groups_row * SB);
+                const __amdgpu_buffer_rsrc_t rb =
+                    make_rsrc(static_cast<const char*>(a.biases[t]) + erow * groups_row * SB,
+                              (uint32_t)a.R * groups_row * SB);
+#pragma unroll
+                for (int rho = 0; rho < R; ++rho) {
+                    const int u = 16 * rho + blk, r = r0 + col;
+                    const bool live = u < (int)units_row && r < Rr;
+                    buffer_words<BITS, BITS == 8 ? 0 : kStreamPolicy>(
+                        rw, live ? (uint32_t)r * row_bytes + (uint32_t)u * (4 * BITS) : OOB,
+                        w[t][rho]);
+                    const uint32_t so = live ? (uint32_t)r * groups_row * SB + gofs[rho] : OOB;
+                    sv[t][rho] = buffer_elem<DT>(rs, so);
+                    bv[t][rho] = buffer_elem<DT>(rb, so);
+                }
+            }
+        };
+        auto quad_row = [&](int j) {
+            return ((int)blockIdx.x * kMoeRowQuads * kMoeRowWaves + j * kMoeRowWaves + wv) * 4;
+        };
+        load(quad_row(0));
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Permuted slices and their sums into LDS (pair HALF i + t of a slice
+        // holds x[CPW i + t] and x[CPW i + t + HALF]).
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int idx = (int)threadIdx.x + THREADS * e, m = idx / UNITS, u = idx % UNITS;
+            if (idx < ENTRIES) {
+                uint32_t p[16];
+#pragma unroll
+                for (int i = 0; i < BITS; ++i)
+#pragma unroll
+                    for (int t = 0; t < HALF; ++t) {
+                        const int k0 = CPW * i + t, k1 = k0 + HALF;
+                        const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
+                        const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
+                        p[HALF * i + t] = lo | (hi << 16);
+                    }
+                float sum = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 32; ++k)
+                    sum += E::to_f32((uint16_t)(raw[e][k / 2] >> (16 * (k & 1))));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xl[m][q][u] = u32x4_t{p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]};
+                sl[u][m] = sum;
+            }
+        }
+        __syncthreads();
+
+        for (int j = 0; j < kMoeRowQuads; ++j) {
+            const int r0 = quad_row(j);
+            if (r0 >= Rr)
+                break;
+            if (j > 0)
+                load(r0);
+            auto code_pair = [&](int t, int rho, int p) -> uint32_t {
+                const uint32_t codes = (w[t][rho][p / HALF] >> (BITS * (p % HALF))) & MASK;
+                if constexpr (CONVERT)
+                    return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)(float)(codes & 0xFFu),
+                                                                 (__bf16)(float)(codes >> 16)});
+                else
+                    return codes | PX::MAGIC;
+            };
+            f32x4_t acc[NMAT][MC];
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+                for (int ch = 0; ch < MC; ++ch)
+                    acc[t][ch] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int rho = 0; rho < R; ++rho) {
+                const int u = 16 * rho + blk;
+                f32x4_t c[NMAT][MC];
+#pragma unroll
+                for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+                    for (int ch = 0; ch < MC; ++ch)
+                        c[t][ch] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u32x4_t xv[MC];
+#pragma unroll
+                    for (int ch = 0; ch < MC; ++ch)
+                        xv[ch] = xl[4 * ch + col][q][u];
+#pragma unroll
+                    for (int t = 0; t < NMAT; ++t) {
+                        const u32x2_t b0{code_pair(t, rho, 4 * q), code_pair(t, rho, 4 * q + 1)};
+                        const u32x2_t b1{code_pair(t, rho, 4 * q + 2), code_pair(t, rho, 4 * q + 3)};
+#pragma unroll
+                        for (int ch = 0; ch < MC; ++ch) {
+                            c[t][ch] = RowMfma<DT>::mma(u32x2_t{xv[ch].x, xv[ch].y}, b0, c[t][ch]);
+                            c[t][ch] = RowMfma<DT>::mma(u32x2_t{xv[ch].z, xv[ch].w}, b1, c[t][ch]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NMAT; ++t) {
+                    const float s = E::to_f32(sv[t][rho]), b = E::to_f32(bv[t][rho]);
+#pragma unroll
+                    for (int ch = 0; ch < MC; ++ch)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float xs = sl[u][4 * ch + i];
+                            acc[t][ch][i] = __builtin_fmaf(s, c[t][ch][i] - OFFSET * xs,
+                                                           __builtin_fmaf(b, xs, acc[t][ch][i]));
+                        }
+                }
+                // One round's activation vectors live at a time.
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // Sum over the sixteen blocks, then lanes 0..3 store weight row
+            // r0 + lane for every pair of the tile.
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+                for (int ch = 0; ch < MC; ++ch)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = acc[t][ch][i];
+                        v += dpp_f32<0x124>(v);
+                        v += dpp_f32<0x128>(v);
+                        v += __shfl_xor(v, 16, 64);
+                        v += __shfl_xor(v, 32, 64);
+                        acc[t][ch][i] = v;
+                    }
+            const int row = r0 + lane;
+            if (lane < 4 && row < Rr) {
+#pragma unroll
+                for (int ch = 0; ch < MC; ++ch)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = 4 * ch + i;
+                        if (m < count) {
+                            float v = acc[0][ch][i];
+                            if constexpr (NMAT == 2)
+                                v = silu_f32(acc[0][ch][i]) * acc[1][ch][i];
+                            const uint32_t p = a.perm != nullptr ? (uint32_t)a.perm[start + m]
+                                                                 : (uint32_t)(start + m);
+                            buffer_store_elem<DT>(E::from_f32(v), ro,
+                                                  (p * (uint32_t)a.R + (uint32_t)row) * (uint32_t)SB);
+                        }
+                    }
+            }
+        }
+        __syncthreads();   // the slices are rebuilt for the next tile
+    }
+}
+
+} // namespace qp
