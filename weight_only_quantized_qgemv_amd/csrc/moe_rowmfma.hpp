@@ -24,8 +24,14 @@
 
 namespace qp {
 
-constexpr int kMoeRowWaves = 4;
-constexpr int kMoeRowQuads = 4;                      // row quads per wave and tile
+#ifndef QP_MOE_ROW_WAVES
+#define QP_MOE_ROW_WAVES 4
+#endif
+#ifndef QP_MOE_ROW_QUADS
+#define QP_MOE_ROW_QUADS 4
+#endif
+constexpr int kMoeRowWaves = QP_MOE_ROW_WAVES;
+constexpr int kMoeRowQuads = QP_MOE_ROW_QUADS;       // row quads per wave and tile
 
 template <int BITS, int DT, int R, int NMAT, int MC>
 __global__ __launch_bounds__(64 * kMoeRowWaves) void qgemv_moe_rowmfma_kernel(GemvKernelArgs a)
