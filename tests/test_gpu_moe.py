@@ -147,6 +147,35 @@ def test_moe_fused_few_pairs_per_expert(bits, dt, T, top_k, E, R, C, gs, skew):
     check_fused(out, ref, dt, "few pairs gate_up")
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("T,top_k,E,R,C,gs", [
+    (1, 8, 128, 130, 2048, 64),   # one token over 128 experts, ragged rows
+    (2, 3, 96, 64, 96, 32),       # 3 units per row, odd group count
+    (1, 4, 64, 72, 4096, 128),    # two units per lane
+])
+def test_moe_one_pair_tiles(bits, dt, T, top_k, E, R, C, gs):
+    """Few pairs over many experts: every pair is its own tile, on the
+    dot-product row kernel for the fused form (and for the plain form at this
+    density); the plain product also reads through a non-zero inner stride."""
+    log(f"moe one-pair bits={bits} dt={dt} T={T} top_k={top_k} E={E} R={R} C={C}")
+    gate_h, gate_d = stack(E, R, C, bits, gs, dt, 81 + bits)
+    up_h, up_d = stack(E, R, C, bits, gs, dt, 82 + bits)
+    ids = synth.moe_ids(T, top_k, E, seed=85).ravel()
+    ids_d = torch.from_numpy(ids).to(dev())
+    a_s, a_d = activations((T, C), dt, 84)
+    out = qp.qgemv_moe_id_gate_up_silu(a_d, ids_d, T, top_k, C, 0, gate_d, up_d, bits, gs)
+    torch.cuda.synchronize()
+    ref = qref.moe_gate_up_silu(a_s, dt, ids, T, top_k, C, 0, gate_h, up_h, dt, E, R, C, bits, gs)
+    check_fused(out, ref, dt, "one-pair gate_up")
+    # Plain product over the pairs' own rows (inner stride = row length).
+    h_s, h_d = activations((T * top_k, C), dt, 86)
+    out_p = qp.qgemv_moe_id(h_d, ids_d, T, top_k, top_k * C, C, *gate_d, bits, gs)
+    torch.cuda.synchronize()
+    ref_p, S_p = qref.moe(h_s, dt, ids, T, top_k, top_k * C, C, *gate_h, dt, E, R, C, bits, gs)
+    assert_within(out_p, ref_p, S_p, dt, "one-pair plain")
+
+
 @pytest.mark.parametrize("T", [1, 64, 512])
 def test_moe_config_sampled(T):
     """128 experts, top-8, gate/up [128, 768, 2048], down [128, 2048, 768], 4-bit

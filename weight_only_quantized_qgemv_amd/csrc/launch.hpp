@@ -110,6 +110,7 @@ struct MoeRouting {
     int nb;                 // > 0: matrix-core tiles of 16 * nb pairs (mt == 16 * nb)
     int gemm_bm;            // > 0: routed GEMM tiles of gemm_bm pairs (mt == gemm_bm)
     int rowmfma;            // > 0: four-row matrix-instruction tiles of mt <= 8 pairs
+    int rowstream;          // > 0: one-pair tiles on the dot-product row kernel (mt == 1)
 };
 hipError_t launch_moe_route(const MoeArgs& a, int mt, MoeRouting* r, hipStream_t stream);
 int moe_tile_height(int64_t n_pairs, int64_t num_experts, int bits, int dt);
@@ -121,6 +122,10 @@ int moe_mfma_nb(const MoeArgs& a);
 // kernel (the fused gate + up form, 2-, 4- and 8-bit codes, 16-bit
 // activations, K <= 2048, two to four pairs per expert), else 0.
 int moe_rowmfma_mt(const MoeArgs& a);
+// True when one-pair tiles go to the dot-product row kernel (2-, 4- and 8-bit
+// codes, 16-bit activations, K <= 4096, one tile per pair, few pairs per
+// expert).
+bool moe_rowstream_ok(const MoeArgs& a, int mt);
 // Pairs per routed-GEMM tile for this call, or 0 when the GEMV kernels take
 // it (fp32 activations, few pairs per expert, K not a multiple of 64, or
 // operands the 16-byte / 32-bit-offset accesses cannot cover).

@@ -269,6 +269,35 @@ int moe_rowmfma_mt(const MoeArgs& a)
     return vec && small ? 8 : 0;
 }
 
+bool moe_rowstream_ok(const MoeArgs& a, int mt)
+{
+    if (mt != 1 || a.dt == DT_F32 || !(a.bits == 2 || a.bits == 4 || a.bits == 8) ||
+        a.n_cols % 32 != 0 || a.n_cols > 4096)
+        return false;
+#ifdef QP_TUNING
+    const int force = tuning_env_moe("QP_MOE_ROWS1", -1);
+    if (force >= 0)
+        return force == 1;
+#endif
+    // Measured on 128 experts, 4-bit ([768, 2048] gate / up, [2048, 768]
+    // down), device time of graph-replayed calls: the fused form 6.4 against
+    // 6.8 us at 8 pairs, 8.1 against 9.0 at 16, 13.1 against 16.1 at 32, 22.6
+    // against 23.0 at 64, slower from 128 pairs; the plain form 5.6 against
+    // 6.5 us at 8 pairs, slower from 16 (its K = 768 leaves most lanes of a
+    // wave per row idle).
+    const int64_t P = a.n_tokens * a.top_k;
+    if (a.fused_silu ? 2 * P > a.E : 16 * P > a.E)
+        return false;
+    const int64_t es = 2;
+    const bool vec = reinterpret_cast<uintptr_t>(a.a) % 16 == 0 && (a.a_outer * es) % 16 == 0 &&
+                     (a.a_inner * es) % 16 == 0;
+    const int64_t x_span = ((a.n_tokens - 1) * a.a_outer + (a.top_k - 1) * a.a_inner + a.n_cols) * es;
+    return vec && x_span < (int64_t(1) << 31) &&
+           a.n_rows * (a.n_cols * a.bits / 8) < (int64_t(1) << 31) &&
+           a.n_rows * (a.n_cols / a.gs) * es < (int64_t(1) << 31) &&
+           P * a.n_rows * es < (int64_t(1) << 31);
+}
+
 int moe_gemm_bm(const MoeArgs& a)
 {
     if (a.dt == DT_F32 || a.n_cols % 64 != 0)
@@ -322,6 +351,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
     r.nb = nb;
     r.gemm_bm = bm;
     r.rowmfma = rm;
+    r.rowstream = moe_rowstream_ok(a, r.mt) ? 1 : 0;
     const bool f = a.fused_silu;
     switch (a.bits) {
     case 2: return f ? launch_moe_b2_n2(a, r, st) : launch_moe_b2_n1(a, r, st);

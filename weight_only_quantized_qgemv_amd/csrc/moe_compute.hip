@@ -182,6 +182,33 @@ hipError_t run_rowmfma_tiles(const GemvKernelArgs& k, int64_t max_tiles, hipStre
     }
 }
 
+// One-pair tiles on the dot-product row kernel (moe_rowmfma.hpp): grid x covers
+// the expert's rows 4 D at a time, y strides over the tiles.
+template <int BITS, int DT, int NMAT, int UPL>
+hipError_t run_rowstream_tiles_upl(const GemvKernelArgs& k, int64_t max_tiles, hipStream_t st)
+{
+    constexpr int D = rowstream_depth<BITS, UPL * NMAT>();
+    int64_t gy = max_tiles < 65535 ? max_tiles : 65535;
+    gy = gy < 1 ? 1 : gy;
+    const dim3 grid((unsigned)((k.R + 4 * D - 1) / (4 * D)), (unsigned)gy);
+    hipLaunchKernelGGL((qgemv_moe_rowstream_kernel<BITS, DT, UPL, NMAT>), grid, dim3(256), 0, st, k);
+    return hipGetLastError();
+}
+
+template <int BITS, int DT, int NMAT>
+hipError_t run_rowstream_tiles(const GemvKernelArgs& k, int64_t max_tiles, hipStream_t st)
+{
+    if constexpr ((BITS == 2 || BITS == 4 || BITS == 8) && DT != DT_F32) {
+        const int64_t upl = (k.K / 32 + 63) / 64;
+        if (upl <= 1) return run_rowstream_tiles_upl<BITS, DT, NMAT, 1>(k, max_tiles, st);
+        if (upl <= 2) return run_rowstream_tiles_upl<BITS, DT, NMAT, 2>(k, max_tiles, st);
+        return hipErrorInvalidValue;
+    } else {
+        (void)k; (void)max_tiles; (void)st;
+        return hipErrorInvalidValue;
+    }
+}
+
 template <int BITS, int DT, int NMAT>
 hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
 {
@@ -226,6 +253,8 @@ hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     } else {
         if (r.rowmfma > 0)
             return run_rowmfma_tiles<BITS, DT, NMAT>(k, r.max_tiles, st);
+        if (r.rowstream > 0)
+            return run_rowstream_tiles<BITS, DT, NMAT>(k, r.max_tiles, st);
         if (r.gemm_bm == 64)
             return run_gemm_tiles<BITS, DT, NMAT, 64>(a, r, st);
         switch (r.nb) {

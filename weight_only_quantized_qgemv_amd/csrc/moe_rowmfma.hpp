@@ -254,4 +254,172 @@ __global__ __launch_bounds__(64 * kMoeRowWaves) void qgemv_moe_rowmfma_kernel(Ge
     }
 }
 
+// Routed tiles of one pair (few pairs per expert, tile t = pair t) on the
+// dot-product row kernel (rowstream.hpp, `qgemv_rowstream_kernel`): the block
+// gathers the pair's activation row into LDS as permuted slices with their
+// sums, each wave owns D rows of the expert's matrix (of both matrices in the
+// fused form) with lane l on units l, l + 64, ..., and lane 63 stores the
+// reduced rows, through SiLU(gate) * up in the fused form.
+template <int BITS, int DT, int UPL, int NMAT>
+__global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs a)
+{
+    using PX = RowStreamPair<DT>;
+    using E = Elem<DT>;
+    using St = typename E::storage;
+    static_assert(BITS == 2 || BITS == 4 || BITS == 8, "codes in whole 16-bit halves");
+    constexpr int D = rowstream_depth<BITS, UPL * NMAT>();
+    constexpr int CPW = 32 / BITS;
+    constexpr int HALF = CPW / 2;
+    constexpr bool CONVERT = BITS == 8 && DT == DT_BF16;
+    constexpr float OFFSET = CONVERT ? 0.0f : PX::OFFSET;
+    constexpr uint32_t M1 = (1u << BITS) - 1u;
+    constexpr uint32_t MASK = M1 | (M1 << 16);
+    constexpr int UNITS = 64 * UPL;                  // unit slots of the pair's row
+    constexpr int EPT = (UNITS + 255) / 256;
+    constexpr int SB = (int)sizeof(St);
+    __shared__ u32x4_t xl[4][UNITS];
+    __shared__ float sl[UNITS];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = (int)(threadIdx.x >> 6);
+    const int r0 = ((int)blockIdx.x * 4 + wv) * D;   // first weight row of the wave
+    const int Rr = (int)a.R;
+    const uint32_t units_row = (uint32_t)(a.K / 32);
+    const uint32_t row_bytes = (uint32_t)a.K * BITS / 8;
+    const uint32_t groups_row = (uint32_t)(a.K / a.gs);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out, a.out_bytes);
+    uint32_t gofs[UPL];
+#pragma unroll
+    for (int j = 0; j < UPL; ++j)
+        gofs[j] = (uint32_t)((32 * (lane + 64 * j)) / a.gs) * SB;
+
+    const int ntiles = gemv_num_tiles(a);
+    for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
+        int expert, start, count;
+        if (!gemv_tile(a, tile, expert, start, count))
+            continue;
+        const uint32_t p = a.perm != nullptr ? (uint32_t)a.perm[start] : (uint32_t)start;
+        const uint32_t tk = (uint32_t)a.top_k;
+        const uint32_t xrow = (p / tk) * (uint32_t)a.outer + (p % tk) * (uint32_t)a.inner;
+        uint32_t raw[EPT][16];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int u = (int)threadIdx.x + 256 * e;
+            const bool live = u < UNITS && u < (int)units_row;
+            buffer_words<16>(rx, live ? (xrow + 32u * (uint32_t)u) * (uint32_t)SB : OOB, raw[e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        const int64_t erow = (int64_t)expert * a.R;
+        uint32_t w[NMAT][D][UPL][BITS];
+        St sv[NMAT][D][UPL], bv[NMAT][D][UPL];
+#pragma unroll
+        for (int t = 0; t < NMAT; ++t) {
+            const __amdgpu_buffer_rsrc_t rw =
+                make_rsrc(reinterpret_cast<const char*>(a.wq[t]) + erow * row_bytes,
+                          (uint32_t)a.R * row_bytes);
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(static_cast<const char*>(a.scales[t]) + erow * groups_row * SB,
+                          (uint32_t)a.R * groups_row * SB);
+            const __amdgpu_buffer_rsrc_t rb =
+                make_rsrc(static_cast<const char*>(a.biases[t]) + erow * groups_row * SB,
+                          (uint32_t)a.R * groups_row * SB);
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+#pragma unroll
+                for (int j = 0; j < UPL; ++j) {
+                    const int u = lane + 64 * j, r = r0 + d;
+                    const bool live = u < (int)units_row && r < Rr;
+                    buffer_words<BITS, BITS == 8 ? 0 : kStreamPolicy>(
+                        rw, live ? (uint32_t)r * row_bytes + (uint32_t)u * (4 * BITS) : OOB,
+                        w[t][d][j]);
+                    const uint32_t so = live ? (uint32_t)r * groups_row * SB + gofs[j] : OOB;
+                    sv[t][d][j] = buffer_elem<DT>(rs, so);
+                    bv[t][d][j] = buffer_elem<DT>(rb, so);
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int u = (int)threadIdx.x + 256 * e;
+            if (u < UNITS) {
+                uint32_t q4[16];
+#pragma unroll
+                for (int i = 0; i < BITS; ++i)
+#pragma unroll
+                    for (int t = 0; t < HALF; ++t) {
+                        const int k0 = CPW * i + t, k1 = k0 + HALF;
+                        const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
+                        const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
+                        q4[HALF * i + t] = lo | (hi << 16);
+                    }
+                float sum = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 32; ++k)
+                    sum += E::to_f32((uint16_t)(raw[e][k / 2] >> (16 * (k & 1))));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xl[q][u] = u32x4_t{q4[4 * q], q4[4 * q + 1], q4[4 * q + 2], q4[4 * q + 3]};
+                sl[u] = sum;
+            }
+        }
+        __syncthreads();
+        uint32_t xr[UPL][16];
+        float xs[UPL];
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+            const int u = lane + 64 * j;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4_t v = xl[q][u];
+                xr[j][4 * q] = v.x; xr[j][4 * q + 1] = v.y;
+                xr[j][4 * q + 2] = v.z; xr[j][4 * q + 3] = v.w;
+            }
+            xs[j] = sl[u];
+        }
+
+        float acc[NMAT * D];
+#pragma unroll
+        for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                float total = 0.0f;
+#pragma unroll
+                for (int j = 0; j < UPL; ++j) {
+                    float part = 0.0f;
+#pragma unroll
+                    for (int pp = 0; pp < 16; ++pp) {
+                        const uint32_t codes = (w[t][d][j][pp / HALF] >> (BITS * (pp % HALF))) & MASK;
+                        uint32_t pair;
+                        if constexpr (CONVERT)
+                            pair = __builtin_bit_cast(uint32_t,
+                                                      bf16x2_t{(__bf16)(float)(codes & 0xFFu),
+                                                               (__bf16)(float)(codes >> 16)});
+                        else
+                            pair = codes | PX::MAGIC;
+                        part = PX::dot(pair, xr[j][pp], part);
+                    }
+                    const float s = E::to_f32(sv[t][d][j]), b = E::to_f32(bv[t][d][j]);
+                    total = __builtin_fmaf(s, part - OFFSET * xs[j], __builtin_fmaf(b, xs[j], total));
+                }
+                acc[t * D + d] = total;
+            }
+        reduce_slots<NMAT * D, 64>(acc);
+        if (lane == 63) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                float v = acc[d];
+                if constexpr (NMAT == 2)
+                    v = silu_f32(acc[d]) * acc[D + d];
+                if (r0 + d < Rr)
+                    buffer_store_elem<DT>(E::from_f32(v), ro,
+                                          (p * (uint32_t)a.R + (uint32_t)(r0 + d)) * (uint32_t)SB);
+            }
+        }
+        __syncthreads();   // the slices are rebuilt for the next tile
+    }
+}
+
 } // namespace qp
