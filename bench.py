@@ -97,7 +97,37 @@ def time_calls(fn, steps, warmup, stream, reps=5):
     return statistics.median(out)
 
 
-def bench_dense(N, K, M, bits, gs, dt, steps, warmup, stream, dev, seed=21):
+def graph_ms(fn, n, stream, reps=5):
+    """Median over `reps` of the device period per call of n calls replayed from
+    one captured HIP graph (no host issue between the launches), HIP events
+    recorded on `stream` around each replay. For calls shorter than the host's
+    issue time of one call, where back-to-back eager calls time the host."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        out.append(start.elapsed_time(end) / n)
+    del g
+    return statistics.median(out)
+
+
+def bench_dense(N, K, M, bits, gs, dt, steps, warmup, stream, dev, seed=21, graph=False):
     import torch
     import weight_only_quantized_qgemv_amd as qp
     from weight_only_quantized_qgemv_amd import synth
@@ -113,6 +143,8 @@ def bench_dense(N, K, M, bits, gs, dt, steps, warmup, stream, dev, seed=21):
         qp.qmatmul(x, wq, s, b, bits, gs, out=y)
 
     ms = time_calls(step, steps, warmup, stream)
+    if graph:
+        ms = (ms, graph_ms(step, 8 * copies, stream))
     del sets
     torch.cuda.empty_cache()
     return ms, wb, copies
@@ -234,11 +266,14 @@ def bench_moe(T, steps, warmup, stream, dev):
     ms_gu = time_calls(gate_up, steps, warmup, stream)
     ms_d = time_calls(down, steps, warmup, stream)
     ms_ffn = time_calls(ffn, steps, warmup, stream)
+    graph = {"gate_up_silu_us_graph": graph_ms(gate_up, 40, stream),
+             "down_us_graph": graph_ms(down, 40, stream),
+             "ffn_block_us_graph": graph_ms(ffn, 40, stream)}
     touched = len(np.unique(ids_np))
     per_expert = weight_bytes(F, D, bits, gs, 2)   # one [768, 2048] matrix
     del wsets
     torch.cuda.empty_cache()
-    return ms_gu, ms_d, ms_ffn, touched, per_expert
+    return ms_gu, ms_d, ms_ffn, touched, per_expert, graph
 
 
 def cpu_baseline(n, k, bits, gs, budget_s=12.0):
@@ -358,12 +393,15 @@ def main():
         for bits in (3, 6):
             for gs in (32, 64, 128):
                 for M in (1, 8):
-                    ms_r, wb_r, _ = bench_dense(4096, 4096, M, bits, gs, torch.float16,
-                                                del_steps, 5, stream, dev, seed=31)
+                    (ms_r, ms_g), wb_r, _ = bench_dense(4096, 4096, M, bits, gs, torch.float16,
+                                                        del_steps, 5, stream, dev, seed=31,
+                                                        graph=True)
                     g = wb_r / (ms_r * 1e-3) / 1e9
                     rows[f"crossword_b{bits}_gs{gs}_m{M}"] = {
                         "us": round(ms_r * 1e3, 3), "weight_GBps": round(g, 1),
-                        "frac_hbm": round(g / HBM_PEAK_GBS, 4)}
+                        "frac_hbm": round(g / HBM_PEAK_GBS, 4),
+                        "us_graph": round(ms_g * 1e3, 3),
+                        "weight_GBps_graph": round(wb_r / (ms_g * 1e-3) / 1e9, 1)}
         # Prefill rows: x bf16 [2048, K] against the two MLP shapes.
         for (n, k) in ((14336, 4096), (4096, 14336)):
             ms_r, _, _ = bench_dense(n, k, 2048, 4, 64, bf16, 20, 3, stream, dev, seed=41)
@@ -436,7 +474,8 @@ def main():
         torch.cuda.empty_cache()
         # MoE rows: 128 experts, top-8, 4-bit gs64 bf16.
         for T in (1, 64, 512):
-            ms_gu, ms_d, ms_ffn, touched, per_expert = bench_moe(T, del_steps, 5, stream, dev)
+            ms_gu, ms_d, ms_ffn, touched, per_expert, graph = bench_moe(T, del_steps, 5, stream,
+                                                                        dev)
             gu_bytes, d_bytes = 2 * touched * per_expert, touched * per_expert
             rows[f"moe_t{T}"] = {
                 "experts_touched": touched,
@@ -447,7 +486,8 @@ def main():
                 "tflops_total": round(2.0 * T * 8 * 3 * 768 * 2048 / ((ms_gu + ms_d) * 1e-3)
                                       / 1e12, 2),
                 "ffn_block_us": round(ms_ffn * 1e3, 3),
-                "ffn_block_weight_GBps": round(3 * touched * per_expert / (ms_ffn * 1e-3) / 1e9, 1)}
+                "ffn_block_weight_GBps": round(3 * touched * per_expert / (ms_ffn * 1e-3) / 1e9, 1),
+                **{k: round(v * 1e3, 3) for k, v in graph.items()}}
         result["rows"] = rows
 
     if not args.no_cpu_baseline:
