@@ -111,17 +111,34 @@ def version() -> str:
 
 # ------------------------------------------------------------------ tensors
 
+_DTYPE_CODES = None
+
+
 def dtype_code(dt) -> int:
-    import torch
-    codes = {torch.float32: QP_F32, torch.float16: QP_F16, torch.bfloat16: QP_BF16}
-    if dt not in codes:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+        _DTYPE_CODES = {torch.float32: QP_F32, torch.float16: QP_F16, torch.bfloat16: QP_BF16}
+    code = _DTYPE_CODES.get(dt)
+    if code is None:
         raise TypeError(f"unsupported dtype {dt}")
-    return codes[dt]
+    return code
+
+
+_RAW_STREAM = None
 
 
 def _stream(t) -> int:
-    import torch
-    return torch.cuda.current_stream(t.device).cuda_stream
+    """The handle of the current stream on t's device. torch's raw-handle query
+    costs about 0.06 us per call against about 1.8 us for building the Stream
+    object, which matters for calls of a few microseconds issued one by one."""
+    global _RAW_STREAM
+    if _RAW_STREAM is None:
+        import torch
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _RAW_STREAM = ((lambda dev: raw(dev.index)) if raw is not None
+                       else (lambda dev: torch.cuda.current_stream(dev).cuda_stream))
+    return _RAW_STREAM(t.device)
 
 
 def _dev(t, name):
