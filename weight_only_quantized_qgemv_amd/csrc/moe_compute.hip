@@ -6,7 +6,7 @@
 #include "gemv_core.hpp"
 #include "mfma_gemv.hpp"
 #include "gemm_core.hpp"
-#include "moe_rowmfma.hpp"
+#include "moe_rows.hpp"
 #include "launch.hpp"
 
 #if !defined(QP_BITS) || !defined(QP_NMAT)
@@ -155,7 +155,7 @@ hipError_t run_gemm_tiles(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     return hipGetLastError();
 }
 
-// Four-row matrix-instruction tiles of up to 8 pairs (moe_rowmfma.hpp): grid x
+// Four-row matrix-instruction tiles of up to 8 pairs (moe_rows.hpp): grid x
 // covers the expert's rows 64 at a time, y strides over the tiles.
 template <int BITS, int DT, int NMAT>
 hipError_t run_rowmfma_tiles(const GemvKernelArgs& k, int64_t max_tiles, hipStream_t st)
@@ -182,7 +182,7 @@ hipError_t run_rowmfma_tiles(const GemvKernelArgs& k, int64_t max_tiles, hipStre
     }
 }
 
-// One-pair tiles on the dot-product row kernel (moe_rowmfma.hpp): grid x covers
+// One-pair tiles on the dot-product row kernel (moe_rows.hpp): grid x covers
 // the expert's rows 4 D at a time, y strides over the tiles.
 template <int BITS, int DT, int NMAT, int UPL>
 hipError_t run_rowstream_tiles_upl(const GemvKernelArgs& k, int64_t max_tiles, hipStream_t st)

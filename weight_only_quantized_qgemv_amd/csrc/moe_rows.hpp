@@ -1,7 +1,8 @@
-// moe_rowmfma.hpp — routed MoE tiles of up to 8 pairs on the 4x4x4 matrix
-// instruction (ferrum-kernels src/stacked_expert.rs, `gemv_moe_id_batched` and
-// `gemv_moe_id_gate_up_silu`: every pair of a tile shares its expert's
-// weights, which are read once per tile).
+// moe_rows.hpp — routed MoE tiles on the row kernels (ferrum-kernels
+// src/stacked_expert.rs, `gemv_moe_id_batched` and `gemv_moe_id_gate_up_silu`:
+// every pair of a tile shares its expert's weights, which are read once per
+// tile): tiles of up to 8 pairs on the 4x4x4 matrix instruction, and tiles of
+// one pair on the dot-product row kernel.
 //
 // The dense four-row kernel (rowstream.hpp, `qgemv_rowmfma_kernel`) applied to
 // a routed tile: the tile's pair rows are gathered into the block's LDS as the
