@@ -107,14 +107,16 @@ def test_qmatmul_parity_small(bits, dt, k, m):
                                     (2080, 1, 32), (16384, 2, 64), (12288, 1, 32), (2176, 2, 64),
                                     (2176, 1, 32), (2112, 2, 64), (128, 2, 64), (96, 1, 32),
                                     (4096, 4, 64), (2176, 3, 64), (2112, 4, 64), (96, 3, 32),
-                                    (1024, 4, 128)])
+                                    (1024, 4, 128), (9600, 1, 64), (5120, 2, 32)])
 def test_qmatmul_row_stream_units_per_lane(bits, dt, k, m, gs):
     """2/4/8-bit decode on the row-per-wave kernel: 1 to 8 units of 32 codes
     per lane, ragged unit counts (11008 = 344 units, 2176 = 68, 2080 = 65,
     96 = 3), two rows per pass up to K = 8192 and one beyond, three and four
     rows (activation slices read from LDS) up to K = 4096; rows with an
     even number of groups (scales read as whole rows) and with an odd one
-    (2080 / 32 = 65, 2112 / 64 = 33, 96 / 32 = 3)."""
+    (2080 / 32 = 65, 2112 / 64 = 33, 96 / 32 = 3); units per lane as the row
+    needs them (9600 = 300 units: 5 per lane; 5120 = 160: 3; 11008: 6;
+    14336 = 448: 7)."""
     n = 300
     log(f"row stream bits={bits} dt={dt} n={n} k={k} m={m} gs={gs}")
     y, y_ref, S = run_case(n, k, m, bits, gs, dt, seed=7000 + k + m + gs + bits)

@@ -249,11 +249,23 @@ template <int BITS, int DT, int MT>
 hipError_t run_rowstream_upl(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
 {
     const int64_t upl = (a.K / 32 + 63) / 64;
+#ifdef QP_TUNING
+    const bool exact = tuning_env("QP_RS_EXACT_UPL", 1) != 0;
+#else
+    constexpr bool exact = true;
+#endif
     if (upl <= 1) return run_rowstream<BITS, DT, MT, 1>(a, m0, mc, st);
     if (upl <= 2) return run_rowstream<BITS, DT, MT, 2>(a, m0, mc, st);
+    if (exact && upl <= 3) return run_rowstream<BITS, DT, MT, 3>(a, m0, mc, st);
     if (upl <= 4) return run_rowstream<BITS, DT, MT, 4>(a, m0, mc, st);
-    if constexpr (MT == 1)
+    if constexpr (MT == 1) {
+        // Units per lane as the row needs them (K = 14336: 7), so that no
+        // lane carries a whole unit of zeros through the dot products.
+        if (exact && upl <= 5) return run_rowstream<BITS, DT, MT, 5>(a, m0, mc, st);
+        if (exact && upl <= 6) return run_rowstream<BITS, DT, MT, 6>(a, m0, mc, st);
+        if (exact && upl <= 7) return run_rowstream<BITS, DT, MT, 7>(a, m0, mc, st);
         return run_rowstream<BITS, DT, MT, 8>(a, m0, mc, st);
+    }
     return hipErrorInvalidValue;   // two rows only up to four units per lane
 }
 
