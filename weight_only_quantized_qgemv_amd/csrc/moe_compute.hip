@@ -182,16 +182,27 @@ hipError_t run_rowmfma_tiles(const GemvKernelArgs& k, int64_t max_tiles, hipStre
     }
 }
 
+#ifdef QP_TUNING
+// Path override for tuning builds only (never defined in the library).
+int tuning_env_kl(const char* name, int dflt)
+{
+    const char* v = getenv(name);
+    return v ? atoi(v) : dflt;
+}
+#endif
+
 // One-pair tiles on the dot-product row kernel (moe_rows.hpp): grid x covers
 // the expert's rows 4 D at a time, y strides over the tiles.
-template <int BITS, int DT, int NMAT, int UPL>
+template <int BITS, int DT, int NMAT, int UPL, int KL>
 hipError_t run_rowstream_tiles_upl(const GemvKernelArgs& k, int64_t max_tiles, hipStream_t st)
 {
     constexpr int D = rowstream_depth<BITS, UPL * NMAT>();
+    constexpr int ROWS = 4 * (64 / KL) * D;          // weight rows of a block
     int64_t gy = max_tiles < 65535 ? max_tiles : 65535;
     gy = gy < 1 ? 1 : gy;
-    const dim3 grid((unsigned)((k.R + 4 * D - 1) / (4 * D)), (unsigned)gy);
-    hipLaunchKernelGGL((qgemv_moe_rowstream_kernel<BITS, DT, UPL, NMAT>), grid, dim3(256), 0, st, k);
+    const dim3 grid((unsigned)((k.R + ROWS - 1) / ROWS), (unsigned)gy);
+    hipLaunchKernelGGL((qgemv_moe_rowstream_kernel<BITS, DT, UPL, NMAT, KL>), grid, dim3(256), 0, st,
+                       k);
     return hipGetLastError();
 }
 
@@ -199,9 +210,15 @@ template <int BITS, int DT, int NMAT>
 hipError_t run_rowstream_tiles(const GemvKernelArgs& k, int64_t max_tiles, hipStream_t st)
 {
     if constexpr ((BITS == 2 || BITS == 4 || BITS == 8) && DT != DT_F32) {
-        const int64_t upl = (k.K / 32 + 63) / 64;
-        if (upl <= 1) return run_rowstream_tiles_upl<BITS, DT, NMAT, 1>(k, max_tiles, st);
-        if (upl <= 2) return run_rowstream_tiles_upl<BITS, DT, NMAT, 2>(k, max_tiles, st);
+        const int64_t units = k.K / 32;
+#ifdef QP_TUNING
+        const bool narrow = units <= 32 && tuning_env_kl("QP_MOE_KL32", 1) != 0;
+#else
+        const bool narrow = units <= 32;
+#endif
+        if (narrow) return run_rowstream_tiles_upl<BITS, DT, NMAT, 1, 32>(k, max_tiles, st);
+        if (units <= 64) return run_rowstream_tiles_upl<BITS, DT, NMAT, 1, 64>(k, max_tiles, st);
+        if (units <= 128) return run_rowstream_tiles_upl<BITS, DT, NMAT, 2, 64>(k, max_tiles, st);
         return hipErrorInvalidValue;
     } else {
         (void)k; (void)max_tiles; (void)st;

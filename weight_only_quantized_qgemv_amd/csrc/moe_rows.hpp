@@ -258,10 +258,12 @@ __global__ __launch_bounds__(64 * kMoeRowWaves) void qgemv_moe_rowmfma_kernel(Ge
 // Routed tiles of one pair (few pairs per expert, tile t = pair t) on the
 // dot-product row kernel (rowstream.hpp, `qgemv_rowstream_kernel`): the block
 // gathers the pair's activation row into LDS as permuted slices with their
-// sums, each wave owns D rows of the expert's matrix (of both matrices in the
-// fused form) with lane l on units l, l + 64, ..., and lane 63 stores the
-// reduced rows, through SiLU(gate) * up in the fused form.
-template <int BITS, int DT, int UPL, int NMAT>
+// sums; a wave is 64 / KL slots of KL lanes, each slot owns D rows of the
+// expert's matrix (of both matrices in the fused form) with its lane l on units
+// l, l + KL, ..., and the slot's last lane stores the reduced rows, through
+// SiLU(gate) * up in the fused form. Rows of few units (the down projection's
+// K = 768 is 24 units) take KL = 32, so that fewer lanes idle.
+template <int BITS, int DT, int UPL, int NMAT, int KL>
 __global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs a)
 {
     using PX = RowStreamPair<DT>;
@@ -275,15 +277,18 @@ __global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs
     constexpr float OFFSET = CONVERT ? 0.0f : PX::OFFSET;
     constexpr uint32_t M1 = (1u << BITS) - 1u;
     constexpr uint32_t MASK = M1 | (M1 << 16);
-    constexpr int UNITS = 64 * UPL;                  // unit slots of the pair's row
+    static_assert(KL == 32 || KL == 64, "32 or 64 lanes per row");
+    constexpr int S = 64 / KL;                       // row slots per wave
+    constexpr int UNITS = KL * UPL;                  // unit slots of the pair's row
     constexpr int EPT = (UNITS + 255) / 256;
     constexpr int SB = (int)sizeof(St);
     __shared__ u32x4_t xl[4][UNITS];
     __shared__ float sl[UNITS];
 
     const int lane = threadIdx.x & 63;
+    const int kl = lane % KL, slot = lane / KL;
     const int wv = (int)(threadIdx.x >> 6);
-    const int r0 = ((int)blockIdx.x * 4 + wv) * D;   // first weight row of the wave
+    const int r0 = (((int)blockIdx.x * 4 + wv) * S + slot) * D;   // first weight row of the slot
     const int Rr = (int)a.R;
     const uint32_t units_row = (uint32_t)(a.K / 32);
     const uint32_t row_bytes = (uint32_t)a.K * BITS / 8;
@@ -293,7 +298,7 @@ __global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs
     uint32_t gofs[UPL];
 #pragma unroll
     for (int j = 0; j < UPL; ++j)
-        gofs[j] = (uint32_t)((32 * (lane + 64 * j)) / a.gs) * SB;
+        gofs[j] = (uint32_t)((32 * (kl + KL * j)) / a.gs) * SB;
 
     const int ntiles = gemv_num_tiles(a);
     for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs
             for (int d = 0; d < D; ++d)
 #pragma unroll
                 for (int j = 0; j < UPL; ++j) {
-                    const int u = lane + 64 * j, r = r0 + d;
+                    const int u = kl + KL * j, r = r0 + d;
                     const bool live = u < (int)units_row && r < Rr;
                     buffer_words<BITS, BITS == 8 ? 0 : kStreamPolicy>(
                         rw, live ? (uint32_t)r * row_bytes + (uint32_t)u * (4 * BITS) : OOB,
@@ -371,7 +376,7 @@ __global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs
         float xs[UPL];
 #pragma unroll
         for (int j = 0; j < UPL; ++j) {
-            const int u = lane + 64 * j;
+            const int u = kl + KL * j;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const u32x4_t v = xl[q][u];
@@ -407,8 +412,8 @@ __global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs
                 }
                 acc[t * D + d] = total;
             }
-        reduce_slots<NMAT * D, 64>(acc);
-        if (lane == 63) {
+        reduce_slots<NMAT * D, KL>(acc);
+        if (kl == KL - 1) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 float v = acc[d];
