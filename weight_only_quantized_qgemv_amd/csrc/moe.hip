@@ -282,11 +282,12 @@ bool moe_rowstream_ok(const MoeArgs& a, int mt)
     // Measured on 128 experts, 4-bit ([768, 2048] gate / up, [2048, 768]
     // down), device time of graph-replayed calls: the fused form 6.4 against
     // 6.8 us at 8 pairs, 8.1 against 9.0 at 16, 13.1 against 16.1 at 32, 22.6
-    // against 23.0 at 64, slower from 128 pairs; the down projection (32-lane
-    // row slots for its 24 units) 4.1 against 5.7 us at 8 pairs, 5.8 against
-    // 7.5 at 16, 9.7 against 11.8 at 32, 16.5 against 20.8 at 64.
+    // against 23.0 at 64, level or slower from 128 pairs; the down projection
+    // (32-lane row slots for its 24 units) 4.1 against 5.7 us at 8 pairs, 5.8
+    // against 7.5 at 16, 9.7 against 11.8 at 32, 16.5 against 20.8 at 64 and
+    // 29.7 against 32.4 at 128.
     const int64_t P = a.n_tokens * a.top_k;
-    if (2 * P > a.E)
+    if (a.fused_silu ? 2 * P > a.E : P > a.E)
         return false;
     const int64_t es = 2;
     const bool vec = reinterpret_cast<uintptr_t>(a.a) % 16 == 0 && (a.a_outer * es) % 16 == 0 &&
