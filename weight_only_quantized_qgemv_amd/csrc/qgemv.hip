@@ -220,17 +220,31 @@ hipError_t run_rowstream(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
     k.units_row = (uint32_t)(a.K / 32);
     auto launch = [&](auto wpb) {
         constexpr int WPB = decltype(wpb)::value;
-        int64_t blocks = (a.N + WPB * D - 1) / (WPB * D);
-        blocks = blocks < kMaxBlocks ? blocks : kMaxBlocks;
-        // Scales and biases as whole dword-aligned rows when a row has an
-        // even number of groups.
-        if ((a.K / a.gs) % 2 == 0)
-            hipLaunchKernelGGL((qgemv_rowstream_kernel<BITS, DT, MT, UPL, WPB, true>),
-                               dim3((int)blocks), dim3(64 * WPB), 0, st, k);
-        else
-            hipLaunchKernelGGL((qgemv_rowstream_kernel<BITS, DT, MT, UPL, WPB, false>),
-                               dim3((int)blocks), dim3(64 * WPB), 0, st, k);
-        return hipGetLastError();
+        auto go = [&](auto kl) {
+            constexpr int KL = decltype(kl)::value;
+            constexpr int ROWS = WPB * (64 / KL) * D;   // weight rows of a block
+            int64_t blocks = (a.N + ROWS - 1) / ROWS;
+            blocks = blocks < kMaxBlocks ? blocks : kMaxBlocks;
+            // Scales and biases as whole dword-aligned rows when a row has an
+            // even number of groups.
+            if ((a.K / a.gs) % 2 == 0)
+                hipLaunchKernelGGL((qgemv_rowstream_kernel<BITS, DT, MT, UPL, WPB, true, KL>),
+                                   dim3((int)blocks), dim3(64 * WPB), 0, st, k);
+            else
+                hipLaunchKernelGGL((qgemv_rowstream_kernel<BITS, DT, MT, UPL, WPB, false, KL>),
+                                   dim3((int)blocks), dim3(64 * WPB), 0, st, k);
+            return hipGetLastError();
+        };
+        // Rows of at most 32 units: two rows side by side in a wave.
+        if constexpr (UPL == 1) {
+#ifdef QP_TUNING
+            if (a.K <= 32 * 32 && tuning_env("QP_RS_KL32", 1) != 0)
+#else
+            if (a.K <= 32 * 32)
+#endif
+                return go(std::integral_constant<int, 32>{});
+        }
+        return go(std::integral_constant<int, 64>{});
     };
 #ifdef QP_TUNING
     switch (tuning_env("QP_RS_WPB", 4)) {

@@ -64,7 +64,7 @@ template <int BITS, int UPL> constexpr int rowstream_depth()
     return 32 / (BITS * UPL) < 1 ? 1 : (32 / (BITS * UPL) > 4 ? 4 : 32 / (BITS * UPL));
 }
 
-template <int BITS, int DT, int MT, int UPL, int WPB, bool WIDE>
+template <int BITS, int DT, int MT, int UPL, int WPB, bool WIDE, int KL>
 __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs a)
 {
     using PX = RowStreamPair<DT>;
@@ -79,10 +79,15 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
     constexpr uint32_t M1 = (1u << BITS) - 1u;
     constexpr uint32_t MASK = M1 | (M1 << 16);
     const int lane = threadIdx.x & 63;
+    // A wave is S slots of KL lanes (KL = 32 for rows of at most 32 units, so
+    // that half the wave does not idle); slot s owns D rows.
+    static_assert(KL == 32 || KL == 64, "32 or 64 lanes per row");
+    constexpr int S = 64 / KL;
+    const int kl = lane % KL, slot = lane / KL;
     const int gw = (int)blockIdx.x * WPB + (int)(threadIdx.x >> 6);
     const int GW = (int)gridDim.x * WPB;
 
-    constexpr int UNITS = 64 * UPL;                  // unit slots of one activation row
+    constexpr int UNITS = KL * UPL;                  // unit slots of one activation row
     constexpr int ENTRIES = MT * UNITS;              // (row, unit) slices set up per block
     constexpr int EPT = (ENTRIES + 64 * WPB - 1) / (64 * WPB);   // slices per thread
     // Permuted pairs of slice (m, u) as four 4-word vectors xl[m][q][u], and
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
     uint32_t gofs[UPL];
 #pragma unroll
     for (int j = 0; j < UPL; ++j)
-        gofs[j] = (uint32_t)((32 * (lane + 64 * j)) / a.gs) * 2;
+        gofs[j] = (uint32_t)((32 * (kl + KL * j)) / a.gs) * 2;
 
     // Raw activation slices of this thread: raw[e][k / 2] holds x[k] (low)
     // and x[k + 1] (high) of the 32 activations of its slice (zeros past the
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
     constexpr int NV = (SBD + 63) / 64;
     __shared__ uint32_t sbl[WPB][2][WIDE ? SBD : 1];
     const int wv = (int)(threadIdx.x >> 6);
-    const uint32_t nd = (uint32_t)D * groups_row / 2;
+    const uint32_t nd = (uint32_t)(S * D) * groups_row / 2;   // the wave's S * D rows
     uint32_t sw[NV], bw[NV];
     uint32_t w[D][UPL][BITS];
     St sv[D][UPL], bv[D][UPL];
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
         for (int d = 0; d < D; ++d)
 #pragma unroll
             for (int j = 0; j < UPL; ++j) {
-                const int u = lane + 64 * j, r = r0 + d;
+                const int u = kl + KL * j, r = r0 + slot * D + d;
                 const bool live = u < (int)a.units_row && r < a.N;
                 buffer_words<BITS, BITS == 8 ? 0 : kStreamPolicy>(
                     rw, live ? (uint32_t)r * row_bytes + (uint32_t)u * (4 * BITS) : OOB, w[d][j]);
@@ -169,11 +174,11 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
             for (int d = 0; d < D; ++d)
 #pragma unroll
                 for (int j = 0; j < UPL; ++j) {
-                    const bool live = lane + 64 * j < (int)a.units_row;
+                    const bool live = kl + KL * j < (int)a.units_row;
                     // Element e = d * groups + g of the batch sits in half
                     // e % 2 of slot e / 2 (little-endian); e / 2 < SBD for
                     // every lane, live or not. Read as the slots' own type.
-                    const uint32_t e = (uint32_t)d * groups_row + gofs[j] / 2;
+                    const uint32_t e = (uint32_t)(slot * D + d) * groups_row + gofs[j] / 2;
                     const uint32_t ds = sbl[wv][0][e >> 1], db = sbl[wv][1][e >> 1];
                     const uint32_t sh = 16 * (e & 1);
                     sv[d][j] = live ? St(ds >> sh) : St(0);
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
                 }
         }
     };
-    int r0 = gw * D;
+    int r0 = gw * S * D;
     load(r0);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int j = 0; j < UPL; ++j) {
-            const int u = lane + 64 * j;
+            const int u = kl + KL * j;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const u32x4_t v = xl[m][q][u];
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
             xs[m][j] = sl[m][u];
         }
 
-    for (bool first = true; r0 < a.N; r0 += GW * D, first = false) {
+    for (bool first = true; r0 < a.N; r0 += GW * S * D, first = false) {
         if (!first)
             load(r0);
         exchange();
@@ -261,14 +266,14 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
                 }
                 acc[d * MT + m] = total;
             }
-        reduce_slots<D * MT, 64>(acc);
-        if (lane == 63) {
+        reduce_slots<D * MT, KL>(acc);
+        if (kl == KL - 1) {
 #pragma unroll
             for (int d = 0; d < D; ++d)
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-                    if (r0 + d < a.N && m < a.M)
-                        y[(int64_t)m * a.N + r0 + d] = E::from_f32(acc[d * MT + m]);
+                    if (r0 + slot * D + d < a.N && m < a.M)
+                        y[(int64_t)m * a.N + r0 + slot * D + d] = E::from_f32(acc[d * MT + m]);
         }
     }
 }
