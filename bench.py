@@ -44,7 +44,7 @@ CSRC = os.path.join(ROOT, "weight_only_quantized_qgemv_amd", "csrc")
 # (FETCH_SIZE, WRITE_SIZE) of `bench.py --steps 20 --warmup 2 --no-rows
 # --no-cpu-baseline`, each scaled by the same counter on a plain 1 GiB copy.
 # It holds only while the decode kernel's sources are the ones it was taken on.
-TRAFFIC = {"src_sha": "a3b0845355c74484", "fetch_bytes": 33207546, "write_bytes": 28672,
+TRAFFIC = {"src_sha": "c5b7afb7069cdae8", "fetch_bytes": 33207414, "write_bytes": 28672,
            "fetch_scale": 1.9999, "write_scale": 1.0}
 DECODE_SOURCES = ("rowstream.hpp", "gemv_core.hpp", "common.hpp", "qgemv.hip")
 

@@ -1,11 +1,13 @@
-// rowstream.hpp — the decode GEMV for 2-, 4- and 8-bit codes with one weight
-// row per wave (emily lib/emily/quantization.ex, `quantized_matmul/2`;
-// affine codes of `dequantize_defn/1`):
+// rowstream.hpp — the decode GEMV for 2-, 4- and 8-bit codes with a weight
+// row per wave (or per 32-lane half of one, for rows of at most 32 units),
+// and its three- and four-row form on the 4x4x4 matrix instruction (emily
+// lib/emily/quantization.ex, `quantized_matmul/2`; affine codes of
+// `dequantize_defn/1`):
 //   y[m, n] = sum_g s'[n,g] * sum_{k in g} x q + b'[n,g] * sum_{k in g} x.
 //
-// Lane l of a wave takes the 32-code units l, l + 64, ... of the row, so its
-// slice of the activation rows is fixed for the whole launch and sits in
-// registers. A unit is BITS code words; pair t of a word holds codes t and
+// Lane l of a row's KL lanes takes the 32-code units l, l + KL, ... of the
+// row, so its slice of the activation rows is fixed for the whole launch and
+// sits in registers. A unit is BITS code words; pair t of a word holds codes t and
 // t + 16 / BITS, cut out by one shift and mask-and-or: the code lands in the
 // mantissa of OFFSET (bf16 128, fp16 1024, both with a mantissa step of 1),
 // giving OFFSET + q exactly. (8-bit codes with bf16 activations exceed the
