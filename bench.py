@@ -367,7 +367,7 @@ def main():
                    "rotation_bytes": wb * copies},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "qgemv_rowstream_kernel<BITS=4, bf16, MT=1, UPL=2, WPB=4, WIDE=true>",
+                     "kernel": "qgemv_rowstream_kernel<BITS=4, bf16, MT=1, UPL=2, WPB=4, WIDE=true, KL=64>",
                      "us_per_launch": round(ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": wb},
     }
