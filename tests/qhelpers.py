@@ -5,8 +5,11 @@ bound every floating-point comparison uses.
 Bound (per output element): |y_gpu - y_ref| <= tau * S + half_ulp_out(y_ref),
 with S = sum_k |x| |w'| from the oracle, tau = 2e-3 for 16-bit activations and
 1e-5 for fp32, and half_ulp_out bounded by |y_ref| * 2^-(p+1) for the output
-format's p fraction bits (bf16: 7, fp16: 10, fp32: 23). The half-ulp term
-covers the final rounding of the fp32 accumulator to the output type.
+format's p fraction bits (bf16: 7, fp16: 10, fp32: 23), and by half the
+format's smallest subnormal (fp16: 2^-25, bf16: 2^-134, fp32: 2^-150) where
+y_ref lies in the subnormal range, whose spacing is that fixed quantum. The
+half-ulp term covers the final rounding of the fp32 accumulator to the
+output type.
 """
 from __future__ import annotations
 
@@ -19,6 +22,12 @@ F32, F16, BF16 = qref.F32, qref.F16, qref.BF16
 TORCH_DT = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
 TAU = {F32: 1e-5, F16: 2e-3, BF16: 2e-3}
 HALF_ULP = {F32: 2.0 ** -24, F16: 2.0 ** -11, BF16: 2.0 ** -8}
+HALF_SUBNORMAL = {F32: 2.0 ** -150, F16: 2.0 ** -25, BF16: 2.0 ** -134}
+
+
+def half_ulp_out(y_ref: np.ndarray, dt: int) -> np.ndarray:
+    """Half a unit in the last place of the output type at y_ref (an upper bound)."""
+    return np.maximum(np.abs(y_ref) * HALF_ULP[dt], HALF_SUBNORMAL[dt])
 
 
 def dev():
@@ -66,7 +75,7 @@ def assert_within(y_gpu: torch.Tensor, y_ref: np.ndarray, S: np.ndarray, dt: int
                   tau: float | None = None) -> None:
     tau = TAU[dt] if tau is None else tau
     y = values(y_gpu).reshape(y_ref.shape)
-    bound = tau * S + np.abs(y_ref) * HALF_ULP[dt]
+    bound = tau * S + half_ulp_out(y_ref, dt)
     err = np.abs(y - y_ref)
     bad = ~(err <= bound)
     if bad.any():

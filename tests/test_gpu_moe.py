@@ -16,7 +16,7 @@ import torch
 
 import weight_only_quantized_qgemv_amd as qp
 from oracle import qref
-from qhelpers import (BF16, F16, F32, HALF_ULP, TAU, TORCH_DT, activations, assert_within, dev,
+from qhelpers import (BF16, F16, F32, TAU, half_ulp_out, TORCH_DT, activations, assert_within, dev,
                       log, to_device, to_numpy, values)
 from weight_only_quantized_qgemv_amd import synth
 
@@ -34,7 +34,7 @@ def stack(E, R, C, bits, gs, dt, seed):
 def fused_bound(ref, dt):
     sig = 1.0 / (1.0 + np.exp(-ref["g"]))
     return (TAU[dt] * (1.1 * np.abs(ref["u"]) * ref["Sg"] + np.abs(ref["g"] * sig) * ref["Su"])
-            + np.abs(ref["silu_out"]) * HALF_ULP[dt])
+            + half_ulp_out(ref["silu_out"], dt))
 
 
 def check_fused(out, ref, dt, what, rows=None):

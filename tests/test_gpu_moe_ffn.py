@@ -18,7 +18,7 @@ import torch
 
 import weight_only_quantized_qgemv_amd as qp
 from oracle import qref
-from qhelpers import BF16, F16, F32, HALF_ULP, TAU, TORCH_DT, activations, dev, log, to_device, values
+from qhelpers import BF16, F16, F32, TAU, half_ulp_out, TORCH_DT, activations, dev, log, to_device, values
 from weight_only_quantized_qgemv_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -74,7 +74,7 @@ def reference_and_bound(c, ids=None, rw=None, tokens=None):
     o_vals = values_of(o, dt)
     b_o = TAU[dt] * s_o + s_bh + np.abs(o_vals) * ulp
     b_out = (np.abs(rw.astype(np.float64)).reshape(T, top_k, 1) * b_o.reshape(T, top_k, D)).sum(1)
-    b_out += np.abs(out) * HALF_ULP[dt] + 1e-30
+    b_out += half_ulp_out(out, dt)
     return out, b_out
 
 

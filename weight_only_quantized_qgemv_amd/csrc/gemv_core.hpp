@@ -18,160 +18,39 @@
 //  - weight words come in as 128/64/32-bit non-temporal loads; the next row's
 //    words are requested before the current row is computed and reduced;
 //  - the affine map is folded out of the inner loop:
-//      sum_k x w' = sum_units s' * (sum q x) + b' * (sum x),
-//    with each unit's sum x computed once in the prologue;
-//  - 16-bit activations: codes are OR-ed into the mantissa of 128.0 (bf16) or
-//    1024.0 (fp16), two per register, and fed to v_dot2 with pre-scaled
-//    activation pairs (unpack_plan.hpp); fp32 activations and 8-bit codes with
-//    bf16 use per-code conversion and fp32 FMA;
+//      sum_k x w' = sum_groups s' * (sum q x) + b' * (sum x),
+//    with each unit's sum x computed once in the prologue and the group's
+//    bias taken at the end of the grid nearer zero (codepair.hpp, `orient`);
+//  - activations are held as fp32 and every code is converted exactly and
+//    accumulated with an fp32 FMA (this kernel serves fp32 activations, 3- and
+//    6-bit codes and MoE tiles of a few pairs; the 2-, 4- and 8-bit decode
+//    with 16-bit activations runs on the row kernels);
 //  - partial sums are reduced across a row's lanes with cross-lane shuffles,
 //    through LDS when a row spans more than one wave;
 //  - NMAT = 2 streams a gate and an up matrix together and writes
 //    SiLU(gate) * up (ferrum-kernels `gemv_moe_id_gate_up_silu` docs).
 #pragma once
 
+#include "codepair.hpp"
 #include "common.hpp"
-#include "unpack_plan.hpp"
 
 namespace qp {
 
-// (a & mask) | magic as one v_and_or_b32. Written out because a VOP3
-// instruction on gfx9 cannot take a literal and reads at most one SGPR, so the
-// compiler would otherwise split it into a v_and and a v_or with literals; the
-// mask is kept in a VGPR (materialised once, outside the loops) and the magic
-// constant comes from an SGPR.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic)
-{
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask), "s"(magic));
-    return r;
-}
-
-template <int DT> struct Dot2Traits;
-template <> struct Dot2Traits<DT_BF16> {
-    static constexpr int MANT = 7;
-    static constexpr uint32_t MAGIC2 = 0x43004300u; // 128.0 in both bf16 halves
-    static constexpr float MAGIC = 128.0f;
-    using pair_t = bf16x2_t;
-    static __device__ __forceinline__ float dot(uint32_t v, pair_t x, float acc)
-    {
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v), x, acc, false);
-    }
-    static __device__ __forceinline__ pair_t make(float lo, float hi)
-    {
-        return pair_t{(__bf16)lo, (__bf16)hi};
-    }
-    static __device__ __forceinline__ float lo_f(pair_t p) { return (float)p.x; }
-    static __device__ __forceinline__ float hi_f(pair_t p) { return (float)p.y; }
-};
-template <> struct Dot2Traits<DT_F16> {
-    static constexpr int MANT = 10;
-    static constexpr uint32_t MAGIC2 = 0x64006400u; // 1024.0 in both fp16 halves
-    static constexpr float MAGIC = 1024.0f;
-    using pair_t = f16x2_t;
-    static __device__ __forceinline__ float dot(uint32_t v, pair_t x, float acc)
-    {
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, v), x, acc, false);
-    }
-    static __device__ __forceinline__ pair_t make(float lo, float hi)
-    {
-        return pair_t{(_Float16)lo, (_Float16)hi};
-    }
-    static __device__ __forceinline__ float lo_f(pair_t p) { return (float)p.x; }
-    static __device__ __forceinline__ float hi_f(pair_t p) { return (float)p.y; }
-};
-
-// Whether (BITS, DT) takes the dot2 path.
-template <int BITS, int DT>
-constexpr bool use_dot2()
-{
-    if constexpr (DT == DT_F32)
-        return false;
-    else
-        return make_unpack_plan(BITS, Dot2Traits<DT>::MANT).feasible;
-}
-
 // Largest tile height (activation rows per launch) the register budget allows:
-// activations take MT * 32 * U / 2 VGPRs on the dot2 path (bf16/fp16 pairs),
-// MT * 32 * U on the fp32 path, for U <= 2 units of 32 codes per lane.
+// activations take MT * 32 * U VGPRs (fp32) for U <= 2 units of 32 codes per
+// lane.
 template <int BITS, int DT>
 constexpr int gemv_max_mt()
 {
-    return use_dot2<BITS, DT>() ? 4 : 2;
+    return 2;
 }
 
 constexpr int GEMV_THREADS = 256;
 
-template <int BITS, int DT, bool DOT2> struct UnitX;
-
-// Activations of one 32-code unit for the dot2 path: pre-scaled pairs, the
-// negated magic-offset sum and the plain sum.
-template <int BITS, int DT> struct UnitX<BITS, DT, true> {
-    using T = Dot2Traits<DT>;
-    static constexpr UnpackPlan P = make_unpack_plan(BITS, T::MANT);
-    typename T::pair_t xp[P.n_pair];
-    float xoff, xsum;
-
-    __device__ __forceinline__ void load(const float (&xv)[32])
-    {
-        float s = 0.f;
-#pragma unroll
-        for (int c = 0; c < 32; ++c)
-            s += xv[c];
-        xsum = s;
-        float off = 0.f;
-        static_for<P.n_pair>([&](auto J) {
-            constexpr PlanPair pp = P.pair[J];
-            constexpr float lo_scale = 1.0f / float(1 << pp.lo_off);
-            constexpr float hi_scale = 1.0f / float(1 << pp.hi_off);
-            const float lo = pp.lo >= 0 ? xv[pp.lo >= 0 ? pp.lo : 0] * lo_scale : 0.f;
-            const float hi = pp.hi >= 0 ? xv[pp.hi >= 0 ? pp.hi : 0] * hi_scale : 0.f;
-            xp[J] = T::make(lo, hi);
-            off += T::lo_f(xp[J]) + T::hi_f(xp[J]);
-        });
-        xoff = -(off * T::MAGIC);
-    }
-
-    // acc + (sum over the unit's 32 codes of (magic + q * 2^o) * x * 2^-o); the
-    // caller starts the chain at -(magic offset sums) of the units it covers.
-    __device__ __forceinline__ float qdot(const uint32_t* w, float acc) const
-    {
-        uint32_t win[P.n_win];
-        static_for<P.n_win>([&](auto I) {
-            constexpr int wb = P.win_bit[I], wi = wb / 32, sh = wb % 32;
-            if constexpr (sh == 0)
-                win[I] = w[wi];
-            else if constexpr (wi + 1 < BITS)
-                win[I] = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh);
-            else
-                win[I] = w[wi] >> sh;
-        });
-        // Each pair is formed one step before its dot product, so no pair is
-        // consumed by the instruction right after the one that wrote it (that
-        // adjacency costs a hazard wait state).
-        auto make = [&](auto J) {
-            constexpr PlanPair pp = P.pair[decltype(J)::value];
-            constexpr uint32_t cm = (1u << BITS) - 1u;
-            constexpr uint32_t mask = (pp.lo >= 0 ? cm << pp.lo_off : 0u) |
-                                      (pp.hi >= 0 ? cm << (16 + pp.hi_off) : 0u);
-            return and_or(win[pp.win], mask, T::MAGIC2);
-        };
-        uint32_t v = make(std::integral_constant<int, 0>{});
-        static_for<P.n_pair>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            const uint32_t cur = v;
-            if constexpr (j + 1 < P.n_pair)
-                v = make(std::integral_constant<int, j + 1>{});
-            acc = T::dot(cur, xp[J], acc);
-        });
-        return acc;
-    }
-};
-
-// fp32 path: activations as fp32, one conversion and one FMA per code.
-template <int BITS, int DT> struct UnitX<BITS, DT, false> {
+// Activations of one 32-code unit as fp32, and their sum: one exact code
+// conversion and one FMA per code.
+template <int BITS, int DT> struct UnitX {
     float xf[32];
-    float xoff = 0.f; // no magic offset on this path
     float xsum;
 
     __device__ __forceinline__ void load(const float (&xv)[32])
@@ -185,11 +64,16 @@ template <int BITS, int DT> struct UnitX<BITS, DT, false> {
         xsum = s;
     }
 
-    // acc + sum over the unit's 32 codes of q * x.
-    __device__ __forceinline__ float qdot(const uint32_t* w, float acc) const
+    // acc + sum over the unit's 32 codes of q * x, each code complemented
+    // (q -> 2^BITS - 1 - q) when flip is ~0.
+    __device__ __forceinline__ float qdot(const uint32_t* w, uint32_t flip, float acc) const
     {
+        uint32_t wf[BITS];
+#pragma unroll
+        for (int i = 0; i < BITS; ++i)
+            wf[i] = w[i] ^ flip;
         static_for<32>([&](auto C) {
-            acc = __builtin_fmaf((float)unit_code<BITS, C>(w), xf[C], acc);
+            acc = __builtin_fmaf((float)unit_code<BITS, C>(wf), xf[C], acc);
         });
         return acc;
     }
@@ -313,14 +197,11 @@ __device__ __forceinline__ void buffer_store_elem(typename Elem<DT>::storage v,
         __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }
 
-// Activation words per unit in the block's table: dot2 pairs, or fp32 values.
+// Activation words per unit in the block's table: fp32 values.
 template <int BITS, int DT>
 constexpr int unit_table_words()
 {
-    if constexpr (use_dot2<BITS, DT>())
-        return make_unpack_plan(BITS, Dot2Traits<DT>::MANT).n_pair;
-    else
-        return 32;
+    return 32;
 }
 
 // Ring depth that fits the register budget of a kernel instance: activation
@@ -330,10 +211,7 @@ constexpr int unit_table_words()
 template <int BITS, int DT, int MT, int U, int G, int NMAT, int BUDGET>
 constexpr int ring_depth()
 {
-    constexpr bool dot2 = use_dot2<BITS, DT>();
-    int per_unit = 40; // 32 fp32 values and conversion temporaries
-    if constexpr (dot2)
-        per_unit = make_unpack_plan(BITS, Dot2Traits<DT>::MANT).n_pair;
+    const int per_unit = 40; // 32 fp32 values and conversion temporaries
     const int xr = MT * U * per_unit + MT * G * 2;
     const int slot = NMAT * (U * BITS + 2 * G);
     for (int d = 4; d > 1; --d)
@@ -348,8 +226,8 @@ constexpr int ring_depth()
 // Each lane owns U units of 32 codes; they fall into G groups (G = 1 when the
 // whole slice lies in one quantization group, else G = U).
 //
-//  1. The block prepares the tile's activation table (dot2 pairs, magic-offset
-//     and plain sums for every lane slot and activation row) in LDS, each
+//  1. The block prepares the tile's activation table (fp32 activations and
+//     their sums for every lane slot and activation row) in LDS, each
 //     thread one (row, unit, lane slot) item, so the conversion work is done
 //     once per block rather than once per wave.
 //  2. Every wave keeps D passes of weight words in flight (a ring refilled as
@@ -365,15 +243,14 @@ __global__ __launch_bounds__(MAXT) void qgemv_stream_kernel(GemvKernelArgs a)
 {
     using E = Elem<DT>;
     using St = typename E::storage;
-    constexpr bool DOT2 = use_dot2<BITS, DT>();
-    using UX = UnitX<BITS, DT, DOT2>;
+    using UX = UnitX<BITS, DT>;
     static_assert(G == 1 || G == U, "a lane slice is one group or one group per unit");
     constexpr int UPG = U / G;                              // units per group
     constexpr int D = ring_depth<BITS, DT, MT, U, G, NMAT, (131072 / MAXT < 512 ? 131072 / MAXT : 512)>();
     constexpr int NW = U * BITS;
     constexpr int RPW = 64 / KL;
     constexpr int NP = unit_table_words<BITS, DT>();        // table words per unit
-    constexpr int UWORDS = NP + 2;                          // + offset sum, plain sum
+    constexpr int UWORDS = NP + 1;                          // + the unit's sum
     constexpr int ITEMS = MT * U * KL;                      // table items per tile
     constexpr int XV = 32 * (int)sizeof(St) / 16;           // 16-byte vectors per unit
     constexpr int SB = (int)sizeof(St);
@@ -488,42 +365,27 @@ __global__ __launch_bounds__(MAXT) void qgemv_stream_kernel(GemvKernelArgs a)
             ux.load(xv);
             if (item < ITEMS) {
                 uint32_t* dst = table + ((it_m * U + it_u) * UWORDS) * KL + it_kl;
-                if constexpr (DOT2) {
-                    static_for<NP>([&](auto J) {
-                        dst[J * KL] = __builtin_bit_cast(uint32_t, ux.xp[J]);
-                    });
-                } else {
-                    static_for<32>([&](auto C) {
-                        dst[C * KL] = __builtin_bit_cast(uint32_t, ux.xf[C]);
-                    });
-                }
-                dst[NP * KL] = __builtin_bit_cast(uint32_t, ux.xoff);
-                dst[(NP + 1) * KL] = __builtin_bit_cast(uint32_t, ux.xsum);
+                static_for<32>([&](auto C) {
+                    dst[C * KL] = __builtin_bit_cast(uint32_t, ux.xf[C]);
+                });
+                dst[NP * KL] = __builtin_bit_cast(uint32_t, ux.xsum);
             }
         }
         __syncthreads();
         UX ux[MT][U];
-        float goff[MT][G], gsum[MT][G];
+        float gsum[MT][G];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
 #pragma unroll
             for (int g = 0; g < G; ++g)
-                goff[m][g] = gsum[m][g] = 0.f;
+                gsum[m][g] = 0.f;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t* src = table + ((m * U + u) * UWORDS) * KL + kl;
-                if constexpr (DOT2) {
-                    static_for<NP>([&](auto J) {
-                        ux[m][u].xp[J] =
-                            __builtin_bit_cast(typename UX::T::pair_t, src[J * KL]);
-                    });
-                } else {
-                    static_for<32>([&](auto C) {
-                        ux[m][u].xf[C] = __builtin_bit_cast(float, src[C * KL]);
-                    });
-                }
-                goff[m][u / UPG] += __builtin_bit_cast(float, src[NP * KL]);
-                gsum[m][u / UPG] += __builtin_bit_cast(float, src[(NP + 1) * KL]);
+                static_for<32>([&](auto C) {
+                    ux[m][u].xf[C] = __builtin_bit_cast(float, src[C * KL]);
+                });
+                gsum[m][u / UPG] += __builtin_bit_cast(float, src[NP * KL]);
             }
         }
 
@@ -537,22 +399,25 @@ __global__ __launch_bounds__(MAXT) void qgemv_stream_kernel(GemvKernelArgs a)
             static_for<D>([&](auto J) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int t = 0; t < NMAT; ++t)
+                for (int t = 0; t < NMAT; ++t) {
+                    Orient o[G];
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        o[g] = orient<BITS>(E::to_f32(sv[J][t][g]), E::to_f32(bv[J][t][g]));
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
                         float r = 0.f;
 #pragma unroll
                         for (int g = 0; g < G; ++g) {
-                            float c = goff[m][g];
+                            float c = 0.f;
 #pragma unroll
                             for (int u = g * UPG; u < (g + 1) * UPG; ++u)
-                                c = ux[m][u].qdot(w[J][t] + u * BITS, c);
-                            r = __builtin_fmaf(E::to_f32(sv[J][t][g]), c,
-                                               __builtin_fmaf(E::to_f32(bv[J][t][g]),
-                                                              gsum[m][g], r));
+                                c = ux[m][u].qdot(w[J][t] + u * BITS, o[g].flip, c);
+                            r = __builtin_fmaf(o[g].s, c, __builtin_fmaf(o[g].b, gsum[m][g], r));
                         }
                         acc[J][t][m] = r;
                     }
+                }
                 fetch(p0 + (J + D) * GW, w[J], sv[J], bv[J]);
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -641,7 +506,7 @@ __global__ __launch_bounds__(256) void qgemv_generic_kernel(GemvKernelArgs a)
                 const float s = E::to_f32(srow[g]);
                 const float b = E::to_f32(brow[g]);
                 static_for<32>([&](auto C) {
-                    const float wv = (float)unit_code<BITS, C>(w) * s + b;
+                    const float wv = affine_weight((float)unit_code<BITS, C>(w), s, b);
 #pragma unroll
                     for (int m = 0; m < 16; ++m)
                         if (m < count)

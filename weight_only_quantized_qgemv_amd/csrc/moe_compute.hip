@@ -59,11 +59,15 @@ hipError_t run_generic(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 template <int BITS, int DT, int MT, int NMAT>
 hipError_t run_mt(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 {
-    // One wave per row at K = 2048, eight rows per wave at K = 768.
+    // One wave per row at K = 2048.
     if (k.K == 32 * 64)
         return run_tiles<BITS, DT, MT, 1, 64, NMAT>(k, max_tiles, st);
-    if (k.K == 3 * 32 * 8)
-        return run_tiles<BITS, DT, MT, 3, 8, NMAT>(k, max_tiles, st);
+    // Eight rows per wave at K = 768, one pair per tile (two pairs' fp32
+    // slices of three units would not fit the registers).
+    if constexpr (MT == 1) {
+        if (k.K == 3 * 32 * 8)
+            return run_tiles<BITS, DT, MT, 3, 8, NMAT>(k, max_tiles, st);
+    }
     return run_generic<BITS, DT, NMAT>(k, max_tiles, st);
 }
 

@@ -9,7 +9,7 @@
 // same permuted activation slices, and each wave owns four rows of the
 // expert's matrix (or of both matrices of the fused form). Block b of a wave
 // is unit 16 rho + b at round rho; lane 4 b + c holds activation row c of each
-// 4-row chunk (A) and weight row r0 + c (B, OFFSET + q pairs). Per unit the
+// 4-row chunk (A) and weight row r0 + c (B, exact code pairs). Per unit the
 // group's scale and bias are applied per lane; the sixteen blocks are summed at
 // the end, and lanes 0..3 store their row for every pair of the tile, through
 // SiLU(gate) * up in the fused form.
@@ -37,16 +37,10 @@ constexpr int kMoeRowQuads = QP_MOE_ROW_QUADS;       // row quads per wave and t
 template <int BITS, int DT, int R, int NMAT, int MC>
 __global__ __launch_bounds__(64 * kMoeRowWaves) void qgemv_moe_rowmfma_kernel(GemvKernelArgs a)
 {
-    using PX = RowStreamPair<DT>;
     using E = Elem<DT>;
     using St = typename E::storage;
     static_assert(BITS == 2 || BITS == 4 || BITS == 8, "codes in whole 16-bit halves");
-    constexpr int CPW = 32 / BITS;
-    constexpr int HALF = CPW / 2;
-    constexpr bool CONVERT = BITS == 8 && DT == DT_BF16;
-    constexpr float OFFSET = CONVERT ? 0.0f : PX::OFFSET;
-    constexpr uint32_t M1 = (1u << BITS) - 1u;
-    constexpr uint32_t MASK = M1 | (M1 << 16);
+    using CO = CodeOrder<BITS>;
     constexpr int MT = 4 * MC;                       // pairs per tile at most
     constexpr int UNITS = 16 * R;                    // unit slots of a row
     constexpr int ENTRIES = MT * UNITS;              // (pair, unit) slices
@@ -128,22 +122,20 @@ __global__ __launch_bounds__(64 * kMoeRowWaves) void qgemv_moe_rowmfma_kernel(Ge
         load(quad_row(0));
         __builtin_amdgcn_sched_barrier(0);
 
-        // Permuted slices and their sums into LDS (pair HALF i + t of a slice
-        // holds x[CPW i + t] and x[CPW i + t + HALF]).
+        // Permuted slices and their sums into LDS (pair q of a slice holds the
+        // activations of codes lo_code(q) and hi_code(q) of the unit).
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const int idx = (int)threadIdx.x + THREADS * e, m = idx / UNITS, u = idx % UNITS;
             if (idx < ENTRIES) {
                 uint32_t p[16];
 #pragma unroll
-                for (int i = 0; i < BITS; ++i)
-#pragma unroll
-                    for (int t = 0; t < HALF; ++t) {
-                        const int k0 = CPW * i + t, k1 = k0 + HALF;
-                        const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
-                        const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
-                        p[HALF * i + t] = lo | (hi << 16);
-                    }
+                for (int q = 0; q < 16; ++q) {
+                    const int k0 = CO::lo_code(q), k1 = CO::hi_code(q);
+                    const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
+                    const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
+                    p[q] = lo | (hi << 16);
+                }
                 float sum = 0.0f;
 #pragma unroll
                 for (int k = 0; k < 32; ++k)
@@ -162,14 +154,6 @@ __global__ __launch_bounds__(64 * kMoeRowWaves) void qgemv_moe_rowmfma_kernel(Ge
                 break;
             if (j > 0)
                 load(r0);
-            auto code_pair = [&](int t, int rho, int p) -> uint32_t {
-                const uint32_t codes = (w[t][rho][p / HALF] >> (BITS * (p % HALF))) & MASK;
-                if constexpr (CONVERT)
-                    return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)(float)(codes & 0xFFu),
-                                                                 (__bf16)(float)(codes >> 16)});
-                else
-                    return codes | PX::MAGIC;
-            };
             f32x4_t acc[NMAT][MC];
 #pragma unroll
             for (int t = 0; t < NMAT; ++t)
@@ -180,11 +164,17 @@ __global__ __launch_bounds__(64 * kMoeRowWaves) void qgemv_moe_rowmfma_kernel(Ge
             for (int rho = 0; rho < R; ++rho) {
                 const int u = 16 * rho + blk;
                 f32x4_t c[NMAT][MC];
+                Orient o[NMAT];
+                uint32_t cp[NMAT][16];
 #pragma unroll
-                for (int t = 0; t < NMAT; ++t)
+                for (int t = 0; t < NMAT; ++t) {
 #pragma unroll
                     for (int ch = 0; ch < MC; ++ch)
                         c[t][ch] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    o[t] = orient<BITS>(E::to_f32(sv[t][rho]), E::to_f32(bv[t][rho]));
+                    code_pairs<BITS, DT>(w[t][rho], o[t].flip, cp[t]);
+                }
+                auto code_pair = [&](int t, int, int p) -> uint32_t { return cp[t][p]; };
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     u32x4_t xv[MC];
@@ -204,14 +194,13 @@ __global__ __launch_bounds__(64 * kMoeRowWaves) void qgemv_moe_rowmfma_kernel(Ge
                 }
 #pragma unroll
                 for (int t = 0; t < NMAT; ++t) {
-                    const float s = E::to_f32(sv[t][rho]), b = E::to_f32(bv[t][rho]);
 #pragma unroll
                     for (int ch = 0; ch < MC; ++ch)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float xs = sl[u][4 * ch + i];
-                            acc[t][ch][i] = __builtin_fmaf(s, c[t][ch][i] - OFFSET * xs,
-                                                           __builtin_fmaf(b, xs, acc[t][ch][i]));
+                            acc[t][ch][i] = __builtin_fmaf(o[t].s, c[t][ch][i],
+                                                           __builtin_fmaf(o[t].b, xs, acc[t][ch][i]));
                         }
                 }
                 // One round's activation vectors live at a time.
@@ -271,12 +260,7 @@ __global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs
     using St = typename E::storage;
     static_assert(BITS == 2 || BITS == 4 || BITS == 8, "codes in whole 16-bit halves");
     constexpr int D = rowstream_depth<BITS, UPL * NMAT>();
-    constexpr int CPW = 32 / BITS;
-    constexpr int HALF = CPW / 2;
-    constexpr bool CONVERT = BITS == 8 && DT == DT_BF16;
-    constexpr float OFFSET = CONVERT ? 0.0f : PX::OFFSET;
-    constexpr uint32_t M1 = (1u << BITS) - 1u;
-    constexpr uint32_t MASK = M1 | (M1 << 16);
+    using CO = CodeOrder<BITS>;
     static_assert(KL == 32 || KL == 64, "32 or 64 lanes per row");
     constexpr int S = 64 / KL;                       // row slots per wave
     constexpr int UNITS = KL * UPL;                  // unit slots of the pair's row
@@ -353,14 +337,12 @@ __global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs
             if (u < UNITS) {
                 uint32_t q4[16];
 #pragma unroll
-                for (int i = 0; i < BITS; ++i)
-#pragma unroll
-                    for (int t = 0; t < HALF; ++t) {
-                        const int k0 = CPW * i + t, k1 = k0 + HALF;
-                        const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
-                        const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
-                        q4[HALF * i + t] = lo | (hi << 16);
-                    }
+                for (int q = 0; q < 16; ++q) {
+                    const int k0 = CO::lo_code(q), k1 = CO::hi_code(q);
+                    const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
+                    const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
+                    q4[q] = lo | (hi << 16);
+                }
                 float sum = 0.0f;
 #pragma unroll
                 for (int k = 0; k < 32; ++k)
@@ -394,21 +376,14 @@ __global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs
                 float total = 0.0f;
 #pragma unroll
                 for (int j = 0; j < UPL; ++j) {
+                    const Orient o = orient<BITS>(E::to_f32(sv[t][d][j]), E::to_f32(bv[t][d][j]));
+                    uint32_t cp[16];
+                    code_pairs<BITS, DT>(w[t][d][j], o.flip, cp);
                     float part = 0.0f;
 #pragma unroll
-                    for (int pp = 0; pp < 16; ++pp) {
-                        const uint32_t codes = (w[t][d][j][pp / HALF] >> (BITS * (pp % HALF))) & MASK;
-                        uint32_t pair;
-                        if constexpr (CONVERT)
-                            pair = __builtin_bit_cast(uint32_t,
-                                                      bf16x2_t{(__bf16)(float)(codes & 0xFFu),
-                                                               (__bf16)(float)(codes >> 16)});
-                        else
-                            pair = codes | PX::MAGIC;
-                        part = PX::dot(pair, xr[j][pp], part);
-                    }
-                    const float s = E::to_f32(sv[t][d][j]), b = E::to_f32(bv[t][d][j]);
-                    total = __builtin_fmaf(s, part - OFFSET * xs[j], __builtin_fmaf(b, xs[j], total));
+                    for (int pp = 0; pp < 16; ++pp)
+                        part = PX::dot(cp[pp], xr[j][pp], part);
+                    total = __builtin_fmaf(o.s, part, __builtin_fmaf(o.b, xs[j], total));
                 }
                 acc[t * D + d] = total;
             }

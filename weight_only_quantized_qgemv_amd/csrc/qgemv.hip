@@ -70,10 +70,9 @@ constexpr int kCUs = 256;
 template <int BITS, int DT, int MT, int U, int G, int KL>
 hipError_t run_fast(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
 {
-    // 1024-thread blocks (128 VGPRs per lane) for the lean dot2 kernel at one
-    // activation row; 512 threads (256 VGPRs) for the heavier variants.
-    constexpr int MAXT = (MT == 1 && use_dot2<BITS, DT>() && U != 3) ? 1024
-                         : (U == 3 || MT == 4) ? 256 : 512;
+    // 512-thread blocks (256 VGPRs per lane): the fp32 activation slices take
+    // 32 VGPRs per unit and activation row.
+    constexpr int MAXT = (U == 3 || MT == 4) ? 256 : 512;
     // Waves per block: 10 measured best for the 14336 x 4096 decode shape.
     constexpr int WMAX = MAXT / 64 < 10 ? MAXT / 64 : 10;
     constexpr int D = ring_depth<BITS, DT, MT, U, G, 1, (131072 / MAXT < 512 ? 131072 / MAXT : 512)>();
@@ -117,12 +116,16 @@ hipError_t run_chunk(const GemvArgs& a, int64_t m0, int mc, hipStream_t st, bool
     const int64_t K = a.K;
     if (K == 2 * 32 * 64) return run_slice<BITS, DT, MT, 2, 64>(a, m0, mc, st);
     if (K == 1 * 32 * 64) return run_slice<BITS, DT, MT, 1, 64>(a, m0, mc, st);
-    if (K == 3 * 32 * 8) return run_fast<BITS, DT, MT, 3, 3, 8>(a, m0, mc, st);
+    if (K == 3 * 32 * 8) {
+        // One activation row per pass: two rows' fp32 slices of three units
+        // would not fit the registers.
+        for (int i = 0; i < mc; ++i)
+            if (hipError_t e = run_fast<BITS, DT, 1, 3, 3, 8>(a, m0 + i, 1, st); e != hipSuccess)
+                return e;
+        return hipSuccess;
+    }
     if constexpr (MT <= 2) {
         if (K == 32 * 32) return run_slice<BITS, DT, MT, 1, 32>(a, m0, mc, st);
-    }
-    if constexpr (MT == 1 && DT != DT_F32) {
-        if (K == 4 * 32 * 64) return run_slice<BITS, DT, MT, 4, 64>(a, m0, mc, st);
     }
     *done = false;
     return hipSuccess;

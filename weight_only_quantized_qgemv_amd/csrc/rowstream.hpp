@@ -7,15 +7,12 @@
 //
 // Lane l of a row's KL lanes takes the 32-code units l, l + KL, ... of the
 // row, so its slice of the activation rows is fixed for the whole launch and
-// sits in registers. A unit is BITS code words; pair t of a word holds codes t and
-// t + 16 / BITS, cut out by one shift and mask-and-or: the code lands in the
-// mantissa of OFFSET (bf16 128, fp16 1024, both with a mantissa step of 1),
-// giving OFFSET + q exactly. (8-bit codes with bf16 activations exceed the
-// bf16 mantissa, so those bytes are converted instead, with no offset.) The
-// activation pairs are stored permuted to match. v_dot2 forms
-// sum x (OFFSET + q) per unit, the unit's activation sum removes the offset,
-// and the group's scale and bias are applied once per unit. D rows are
-// loaded before any is reduced.
+// sits in registers. A unit is BITS code words; its 32 codes become 16 exact
+// 16-bit pairs (codepair.hpp: FP8 / FP4 conversion of split code bytes, or
+// bytes through fp32 at 8 bits), and the activation pairs are stored in the
+// same order. v_dot2 forms sum x q per unit, and the group's scale and bias,
+// oriented so that the folded bias does not cancel against the codes, are
+// applied once per unit. D rows are loaded before any is reduced.
 //
 // Every wave of a block needs the same activation slices, so the block
 // prepares them once: its threads load the raw activation units, permute
@@ -26,6 +23,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "codepair.hpp"
 #include "gemv_core.hpp"
 
 namespace qp {
@@ -42,8 +40,6 @@ struct RowStreamArgs {
 
 template <int DT> struct RowStreamPair;
 template <> struct RowStreamPair<DT_BF16> {
-    static constexpr uint32_t MAGIC = 0x43004300u;   // bf16 pair (128, 128)
-    static constexpr float OFFSET = 128.0f;
     static __device__ __forceinline__ float dot(uint32_t a, uint32_t x, float acc)
     {
         return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -51,8 +47,6 @@ template <> struct RowStreamPair<DT_BF16> {
     }
 };
 template <> struct RowStreamPair<DT_F16> {
-    static constexpr uint32_t MAGIC = 0x64006400u;   // fp16 pair (1024, 1024)
-    static constexpr float OFFSET = 1024.0f;
     static __device__ __forceinline__ float dot(uint32_t a, uint32_t x, float acc)
     {
         return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, x),
@@ -74,12 +68,7 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
     using St = typename E::storage;
     static_assert(BITS == 2 || BITS == 4 || BITS == 8, "codes in whole 16-bit halves");
     constexpr int D = rowstream_depth<BITS, UPL>();
-    constexpr int CPW = 32 / BITS;                   // codes per word
-    constexpr int HALF = CPW / 2;                    // pairs per word
-    constexpr bool CONVERT = BITS == 8 && DT == DT_BF16;
-    constexpr float OFFSET = CONVERT ? 0.0f : PX::OFFSET;
-    constexpr uint32_t M1 = (1u << BITS) - 1u;
-    constexpr uint32_t MASK = M1 | (M1 << 16);
+    using CO = CodeOrder<BITS>;
     const int lane = threadIdx.x & 63;
     // A wave is S slots of KL lanes (KL = 32 for rows of at most 32 units, so
     // that half the wave does not idle); slot s owns D rows.
@@ -192,22 +181,20 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
     load(r0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // Pair HALF i + t of a slice holds x[CPW i + t] (low) and
-    // x[CPW i + t + HALF] (high).
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const int idx = (int)threadIdx.x + 64 * WPB * e, m = idx / UNITS, u = idx % UNITS;
         if (idx < ENTRIES) {
+            // Pair q holds the activations of codes lo_code(q) (low half) and
+            // hi_code(q) (high half) of the unit.
             uint32_t p[16];
 #pragma unroll
-            for (int i = 0; i < BITS; ++i)
-#pragma unroll
-                for (int t = 0; t < HALF; ++t) {
-                    const int k0 = CPW * i + t, k1 = k0 + HALF;
-                    const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
-                    const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
-                    p[HALF * i + t] = lo | (hi << 16);
-                }
+            for (int q = 0; q < 16; ++q) {
+                const int k0 = CO::lo_code(q), k1 = CO::hi_code(q);
+                const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
+                const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
+                p[q] = lo | (hi << 16);
+            }
             float sum = 0.0f;
 #pragma unroll
             for (int k = 0; k < 32; ++k)
@@ -241,33 +228,30 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
             load(r0);
         exchange();
         float acc[D * MT];
-        // Code pair p = HALF i + t of a unit: codes t and t + HALF of word i,
-        // as a 16-bit pair (OFFSET + q, or q converted).
-        auto code_pair = [&](int d, int j, int p) -> uint32_t {
-            const uint32_t codes = (w[d][j][p / HALF] >> (BITS * (p % HALF))) & MASK;
-            if constexpr (CONVERT)
-                return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)(float)(codes & 0xFFu),
-                                                             (__bf16)(float)(codes >> 16)});
-            else
-                return codes | PX::MAGIC;
-        };
 #pragma unroll
-        for (int d = 0; d < D; ++d)
+        for (int d = 0; d < D; ++d) {
+            float total[MT];
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                float total = 0.0f;
+            for (int m = 0; m < MT; ++m)
+                total[m] = 0.0f;
 #pragma unroll
-                for (int j = 0; j < UPL; ++j) {
+            for (int j = 0; j < UPL; ++j) {
+                const Orient o = orient<BITS>(E::to_f32(sv[d][j]), E::to_f32(bv[d][j]));
+                uint32_t cp[16];
+                code_pairs<BITS, DT>(w[d][j], o.flip, cp);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
                     float part = 0.0f;
 #pragma unroll
                     for (int p = 0; p < 16; ++p)
-                        part = PX::dot(code_pair(d, j, p), xr[m][j][p], part);
-                    const float s = E::to_f32(sv[d][j]), b = E::to_f32(bv[d][j]);
-                    const float qx = part - OFFSET * xs[m][j];
-                    total = __builtin_fmaf(s, qx, __builtin_fmaf(b, xs[m][j], total));
+                        part = PX::dot(cp[p], xr[m][j][p], part);
+                    total[m] = __builtin_fmaf(o.s, part, __builtin_fmaf(o.b, xs[m][j], total[m]));
                 }
-                acc[d * MT + m] = total;
             }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                acc[d * MT + m] = total[m];
+        }
         reduce_slots<D * MT, KL>(acc);
         if (kl == KL - 1) {
 #pragma unroll
@@ -284,8 +268,8 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
 // holds sixteen independent 4 x 4 blocks per wave, and here block b of a wave
 // is unit 16 rho + b of the wave's four weight rows at round rho. Lane 4 b + c
 // holds, for its block, activation row c (operand A, four activations of the
-// unit) and weight row r0 + c (operand B, the same four positions as OFFSET + q
-// pairs), and ends with the sums for weight row r0 + c over activation rows
+// unit) and weight row r0 + c (operand B, the same four positions as exact
+// code pairs), and ends with the sums for weight row r0 + c over activation rows
 // 0..3 (one per accumulator register). A unit takes eight instructions; its
 // group's scale and bias are then applied per lane, and the sixteen blocks are
 // summed at the end. Per code this is the same extraction work as one
@@ -312,16 +296,10 @@ template <> struct RowMfma<DT_F16> {
 template <int BITS, int DT, int R, bool WIDE>
 __global__ __launch_bounds__(256) void qgemv_rowmfma_kernel(RowStreamArgs a)
 {
-    using PX = RowStreamPair<DT>;
     using E = Elem<DT>;
     using St = typename E::storage;
     static_assert(BITS == 2 || BITS == 4 || BITS == 8, "codes in whole 16-bit halves");
-    constexpr int CPW = 32 / BITS;                   // codes per word
-    constexpr int HALF = CPW / 2;                    // pairs per word
-    constexpr bool CONVERT = BITS == 8 && DT == DT_BF16;
-    constexpr float OFFSET = CONVERT ? 0.0f : PX::OFFSET;
-    constexpr uint32_t M1 = (1u << BITS) - 1u;
-    constexpr uint32_t MASK = M1 | (M1 << 16);
+    using CO = CodeOrder<BITS>;
     constexpr int UNITS = 16 * R;                    // unit slots of a row
     constexpr int ENTRIES = 4 * UNITS;               // (activation row, unit) slices
     constexpr int EPT = (ENTRIES + 255) / 256;
@@ -418,16 +396,16 @@ __global__ __launch_bounds__(256) void qgemv_rowmfma_kernel(RowStreamArgs a)
     for (int e = 0; e < EPT; ++e) {
         const int idx = (int)threadIdx.x + 256 * e, m = idx / UNITS, u = idx % UNITS;
         if (idx < ENTRIES) {
+            // Pair q holds the activations of codes lo_code(q) (low half) and
+            // hi_code(q) (high half) of the unit.
             uint32_t p[16];
 #pragma unroll
-            for (int i = 0; i < BITS; ++i)
-#pragma unroll
-                for (int t = 0; t < HALF; ++t) {
-                    const int k0 = CPW * i + t, k1 = k0 + HALF;
-                    const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
-                    const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
-                    p[HALF * i + t] = lo | (hi << 16);
-                }
+            for (int q = 0; q < 16; ++q) {
+                const int k0 = CO::lo_code(q), k1 = CO::hi_code(q);
+                const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
+                const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
+                p[q] = lo | (hi << 16);
+            }
             float sum = 0.0f;
 #pragma unroll
             for (int k = 0; k < 32; ++k)
@@ -444,23 +422,21 @@ __global__ __launch_bounds__(256) void qgemv_rowmfma_kernel(RowStreamArgs a)
         if (!first)
             load(r0);
         exchange();
-        auto code_pair = [&](int rho, int p) -> uint32_t {
-            const uint32_t codes = (w[rho][p / HALF] >> (BITS * (p % HALF))) & MASK;
-            if constexpr (CONVERT)
-                return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)(float)(codes & 0xFFu),
-                                                             (__bf16)(float)(codes >> 16)});
-            else
-                return codes | PX::MAGIC;
-        };
         // Two rounds at a time, their instruction chains interleaved.
         constexpr int RP = R >= 2 ? 2 : 1;
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int r2 = 0; r2 < R; r2 += RP) {
             f32x4_t c[RP];
+            Orient o[RP];
+            uint32_t cp[RP][16];
 #pragma unroll
-            for (int h = 0; h < RP; ++h)
+            for (int h = 0; h < RP; ++h) {
                 c[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                o[h] = orient<BITS>(E::to_f32(sv[r2 + h]), E::to_f32(bv[r2 + h]));
+                code_pairs<BITS, DT>(w[r2 + h], o[h].flip, cp[h]);
+            }
+            auto code_pair = [&](int h, int p) -> uint32_t { return cp[h][p]; };
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 u32x4_t xv[RP];
@@ -469,23 +445,22 @@ __global__ __launch_bounds__(256) void qgemv_rowmfma_kernel(RowStreamArgs a)
                     xv[h] = xl[col][q][16 * (r2 + h) + blk];
 #pragma unroll
                 for (int h = 0; h < RP; ++h)
-                    c[h] = RowMfma<DT>::mma(
-                        u32x2_t{xv[h].x, xv[h].y},
-                        u32x2_t{code_pair(r2 + h, 4 * q), code_pair(r2 + h, 4 * q + 1)}, c[h]);
+                    c[h] = RowMfma<DT>::mma(u32x2_t{xv[h].x, xv[h].y},
+                                            u32x2_t{code_pair(h, 4 * q), code_pair(h, 4 * q + 1)},
+                                            c[h]);
 #pragma unroll
                 for (int h = 0; h < RP; ++h)
-                    c[h] = RowMfma<DT>::mma(
-                        u32x2_t{xv[h].z, xv[h].w},
-                        u32x2_t{code_pair(r2 + h, 4 * q + 2), code_pair(r2 + h, 4 * q + 3)}, c[h]);
+                    c[h] = RowMfma<DT>::mma(u32x2_t{xv[h].z, xv[h].w},
+                                            u32x2_t{code_pair(h, 4 * q + 2), code_pair(h, 4 * q + 3)},
+                                            c[h]);
             }
 #pragma unroll
             for (int h = 0; h < RP; ++h) {
                 const int u = 16 * (r2 + h) + blk;
-                const float s = E::to_f32(sv[r2 + h]), b = E::to_f32(bv[r2 + h]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float xs = sl[u][i];
-                    acc[i] = __builtin_fmaf(s, c[h][i] - OFFSET * xs, __builtin_fmaf(b, xs, acc[i]));
+                    acc[i] = __builtin_fmaf(o[h].s, c[h][i], __builtin_fmaf(o[h].b, xs, acc[i]));
                 }
             }
             // Two rounds' activation vectors live at a time.
