@@ -224,6 +224,34 @@ qp_status qgemv_moe_id_gate_up_silu(const void* a, qp_dtype a_dtype, const int32
                                     void* silu_out, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/*
+ * Scratch bytes of qgemv_moe_id_noalloc on each GPU: room for the routing
+ * tables of up to about 60,000 pairs over 4096 experts (qgemv_moe_workspace_bytes
+ * of the call must not exceed it).
+ */
+#define QP_NOALLOC_SCRATCH_BYTES (2u << 20)
+
+/*
+ * qgemv_moe_id without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation, harnesses without an allocator). The routing tables go
+ * to a library-owned device array of QP_NOALLOC_SCRATCH_BYTES bytes per GPU,
+ * present from load to process end; the call itself allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine). Arguments, result and
+ * errors as qgemv_moe_id; QP_ERR_WORKSPACE when
+ * qgemv_moe_workspace_bytes(n_tokens*top_k, num_experts) exceeds
+ * QP_NOALLOC_SCRATCH_BYTES. Every call on one GPU shares that GPU's array
+ * and overwrites it (nothing in it needs clearing: each call's routing
+ * writes every table entry it reads), so calls that overlap in time on one
+ * GPU (on different streams) race; calls ordered on one stream do not.
+ */
+qp_status qgemv_moe_id_noalloc(const void* a, qp_dtype a_dtype, const int32_t* ids,
+                               int64_t n_tokens, int64_t top_k, int64_t a_outer_stride,
+                               int64_t a_inner_stride, const uint32_t* wq, const void* scales,
+                               const void* biases, qp_dtype sb_dtype, int64_t num_experts,
+                               int64_t n_rows, int64_t n_cols, int32_t bits, int32_t group_size,
+                               void* out, hipStream_t stream);
+
 /* Description of the calling thread's last error ("" if none). */
 const char* qpack_last_error(void);
 

@@ -253,6 +253,37 @@ def test_moe_empty_is_a_noop(fused):
     assert moe(fused=fused, R=0, ids=None, out=None, ws=None) == OK
 
 
+def moe_noalloc(a=A, dt=BF16, ids=A, T=2, top_k=2, outer=64, inner=0, sdt=BF16, E=4, R=8, C=64,
+                bits=4, gs=64, out=A):
+    return qp.lib().qgemv_moe_id_noalloc(a, dt, ids, T, top_k, outer, inner, A, A, A, sdt, E, R,
+                                         C, bits, gs, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=5), UNSUPPORTED), (dict(C=96), SHAPE), (dict(dt=F16), MISMATCH),
+    (dict(T=-1), INVALID), (dict(outer=-64), INVALID), (dict(ids=None), INVALID),
+    (dict(out=None), INVALID), (dict(a=None), INVALID), (dict(E=5000), UNSUPPORTED),
+    (dict(E=0), INVALID), (dict(out=ODD), ALIGN), (dict(ids=P(0x10002)), ALIGN),
+    # Routing tables above the scratch maximum: 2^18 pairs need about 4 MB.
+    (dict(T=1 << 16, top_k=4, E=128), WORKSPACE),
+])
+def test_moe_noalloc_argument_errors(kw, status):
+    """Every check of the allocation-free call runs before any HIP call."""
+    assert moe_noalloc(**kw) == status
+
+
+def test_moe_noalloc_empty_is_a_noop():
+    assert moe_noalloc(T=0, ids=None, out=None) == OK
+    assert moe_noalloc(R=0, ids=None, out=None) == OK
+
+
+def test_moe_noalloc_limit_covers_the_moe_workloads():
+    """The largest routed MoE workload here (512 tokens x top-8 over 128
+    experts) fits the scratch with room to spare."""
+    L = qp.lib()
+    assert L.qgemv_moe_workspace_bytes(512 * 8, 128) * 8 < 2 << 20
+
+
 def test_workspace_bytes_grow_with_pairs_and_experts():
     L = qp.lib()
     a = L.qgemv_moe_workspace_bytes(8, 128)

@@ -28,7 +28,8 @@ STATUS = {0: "QP_OK", 1: "QP_ERR_INVALID_ARG", 2: "QP_ERR_UNSUPPORTED",
 
 # Every symbol include/qpack.h declares.
 EXPORTS = ("qpack_quantize", "qpack_dequantize", "qpack_dequantize_mx", "qmatmul", "qmatmul_mx",
-           "qgemv_moe_workspace_bytes", "qgemv_moe_id", "qgemv_moe_id_gate_up_silu",
+           "qgemv_moe_workspace_bytes", "qgemv_moe_id", "qgemv_moe_id_noalloc",
+           "qgemv_moe_id_gate_up_silu",
            "qgemv_moe_ffn_workspace_bytes", "qgemv_moe_ffn", "qpack_quantize_int8_tensor",
            "qpack_dequantize_int8_tensor", "qmatmul_int8_tensor", "qmatmul_t_workspace_bytes",
            "qmatmul_t", "qpack_last_error",
@@ -70,6 +71,9 @@ def lib() -> ctypes.CDLL:
         L.qgemv_moe_id.argtypes = [P, ctypes.c_int, P, I64, I64, I64, I64, P, P, P, ctypes.c_int,
                                    I64, I64, I64, I32, I32, P, P, SZ, P]
         L.qgemv_moe_id.restype = ctypes.c_int
+        L.qgemv_moe_id_noalloc.argtypes = [P, ctypes.c_int, P, I64, I64, I64, I64, P, P, P,
+                                           ctypes.c_int, I64, I64, I64, I32, I32, P, P]
+        L.qgemv_moe_id_noalloc.restype = ctypes.c_int
         L.qgemv_moe_id_gate_up_silu.argtypes = [P, ctypes.c_int, P, I64, I64, I64, I64, P, P, P,
                                                 P, P, P, ctypes.c_int, I64, I64, I64, I32, I32,
                                                 P, P, SZ, P]
@@ -281,6 +285,19 @@ def qgemv_moe_id(a, ids, n_tokens: int, top_k: int, a_outer: int, a_inner: int, 
                              a_inner, _ptr(wq), _ptr(scales), _ptr(biases),
                              dtype_code(scales.dtype), E, n_rows, n_cols, bits, group_size,
                              _ptr(out), _ptr(workspace), workspace.numel(), _stream(a)))
+    return out
+
+
+def qgemv_moe_id_noalloc(a, ids, n_tokens: int, top_k: int, a_outer: int, a_inner: int, wq,
+                         scales, biases, bits: int, group_size: int, out):
+    """qgemv_moe_id with the routing tables in the library's own device
+    scratch (no workspace; `out` is the caller's)."""
+    E, n_rows = wq.shape[0], wq.shape[1]
+    n_cols = wq.shape[2] * 32 // bits
+    check(lib().qgemv_moe_id_noalloc(_ptr(a), dtype_code(a.dtype), _ptr(ids), n_tokens, top_k,
+                                     a_outer, a_inner, _ptr(wq), _ptr(scales), _ptr(biases),
+                                     dtype_code(scales.dtype), E, n_rows, n_cols, bits,
+                                     group_size, _ptr(out), _stream(a)))
     return out
 
 

@@ -15,6 +15,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/qpack.h"
@@ -252,7 +253,10 @@ size_t qgemv_moe_workspace_bytes(int64_t n_pairs, int64_t num_experts)
     return qp::moe_workspace_bytes(n_pairs, num_experts);
 }
 
-static qp_status moe_common(const qp::MoeArgs& a, const char* what)
+// check_ws: the caller brings the workspace (pointer, size and alignment are
+// checked); false for the allocation-free call, whose scratch is the
+// library's own.
+static qp_status moe_common(const qp::MoeArgs& a, const char* what, bool check_ws = true)
 {
     if (a.n_tokens < 0 || a.top_k < 0 || a.E < 0 || a.n_rows < 0 || a.n_cols < 0 ||
         a.a_outer < 0 || a.a_inner < 0)
@@ -272,13 +276,13 @@ static qp_status moe_common(const qp::MoeArgs& a, const char* what)
         return QP_OK;
     if (a.E == 0)
         return fail(QP_ERR_INVALID_ARG, "%s: no experts for %lld pairs", what, (long long)P);
-    if (!a.ids || !a.out || !a.workspace)
+    if (!a.ids || !a.out || (check_ws && !a.workspace))
         return fail(QP_ERR_INVALID_ARG, "%s: null pointer", what);
     if (a.ws_bytes < qp::moe_workspace_bytes(P, a.E))
         return fail(QP_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", what, a.ws_bytes,
                     qp::moe_workspace_bytes(P, a.E));
     const size_t es = esize(a.dt);
-    if (!aligned(a.out, es) || !aligned(a.ids, 4) || !aligned(a.workspace, 16))
+    if (!aligned(a.out, es) || !aligned(a.ids, 4) || (check_ws && !aligned(a.workspace, 16)))
         return fail(QP_ERR_ALIGN, "%s: pointer not aligned", what);
     if (a.n_cols > 0) {
         if (!a.a)
@@ -295,6 +299,44 @@ static qp_status moe_common(const qp::MoeArgs& a, const char* what)
     return QP_OK;
 }
 
+} // extern "C"
+
+static qp_status scratch_address(void** out, const char* what);
+
+// qgemv_moe_id with the caller's workspace, or (scratch) with the library's
+// own scratch array in its place.
+static qp_status moe_id_run(const void* a, qp_dtype a_dtype, const int32_t* ids, int64_t n_tokens,
+                            int64_t top_k, int64_t a_outer_stride, int64_t a_inner_stride,
+                            const uint32_t* wq, const void* scales, const void* biases,
+                            qp_dtype sb_dtype, int64_t num_experts, int64_t n_rows,
+                            int64_t n_cols, int32_t bits, int32_t group_size, void* out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream,
+                            bool scratch, const char* what)
+{
+    if (dtype_ok(a_dtype) && dtype_ok(sb_dtype) && a_dtype != sb_dtype)
+        return fail(QP_ERR_DTYPE_MISMATCH, "%s: input dtype must match scales dtype", what);
+    qp::MoeArgs m{};
+    m.a = a; m.dt = (int)a_dtype; m.ids = ids;
+    m.n_tokens = n_tokens; m.top_k = top_k; m.a_outer = a_outer_stride; m.a_inner = a_inner_stride;
+    m.wq[0] = m.wq[1] = wq; m.scales[0] = m.scales[1] = scales; m.biases[0] = m.biases[1] = biases;
+    m.E = num_experts; m.n_rows = n_rows; m.n_cols = n_cols; m.bits = bits; m.gs = group_size;
+    m.fused_silu = false; m.out = out; m.workspace = workspace; m.ws_bytes = workspace_bytes;
+    if (qp_status s = moe_common(m, what, !scratch); s != QP_OK)
+        return s;
+    const int64_t P = n_tokens * top_k;
+    if (P == 0 || n_rows == 0)
+        return ok();
+    if (n_cols == 0)
+        return hip_result(qp::launch_fill_zero(out, (int)a_dtype, P * n_rows, stream), what);
+    if (scratch) {
+        if (qp_status s = scratch_address(&m.workspace, what); s != QP_OK)
+            return s;
+    }
+    return hip_result(qp::launch_moe(m, stream), what);
+}
+
+extern "C" {
+
 qp_status qgemv_moe_id(const void* a, qp_dtype a_dtype, const int32_t* ids, int64_t n_tokens,
                        int64_t top_k, int64_t a_outer_stride, int64_t a_inner_stride,
                        const uint32_t* wq, const void* scales, const void* biases,
@@ -302,23 +344,71 @@ qp_status qgemv_moe_id(const void* a, qp_dtype a_dtype, const int32_t* ids, int6
                        int32_t bits, int32_t group_size, void* out, void* workspace,
                        size_t workspace_bytes, hipStream_t stream)
 {
-    if (dtype_ok(a_dtype) && dtype_ok(sb_dtype) && a_dtype != sb_dtype)
-        return fail(QP_ERR_DTYPE_MISMATCH, "qgemv_moe_id: input dtype must match scales dtype");
-    qp::MoeArgs m{};
-    m.a = a; m.dt = (int)a_dtype; m.ids = ids;
-    m.n_tokens = n_tokens; m.top_k = top_k; m.a_outer = a_outer_stride; m.a_inner = a_inner_stride;
-    m.wq[0] = m.wq[1] = wq; m.scales[0] = m.scales[1] = scales; m.biases[0] = m.biases[1] = biases;
-    m.E = num_experts; m.n_rows = n_rows; m.n_cols = n_cols; m.bits = bits; m.gs = group_size;
-    m.fused_silu = false; m.out = out; m.workspace = workspace; m.ws_bytes = workspace_bytes;
-    if (qp_status s = moe_common(m, "qgemv_moe_id"); s != QP_OK)
-        return s;
-    const int64_t P = n_tokens * top_k;
-    if (P == 0 || n_rows == 0)
-        return ok();
-    if (n_cols == 0)
-        return hip_result(qp::launch_fill_zero(out, (int)a_dtype, P * n_rows, stream),
-                          "qgemv_moe_id");
-    return hip_result(qp::launch_moe(m, stream), "qgemv_moe_id");
+    return moe_id_run(a, a_dtype, ids, n_tokens, top_k, a_outer_stride, a_inner_stride, wq,
+                      scales, biases, sb_dtype, num_experts, n_rows, n_cols, bits, group_size, out,
+                      workspace, workspace_bytes, stream, false, "qgemv_moe_id");
+}
+
+} // extern "C"
+
+// Routing tables of qgemv_moe_id_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends. Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol); it
+// resolves the array's device address once per device with the device
+// current and passes that address as the workspace.
+static __device__ __align__(256) unsigned char scratch[QP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+} // namespace
+
+static qp_status scratch_address(void** out, const char* what)
+{
+    int dev = -1;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return hip_result(e, what);
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(QP_ERR_UNSUPPORTED, "%s: device %d above the %d the scratch table covers", what,
+                    dev, kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess)
+            return hip_result(e, what);
+        if (p == nullptr)
+            return fail(QP_ERR_HIP, "%s: no device address for the scratch array", what);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QP_OK;
+}
+
+extern "C" {
+
+qp_status qgemv_moe_id_noalloc(const void* a, qp_dtype a_dtype, const int32_t* ids,
+                               int64_t n_tokens, int64_t top_k, int64_t a_outer_stride,
+                               int64_t a_inner_stride, const uint32_t* wq, const void* scales,
+                               const void* biases, qp_dtype sb_dtype, int64_t num_experts,
+                               int64_t n_rows, int64_t n_cols, int32_t bits, int32_t group_size,
+                               void* out, hipStream_t stream)
+{
+    const char* what = "qgemv_moe_id_noalloc";
+    if (n_tokens >= 0 && top_k >= 0 && num_experts >= 0 && num_experts <= 4096 &&
+        mul_ok(n_tokens, top_k) && n_tokens * top_k <= (int64_t)INT32_MAX / 2) {
+        const size_t need = qp::moe_workspace_bytes(n_tokens * top_k, num_experts);
+        if (need > QP_NOALLOC_SCRATCH_BYTES)
+            return fail(QP_ERR_WORKSPACE,
+                        "%s: %lld pairs over %lld experts need %zu bytes of scratch, above the "
+                        "%u-byte maximum", what, (long long)(n_tokens * top_k),
+                        (long long)num_experts, need, (unsigned)QP_NOALLOC_SCRATCH_BYTES);
+    }
+    return moe_id_run(a, a_dtype, ids, n_tokens, top_k, a_outer_stride, a_inner_stride, wq,
+                      scales, biases, sb_dtype, num_experts, n_rows, n_cols, bits, group_size, out,
+                      nullptr, QP_NOALLOC_SCRATCH_BYTES, stream, true, what);
 }
 
 qp_status qgemv_moe_id_gate_up_silu(const void* a, qp_dtype a_dtype, const int32_t* ids,
