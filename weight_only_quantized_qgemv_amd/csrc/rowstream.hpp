@@ -54,10 +54,17 @@ template <> struct RowStreamPair<DT_F16> {
     }
 };
 
-// Rows in flight: about 32 VGPRs of codes.
+// Rows per wave: about 24 VGPRs of codes, from 1 to 4 rows. Each wave
+// computes its rows after they arrive, so the rows of the last waves to be
+// served are the kernel's tail; fewer rows per wave (and more waves) shorten
+// it. Measured on the 14336 x 4096 decode (device time, events over
+// back-to-back launches): 4-bit 3 rows 8.0 us against 4 rows 8.6 us and 2
+// rows 8.2 us; 8-bit 1 row 11.8 us against 2 rows 12.2 us; 2-bit 4 rows 7.0
+// us against 3 rows 7.2 us and 6 rows 8.0 us; at K = 14336 (seven units per
+// lane) one row 10.3 us against two 11.1 us.
 template <int BITS, int UPL> constexpr int rowstream_depth()
 {
-    return 32 / (BITS * UPL) < 1 ? 1 : (32 / (BITS * UPL) > 4 ? 4 : 32 / (BITS * UPL));
+    return 24 / (BITS * UPL) < 1 ? 1 : (24 / (BITS * UPL) > 4 ? 4 : 24 / (BITS * UPL));
 }
 
 template <int BITS, int DT, int MT, int UPL, int WPB, bool WIDE, int KL>
