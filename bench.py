@@ -46,7 +46,7 @@ CSRC = os.path.join(ROOT, "weight_only_quantized_qgemv_amd", "csrc")
 # It holds only while the decode kernel's sources are the ones it was taken on.
 TRAFFIC = {"src_sha": "c5b7afb7069cdae8", "fetch_bytes": 33207414, "write_bytes": 28672,
            "fetch_scale": 1.9999, "write_scale": 1.0}
-DECODE_SOURCES = ("rowstream.hpp", "gemv_core.hpp", "common.hpp", "qgemv.hip")
+DECODE_SOURCES = ("rowstream.hpp", "codepair.hpp", "gemv_core.hpp", "common.hpp", "qgemv.hip")
 
 
 def decode_src_sha() -> str:

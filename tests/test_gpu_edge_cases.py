@@ -39,9 +39,6 @@ pytestmark = pytest.mark.gpu
 
 
 TAU_TILE_BF16 = 2.0 ** -8 + 2.0 ** -12
-SKINNY_BF16 = pytest.mark.xfail(
-    reason="the skinny matrix-core kernel rounds dequantized weights to bf16 (2^-8 per product)",
-    strict=False)
 
 
 def tile_tau(m, dt):
@@ -79,21 +76,14 @@ DENSE_16 = [(1, 16384, 128), (1, 4096, 64), (1, 1024, 32), (2, 8192, 64), (2, 16
             (3, 4096, 64), (4, 4096, 128), (8, 4096, 64), (16, 14336, 64), (40, 4096, 64)]
 
 
-def with_dtypes(cases, skinny_rows):
-    """(m, k, gs) x {bf16, fp16}; bf16 with m in `skinny_rows` (the skinny
-    matrix-core kernel) is expected to fail until that kernel keeps the codes
-    exact."""
-    out = []
-    for (m, k, gs) in cases:
-        out.append(pytest.param(m, k, gs, BF16, marks=SKINNY_BF16) if m in skinny_rows
-                   else (m, k, gs, BF16))
-        out.append((m, k, gs, F16))
-    return out
+def with_dtypes(cases):
+    """(m, k, gs) x {bf16, fp16}."""
+    return [(m, k, gs, dt) for (m, k, gs) in cases for dt in (BF16, F16)]
 
 
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("bits", [2, 4, 8])
-@pytest.mark.parametrize("m,k,gs,dt", with_dtypes(DENSE_16, range(5, 17)))
+@pytest.mark.parametrize("m,k,gs,dt", with_dtypes(DENSE_16))
 def test_edge_integral_widths(m, k, gs, bits, dt, act):
     log(f"edge bits={bits} dt={dt} m={m} k={k} gs={gs} act={act}")
     edge_case(64, k, m, bits, gs, dt, seed=9000 + m + k + gs + bits, act=act)
@@ -105,7 +95,7 @@ DENSE_CROSS = [(1, 4096, 32), (1, 4096, 128), (2, 4096, 64), (1, 14336, 64), (8,
 
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("bits", [3, 6])
-@pytest.mark.parametrize("m,k,gs,dt", with_dtypes(DENSE_CROSS, range(3, 17)))
+@pytest.mark.parametrize("m,k,gs,dt", with_dtypes(DENSE_CROSS))
 def test_edge_cross_word_widths(m, k, gs, bits, dt, act):
     log(f"edge cross bits={bits} dt={dt} m={m} k={k} gs={gs} act={act}")
     edge_case(64, k, m, bits, gs, dt, seed=9500 + m + k + gs + bits, act=act)

@@ -84,10 +84,12 @@ def test_moe_gate_up_and_down_small(bits, dt, T, top_k, E):
     (32, 2, 16, 200, 352, 32),    # 4 pairs per expert: 16-pair tiles
     (64, 4, 8, 96, 256, 64),      # 32 per expert: 32-pair tiles
     (200, 2, 4, 130, 256, 128),   # 100 per expert: 64-pair tiles, several per expert
+    (32, 2, 16, 301, 96, 32),     # 16-pair tiles; 1806-byte scale rows per expert (not 16-aligned)
 ])
 def test_moe_matrix_core_tiles(bits, dt, T, top_k, E, R, C, gs):
     """Enough pairs per expert for the matrix-core tiles, with row counts that
-    are not multiples of a row group and K not a multiple of 128."""
+    are not multiples of a row group, K not a multiple of 128, and experts
+    whose scale and bias rows start off a 16-byte boundary."""
     log(f"moe tiles bits={bits} dt={dt} T={T} top_k={top_k} E={E} R={R} C={C}")
     gate_h, gate_d = stack(E, R, C, bits, gs, dt, 61 + bits)
     up_h, up_d = stack(E, R, C, bits, gs, dt, 62 + bits)

@@ -130,8 +130,6 @@ bool moe_rowstream_ok(const MoeArgs& a, int mt);
 // it (fp32 activations, few pairs per expert, K not a multiple of 64, or
 // operands the 16-byte / 32-bit-offset accesses cannot cover).
 int moe_gemm_bm(const MoeArgs& a);
-// LDS budget of the matrix-core tile kernels.
-constexpr unsigned kMfmaLdsBytes = 160 * 1024;
 #define QP_MOE_DECL(B)                                                                          \
     hipError_t launch_moe_b##B##_n1(const MoeArgs& a, const MoeRouting& r, hipStream_t stream); \
     hipError_t launch_moe_b##B##_n2(const MoeArgs& a, const MoeRouting& r, hipStream_t stream);

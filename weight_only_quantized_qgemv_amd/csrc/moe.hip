@@ -10,7 +10,7 @@
 //     counts, writes a tile list (each tile: up to MT pairs of one expert) and
 //     scatters the pair indices into expert order, all in the workspace;
 //  2. compute: over the tile list, one of the routed tile GEMM
-//     (gemm_core.hpp), the skinny matrix-core kernel (mfma_gemv.hpp) or the
+//     (gemm_core.hpp), the skinny matrix-core kernel (skinny.hpp) or the
 //     streaming GEMV (gemv_core.hpp); blocks past the device-written tile
 //     count exit at once. Each tile streams its expert's weights once, so an
 //     expert's weights are read once per launch when its pairs fit one tile.
@@ -19,7 +19,7 @@
 // Each pair's accumulation order does not depend on its slot in a tile, so the
 // (unordered) scatter cannot change any output value.
 #include "gemv_core.hpp"
-#include "mfma_gemv.hpp"
+#include "skinny.hpp"
 #include "launch.hpp"
 
 namespace qp {
@@ -173,12 +173,11 @@ int pick_mt(int64_t P, int64_t E, int mtmax)
 
 } // namespace
 
-int moe_tile_height(int64_t n_pairs, int64_t num_experts, int bits, int dt)
+int moe_tile_height(int64_t n_pairs, int64_t num_experts, int, int)
 {
-    // The register-resident kernel holds up to 4 activation rows with the dot2
-    // path, 2 with the fp32 path (fp32 activations, 8-bit codes with bf16).
-    const bool dot2 = dt != DT_F32 && !(bits == 8 && dt == DT_BF16);
-    return pick_mt(n_pairs, num_experts, dot2 ? 4 : 2);
+    // The register-resident kernel holds up to 2 activation rows (fp32
+    // activations and exact fp32 codes, whatever the precision).
+    return pick_mt(n_pairs, num_experts, 2);
 }
 
 hipError_t launch_moe_route(const MoeArgs& a, int mt, MoeRouting* r, hipStream_t st)
@@ -224,17 +223,12 @@ int moe_mfma_nb(const MoeArgs& a)
                        P * a.n_rows * es < (int64_t(1) << 31);
     if (!vec || !small)
         return 0;
-    const int64_t kpad = (a.n_cols + 127) / 128 * 128;
-    const int64_t avg = (P + a.E - 1) / a.E;
-    int nb = 0;
-    for (int c = 1; c <= 4; c *= 2) {
-        if (mfma_lds_bytes(512, c, a.fused_silu ? 2 : 1, (int)kpad, 1, a.gs) > kMfmaLdsBytes)
-            break;
-        nb = c;
-        if (16 * c >= avg)
-            break;
-    }
-    return nb;
+    // Tiles of 16 pairs, where a 16-row activation table of a K-long row fits
+    // the LDS.
+    return a.n_cols % 32 == 0 &&
+                   skinny_table_rows(16, a.n_cols, a.gs, kSkinnyMaxWaves, a.fused_silu ? 2 : 1, 1) == 16
+               ? 1
+               : 0;
 }
 
 int moe_rowmfma_mt(const MoeArgs& a)

@@ -4,7 +4,7 @@
 // SiLU(gate) * up), so the kernel instantiations spread over parallel
 // translation units.
 #include "gemv_core.hpp"
-#include "mfma_gemv.hpp"
+#include "skinny.hpp"
 #include "gemm_core.hpp"
 #include "moe_rows.hpp"
 #include "launch.hpp"
@@ -71,31 +71,29 @@ hipError_t run_mt(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
     return run_generic<BITS, DT, NMAT>(k, max_tiles, st);
 }
 
-// Matrix-core tiles of up to 16 * NB pairs: grid x over row groups of 128
-// rows of an expert matrix (8 waves of 16 rows), y over the device-written
-// tiles.
-constexpr int kMoeMfmaThreads = 512;
-
-template <int BITS, int DT, int NB, int NMAT>
-hipError_t run_mfma_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
+// Matrix-core tiles of up to 16 pairs with exact codes (skinny.hpp): grid x
+// over blocks of 128 rows of the expert's matrix (8 waves of 16 rows), y over
+// the device-written tiles.
+template <int BITS, int DT, int NMAT>
+hipError_t run_skinny_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 {
-    static bool attr_set = false; // per instantiation; set before its first launch
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&qgemv_mfma_kernel<BITS, DT, NB, NMAT, kMoeMfmaThreads>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaLdsBytes);
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
+    if constexpr (DT == DT_F32) {
+        (void)k; (void)max_tiles; (void)st;
+        return hipErrorInvalidValue;
+    } else {
+        int64_t gy = max_tiles < 65535 ? max_tiles : 65535;
+        gy = gy < 1 ? 1 : gy;
+        SkinnyShape sh{};
+        sh.rows_per_block = 16 * kSkinnyMaxWaves;
+        sh.n_rg = kSkinnyMaxWaves;
+        sh.ks = 1;
+        sh.mt = skinny_table_rows(16, k.K, k.gs, kSkinnyMaxWaves, NMAT, 1);
+        sh.row_stride = skinny_row_stride(k.K);
+        if (sh.mt < 16)
+            return hipErrorInvalidValue;   // the routing chose these tiles only where they fit
+        const dim3 grid((unsigned)((k.R + sh.rows_per_block - 1) / sh.rows_per_block), (unsigned)gy);
+        return skinny_launch<BITS, DT, NMAT>(k, sh, grid, st);
     }
-    const int kpad = (int)((k.K + 127) / 128 * 128);
-    const int n_rg = (int)((k.R + 127) / 128);
-    int64_t gy = max_tiles < 65535 ? max_tiles : 65535;
-    gy = gy < 1 ? 1 : gy;
-    const uint32_t lds = mfma_lds_bytes(kMoeMfmaThreads, NB, NMAT, kpad, 1, k.gs);
-    hipLaunchKernelGGL((qgemv_mfma_kernel<BITS, DT, NB, NMAT, kMoeMfmaThreads>),
-                       dim3(n_rg, (int)gy), dim3(kMoeMfmaThreads), lds, st, k, kpad, 1, n_rg);
-    return hipGetLastError();
 }
 
 // Routed GEMM (gemm_core.hpp): tiles of BM pairs of one expert times BN / NMAT
@@ -278,21 +276,13 @@ hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
             return run_rowstream_tiles<BITS, DT, NMAT>(k, r.max_tiles, st);
         if (r.gemm_bm == 64)
             return run_gemm_tiles<BITS, DT, NMAT, 64>(a, r, st);
-        switch (r.nb) {
-        case 1: return run_mfma_tiles<BITS, DT, 1, NMAT>(k, r.max_tiles, st);
-        case 2: return run_mfma_tiles<BITS, DT, 2, NMAT>(k, r.max_tiles, st);
-        case 4: return run_mfma_tiles<BITS, DT, 4, NMAT>(k, r.max_tiles, st);
-        }
+        if (r.nb > 0)
+            return run_skinny_tiles<BITS, DT, NMAT>(k, r.max_tiles, st);
         if (!x_vec)
             return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
-        constexpr int MTMAX = gemv_max_mt<BITS, DT>();
         switch (r.mt) {
         case 1: return run_mt<BITS, DT, 1, NMAT>(k, r.max_tiles, st);
         case 2: return run_mt<BITS, DT, 2, NMAT>(k, r.max_tiles, st);
-        }
-        if constexpr (MTMAX >= 4) {
-            if (r.mt == 4)
-                return run_mt<BITS, DT, 4, NMAT>(k, r.max_tiles, st);
         }
         return run_generic<BITS, DT, NMAT>(k, r.max_tiles, st);
     }

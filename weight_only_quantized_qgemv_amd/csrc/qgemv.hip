@@ -6,7 +6,7 @@
 #include <stdlib.h>
 
 #include "gemv_core.hpp"
-#include "mfma_gemv.hpp"
+#include "skinny.hpp"
 #include "rowstream.hpp"
 #include "launch.hpp"
 
@@ -149,55 +149,29 @@ hipError_t run_generic(const GemvArgs& a, hipStream_t st)
     return hipSuccess;
 }
 
-// Tiles of 2..16 activation rows (16-bit activations) on the matrix cores:
-// 8-wave blocks, one per CU (the activation table takes most of the LDS).
-// KS waves split each row block's K range; KS is picked so that the row
-// groups of 16 * 8 / KS rows cover the CUs with the least padding of K.
-constexpr int kMfmaThreads = 512;
-
+// Three to sixteen activation rows (16-bit activations) on the 16x16x32
+// matrix instruction with exact codes (skinny.hpp): about one block per CU
+// over a contiguous range of weight rows, at most 16 activation rows per
+// launch (fewer where a K-long activation table would outgrow the LDS).
 template <int BITS, int DT>
-hipError_t run_mfma(const GemvArgs& a, hipStream_t st, bool* done)
+hipError_t run_skinny(const GemvArgs& a, hipStream_t st, bool* done)
 {
     *done = false;
-    constexpr int WAVES = kMfmaThreads / 64;
-    const int64_t n16 = (a.N + 15) / 16;
-    const int64_t quads = (a.K + 127) / 128;
-    int KS = 1;
-    double best = -1.0;
-    for (int ks : {1, 2, 4, 8}) {
-        if (ks > 1 && quads < ks)
-            break;
-        const int64_t rg = (n16 + WAVES / ks - 1) / (WAVES / ks);
-        const int64_t kp = (a.K + 128 * ks - 1) / (128 * ks) * (128 * ks);
-        const double fill = (double)rg / (double)(kCUs * ((rg + kCUs - 1) / kCUs));
-        const double score = fill * (double)a.K / (double)kp;
-        if (score > best + 1e-9) {
-            best = score;
-            KS = ks;
-        }
-    }
-    const int kpad = (int)((a.K + 128 * KS - 1) / (128 * KS) * (128 * KS));
-    const uint64_t lds = mfma_lds_bytes(kMfmaThreads, 1, 1, kpad, KS, a.gs);
-    if (lds > kMfmaLdsBytes)
-        return hipSuccess;   // the streaming kernel takes this shape
-    static bool attr_set = false; // per instantiation; set before its first launch
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&qgemv_mfma_kernel<BITS, DT, 1, 1, kMfmaThreads>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaLdsBytes);
-        if (e != hipSuccess)
+    SkinnyShape sh{};
+    dim3 grid;
+    skinny_dense_shape(a.N, a.K, 16, &sh, &grid);
+    const int waves = sh.n_rg * sh.ks;
+    const int mt = skinny_table_rows(16, a.K, a.gs, waves, 1, sh.ks);
+    // The activation table is fetched in 16-byte pieces of each row.
+    if (mt == 0 || a.K % 32 != 0 || reinterpret_cast<uintptr_t>(a.x) % 16 != 0)
+        return hipSuccess;   // another kernel takes this shape
+    for (int64_t m0 = 0; m0 < a.M;) {
+        const int rows = (int)((a.M - m0) < mt ? (a.M - m0) : mt);
+        sh.mt = skinny_table_rows(rows, a.K, a.gs, waves, 1, sh.ks);
+        GemvKernelArgs k = dense_args(a, m0, rows, (int)sizeof(St<DT>), 0);
+        if (hipError_t e = skinny_launch<BITS, DT, 1>(k, sh, grid, st); e != hipSuccess)
             return e;
-        attr_set = true;
-    }
-    const int n_rg = (int)((n16 + WAVES / KS - 1) / (WAVES / KS));
-    // One launch per 16 activation rows (the tile height of the kernel).
-    for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
-        const int mc = (int)((a.M - m0) < 16 ? (a.M - m0) : 16);
-        GemvKernelArgs k = dense_args(a, m0, mc, (int)sizeof(St<DT>), 0);
-        hipLaunchKernelGGL((qgemv_mfma_kernel<BITS, DT, 1, 1, kMfmaThreads>), dim3(n_rg),
-                           dim3(kMfmaThreads), (uint32_t)lds, st, k, kpad, KS, n_rg);
-        if (hipError_t e = hipGetLastError(); e != hipSuccess)
-            return e;
+        m0 += rows;
     }
     *done = true;
     return hipSuccess;
@@ -356,7 +330,7 @@ hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
         }
         if (a.M >= min_m) {
             bool done = false;
-            hipError_t e = run_mfma<BITS, DT>(a, st, &done);
+            hipError_t e = run_skinny<BITS, DT>(a, st, &done);
             if (e != hipSuccess || done)
                 return e;
         }
