@@ -223,12 +223,8 @@ int moe_mfma_nb(const MoeArgs& a)
                        P * a.n_rows * es < (int64_t(1) << 31);
     if (!vec || !small)
         return 0;
-    // Tiles of 16 pairs, where a 16-row activation table of a K-long row fits
-    // the LDS.
-    return a.n_cols % 32 == 0 &&
-                   skinny_table_rows(16, a.n_cols, a.gs, kSkinnyMaxWaves, a.fused_silu ? 2 : 1, 1) == 16
-               ? 1
-               : 0;
+    // Tiles of 16 pairs (activation rows read in 16-byte pieces).
+    return a.n_cols % 32 == 0 ? 1 : 0;
 }
 
 int moe_rowmfma_mt(const MoeArgs& a)
@@ -300,10 +296,10 @@ int moe_gemm_bm(const MoeArgs& a)
     const int64_t P = a.n_tokens * a.top_k;
     // The routed GEMM dequantizes each expert's weights once per 64-pair tile;
     // it takes over from the GEMV tiles once experts see enough pairs each.
-    // The skinny kernel refills its activation table for every 128 weight
-    // rows, which costs relatively more at short K: for the plain form with
-    // K <= 1024 (the down projection) the routed GEMM wins from 2 pairs per
-    // expert (measured 53 vs 60 us at 4, 47 vs 54 us at 2, [128, 2048, 768]).
+    // The skinny tiles read a tile's activations once per row block, which
+    // costs relatively more at short K: for the plain form with K <= 1024
+    // (the down projection) the routed GEMM won from 2 pairs per expert
+    // (measured 53 vs 60 us at 4, 47 vs 54 us at 2, [128, 2048, 768]).
     const int64_t min_pairs =
         (!a.fused_silu && a.n_cols <= 1024) ? 2 : kMoeGemmMinPairsPerExpert;
     if (P < min_pairs * a.E)

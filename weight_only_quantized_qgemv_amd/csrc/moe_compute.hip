@@ -72,8 +72,7 @@ hipError_t run_mt(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 }
 
 // Matrix-core tiles of up to 16 pairs with exact codes (skinny.hpp): grid x
-// over blocks of 128 rows of the expert's matrix (8 waves of 16 rows), y over
-// the device-written tiles.
+// over row blocks of the expert's matrix, y over the device-written tiles.
 template <int BITS, int DT, int NMAT>
 hipError_t run_skinny_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 {
@@ -84,15 +83,9 @@ hipError_t run_skinny_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
         int64_t gy = max_tiles < 65535 ? max_tiles : 65535;
         gy = gy < 1 ? 1 : gy;
         SkinnyShape sh{};
-        sh.rows_per_block = 16 * kSkinnyMaxWaves;
-        sh.n_rg = kSkinnyMaxWaves;
-        sh.ks = 1;
-        sh.mt = skinny_table_rows(16, k.K, k.gs, kSkinnyMaxWaves, NMAT, 1);
-        sh.row_stride = skinny_row_stride(k.K);
-        if (sh.mt < 16)
-            return hipErrorInvalidValue;   // the routing chose these tiles only where they fit
-        const dim3 grid((unsigned)((k.R + sh.rows_per_block - 1) / sh.rows_per_block), (unsigned)gy);
-        return skinny_launch<BITS, DT, NMAT>(k, sh, grid, st);
+        unsigned gx = 0;
+        skinny_moe_shape(k.R, k.K, max_tiles, &sh, &gx);
+        return skinny_launch<BITS, DT, NMAT>(k, sh, dim3(gx, (unsigned)gy), st);
     }
 }
 

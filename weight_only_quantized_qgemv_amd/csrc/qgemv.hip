@@ -151,27 +151,22 @@ hipError_t run_generic(const GemvArgs& a, hipStream_t st)
 
 // Three to sixteen activation rows (16-bit activations) on the 16x16x32
 // matrix instruction with exact codes (skinny.hpp): about one block per CU
-// over a contiguous range of weight rows, at most 16 activation rows per
-// launch (fewer where a K-long activation table would outgrow the LDS).
+// over a contiguous range of weight rows, 16 activation rows per launch.
 template <int BITS, int DT>
 hipError_t run_skinny(const GemvArgs& a, hipStream_t st, bool* done)
 {
     *done = false;
+    // Activation rows are read in 16-byte pieces.
+    if (a.K % 32 != 0 || reinterpret_cast<uintptr_t>(a.x) % 16 != 0)
+        return hipSuccess;   // another kernel takes this shape
     SkinnyShape sh{};
     dim3 grid;
-    skinny_dense_shape(a.N, a.K, 16, &sh, &grid);
-    const int waves = sh.n_rg * sh.ks;
-    const int mt = skinny_table_rows(16, a.K, a.gs, waves, 1, sh.ks);
-    // The activation table is fetched in 16-byte pieces of each row.
-    if (mt == 0 || a.K % 32 != 0 || reinterpret_cast<uintptr_t>(a.x) % 16 != 0)
-        return hipSuccess;   // another kernel takes this shape
-    for (int64_t m0 = 0; m0 < a.M;) {
-        const int rows = (int)((a.M - m0) < mt ? (a.M - m0) : mt);
-        sh.mt = skinny_table_rows(rows, a.K, a.gs, waves, 1, sh.ks);
+    skinny_dense_shape(a.N, a.K, &sh, &grid);
+    for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
+        const int rows = (int)((a.M - m0) < 16 ? (a.M - m0) : 16);
         GemvKernelArgs k = dense_args(a, m0, rows, (int)sizeof(St<DT>), 0);
         if (hipError_t e = skinny_launch<BITS, DT, 1>(k, sh, grid, st); e != hipSuccess)
             return e;
-        m0 += rows;
     }
     *done = true;
     return hipSuccess;

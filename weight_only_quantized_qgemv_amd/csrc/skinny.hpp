@@ -5,35 +5,36 @@
 // `gemv_moe_id_gate_up_silu`):
 //   out[m, n] = sum_g s'[n,g] * sum_{k in g} x[m,k] q[n,k] + b'[n,g] * sum_{k in g} x[m,k].
 //
-// One instruction contracts 32 consecutive k: operand B holds the codes (lane
-// (g, n) of the wave: weight row n, codes 8g .. 8g+7 of the k-block) as exact
-// 16-bit values, operand A the activations (lane (g, i): row i of A, the same
-// k). A chunk is 128 k of 16 weight rows: lane (g, n) owns unit 4c + g (32
-// codes) of row n and feeds codes 8j .. 8j+7 of it to instruction j = 0..3, so
-// that instruction mixes the four units of the chunk. The 16 rows of A keep
-// their groups apart: with SLOTS = 128 / group_size groups per chunk, row i of
-// A is activation row i % MS of group slot i / MS (MS = 16 / SLOTS), and a lane
-// of A whose slot is not its unit's group reads zeros. Output lane (g, n) then
-// holds weight row n against four activation rows of one group slot, the
-// slot of its own unit: one group's sum per lane, folded at once as
+// One instruction contracts 32 k: operand A holds the activations (lane
+// (g, m): row m, k-slot 8g .. 8g+7), operand B the codes as exact 16-bit
+// values (lane (g, n): weight row n, the same k-slot), and the 16x16 result
+// lands as lane (g, n) holding weight row n against activation rows
+// 4g .. 4g+3. Here every instruction takes one unit (32 consecutive codes) of
+// 16 weight rows, so its k never spans two groups, and a group's units chain
+// into one result that is folded at once:
 //   acc += s_eff * D + b_eff * (sum of the group's activations),
-// with the group's scale and bias oriented so that the folded bias does not
-// cancel against the codes (codepair.hpp, `orient`). More activation rows than
-// MS take MP passes of the same codes against further rows of A.
+// with the scale and bias oriented so that the folded bias does not cancel
+// against the codes (codepair.hpp, `orient`).
 //
-// Activations: the tile's rows sit in LDS as a table (row m at m * row_stride,
-// natural order), with each group's sum beside it; each row group's scales
-// and biases sit there too. Every wave first issues its share of those as
-// LDS DMA (1 KB per instruction, every offset in a register of its own so no
-// transfer waits for another), then its first chunks of codes, then waits
-// once for the DMA alone: a load that had to land before the next was issued
-// costs a full memory latency under the weight stream. Group sums come from
-// the table afterwards (a dot2 with (1, 1) per lane, then a fixed butterfly
-// over the group's lanes). One block per CU covers a range of weight rows: its waves split into
-// n_rg groups of 16 rows and ks waves along K (interleaved chunks), so the
-// table is filled once per block, not once per 16 rows. Codes are loaded row
-// by row (four neighbouring lanes read one row's 4 units, 16 * BITS contiguous
-// bytes) and moved to operand order with one ds_bpermute per word.
+// Codes. A wave reads an item: UI units of 16 weight rows, lane (g, n)
+// loading the g-th quarter of row n's UI * 4 * BITS bytes (one 16- or 12-byte
+// load, or two); a transpose across the wave's four rows of 16 lanes (four
+// v_permlane*_swap per 32-bit word) then gives lane (g, n) the 8-code slice g
+// of each unit. Each slice becomes four exact 16-bit pairs: FP8-E4M3
+// conversions for codes up to 15 (3- and 4-bit, the 3-bit fields first spread
+// to bytes), FP4-E2M1 for 2-bit codes, fp32 conversions of bytes for 6- and
+// 8-bit codes. Activation k-slots follow the slice's pair order (even codes,
+// then odd ones, for 2, 3 and 4 bits).
+//
+// Activations stay in registers: each wave owns a slice of KW = 16 units of
+// K (64 VGPRs for 16 rows) and sweeps the weight rows of its block through
+// it, so a block reads its activations once per slice, not once per row
+// group. A block's waves split into ks slices along K times wr wave rows
+// (every wr-th row group); the per-row-group partial sums meet in LDS at the
+// end of the block. Each group's orientation is computed by one lane in four
+// (the lanes of weight row n take groups g mod NG) and passed to the others
+// with the same row swaps. Group sums of the activations are reduced across
+// the four lane rows once per slice and kept in LDS next to the partial sums.
 #pragma once
 
 #include "codepair.hpp"
@@ -48,6 +49,12 @@ template <> struct SkMfma<DT_BF16> {
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
+    // acc + x.lo + x.hi for a pair of activations (one v_dot2 against 1, 1).
+    static __device__ __forceinline__ float pair_sum(uint32_t x, float acc)
+    {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
+                                               __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
+    }
 };
 template <> struct SkMfma<DT_F16> {
     using frag_t = f16x8_t;
@@ -55,482 +62,637 @@ template <> struct SkMfma<DT_F16> {
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
-};
-
-// acc + x.lo + x.hi for a pair of 16-bit activations (one v_dot2 against 1, 1).
-template <int DT> struct RowStreamPairSk;
-template <> struct RowStreamPairSk<DT_BF16> {
-    static __device__ __forceinline__ float dot(uint32_t x, float acc)
-    {
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
-                                               __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
-    }
-};
-template <> struct RowStreamPairSk<DT_F16> {
-    static __device__ __forceinline__ float dot(uint32_t x, float acc)
+    static __device__ __forceinline__ float pair_sum(uint32_t x, float acc)
     {
         return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, x), __builtin_bit_cast(f16x2_t, 0x3C003C00u),
                                       acc, false);
     }
 };
 
-// The 16 exact code pairs of one unit in natural order (pair q = codes 2q and
-// 2q + 1), every code first complemented when flip is ~0.
-template <int BITS, int DT>
-__device__ __forceinline__ void natural_pairs(const uint32_t* win, uint32_t flip, uint32_t (&p)[16])
+// Lane rows: the wave as four rows of 16 lanes (row g = lanes 16g .. 16g+15).
+// rows_transpose: on entry row g holds v[g][i] in r[i]; on exit v[i][g].
+__device__ __forceinline__ void rows_transpose(uint32_t& r0, uint32_t& r1, uint32_t& r2, uint32_t& r3)
 {
-    using C = ExactCvt<DT>;
-    uint32_t w[BITS];
-#pragma unroll
-    for (int i = 0; i < BITS; ++i)
-        w[i] = win[i] ^ flip;
-    if constexpr (BITS == 4) {
-        // lo / hi bytes hold codes 8i + 2b / 8i + 2b + 1; byte-interleave them
-        // into codes 8i .. 8i+3 and 8i+4 .. 8i+7, each converted as FP8 pairs.
+    const auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);   // rows 2,3 of r0 <-> rows 0,1 of r2
+    const auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);   // odd rows <-> even rows
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    r0 = c[0];
+    r1 = c[1];
+    r2 = d[0];
+    r3 = d[1];
+}
+// The row exchange that leaves each instruction's 32 k inside one group when
+// lane row g starts with unit g's slices 0..3 in r0..r3 (GU units per group):
+// GU = 1 transposes (register f: slice g of unit f); GU = 2 swaps row pairs
+// (register f: unit 2 (f / 2) + g % 2, slice f % 2 + 2 (g / 2)); GU = 4 keeps
+// the rows (register f: slice f of unit g).
+template <int GU>
+__device__ __forceinline__ void rows_exchange(uint32_t& r0, uint32_t& r1, uint32_t& r2, uint32_t& r3)
+{
+    if constexpr (GU == 1) {
+        rows_transpose(r0, r1, r2, r3);
+    } else if constexpr (GU == 2) {
+        const auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+        r0 = a[0];
+        r2 = a[1];
+        r1 = b[0];
+        r3 = b[1];
+    }
+}
+template <int GU> __device__ __forceinline__ int frag_unit(int f, int g)
+{
+    return GU == 1 ? f : GU == 2 ? 2 * (f / 2) + g % 2 : g;
+}
+template <int GU> __device__ __forceinline__ int frag_slice(int f, int g)
+{
+    return GU == 1 ? g : GU == 2 ? f % 2 + 2 * (g / 2) : f;
+}
+
+// Every lane gets rows 0 and 1's values of v, where rows g and g + 2 agree.
+__device__ __forceinline__ void rows_gather2(uint32_t v, uint32_t (&o)[2])
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    o[0] = a[0];
+    o[1] = a[1];
+}
+// Every lane gets the four rows' values of v.
+__device__ __forceinline__ void rows_gather4(uint32_t v, uint32_t (&o)[4])
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);     // rows (0,1,0,1), (2,3,2,3)
+    const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+    o[0] = b[0];
+    o[1] = b[1];
+    o[2] = c[0];
+    o[3] = c[1];
+}
+// Sum over the four rows (the same order in every lane).
+__device__ __forceinline__ float rows_sum(float v)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float s = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+    const uint32_t su = __builtin_bit_cast(uint32_t, s);
+    const auto b = __builtin_amdgcn_permlane16_swap(su, su, false, false);
+    return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
+}
+
+// Three-bit fields at bits 0, 6, 12, 18 of s to the low bits of bytes 0..3.
+__device__ __forceinline__ uint32_t spread3(uint32_t s)
+{
+    const uint32_t y = (s & 0x1C7u) | ((s & 0x1C7000u) << 4);    // fields at 0, 6, 16, 22
+    return (y & 0x70007u) | ((y & 0x1C001C0u) << 2);
+}
+// Six-bit fields at bits 0, 6, 12, 18 of s to the low bits of bytes 0..3.
+__device__ __forceinline__ uint32_t spread6(uint32_t s)
+{
+    const uint32_t y = (s & 0xFFFu) | ((s & 0xFFF000u) << 4);    // fields at 0, 6, 16, 22
+    return (y & 0x3F003Fu) | ((y & 0xFC00FC0u) << 2);
+}
+
+// Per code width: UI units per item, LW registers per lane per item (the
+// lane's quarter of the item's row bytes, plus scratch), the activation slot
+// order, the exchange level XG the slices take for GU units per group, the
+// slices after it, and fragment I's operand from them with every code
+// complemented when flip is ~0.
+template <int BITS> struct SkW;
+template <> struct SkW<4> {
+    static constexpr int UI = 4, LW = 4, WORDS = 4;
+    static constexpr bool EO = true;   // slice pairs (0,2) (4,6) (1,3) (5,7)
+    template <int GU> static constexpr int XG = GU;
+    template <int GU> __device__ __forceinline__ static void prepare(uint32_t (&w)[LW])
+    {
+        rows_exchange<GU>(w[0], w[1], w[2], w[3]);
+    }
+    template <int DT, int I> __device__ __forceinline__ static u32x4_t frag(const uint32_t (&w)[LW], uint32_t flip)
+    {
+        using C = ExactCvt<DT>;
+        const uint32_t lo = (w[I] ^ flip) & 0x0F0F0F0Fu;
+        const uint32_t hi = ((w[I] >> 4) ^ flip) & 0x0F0F0F0Fu;
+        return u32x4_t{C::template fp8<false>(lo), C::template fp8<true>(lo), C::template fp8<false>(hi),
+                       C::template fp8<true>(hi)};
+    }
+};
+template <> struct SkW<2> {
+    static constexpr int UI = 8, LW = 4, WORDS = 4;   // the lane loads units 2g, 2g + 1
+    static constexpr bool EO = true;
+    template <int GU> static constexpr int XG = 1;   // fragment f: slice g of unit f
+    template <int GU> __device__ __forceinline__ static void prepare(uint32_t (&w)[LW])
+    {
+        // Slice j (16 bits) of unit 2g in the low half, of unit 2g + 1 in the high.
+        const uint32_t s0 = __builtin_amdgcn_perm(w[2], w[0], 0x05040100u);
+        const uint32_t s1 = __builtin_amdgcn_perm(w[2], w[0], 0x07060302u);
+        const uint32_t s2 = __builtin_amdgcn_perm(w[3], w[1], 0x05040100u);
+        const uint32_t s3 = __builtin_amdgcn_perm(w[3], w[1], 0x07060302u);
+        w[0] = s0;
+        w[1] = s1;
+        w[2] = s2;
+        w[3] = s3;
+        rows_transpose(w[0], w[1], w[2], w[3]);   // w[i]: this lane's slice of units 2i, 2i + 1
+    }
+    template <int DT, int I> __device__ __forceinline__ static u32x4_t frag(const uint32_t (&w)[LW], uint32_t flip)
+    {
+        using C = ExactCvt<DT>;
+        constexpr int B = 2 * (I & 1);
+        const uint32_t lo = (w[I / 2] ^ flip) & 0x33333333u;
+        const uint32_t hi = ((w[I / 2] >> 2) ^ flip) & 0x33333333u;
+        return u32x4_t{C::template fp4<B>(lo), C::template fp4<B + 1>(lo), C::template fp4<B>(hi),
+                       C::template fp4<B + 1>(hi)};
+    }
+};
+template <> struct SkW<8> {
+    static constexpr int UI = 4, LW = 8, WORDS = 8;
+    static constexpr bool EO = false;
+    template <int GU> static constexpr int XG = GU;
+    template <int GU> __device__ __forceinline__ static void prepare(uint32_t (&w)[LW])
+    {
+        rows_exchange<GU>(w[0], w[2], w[4], w[6]);   // first words of slices 0..3
+        rows_exchange<GU>(w[1], w[3], w[5], w[7]);   // second words
+    }
+    template <int DT, int I> __device__ __forceinline__ static u32x4_t frag(const uint32_t (&w)[LW], uint32_t flip)
+    {
+        using C = ExactCvt<DT>;
+        const uint32_t a = w[2 * I] ^ flip, b = w[2 * I + 1] ^ flip;
+        return u32x4_t{C::pack((float)(a & 0xFFu), (float)((a >> 8) & 0xFFu)),
+                       C::pack((float)((a >> 16) & 0xFFu), (float)(a >> 24)),
+                       C::pack((float)(b & 0xFFu), (float)((b >> 8) & 0xFFu)),
+                       C::pack((float)((b >> 16) & 0xFFu), (float)(b >> 24))};
+    }
+};
+template <> struct SkW<3> {
+    static constexpr int UI = 4, LW = 4, WORDS = 3;   // w[3] is scratch
+    static constexpr bool EO = true;
+    template <int GU> static constexpr int XG = GU;
+    template <int GU> __device__ __forceinline__ static void prepare(uint32_t (&w)[LW])
+    {
+        // Slice j = bytes 3j .. 3j+2 of the unit, in the low 24 bits.
+        const uint32_t s1 = __builtin_amdgcn_alignbyte(w[1], w[0], 3);
+        const uint32_t s2 = __builtin_amdgcn_alignbyte(w[2], w[1], 2);
+        const uint32_t s3 = w[2] >> 8;
+        w[1] = s1;
+        w[2] = s2;
+        w[3] = s3;
+        rows_exchange<GU>(w[0], w[1], w[2], w[3]);
+    }
+    template <int DT, int I> __device__ __forceinline__ static u32x4_t frag(const uint32_t (&w)[LW], uint32_t flip)
+    {
+        using C = ExactCvt<DT>;
+        const uint32_t s = w[I] ^ flip;
+        const uint32_t even = spread3(s), odd = spread3(s >> 3);
+        return u32x4_t{C::template fp8<false>(even), C::template fp8<true>(even), C::template fp8<false>(odd),
+                       C::template fp8<true>(odd)};
+    }
+};
+template <> struct SkW<6> {
+    static constexpr int UI = 4, LW = 8, WORDS = 6;   // w[6], w[7] are scratch
+    static constexpr bool EO = false;
+    template <int GU> static constexpr int XG = GU;
+    template <int GU> __device__ __forceinline__ static void prepare(uint32_t (&w)[LW])
+    {
+        // Slice j = bytes 6j .. 6j+5: codes 0..3 in h0[j], 4..7 in h1[j] (24 bits each).
+        uint32_t h0[4], h1[4];
+        h0[0] = w[0];
+        h1[0] = __builtin_amdgcn_alignbyte(w[1], w[0], 3);
+        h0[1] = __builtin_amdgcn_alignbyte(w[2], w[1], 2);
+        h1[1] = w[2] >> 8;
+        h0[2] = w[3];
+        h1[2] = __builtin_amdgcn_alignbyte(w[4], w[3], 3);
+        h0[3] = __builtin_amdgcn_alignbyte(w[5], w[4], 2);
+        h1[3] = w[5] >> 8;
+        rows_exchange<GU>(h0[0], h0[1], h0[2], h0[3]);
+        rows_exchange<GU>(h1[0], h1[1], h1[2], h1[3]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
-            const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-            const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-            p[4 * i + 0] = C::template fp8<false>(a);
-            p[4 * i + 1] = C::template fp8<true>(a);
-            p[4 * i + 2] = C::template fp8<false>(b);
-            p[4 * i + 3] = C::template fp8<true>(b);
+            w[2 * i] = h0[i];
+            w[2 * i + 1] = h1[i];
         }
-    } else if constexpr (BITS == 2) {
-        // t0 byte j = codes 4j | 4j+1 << 4, t1 byte j = codes 4j+2 | 4j+3 << 4
-        // (of word i's 16), each byte an FP4 pair.
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t t0 = (w[i] & 0x03030303u) | ((w[i] << 2) & 0x30303030u);
-            const uint32_t t1 = ((w[i] >> 4) & 0x03030303u) | ((w[i] >> 2) & 0x30303030u);
-            p[8 * i + 0] = C::template fp4<0>(t0);
-            p[8 * i + 1] = C::template fp4<0>(t1);
-            p[8 * i + 2] = C::template fp4<1>(t0);
-            p[8 * i + 3] = C::template fp4<1>(t1);
-            p[8 * i + 4] = C::template fp4<2>(t0);
-            p[8 * i + 5] = C::template fp4<2>(t1);
-            p[8 * i + 6] = C::template fp4<3>(t0);
-            p[8 * i + 7] = C::template fp4<3>(t1);
-        }
-    } else if constexpr (BITS == 8) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            p[2 * i + 0] = C::pack((float)(w[i] & 0xFFu), (float)((w[i] >> 8) & 0xFFu));
-            p[2 * i + 1] = C::pack((float)((w[i] >> 16) & 0xFFu), (float)(w[i] >> 24));
-        }
+    }
+    template <int DT, int I> __device__ __forceinline__ static u32x4_t frag(const uint32_t (&w)[LW], uint32_t flip)
+    {
+        using C = ExactCvt<DT>;
+        const uint32_t a = spread6(w[2 * I] ^ flip), b = spread6(w[2 * I + 1] ^ flip);
+        return u32x4_t{C::pack((float)(a & 0xFFu), (float)((a >> 8) & 0xFFu)),
+                       C::pack((float)((a >> 16) & 0xFFu), (float)(a >> 24)),
+                       C::pack((float)(b & 0xFFu), (float)((b >> 8) & 0xFFu)),
+                       C::pack((float)((b >> 16) & 0xFFu), (float)(b >> 24))};
+    }
+};
+
+// The lane's WORDS words of an item (one 16- or 12-byte load, or 16 + 16 /
+// 16 + 8 bytes).
+template <int BITS>
+__device__ __forceinline__ void skinny_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[SkW<BITS>::LW])
+{
+    if constexpr (BITS == 3) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+        w[0] = v[0];
+        w[1] = v[1];
+        w[2] = v[2];
+    } else if constexpr (BITS == 6) {
+        const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        const u32x2_t u = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off + 16, 0, 0));
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        w[4] = u.x; w[5] = u.y;
     } else {
-        static_for<16>([&](auto Q) {
-            constexpr int q = decltype(Q)::value;
-            p[q] = C::pack((float)unit_code<BITS, 2 * q>(w), (float)unit_code<BITS, 2 * q + 1>(w));
-        });
+#pragma unroll
+        for (int i = 0; i < SkW<BITS>::LW; i += 4) {
+            const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0));
+            w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+        }
     }
 }
 
-// Launch shape of one call: blocks of n_rg * ks waves, each block a range of
-// rows_per_block weight rows; the activation table has mt rows of row_stride
-// bytes (K * 2 rounded up to 1 KB, plus 16 so that rows fall on different
-// banks).
+constexpr int kSkinnyKW = 16;        // units per wave slice (64 VGPRs of activations)
+constexpr int kSkinnyRG = 4;         // row groups per wave at most
+constexpr int kSkinnyMaxWaves = 8;
+
+// Items in flight per wave: about 48 VGPRs of codes and scales, a whole
+// number of row groups' items of a slice.
+template <int BITS, int NMAT, int NG> constexpr int skinny_ring()
+{
+    constexpr int per = NMAT * (SkW<BITS>::LW + (NG == 8 ? 4 : 2));
+    constexpr int nq = kSkinnyKW / SkW<BITS>::UI;
+    return 48 / per >= 2 * nq ? 2 * nq : nq;
+}
+
+// Launch shape: blocks of ks * wr waves over rows_per_block weight rows;
+// `slices` K-slices of kSkinnyKW units.
 struct SkinnyShape {
     int rows_per_block;
-    int n_rg;
     int ks;
-    int mt;
-    int row_stride;
+    int wr;
+    int slices;
 };
 
-constexpr int kSkinnyMaxWaves = 8;
-constexpr uint32_t kSkinnyLdsBytes = 156 * 1024;
-
-__host__ __device__ constexpr int skinny_row_stride(int64_t K)
+// LDS, per wave: first its activation slice as loaded (16 rows of 1 KB,
+// each padded by 16 bytes so that a fragment read spreads over the banks);
+// once the fragments are in registers the same bytes hold the partial sums
+// of its row groups (NMAT x 1 KB each), the group sums of the slice (16
+// groups x 16 rows, fp32) and one row group's scales and biases over the
+// slice (16 rows x 16 groups x 2 x NMAT, 16-bit).
+constexpr uint32_t kSkinnyXRow = kSkinnyKW * 64u + 16u;
+__host__ __device__ constexpr uint32_t skinny_wave_lds(int nmat)
 {
-    return (int)((K * 2 + 1023) / 1024 * 1024 + 16);
+    const uint32_t rest = (uint32_t)(kSkinnyRG * nmat + 1 + nmat) * 1024u;
+    return 16u * kSkinnyXRow > rest ? 16u * kSkinnyXRow : rest;
 }
-// LDS: the table, the group sums [groups][mt] (fp32), each row group's scale
-// and bias rows (16 rows x groups, rounded up to 1 KB per array and matrix),
-// a zero fragment; the K-split partial sums reuse the table once every wave is
-// done with it.
-__host__ __device__ constexpr uint32_t skinny_sb_bytes(int64_t K, int gs, int nmat)
+__host__ __device__ constexpr uint32_t skinny_lds_bytes(int waves, int nmat)
 {
-    return (uint32_t)((16 * (K / gs) * 2 + 1023) / 1024 * 1024) * 2u * (uint32_t)nmat;
-}
-__host__ __device__ constexpr uint32_t skinny_lds_bytes(int64_t K, int gs, int mt, int waves, int mp,
-                                                         int nmat, int ks)
-{
-    const uint32_t table = (uint32_t)mt * (uint32_t)skinny_row_stride(K);
-    const uint32_t red = (uint32_t)waves * (uint32_t)(nmat * mp) * 64u * 16u;
-    const uint32_t xg = (uint32_t)((K + 127) / 128 * (128 / gs)) * (uint32_t)mt * 4u;
-    const uint32_t n_rg = (uint32_t)((waves + ks - 1) / ks);
-    return (table > red ? table : red) + xg + n_rg * skinny_sb_bytes(K, gs, nmat) + 64u;
+    return (uint32_t)waves * skinny_wave_lds(nmat);
 }
 
-// Chunks of codes in flight per wave: about 16 VGPRs of codes (each ring
-// slot costs the compiler about four times its codes in registers, and a
-// spill reload waits for every load in flight).
-template <int BITS, int NMAT, int MP> constexpr int skinny_ring()
-{
-    constexpr int d = 16 / (NMAT * BITS * (MP > 2 ? 2 : 1));
-    return d < 2 ? 2 : (d > 8 ? 8 : d);
-}
-
-// Load instructions per unit of BITS words (buffer_words: 16-, 8- or 4-byte
-// loads).
-template <int BITS> constexpr int skinny_loads_per_unit()
-{
-    return BITS % 4 == 0 ? BITS / 4 : BITS % 2 == 0 ? BITS / 2 : BITS;
-}
-
-// Table pieces (1 KB of one row) a wave issues per round of DMA.
-constexpr int kSkinnyXPieces = 4;
-
-// LDS DMA of 16 bytes per lane from byte offset src (OOB: zeros) to
-// dst + 16 * lane.
-__device__ __forceinline__ void skinny_dma(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t src)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, src, 0, 0, 0);
-}
-
-template <int BITS, int DT, int NMAT, int SLOTS, int MP>
-__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny_kernel(GemvKernelArgs a,
-                                                                            SkinnyShape sh)
+template <int BITS, int DT, int NMAT, int GU>
+__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny_kernel(GemvKernelArgs a, SkinnyShape sh)
 {
     using M16 = SkMfma<DT>;
     using frag_t = typename M16::frag_t;
     using E = Elem<DT>;
     using St = typename E::storage;
-    static_assert(SLOTS == 1 || SLOTS == 2 || SLOTS == 4, "group_size 128, 64 or 32");
-    constexpr int MS = 16 / SLOTS;                   // activation rows per pass
-    static_assert(MP * MS <= 16, "at most 16 activation rows");
-    constexpr int D = skinny_ring<BITS, NMAT, MP>();
+    using W = SkW<BITS>;
+    constexpr int UI = W::UI, LW = W::LW;
+    constexpr int NQ = kSkinnyKW / UI;               // items per row group of a slice
+    constexpr int NG = UI / GU;                      // groups per item
+    constexpr int NGL = NG == 8 ? 2 : 1;             // groups whose orientation a lane computes
+    constexpr int NGS = kSkinnyKW / GU;              // groups per slice
+    constexpr int SBL = 16 * NGS / 64;               // scales per lane and row group
+    constexpr int D = skinny_ring<BITS, NMAT, NG>();
+    static_assert(D % NQ == 0, "ring of whole row groups");
     constexpr int SB = (int)sizeof(St);
-    static_assert(SB == 2, "16-bit scales and biases");
+    static_assert(SB == 2, "16-bit activations, scales and biases");
     extern __shared__ __attribute__((aligned(16))) char lds[];
 
-    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int nwaves = (int)(blockDim.x >> 6);
-    const int rg = wave / sh.ks, ks = wave % sh.ks;
-    const int g = lane >> 4, r16 = lane & 15;        // operand lane: k-slice g, row r16
-    const int lrow = lane >> 2, lg = lane & 3;       // load lane: row lrow, unit 4c + lg
-    const int gslot = (g * SLOTS) >> 2;              // group slot of this lane's unit
+    const int ksi = wave / sh.wr, wri = wave % sh.wr;
+    const int g = lane >> 4, l16 = lane & 15;
     const int R = (int)a.R;
     const int K = (int)a.K;
-    const uint32_t row_bytes = (uint32_t)K * BITS / 8;
-    const uint32_t groups_row = (uint32_t)(K / a.gs);
     const int units = K / 32;
-    const int NC = (K + 127) / 128;                  // chunks per row
-    const int nj = ks < NC ? (NC - ks + sh.ks - 1) / sh.ks : 0;   // this wave's chunks
-    const int GC = NC * SLOTS;                       // group slots along K (padded)
-    char* const table = lds;
-    const uint32_t table_bytes = (uint32_t)sh.mt * (uint32_t)sh.row_stride;
-    const uint32_t red_bytes = (uint32_t)nwaves * (uint32_t)(NMAT * MP) * 1024u;
-    char* const xg = lds + (table_bytes > red_bytes ? table_bytes : red_bytes);
-    const uint32_t sb_bytes = skinny_sb_bytes(K, a.gs, NMAT);
-    const uint32_t sb_arr = sb_bytes / (2u * NMAT);                    // one array of one row group
-    char* const sbs = xg + (uint32_t)GC * (uint32_t)sh.mt * 4u;         // [row group][matrix][s, b]
-    char* const sbg = sbs + (uint32_t)rg * sb_bytes;                   // this wave's row group
-    char* const zero = sbs + (uint32_t)sh.n_rg * sb_bytes;
-    if (tid < 4)
-        reinterpret_cast<uint32_t*>(zero)[tid * 4 + 0] = reinterpret_cast<uint32_t*>(zero)[tid * 4 + 1] =
-            reinterpret_cast<uint32_t*>(zero)[tid * 4 + 2] = reinterpret_cast<uint32_t*>(zero)[tid * 4 + 3] = 0u;
+    const uint32_t row_bytes = (uint32_t)K * BITS / 8;
+    const uint32_t G = (uint32_t)(K / a.gs);
+    constexpr uint32_t WL = skinny_wave_lds(NMAT);
+    char* const xst = lds + (uint32_t)wave * WL;                              // [row][k] as loaded
+    char* const red = xst;                                                    // [rg][t] x 1 KB
+    char* const xsw = xst + (uint32_t)(kSkinnyRG * NMAT) * 1024u;             // [group][row] fp32
+    uint16_t* const sbw = reinterpret_cast<uint16_t*>(xsw + 1024u);           // [t][s, b][row][group]
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out, a.out_bytes);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
-    const int bp_addr = (4 * r16 + g) * 4;           // ds_bpermute source: lane 4 n + g
 
     const int ntiles = gemv_num_tiles(a);
     for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
         int expert, start, count;
         if (!gemv_tile(a, tile, expert, start, count))
             continue;   // uniform over the block
-        const int rows = count < sh.mt ? count : sh.mt;
+        const int rows = count < 16 ? count : 16;
         const int r_lo = (int)blockIdx.x * sh.rows_per_block;
         const int r_hi = (r_lo + sh.rows_per_block) < R ? (r_lo + sh.rows_per_block) : R;
-        const int n0 = r_lo + 16 * rg;               // this wave's first weight row
+        const int nrg_b = r_hi > r_lo ? (r_hi - r_lo + 15) / 16 : 0;          // row groups of the block
+        const int nrg_w = wri < nrg_b ? (nrg_b - wri + sh.wr - 1) / sh.wr : 0;   // of this wave
 
+        // Resources over the block's own rows: rows past them read zeros.
         __amdgpu_buffer_rsrc_t rw[NMAT], rs[NMAT], rb[NMAT];
 #pragma unroll
         for (int t = 0; t < NMAT; ++t) {
-            const uint64_t erow = (uint64_t)expert * (uint64_t)R;
-            rw[t] = make_rsrc(reinterpret_cast<const char*>(a.wq[t]) + erow * row_bytes,
-                              (uint32_t)R * row_bytes);
-            rs[t] = make_rsrc(static_cast<const char*>(a.scales[t]) + erow * groups_row * SB,
-                              (uint32_t)R * groups_row * SB);
-            rb[t] = make_rsrc(static_cast<const char*>(a.biases[t]) + erow * groups_row * SB,
-                              (uint32_t)R * groups_row * SB);
+            const uint64_t row_lo = (uint64_t)expert * (uint64_t)R + (uint64_t)r_lo;
+            const uint32_t nrows = (uint32_t)(r_hi - r_lo);
+            rw[t] = make_rsrc(reinterpret_cast<const char*>(a.wq[t]) + row_lo * row_bytes, nrows * row_bytes);
+            rs[t] = make_rsrc(static_cast<const char*>(a.scales[t]) + row_lo * G * SB, nrows * G * SB);
+            rb[t] = make_rsrc(static_cast<const char*>(a.biases[t]) + row_lo * G * SB, nrows * G * SB);
         }
-
-        // 1. Row offsets of the tile's activation rows: lane m < 16 holds row
-        //    m's byte offset (OOB past the tile).
-        uint32_t xoff_l = OOB;
-        if (lane < rows) {
-            const uint32_t p = a.perm != nullptr ? (uint32_t)a.perm[start + lane]
-                                                 : (uint32_t)(start + lane);
+        // Activation row of lane (g, m): m = l16 (OOB past the tile).
+        uint32_t xoff = OOB;
+        if (l16 < rows) {
+            const uint32_t p = a.perm != nullptr ? (uint32_t)a.perm[start + l16] : (uint32_t)(start + l16);
             const uint32_t tk = (uint32_t)a.top_k;
-            xoff_l = ((p / tk) * (uint32_t)a.outer + (p % tk) * (uint32_t)a.inner) * SB;
+            xoff = ((p / tk) * (uint32_t)a.outer + (p % tk) * (uint32_t)a.inner) * SB;
         }
-        __builtin_amdgcn_s_waitcnt(0);   // nothing else is in flight yet
 
-        // 2. LDS DMA of the table: piece q = wave + nwaves i is row q / ppr,
-        //    bytes (q % ppr) KB of it (bytes past K read zeros); then the
-        //    scale and bias rows of this wave's row group (by its first wave
-        //    along K). Rounds of kSkinnyXPieces pieces; offsets stay live
-        //    until the wait below.
-        const int ppr = (sh.row_stride - 16) / 1024;
-        const int pieces = sh.mt * ppr;
-        const int per_wave = (pieces + nwaves - 1) / nwaves;
-        uint32_t xo[kSkinnyXPieces];
-        for (int q0 = 0; q0 < per_wave; q0 += kSkinnyXPieces) {
-            if (q0 > 0)
-                __builtin_amdgcn_s_waitcnt(0);   // more than one round: before any code load
+        for (int si = 0; si * sh.ks + ksi < sh.slices; ++si) {
+            const int u0 = (si * sh.ks + ksi) * kSkinnyKW;   // first unit of the slice
+            const int nitems = nrg_w * NQ;
+
+            // Activations of the slice: fragment f of item q takes row l16 at
+            // the unit and slice the code exchange gives lane row g there.
+            constexpr int XG = W::template XG<GU>;
+            // A wave with one slice loads its 16 rows whole (1 KB of a row
+            // per instruction) and regroups them through LDS; a wave with
+            // several slices keeps partial sums in that LDS between slices
+            // and loads each fragment directly.
+            const bool staged = sh.slices <= sh.ks;   // uniform
+            u32x4_t raw[kSkinnyKW];
+            if (staged) {
 #pragma unroll
-            for (int i = 0; i < kSkinnyXPieces; ++i) {
-                const int q = wave + nwaves * (q0 + i);
-                const int m = q / ppr, part = q % ppr;
-                const uint32_t rowoff = (uint32_t)__builtin_amdgcn_readlane((int)xoff_l, m < 16 ? m : 0);
-                const uint32_t kb = (uint32_t)part * 1024u + (uint32_t)lane * 16u;
-                xo[i] = (q0 + i < per_wave && q < pieces && m < rows && kb < (uint32_t)K * 2u && rowoff != OOB)
-                    ? rowoff + kb : OOB;
-                if (q0 + i < per_wave && q < pieces)
-                    skinny_dma(rx, table + (uint32_t)m * (uint32_t)sh.row_stride + (uint32_t)part * 1024u, xo[i]);
-            }
-        }
-        // Scale and bias rows: 16-byte DMA pieces, except for a row group that
-        // ends past the matrix or an array that does not start on 16 bytes,
-        // which go element by element (the range check would not return a
-        // piece that crosses the buffer's end whole).
-        uint32_t so[4 * NMAT];
-        {
-            const uint32_t bytes = 16u * groups_row * (uint32_t)SB;   // one array of 16 rows
-            const uint32_t base = (uint32_t)n0 * groups_row * (uint32_t)SB;
-            const int npc = (int)(sb_arr / 1024u);
-            const uint64_t eoff = (uint64_t)expert * (uint64_t)R * groups_row * SB;
-#pragma unroll
-            for (int t = 0; t < NMAT; ++t) {
-                const bool plain = n0 + 16 > R ||
-                    ((reinterpret_cast<uintptr_t>(a.scales[t]) + eoff) & 15u) != 0 ||
-                    ((reinterpret_cast<uintptr_t>(a.biases[t]) + eoff) & 15u) != 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t off = (uint32_t)i * 1024u + (uint32_t)lane * 16u;
-                    so[4 * t + i] = off < bytes ? base + off : OOB;
-                    if (ks == 0 && !plain && i < npc) {
-                        skinny_dma(rs[t], sbg + (uint32_t)(2 * t) * sb_arr + (uint32_t)i * 1024u, so[4 * t + i]);
-                        skinny_dma(rb[t], sbg + (uint32_t)(2 * t + 1) * sb_arr + (uint32_t)i * 1024u, so[4 * t + i]);
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t xr = (uint32_t)__builtin_amdgcn_readlane((int)xoff, r);
+                    const uint32_t off = (xr != OOB && u0 * 32 + 8 * lane < K)
+                        ? xr + (uint32_t)(u0 * 32 + 8 * lane) * 2u : OOB;
+                    raw[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
                 }
-                if (ks == 0 && !plain)
-                    for (int i = 4; i < npc; ++i) {   // longer scale rows (K / gs above 128)
-                        const uint32_t off = (uint32_t)i * 1024u + (uint32_t)lane * 16u;
-                        const uint32_t o2 = off < bytes ? base + off : OOB;
-                        skinny_dma(rs[t], sbg + (uint32_t)(2 * t) * sb_arr + (uint32_t)i * 1024u, o2);
-                        skinny_dma(rb[t], sbg + (uint32_t)(2 * t + 1) * sb_arr + (uint32_t)i * 1024u, o2);
-                    }
-                if (ks == 0 && plain) {
-                    // Elements up to 15 G + GC: the padded group slots of row
-                    // 15 read zeros, as they do after the DMA.
-                    const uint32_t n_el = 15u * groups_row + (uint32_t)GC;
-                    for (uint32_t e = (uint32_t)lane; e < n_el; e += 64u) {
-                        // Rows past the matrix read zeros.
-                        const uint32_t off = e < 16u * groups_row ? base + e * (uint32_t)SB : OOB;
-                        reinterpret_cast<uint16_t*>(sbg + (uint32_t)(2 * t) * sb_arr)[e] =
-                            __builtin_amdgcn_raw_buffer_load_b16(rs[t], off, 0, 0);
-                        reinterpret_cast<uint16_t*>(sbg + (uint32_t)(2 * t + 1) * sb_arr)[e] =
-                            __builtin_amdgcn_raw_buffer_load_b16(rb[t], off, 0, 0);
-                    }
+            } else {
+#pragma unroll
+                for (int u = 0; u < kSkinnyKW; ++u) {
+                    const int un = u0 + (u / UI) * UI + frag_unit<XG>(u % UI, g);
+                    const uint32_t off = (xoff != OOB && un < units)
+                        ? xoff + (uint32_t)(un * 32 + 8 * frag_slice<XG>(u % UI, g)) * 2u : OOB;
+                    raw[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
                 }
             }
-        }
-
-        // 3. The code ring: chunk j of this wave is c = ks + KS j; load lane
-        //    (lrow, lg) reads unit 4c + lg of row n0 + lrow. Rows past the
-        //    block or the matrix, units past K and chunks past the wave's read
-        //    zeros.
-        const bool lrow_ok = n0 + lrow < r_hi && rg < sh.n_rg;
-        uint32_t w[D][NMAT][BITS];
-        auto fetch = [&](int j, uint32_t (&dw)[NMAT][BITS]) {
-            const int c = ks + sh.ks * j;
-            const int u = 4 * c + lg;
-            const uint32_t woff = (j < nj && lrow_ok && u < units)
-                ? (uint32_t)(n0 + lrow) * row_bytes + (uint32_t)u * (4 * BITS) : OOB;
-#pragma unroll
-            for (int t = 0; t < NMAT; ++t)
-                buffer_words<BITS>(rw[t], woff, dw[t]);
-        };
-        static_for<D>([&](auto J) {
-            fetch(J, w[J]);
+            // Activations are requested before the first codes (waiting for
+            // them must not wait for codes too).
             __builtin_amdgcn_sched_barrier(0);
-        });
-        // The DMA (issued first) has landed once at most the ring's loads are
-        // outstanding.
-        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(D * NMAT * skinny_loads_per_unit<BITS>()) : "memory");
-#pragma unroll
-        for (int i = 0; i < kSkinnyXPieces; ++i)
-            asm volatile("" :: "v"(xo[i]));
-#pragma unroll
-        for (int i = 0; i < 4 * NMAT; ++i)
-            asm volatile("" :: "v"(so[i]));
-        __syncthreads();
 
-        // 3b. Group sums: the lanes of one group (gs / 8 of them) each take 8
-        //     activations with dot2 and meet in a butterfly; the group's first
-        //     lane writes xg[group * mt + m].
-        {
-            using PX = RowStreamPairSk<DT>;
-            const int lpg = a.gs / 8;
-            for (int i = 0; i < per_wave; ++i) {
-                const int q = wave + nwaves * i;
-                if (q < pieces) {
-                    const int m = q / ppr, part = q % ppr;
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
-                        table + (uint32_t)m * (uint32_t)sh.row_stride + (uint32_t)part * 1024u + (uint32_t)lane * 16u);
-                    float sum = PX::dot(v.x, 0.0f);
-                    sum = PX::dot(v.y, sum);
-                    sum = PX::dot(v.z, sum);
-                    sum = PX::dot(v.w, sum);
-                    for (int off = 1; off < lpg; off <<= 1)
-                        sum += __shfl_xor(sum, off, 64);
-                    const uint32_t k0 = (uint32_t)part * 512u + (uint32_t)lane * 8u;
-                    if (lane % lpg == 0 && k0 < (uint32_t)(NC * 128))
-                        reinterpret_cast<float*>(xg)[(k0 / (uint32_t)a.gs) * (uint32_t)sh.mt + (uint32_t)m] = sum;
-                }
+            // The ring: item j is row group rg = wri + wr (j / NQ), units
+            // u0 + UI (j % NQ) ...; lane (g, n) loads quarter g of weight row
+            // n's bytes of them. The first item of a row group also carries
+            // its scales and biases over the slice (16 rows x NGS groups,
+            // SBL per lane), which go to LDS when that item is processed.
+            struct Slot {
+                uint32_t w[NMAT][LW];
+                St sb[NMAT][2][SBL];
+            };
+            Slot ring[D];
+            // Per lane, once per slice: the byte offsets of its first row
+            // group's codes and scales in the block; an item adds whole row
+            // groups and units to them. No test guards the code loads: rows
+            // past the block are out of range, and a unit past K (an item
+            // straddling the end of a row) reads codes that meet zero
+            // activations. Groups past K / gs would read another row's
+            // scales, so those lanes' offsets get the out-of-range bit.
+            const int row0 = 16 * wri + l16;
+            const int lane_grp = NG == 1 ? 0 : g % (NG < 4 ? NG : 4);
+            const uint32_t wbase = (uint32_t)row0 * row_bytes + (uint32_t)u0 * (4u * BITS) + (uint32_t)(UI * BITS * g);
+            const uint32_t wstep = 16u * (uint32_t)sh.wr * row_bytes, sstep = 16u * (uint32_t)sh.wr * G * SB;
+            uint32_t sboff[SBL];                                  // scale v = lane + 64 i: row v / NGS, group v % NGS
+#pragma unroll
+            for (int i = 0; i < SBL; ++i) {
+                const int v = lane + 64 * i, gl = u0 / GU + v % NGS;
+                sboff[i] = (((uint32_t)(16 * wri + v / NGS) * G + (uint32_t)gl) * SB) | ((uint32_t)gl >= G ? OOB : 0u);
             }
-        }
-        __syncthreads();
-
-        // 4. Stream the chunks.
-        f32x4_t acc[NMAT][MP];
-#pragma unroll
-        for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-            for (int p = 0; p < MP; ++p)
-                acc[t][p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        auto process = [&](int j, const uint32_t (&dw)[NMAT][BITS]) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int c = ks + sh.ks * j;
-            const int grp = c * SLOTS + gslot;       // this lane's group slot along K
-            uint32_t cp[NMAT][16];
-            Orient o[NMAT];
-#pragma unroll
-            for (int t = 0; t < NMAT; ++t) {
-                uint32_t wo[BITS];
-#pragma unroll
-                for (int i = 0; i < BITS; ++i)
-                    wo[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(bp_addr, (int)dw[t][i]);
-                const uint32_t e = (uint32_t)r16 * groups_row + (uint32_t)grp;
-                const St sv = reinterpret_cast<const St*>(sbg + (uint32_t)(2 * t) * sb_arr)[e];
-                const St bv = reinterpret_cast<const St*>(sbg + (uint32_t)(2 * t + 1) * sb_arr)[e];
-                o[t] = orient<BITS>(E::to_f32(sv), E::to_f32(bv));
-                natural_pairs<BITS, DT>(wo, o[t].flip, cp[t]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int p = 0; p < MP; ++p) {
-                // Operand A: row i = r16 of A is activation row p MS + i % MS of
-                // group slot i / MS; a lane whose slot is not its unit's reads
-                // the zero fragment.
-                const int m = p * MS + (r16 % MS);
-                const bool match = (r16 / MS) == gslot;
-                const char* ab = match
-                    ? table + (uint32_t)m * (uint32_t)sh.row_stride +
-                          (uint32_t)(32 * (4 * c + g)) * 2u
-                    : zero;
-                const int astep = match ? 16 : 0;
-                frag_t af[4];
-#pragma unroll
-                for (int im = 0; im < 4; ++im)
-                    af[im] = *reinterpret_cast<const frag_t*>(ab + im * astep);
-                // This lane's four output rows: activation rows
-                // p MS + (4 g + r) % MS of its own group slot.
-                const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(
-                    xg + ((uint32_t)grp * (uint32_t)sh.mt + (uint32_t)(p * MS + (4 * g) % MS)) * 4u);
+            auto fetch = [&](int j, auto Q, Slot& sl) {
+                constexpr int q = decltype(Q)::value;
+                const uint32_t rgi = (uint32_t)(j / NQ);
+                const uint32_t woff = wbase + rgi * wstep + (uint32_t)(q * UI * 4 * BITS);
 #pragma unroll
                 for (int t = 0; t < NMAT; ++t) {
-                    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+                    skinny_load<BITS>(rw[t], woff, sl.w[t]);
+                    if constexpr (q == 0) {
 #pragma unroll
-                    for (int im = 0; im < 4; ++im)
-                        d = M16::mma(af[im],
-                                     __builtin_bit_cast(frag_t, u32x4_t{cp[t][4 * im], cp[t][4 * im + 1],
-                                                                         cp[t][4 * im + 2], cp[t][4 * im + 3]}),
-                                     d);
+                        for (int i = 0; i < SBL; ++i) {
+                            sl.sb[t][0][i] = __builtin_amdgcn_raw_buffer_load_b16(rs[t], sboff[i] + rgi * sstep, 0, 0);
+                            sl.sb[t][1][i] = __builtin_amdgcn_raw_buffer_load_b16(rb[t], sboff[i] + rgi * sstep, 0, 0);
+                        }
+                    }
+                }
+            };
+            static_for<D>([&](auto J) {
+                fetch((int)J, std::integral_constant<int, (int)J % NQ>{}, ring[J]);
+                __builtin_amdgcn_sched_barrier(0);   // slot by slot, in order
+            });
+
+            if (staged) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[t][p][r] = __builtin_fmaf(o[t].s, d[r], __builtin_fmaf(o[t].b, xs[r], acc[t][p][r]));
+                for (int r = 0; r < 16; ++r)
+                    *reinterpret_cast<u32x4_t*>(xst + (uint32_t)r * kSkinnyXRow + 16u * (uint32_t)lane) = raw[r];
+#pragma unroll
+                for (int u = 0; u < kSkinnyKW; ++u) {
+                    const int ur = (u / UI) * UI + frag_unit<XG>(u % UI, g);
+                    raw[u] = *reinterpret_cast<const u32x4_t*>(
+                        xst + (uint32_t)l16 * kSkinnyXRow + (uint32_t)(ur * 32 + 8 * frag_slice<XG>(u % UI, g)) * 2u);
+                }
+            }
+            // Activation slots in the codes' pair order.
+            frag_t xa[kSkinnyKW];
+#pragma unroll
+            for (int u = 0; u < kSkinnyKW; ++u) {
+                u32x4_t v = raw[u];
+                if constexpr (W::EO)
+                    v = u32x4_t{__builtin_amdgcn_perm(raw[u].y, raw[u].x, 0x05040100u),
+                                __builtin_amdgcn_perm(raw[u].w, raw[u].z, 0x05040100u),
+                                __builtin_amdgcn_perm(raw[u].y, raw[u].x, 0x07060302u),
+                                __builtin_amdgcn_perm(raw[u].w, raw[u].z, 0x07060302u)};
+                xa[u] = __builtin_bit_cast(frag_t, v);
+            }
+
+            // Group sums of the slice's activations: per unit a dot2 against
+            // (1, 1) per pair, per group over its units, then over the four
+            // lane rows; stored as xsw[group][row].
+            static_for<kSkinnyKW / GU>([&](auto GI) {
+                constexpr int gi = decltype(GI)::value;
+                float p = 0.f;
+#pragma unroll
+                for (int u = gi * GU; u < gi * GU + GU; ++u) {
+                    const u32x4_t v = __builtin_bit_cast(u32x4_t, xa[u]);
+                    p = M16::pair_sum(v.x, p);
+                    p = M16::pair_sum(v.y, p);
+                    p = M16::pair_sum(v.z, p);
+                    p = M16::pair_sum(v.w, p);
+                }
+                p = rows_sum(p);
+                if (g == 0)
+                    reinterpret_cast<float*>(xsw)[gi * 16 + l16] = p;
+            });
+
+            f32x4_t acc[NMAT];
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t)
+                acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+            auto process = [&](int j, auto Q, const Slot& sl) {
+                constexpr int q = decltype(Q)::value;
+                __builtin_amdgcn_sched_barrier(0);
+                // Orientation of the lane's group(s); then every lane gets the item's NG.
+                float se[NMAT][NG], be[NMAT][NG];
+                uint32_t fl[NMAT][NG];
+                // The slot is read here and not earlier: an empty asm per
+                // value keeps the compiler from hoisting work on it (which
+                // would wait for its load before earlier items run).
+                uint32_t sv[NMAT][NGL], bv[NMAT][NGL];
+                uint32_t cw[NMAT][LW];
+#pragma unroll
+                for (int t = 0; t < NMAT; ++t) {
+                    if constexpr (q == 0) {
+                        // The row group's scales and biases to LDS.
+#pragma unroll
+                        for (int i = 0; i < SBL; ++i) {
+                            uint32_t a0 = sl.sb[t][0][i], a1 = sl.sb[t][1][i];
+                            asm volatile("" : "+v"(a0), "+v"(a1));
+                            sbw[(t * 2 + 0) * 16 * NGS + lane + 64 * i] = (uint16_t)a0;
+                            sbw[(t * 2 + 1) * 16 * NGS + lane + 64 * i] = (uint16_t)a1;
+                        }
+                    }
+#pragma unroll
+                    for (int h = 0; h < NGL; ++h) {
+                        const int e = l16 * NGS + q * NG + lane_grp + 4 * h;
+                        sv[t][h] = sbw[(t * 2 + 0) * 16 * NGS + e];
+                        bv[t][h] = sbw[(t * 2 + 1) * 16 * NGS + e];
+                    }
+#pragma unroll
+                    for (int i = 0; i < W::WORDS; ++i) {
+                        cw[t][i] = sl.w[t][i];
+                        asm volatile("" : "+v"(cw[t][i]));
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NMAT; ++t) {
+#pragma unroll
+                    for (int h = 0; h < NGL; ++h) {
+                        const Orient o = orient<BITS>(E::to_f32((St)sv[t][h]), E::to_f32((St)bv[t][h]));
+                        const uint32_t vs = __builtin_bit_cast(uint32_t, o.s), vb = __builtin_bit_cast(uint32_t, o.b);
+                        if constexpr (NG == 1) {
+                            se[t][0] = o.s;
+                            be[t][0] = o.b;
+                            fl[t][0] = o.flip;
+                        } else if constexpr (NG == 2) {
+                            uint32_t s2[2], b2[2], f2[2];
+                            rows_gather2(vs, s2);
+                            rows_gather2(vb, b2);
+                            rows_gather2(o.flip, f2);
+#pragma unroll
+                            for (int i = 0; i < 2; ++i) {
+                                se[t][i] = __builtin_bit_cast(float, s2[i]);
+                                be[t][i] = __builtin_bit_cast(float, b2[i]);
+                                fl[t][i] = f2[i];
+                            }
+                        } else {
+                            uint32_t s4[4], b4[4], f4[4];
+                            rows_gather4(vs, s4);
+                            rows_gather4(vb, b4);
+                            rows_gather4(o.flip, f4);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                se[t][4 * h + i] = __builtin_bit_cast(float, s4[i]);
+                                be[t][4 * h + i] = __builtin_bit_cast(float, b4[i]);
+                                fl[t][4 * h + i] = f4[i];
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NMAT; ++t)
+                    W::template prepare<GU>(cw[t]);
+                __builtin_amdgcn_sched_barrier(0);
+                static_for<NG>([&](auto JG) {
+                    constexpr int jg = decltype(JG)::value;
+                    const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(
+                        xsw + (uint32_t)(((q * NG + jg) * 16 + 4 * g) * 4));
+#pragma unroll
+                    for (int t = 0; t < NMAT; ++t) {
+                        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+                        static_for<GU>([&](auto UU) {
+                            constexpr int i = jg * GU + decltype(UU)::value;
+                            const u32x4_t bw = W::template frag<DT, i>(cw[t], fl[t][jg]);
+                            d = M16::mma(xa[q * UI + i], __builtin_bit_cast(frag_t, bw), d);
+                        });
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[t][r] = __builtin_fmaf(se[t][jg], d[r], __builtin_fmaf(be[t][jg], xs[r], acc[t][r]));
+                    }
+                });
+                // Last item of a row group: its partial sums go to LDS.
+                if constexpr (q == NQ - 1) {
+                    const int rgi = j / NQ;
+#pragma unroll
+                    for (int t = 0; t < NMAT; ++t) {
+                        f32x4_t* dst = reinterpret_cast<f32x4_t*>(
+                            red + ((uint32_t)(rgi * NMAT + t) * 64u + (uint32_t)lane) * 16u);
+                        if (si == 0)
+                            *dst = acc[t];
+                        else
+                            *dst = *dst + acc[t];
+                        acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-        for (int j0 = 0; j0 < nj; j0 += D) {
-            static_for<D>([&](auto J) {
-                const int j = j0 + (int)J;
-                if (j < nj) {
-                    process(j, w[J]);
-                    fetch(j + D, w[J]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+            };
+            // The whole item sequence of a slice, unrolled: ring slots are
+            // never carried around a loop or through a branch (either makes
+            // the compiler copy a slot, which waits for its load to land).
+            // Refills past the wave's items read zeros.
+            static_for<kSkinnyRG * NQ>([&](auto JJ) {
+                constexpr int j = decltype(JJ)::value;
+                if (j < nitems)
+                    process(j, std::integral_constant<int, j % NQ>{}, ring[j % D]);
+                if constexpr (j + D < kSkinnyRG * NQ)
+                    fetch(j + D, std::integral_constant<int, j % NQ>{}, ring[j % D]);
             });
         }
 
-        // 5. Group slots of one activation row meet (lanes g apart), then the
-        //    K-split waves meet in LDS (over the table, which every wave is
-        //    done with).
-#pragma unroll
-        for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-            for (int p = 0; p < MP; ++p)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = acc[t][p][r];
-                    if constexpr (SLOTS == 4)
-                        v += __shfl_xor(v, 16, 64);
-                    if constexpr (SLOTS >= 2)
-                        v += __shfl_xor(v, 32, 64);
-                    acc[t][p][r] = v;
-                }
+        // The K-slices of each row group meet; lanes store weight row
+        // n = 16 rg + l16 against activation rows 4g .. 4g+3.
         __syncthreads();
-        if (sh.ks > 1) {
-            if (ks != 0) {
+        const int kmax = sh.ks < sh.slices ? sh.ks : sh.slices;
+        for (int rg = wave; rg < nrg_b; rg += nwaves) {
+            const int wr_of = rg % sh.wr, rgi = rg / sh.wr;
+            f32x4_t tot[NMAT];
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t)
+                tot[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int k2 = 0; k2 < kmax; ++k2) {
+                const int w2 = k2 * sh.wr + wr_of;
 #pragma unroll
                 for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-                    for (int p = 0; p < MP; ++p)
-                        *reinterpret_cast<f32x4_t*>(lds + ((uint32_t)((wave * NMAT + t) * MP + p) * 64u +
-                                                           (uint32_t)lane) * 16u) = acc[t][p];
+                    tot[t] += *reinterpret_cast<const f32x4_t*>(
+                        lds + (uint32_t)w2 * WL + ((uint32_t)(rgi * NMAT + t) * 64u + (uint32_t)lane) * 16u);
             }
-            __syncthreads();
-            if (ks == 0) {
-                for (int k2 = 1; k2 < sh.ks; ++k2) {
+            const int n = r_lo + 16 * rg + l16;
 #pragma unroll
-                    for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-                        for (int p = 0; p < MP; ++p)
-                            acc[t][p] += *reinterpret_cast<const f32x4_t*>(
-                                lds + ((uint32_t)(((wave + k2) * NMAT + t) * MP + p) * 64u + (uint32_t)lane) * 16u);
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * g + r;
+                float v = tot[0][r];
+                if constexpr (NMAT == 2)
+                    v = silu_f32(tot[0][r]) * tot[1][r];
+                uint32_t off = OOB;
+                if (m < rows && n < r_hi) {
+                    const uint32_t pr = a.perm != nullptr ? (uint32_t)a.perm[start + m] : (uint32_t)(start + m);
+                    off = (pr * (uint32_t)R + (uint32_t)n) * (uint32_t)SB;
                 }
+                buffer_store_elem<DT>(E::from_f32(v), ro, off);
             }
         }
-
-        // 6. Lanes of group slot 0 store: weight row n0 + r16, activation rows
-        //    p MS + 4 g + r.
-        if (ks == 0 && (4 * g) < MS) {
-            const int n = n0 + r16;
-#pragma unroll
-            for (int p = 0; p < MP; ++p)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = p * MS + 4 * g + r;
-                    float v = acc[0][p][r];
-                    if constexpr (NMAT == 2)
-                        v = silu_f32(acc[0][p][r]) * acc[1][p][r];
-                    uint32_t off = OOB;
-                    if (m < rows && n < r_hi && rg < sh.n_rg) {
-                        const uint32_t pr = a.perm != nullptr ? (uint32_t)a.perm[start + m]
-                                                              : (uint32_t)(start + m);
-                        off = (pr * (uint32_t)R + (uint32_t)n) * (uint32_t)SB;
-                    }
-                    buffer_store_elem<DT>(E::from_f32(v), ro, off);
-                }
-        }
-        // Every wave is done with the table and the partial sums before the
-        // next tile refills them.
+        // Every wave is done with the partial sums before the next tile.
         __syncthreads();
     }
 }
@@ -539,94 +701,72 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny_kernel(Gemv
 
 namespace qp {
 
-// Group slots per 128-k chunk for a group size, and the passes that cover
-// `rows` activation rows (1, 2 or 4 passes of 16 / slots rows).
-inline int skinny_slots(int gs) { return gs == 128 ? 1 : gs == 64 ? 2 : 4; }
-inline int skinny_passes(int rows, int gs)
-{
-    const int ms = 16 / skinny_slots(gs);
-    const int mp = (rows + ms - 1) / ms;
-    return mp <= 1 ? 1 : mp <= 2 ? 2 : 4;
-}
-
 // Launch one instance (the LDS size is set once per instance).
-template <int BITS, int DT, int NMAT, int SLOTS, int MP>
+template <int BITS, int DT, int NMAT, int GU>
 hipError_t skinny_launch_one(const GemvKernelArgs& k, const SkinnyShape& sh, dim3 grid, hipStream_t st)
 {
-    if constexpr (MP * (16 / SLOTS) > 16) {
-        return hipErrorInvalidValue;
-    } else {
-        static bool attr_set = false;   // per instantiation; set before its first launch
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute(
-                reinterpret_cast<const void*>(&qgemv_skinny_kernel<BITS, DT, NMAT, SLOTS, MP>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyLdsBytes);
-            if (e != hipSuccess)
-                return e;
-            attr_set = true;
-        }
-        const int waves = sh.n_rg * sh.ks;
-        const uint32_t lds = skinny_lds_bytes(k.K, k.gs, sh.mt, waves, MP, NMAT, sh.ks);
-        hipLaunchKernelGGL((qgemv_skinny_kernel<BITS, DT, NMAT, SLOTS, MP>), grid, dim3(64 * waves), lds,
-                           st, k, sh);
-        return hipGetLastError();
+    static bool attr_set = false;   // per instantiation; set before its first launch
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemv_skinny_kernel<BITS, DT, NMAT, GU>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)skinny_lds_bytes(kSkinnyMaxWaves, NMAT));
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
     }
+    const int waves = sh.ks * sh.wr;
+    hipLaunchKernelGGL((qgemv_skinny_kernel<BITS, DT, NMAT, GU>), grid, dim3(64 * waves),
+                       skinny_lds_bytes(waves, NMAT), st, k, sh);
+    return hipGetLastError();
 }
 
 template <int BITS, int DT, int NMAT>
 hipError_t skinny_launch(const GemvKernelArgs& k, const SkinnyShape& sh, dim3 grid, hipStream_t st)
 {
-    const int slots = skinny_slots(k.gs), mp = sh.mt / (16 / slots);
-    switch (slots * 8 + mp) {
-    case 1 * 8 + 1: return skinny_launch_one<BITS, DT, NMAT, 1, 1>(k, sh, grid, st);
-    case 2 * 8 + 1: return skinny_launch_one<BITS, DT, NMAT, 2, 1>(k, sh, grid, st);
-    case 2 * 8 + 2: return skinny_launch_one<BITS, DT, NMAT, 2, 2>(k, sh, grid, st);
-    case 4 * 8 + 1: return skinny_launch_one<BITS, DT, NMAT, 4, 1>(k, sh, grid, st);
-    case 4 * 8 + 2: return skinny_launch_one<BITS, DT, NMAT, 4, 2>(k, sh, grid, st);
-    case 4 * 8 + 4: return skinny_launch_one<BITS, DT, NMAT, 4, 4>(k, sh, grid, st);
+    switch (k.gs) {
+    case 32: return skinny_launch_one<BITS, DT, NMAT, 1>(k, sh, grid, st);
+    case 64: return skinny_launch_one<BITS, DT, NMAT, 2>(k, sh, grid, st);
+    case 128: return skinny_launch_one<BITS, DT, NMAT, 4>(k, sh, grid, st);
     }
     return hipErrorInvalidValue;
 }
 
-// Table rows (a multiple of 16 / slots, at most 16) for `rows` activation
-// rows, shrunk until the table of a K-long row fits the LDS; 0 if not even
-// one pass fits.
-inline int skinny_table_rows(int rows, int64_t K, int gs, int waves, int nmat, int ks)
+// Waves along K (one per slice, at most 8) and along row groups (the rest of
+// the 8 waves, at most the row groups there are).
+inline SkinnyShape skinny_waves(int64_t K, int64_t rgs_per_block)
 {
-    const int ms = 16 / skinny_slots(gs);
-    for (int mp = skinny_passes(rows < 16 ? rows : 16, gs); mp >= 1; mp /= 2)
-        if (skinny_lds_bytes(K, gs, mp * ms, waves, mp, nmat, ks) <= kSkinnyLdsBytes)
-            return mp * ms;
-    return 0;
+    SkinnyShape sh{};
+    const int64_t units = K / 32;
+    sh.slices = (int)((units + kSkinnyKW - 1) / kSkinnyKW);
+    sh.ks = sh.slices < kSkinnyMaxWaves ? sh.slices : kSkinnyMaxWaves;
+    int64_t wr = kSkinnyMaxWaves / sh.ks;
+    wr = wr < rgs_per_block ? wr : rgs_per_block;
+    sh.wr = (int)(wr < 1 ? 1 : wr);
+    return sh;
 }
 
-// Dense launch shape: about one block per CU over contiguous row ranges, up to
-// 8 waves per block as groups of 16 rows times waves along K.
-inline void skinny_dense_shape(int64_t N, int64_t K, int mt, SkinnyShape* sh, dim3* grid)
+// Dense shape: about one block per CU over contiguous row ranges.
+inline void skinny_dense_shape(int64_t N, int64_t K, SkinnyShape* sh, dim3* grid)
 {
-    const int64_t nrg = (N + 15) / 16;
-    const int nc = (int)((K + 127) / 128);
-    int64_t blocks;
-    int rows;
-    if (nrg >= 256) {
-        blocks = 256;
-        rows = (int)((N + 255) / 256);
-        if ((rows + 15) / 16 > kSkinnyMaxWaves) {
-            rows = 16 * kSkinnyMaxWaves;
-            blocks = (N + rows - 1) / rows;
-        }
-    } else {
-        blocks = nrg;
-        rows = 16;
-    }
-    sh->rows_per_block = rows;
-    sh->n_rg = (rows + 15) / 16;
-    int ks = kSkinnyMaxWaves / sh->n_rg;
-    ks = ks < 1 ? 1 : (ks > nc ? nc : ks);
-    sh->ks = ks;
-    sh->mt = mt;
-    sh->row_stride = skinny_row_stride(K);
-    *grid = dim3((unsigned)blocks, 1);
+    int64_t rpb = (N + 255) / 256;
+    rpb = rpb < 16 ? 16 : rpb;
+    *sh = skinny_waves(K, (rpb + 15) / 16);
+    const int64_t cap = 16 * (int64_t)sh->wr * kSkinnyRG;
+    rpb = rpb < cap ? rpb : cap;
+    sh->rows_per_block = (int)rpb;
+    *grid = dim3((unsigned)((N + rpb - 1) / rpb), 1);
+}
+
+// MoE shape: row blocks per tile, fewer rows per block until the largest
+// possible tile list gives about 512 blocks.
+inline void skinny_moe_shape(int64_t R, int64_t K, int64_t max_tiles, SkinnyShape* sh, unsigned* gx)
+{
+    *sh = skinny_waves(K, (R + 15) / 16);
+    int rgw = kSkinnyRG;
+    while (rgw > 1 && max_tiles * ((R + 16 * sh->wr * rgw - 1) / (16 * sh->wr * rgw)) < 512)
+        rgw /= 2;
+    sh->rows_per_block = 16 * sh->wr * rgw;
+    *gx = (unsigned)((R + sh->rows_per_block - 1) / sh->rows_per_block);
 }
 
 } // namespace qp
