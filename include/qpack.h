@@ -52,7 +52,16 @@
 extern "C" {
 #endif
 
-typedef enum qp_status {
+/* The enums are int-sized in C and C++ alike; in C++ they have int as their
+ * fixed underlying type, so that any int a caller passes (an out-of-range
+ * one included, which the calls reject) is a valid value of the type. */
+#ifdef __cplusplus
+#define QP_ENUM(name) enum name : int
+#else
+#define QP_ENUM(name) enum name
+#endif
+
+typedef QP_ENUM(qp_status) {
     QP_OK = 0,
     QP_ERR_INVALID_ARG = 1,    /* null pointer, negative size, size overflow */
     QP_ERR_UNSUPPORTED = 2,    /* bits not in {2,3,4,6,8}, group_size not in {32,64,128} */
@@ -63,7 +72,7 @@ typedef enum qp_status {
     QP_ERR_HIP = 7             /* a HIP launch failed */
 } qp_status;
 
-typedef enum qp_dtype { QP_F32 = 0, QP_F16 = 1, QP_BF16 = 2 } qp_dtype;
+typedef QP_ENUM(qp_dtype) { QP_F32 = 0, QP_F16 = 1, QP_BF16 = 2 } qp_dtype;
 
 /* Microscaled modes (emily "Defn-native dequantize", the mxfp4 / mxfp8 /
  * nvfp4 implementations; group sizes as in ollama quantize.go
@@ -73,7 +82,7 @@ typedef enum qp_dtype { QP_F32 = 0, QP_F16 = 1, QP_BF16 = 2 } qp_dtype;
  *   QP_NVFP4: 4-bit FP4-E2M1 lanes, groups of 16, FP8-E4M3 scales.
  * FP8-E4M3 is decoded as MLX decodes it: bias 7, subnormals, and no NaN
  * (0x7F / 0xFF are +-480). Lanes are packed as in the affine mode. */
-typedef enum qp_mode { QP_MXFP4 = 1, QP_MXFP8 = 2, QP_NVFP4 = 3 } qp_mode;
+typedef QP_ENUM(qp_mode) { QP_MXFP4 = 1, QP_MXFP8 = 2, QP_NVFP4 = 3 } qp_mode;
 
 /*
  * Affine group quantization (ollama quantize.go `loadAndQuantizeArray`,
@@ -193,7 +202,12 @@ size_t qgemv_moe_workspace_bytes(int64_t n_pairs, int64_t num_experts);
  * device and grouped into tiles of one expert, so each expert's weights are
  * streamed once per tile (with at most one pair per expert on average every
  * pair is its own tile and the sort is skipped). A pair whose id is out of
- * range is skipped (its output row is left unwritten).
+ * range is skipped (its output row is left unwritten). When the pairs are
+ * sorted, the workspace afterwards begins with two device-written int32: the
+ * number of tiles and the number of pairs skipped for an out-of-range id
+ * (read them once the stream has synchronised). The order of one expert's
+ * pairs in the sort is not specified (they are scattered with atomics);
+ * every pair's output row is computed on its own, so it changes no value.
  */
 qp_status qgemv_moe_id(const void* a, qp_dtype a_dtype, const int32_t* ids,
                        int64_t n_tokens, int64_t top_k, int64_t a_outer_stride,

@@ -198,29 +198,33 @@ def sampled_check(y, xs, dt, rq, rs, rb, k, bits, gs, n_samples=3000, seed=0, ta
 
 @pytest.mark.parametrize("bits", [4, 8, 2])
 @pytest.mark.parametrize("m", [1, 4, 16])
-def test_qmatmul_decode_config_sampled(bits, m):
-    """W [14336, 4096] N(0, 0.02) (seed 21), gs64, bf16 scales; x bf16 [m, 4096] (seed 22)."""
+def test_qmatmul_decode_config_full(bits, m):
+    """W [14336, 4096] N(0, 0.02) (seed 21), gs64, bf16 scales; x bf16 [m, 4096]
+    (seed 22). Every output against the oracle (at most 16 x 14336 of them)."""
     log(f"decode config bits={bits} m={m}")
     w = synth.normal_f32((14336, 4096), 0.02, 21)
     (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, bits, 64, BF16)
     xs, xt = activations((m, 4096), BF16, 22)
     y = qp.qmatmul(xt, gq, gs_, gb, bits, 64)
     torch.cuda.synchronize()
-    sampled_check(y, xs, BF16, rq, rs, rb, 4096, bits, 64, seed=bits * 100 + m)
+    y_ref, S = qref.qmatmul(xs, BF16, rq, rs, rb, BF16, 4096, bits, 64)
+    assert_within(y, y_ref, S, BF16, f"decode config b{bits} m{m}")
 
 
 @pytest.mark.parametrize("bits", [3, 6])
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("m", [1, 8])
-def test_qmatmul_cross_word_config_sampled(bits, gs, m):
-    """W [4096, 4096] N(0, 0.02) (seed 31), fp16 scales; x fp16 [m, 4096] (seed 32)."""
+def test_qmatmul_cross_word_config_full(bits, gs, m):
+    """W [4096, 4096] N(0, 0.02) (seed 31), fp16 scales; x fp16 [m, 4096]
+    (seed 32). Every output against the oracle."""
     log(f"cross-word config bits={bits} gs={gs} m={m}")
     w = synth.normal_f32((4096, 4096), 0.02, 31)
     (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, bits, gs, F16)
     xs, xt = activations((m, 4096), F16, 32)
     y = qp.qmatmul(xt, gq, gs_, gb, bits, gs)
     torch.cuda.synchronize()
-    sampled_check(y, xs, F16, rq, rs, rb, 4096, bits, gs, seed=bits * 10 + gs + m)
+    y_ref, S = qref.qmatmul(xs, F16, rq, rs, rb, F16, 4096, bits, gs)
+    assert_within(y, y_ref, S, F16, f"cross-word config b{bits} gs{gs} m{m}")
 
 
 @pytest.mark.parametrize("m", [17, 64, 100, 257])

@@ -154,15 +154,6 @@ size_t moe_workspace_bytes(int64_t n_pairs, int64_t num_experts)
 
 namespace {
 
-#ifdef QP_TUNING
-// Path override for tuning builds only (never defined in the library).
-int tuning_env_moe(const char* name, int dflt)
-{
-    const char* v = getenv(name);
-    return v ? atoi(v) : dflt;
-}
-#endif
-
 int pick_mt(int64_t P, int64_t E, int mtmax)
 {
     int mt = 1;
@@ -238,14 +229,7 @@ int moe_rowmfma_mt(const MoeArgs& a)
     // 128 experts ([768, 2048] matrices, 4-bit), where the 16-pair
     // matrix-core tiles took it. At 128 and 1024 pairs, and for the plain
     // down projection (against the routed GEMM), it was slower.
-#ifdef QP_TUNING
-    const int force = tuning_env_moe("QP_MOE_ROW", -1);
-    if (force == 0)
-        return 0;
-    const bool dense_enough = force == 1 || (a.fused_silu && P >= 2 * a.E && P <= 4 * a.E);
-#else
     const bool dense_enough = a.fused_silu && P >= 2 * a.E && P <= 4 * a.E;
-#endif
     if (!dense_enough)
         return 0;
     const int64_t es = 2;
@@ -264,11 +248,6 @@ bool moe_rowstream_ok(const MoeArgs& a, int mt)
     if (mt != 1 || a.dt == DT_F32 || !(a.bits == 2 || a.bits == 4 || a.bits == 8) ||
         a.n_cols % 32 != 0 || a.n_cols > 4096)
         return false;
-#ifdef QP_TUNING
-    const int force = tuning_env_moe("QP_MOE_ROWS1", -1);
-    if (force >= 0)
-        return force == 1;
-#endif
     // Measured on 128 experts, 4-bit ([768, 2048] gate / up, [2048, 768]
     // down), device time of graph-replayed calls: the fused form 6.4 against
     // 6.8 us at 8 pairs, 8.1 against 9.0 at 16, 13.1 against 16.1 at 32, 22.6

@@ -177,15 +177,6 @@ hipError_t run_rowmfma_tiles(const GemvKernelArgs& k, int64_t max_tiles, hipStre
     }
 }
 
-#ifdef QP_TUNING
-// Path override for tuning builds only (never defined in the library).
-int tuning_env_kl(const char* name, int dflt)
-{
-    const char* v = getenv(name);
-    return v ? atoi(v) : dflt;
-}
-#endif
-
 // One-pair tiles on the dot-product row kernel (moe_rows.hpp): grid x covers
 // the expert's rows 4 D at a time, y strides over the tiles.
 template <int BITS, int DT, int NMAT, int UPL, int KL>
@@ -206,11 +197,7 @@ hipError_t run_rowstream_tiles(const GemvKernelArgs& k, int64_t max_tiles, hipSt
 {
     if constexpr ((BITS == 2 || BITS == 4 || BITS == 8) && DT != DT_F32) {
         const int64_t units = k.K / 32;
-#ifdef QP_TUNING
-        const bool narrow = units <= 32 && tuning_env_kl("QP_MOE_KL32", 1) != 0;
-#else
         const bool narrow = units <= 32;
-#endif
         if (narrow) return run_rowstream_tiles_upl<BITS, DT, NMAT, 1, 32>(k, max_tiles, st);
         if (units <= 64) return run_rowstream_tiles_upl<BITS, DT, NMAT, 1, 64>(k, max_tiles, st);
         if (units <= 128) return run_rowstream_tiles_upl<BITS, DT, NMAT, 2, 64>(k, max_tiles, st);

@@ -52,14 +52,6 @@ GemvKernelArgs dense_args(const GemvArgs& a, int64_t m0, int mc, int elem_size, 
     return k;
 }
 
-#ifdef QP_TUNING
-// Launch-shape override for tuning builds only (never defined in the library).
-int tuning_env(const char* name, int dflt)
-{
-    const char* v = getenv(name);
-    return v ? atoi(v) : dflt;
-}
-#endif
 
 // Launch shape: at most one block per CU (256 blocks) holding W waves
 // (4 <= W <= 10) so that all CUs get the same share; each wave keeps D rows
@@ -83,10 +75,6 @@ hipError_t run_fast(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
     W = W < 4 ? 4 : (W > WMAX ? WMAX : W);
     int64_t blocks = (waves + W - 1) / W;
     blocks = blocks < kCUs ? blocks : kCUs;
-#ifdef QP_TUNING
-    W = tuning_env("QP_GEMV_W", (int)W);
-    blocks = tuning_env("QP_GEMV_BLOCKS", (int)blocks);
-#endif
     GemvKernelArgs k = dense_args(a, m0, mc, (int)sizeof(St<DT>), KL);
     hipLaunchKernelGGL((qgemv_stream_kernel<BITS, DT, MT, U, G, KL, 1, MAXT>),
                        dim3((int)blocks), dim3((int)W * 64), 0, st, k);
@@ -209,25 +197,11 @@ hipError_t run_rowstream(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
         };
         // Rows of at most 32 units: two rows side by side in a wave.
         if constexpr (UPL == 1) {
-#ifdef QP_TUNING
-            if (a.K <= 32 * 32 && tuning_env("QP_RS_KL32", 1) != 0)
-#else
             if (a.K <= 32 * 32)
-#endif
                 return go(std::integral_constant<int, 32>{});
         }
         return go(std::integral_constant<int, 64>{});
     };
-#ifdef QP_TUNING
-    switch (tuning_env("QP_RS_WPB", 4)) {
-    case 2: return launch(std::integral_constant<int, 2>{});
-    case 7: return launch(std::integral_constant<int, 7>{});
-    case 8: return launch(std::integral_constant<int, 8>{});
-    case 14: return launch(std::integral_constant<int, 14>{});
-    case 16: return launch(std::integral_constant<int, 16>{});
-    default: break;
-    }
-#endif
     return launch(std::integral_constant<int, 4>{});
 }
 
@@ -235,11 +209,7 @@ template <int BITS, int DT, int MT>
 hipError_t run_rowstream_upl(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
 {
     const int64_t upl = (a.K / 32 + 63) / 64;
-#ifdef QP_TUNING
-    const bool exact = tuning_env("QP_RS_EXACT_UPL", 1) != 0;
-#else
     constexpr bool exact = true;
-#endif
     if (upl <= 1) return run_rowstream<BITS, DT, MT, 1>(a, m0, mc, st);
     if (upl <= 2) return run_rowstream<BITS, DT, MT, 2>(a, m0, mc, st);
     if (exact && upl <= 3) return run_rowstream<BITS, DT, MT, 3>(a, m0, mc, st);
@@ -308,13 +278,9 @@ hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
     if (!x_vec || !small)
         return run_generic<BITS, DT>(a, st);
     if constexpr (DT != DT_F32) {
-#ifdef QP_TUNING
-        const int min_m = tuning_env("QP_MFMA_MIN_M", 3);
-#else
         // Two rows stream faster with dot products (measured 15.0 vs 16.4 us
         // on the 14336 x 4096 decode shape); three and more go to the matrix cores.
         constexpr int min_m = 3;
-#endif
         // Three and four rows: measured 12.0 us at 4 bits on 14336 x 4096
         // (15.5 on the tile path below, 14.6 with dot products on four
         // activation rows); one and two rows stay on the dot-product stream
