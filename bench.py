@@ -20,6 +20,7 @@ at decode, prefill and dense-weight shapes.
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
   python bench.py --copy-calibration   # plain 1 GiB copies, to scale HBM counters
+  python bench.py --case NAME          # one workload (profiler runs); NAME in CASES
 """
 from __future__ import annotations
 
@@ -41,11 +42,11 @@ ROTATE_BYTES = 2 * MALL_BYTES
 CSRC = os.path.join(ROOT, "weight_only_quantized_qgemv_amd", "csrc")
 
 # HBM traffic of the headline kernel per launch, from two rocprofv3 --pmc runs
-# (FETCH_SIZE, WRITE_SIZE) of `bench.py --steps 20 --warmup 2 --no-rows
-# --no-cpu-baseline`, each scaled by the same counter on a plain 1 GiB copy.
+# (FETCH_SIZE, WRITE_SIZE) of `bench.py --case decode_b4_m1 --steps 20
+# --warmup 2`, each scaled by the same counter on a plain 1 GiB copy.
 # It holds only while the decode kernel's sources are the ones it was taken on.
-TRAFFIC = {"src_sha": "c5b7afb7069cdae8", "fetch_bytes": 33207414, "write_bytes": 28672,
-           "fetch_scale": 1.9999, "write_scale": 1.0}
+TRAFFIC = {"src_sha": "53f0d1d4b3460c6c", "fetch_bytes": 33204634, "write_bytes": 57344,
+           "fetch_scale": 2.0, "write_scale": 1.0}
 DECODE_SOURCES = ("rowstream.hpp", "codepair.hpp", "gemv_core.hpp", "common.hpp", "qgemv.hip")
 
 
@@ -221,9 +222,24 @@ def bench_mx(mode, M, steps, warmup, stream, dev, no_nan_codes=False, what="matm
     return ms, wb
 
 
+def moe_id_sets(T, top_k, E):
+    """Expert-id sets the MoE rows cycle through. One token touches only top_k
+    experts, so at T = 1 the calls walk a seeded permutation of all E experts
+    in disjoint sets of top_k (with two weight sets, every expert's weights of
+    both sets pass once per cycle: far more than the Infinity Cache holds).
+    Larger T touch nearly every expert per call and keep one id set."""
+    import numpy as np
+    from weight_only_quantized_qgemv_amd import synth
+    if T == 1:
+        perm = synth.rng(57).permutation(E).astype(np.int32)
+        return [perm[i:i + top_k] for i in range(0, E - top_k + 1, top_k)]
+    return [synth.moe_ids(T, top_k, E, seed=55).ravel()]
+
+
 def bench_moe(T, steps, warmup, stream, dev):
     """Gate+up+SiLU then down of a 128-expert top-8 MoE block (d = 2048,
-    ffn = 768), 4-bit gs64 bf16; two weight sets alternate."""
+    ffn = 768), 4-bit gs64 bf16; two weight sets alternate, and at T = 1 the
+    expert ids cycle through disjoint sets (moe_id_sets)."""
     import numpy as np
     import torch
     import weight_only_quantized_qgemv_amd as qp
@@ -238,20 +254,24 @@ def bench_moe(T, steps, warmup, stream, dev):
         d = [t.reshape(E, D, -1) for t in make_weights(E * D, F, bits, gs, torch.bfloat16, 1,
                                                        53 + 10 * c, dev)[0]]
         wsets.append((g, u, d))
-    ids_np = synth.moe_ids(T, top_k, E, seed=55).ravel()
-    ids = torch.from_numpy(ids_np).to(dev)
+    id_sets = moe_id_sets(T, top_k, E)
+    ids_d = [torch.from_numpy(i).to(dev) for i in id_sets]
+    n_ids = len(ids_d)
     a = torch.from_numpy(synth.normal_f32((T, D), 1.0, 54)).to(torch.bfloat16).to(dev)
     P = T * top_k
     h = torch.empty((P, F), dtype=torch.bfloat16, device=dev)
     o = torch.empty((P, D), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(qp.qgemv_moe_workspace_bytes(P, E), dtype=torch.uint8, device=dev)
 
+    def pick(i):
+        return wsets[i % 2], ids_d[(i // 2) % n_ids]
+
     def gate_up(i):
-        g, u, _ = wsets[i % 2]
+        (g, u, _), ids = pick(i)
         qp.qgemv_moe_id_gate_up_silu(a, ids, T, top_k, D, 0, g, u, bits, gs, out=h, workspace=ws)
 
     def down(i):
-        _, _, d = wsets[i % 2]
+        (_, _, d), ids = pick(i)
         qp.qgemv_moe_id(h, ids, T, top_k, top_k * F, F, *d, bits, gs, out=o, workspace=ws)
 
     rw = torch.from_numpy(synth.normal_f32((P,), 0.4, 56)).to(dev)
@@ -260,20 +280,35 @@ def bench_moe(T, steps, warmup, stream, dev):
                          dtype=torch.uint8, device=dev)
 
     def ffn(i):
-        g, u, d = wsets[i % 2]
+        (g, u, d), ids = pick(i)
         qp.qgemv_moe_ffn(a, ids, rw, top_k, g, u, d, bits, gs, out=out, workspace=ffn_ws)
 
     ms_gu = time_calls(gate_up, steps, warmup, stream)
     ms_d = time_calls(down, steps, warmup, stream)
     ms_ffn = time_calls(ffn, steps, warmup, stream)
-    graph = {"gate_up_silu_us_graph": graph_ms(gate_up, 40, stream),
-             "down_us_graph": graph_ms(down, 40, stream),
-             "ffn_block_us_graph": graph_ms(ffn, 40, stream)}
-    touched = len(np.unique(ids_np))
+    graph = {"gate_up_silu_us_graph": graph_ms(gate_up, max(40, 2 * n_ids), stream),
+             "down_us_graph": graph_ms(down, max(40, 2 * n_ids), stream),
+             "ffn_block_us_graph": graph_ms(ffn, max(40, 2 * n_ids), stream)}
+    touched = int(np.mean([len(np.unique(i)) for i in id_sets]))
     per_expert = weight_bytes(F, D, bits, gs, 2)   # one [768, 2048] matrix
+    rotation = 2 * len({int(e) for i in id_sets for e in np.unique(i)}) * 3 * per_expert
     del wsets
     torch.cuda.empty_cache()
-    return ms_gu, ms_d, ms_ffn, touched, per_expert, graph
+    return ms_gu, ms_d, ms_ffn, touched, per_expert, graph, rotation
+
+
+def moe_call_bytes(T, touched, per_expert, top_k=8, D=2048, F=768, E=128):
+    """Bytes one MoE call moves at the least: the touched experts' weights, the
+    activations read, the outputs written, the ids, and the routing tables
+    (pair list and tile descriptors written, then read back)."""
+    P = T * top_k
+    route = 2 * (4 * P + 12 * (P + E))
+    gate_up = 2 * touched * per_expert + T * D * 2 + P * F * 2 + 4 * P + route
+    down = touched * per_expert + P * F * 2 + P * D * 2 + 4 * P + route
+    # The block: gate+up, down, then the weighted combine of the P rows into T.
+    ffn = 3 * touched * per_expert + T * D * 2 + 2 * P * F * 2 + 2 * P * D * 2 + T * D * 2 + \
+        4 * P * 2 + 2 * route
+    return gate_up, down, ffn
 
 
 def cpu_baseline(n, k, bits, gs, budget_s=12.0):
@@ -302,6 +337,61 @@ def cpu_baseline(n, k, bits, gs, budget_s=12.0):
                       f"OpenMP over outputs"}
 
 
+def oracle_single_core():
+    """Run in a child process with one OpenMP thread: the oracle on the small
+    dense workload (W[256,1024], M = 1 and 8), one headline decode call
+    (W[14336,4096], M = 1), one MoE T = 1 call (gate+up+SiLU then down over
+    8 of 128 experts), and the quantizer on the headline weight."""
+    import numpy as np
+    from oracle import qref
+    from weight_only_quantized_qgemv_amd import synth
+
+    def timed(fn, min_s=0.5):
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= min_s:
+                return el / runs
+
+    out = {"cores": qref.num_threads()}
+    w1 = synth.normal_f32((256, 1024), 0.02, 11)
+    q1 = qref.quantize(w1, 4, 64, qref.F32)
+    for m in (1, 8):
+        x = synth.normal_f32((m, 1024), 1.0, 12)
+        out[f"tiny_256x1024_m{m}_ms"] = round(1e3 * timed(lambda: qref.qmatmul(x, qref.F32, *q1, qref.F32,
+                                                                                 1024, 4, 64)), 4)
+    w2 = synth.normal_f32((14336, 4096), 0.02, 21)
+    t0 = time.perf_counter()
+    q2 = qref.quantize(w2, 4, 64, qref.BF16)
+    out["quantize_14336x4096_b4_ms"] = round(1e3 * (time.perf_counter() - t0), 1)
+    xb = synth.normal_f32((1, 4096), 1.0, 22)
+    xs = np.frombuffer(np.float32(xb).tobytes(), np.uint32).reshape(1, 4096)
+    xs = (xs >> 16).astype(np.uint16)   # bf16 bit patterns (truncated: timing only)
+    t0 = time.perf_counter()
+    qref.qmatmul(xs, qref.BF16, *q2, qref.BF16, 4096, 4, 64)
+    el = time.perf_counter() - t0
+    out["decode_14336x4096_m1_ms"] = round(1e3 * el, 1)
+    out["decode_14336x4096_m1_weight_GBps"] = round(weight_bytes(14336, 4096, 4, 64, 2) / el / 1e9, 3)
+    del w2, q2
+    E, top_k, D, F = 128, 8, 2048, 768
+    wg = qref.quantize(synth.normal_f32((E * F, D), 0.02, 51), 4, 64, qref.BF16)
+    wu = qref.quantize(synth.normal_f32((E * F, D), 0.02, 52), 4, 64, qref.BF16)
+    wd = qref.quantize(synth.normal_f32((E * D, F), 0.02, 53), 4, 64, qref.BF16)
+    ids = synth.moe_ids(1, top_k, E, seed=55).ravel()
+    a = (np.frombuffer(synth.normal_f32((1, D), 1.0, 54).tobytes(), np.uint32) >> 16).astype(np.uint16)
+    rs = lambda t, r: tuple(v.reshape(E, r, -1) for v in t)
+    t0 = time.perf_counter()
+    ref = qref.moe_gate_up_silu(a, qref.BF16, ids, 1, top_k, D, 0, rs(wg, F), rs(wu, F), qref.BF16,
+                                E, F, D, 4, 64)
+    hb = (np.frombuffer(np.float32(ref["silu_out"]).tobytes(), np.uint32) >> 16).astype(np.uint16)
+    qref.moe(hb.reshape(top_k, F), qref.BF16, ids, 1, top_k, top_k * F, F, *rs(wd, D), qref.BF16,
+             E, D, F, 4, 64)
+    out["moe_t1_gate_up_down_ms"] = round(1e3 * (time.perf_counter() - t0), 1)
+    return out
+
+
 def copy_calibration():
     """Plain device copies of a known size: the reference that scales the
     FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -317,6 +407,37 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
+# One workload at a time, for profiler runs (counters per kernel):
+#   python bench.py --case NAME --steps 20 --warmup 2
+CASES = {
+    "decode_b4_m1": (14336, 4096, 1, 4, 64, "bf16"),
+    "skinny_b4_m16": (14336, 4096, 16, 4, 64, "bf16"),
+    "skinny_b3_m8": (4096, 4096, 8, 3, 64, "f16"),
+    "prefill_b4_m2048": (14336, 4096, 2048, 4, 64, "bf16"),
+    "moe_t1": 1,
+    "moe_t512": 512,
+}
+
+
+def run_case(name, steps, warmup):
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    spec = CASES[name]
+    if isinstance(spec, int):
+        ms_gu, ms_d, ms_ffn, touched, per_expert, _, rotation = bench_moe(spec, steps, warmup,
+                                                                           stream, dev)
+        print(json.dumps({"case": name, "gate_up_silu_us": round(ms_gu * 1e3, 3),
+                          "down_us": round(ms_d * 1e3, 3), "ffn_block_us": round(ms_ffn * 1e3, 3),
+                          "experts_touched": touched, "rotation_bytes": rotation}), flush=True)
+        return
+    N, K, M, bits, gs, dt = spec
+    dt = torch.bfloat16 if dt == "bf16" else torch.float16
+    ms, wb, copies = bench_dense(N, K, M, bits, gs, dt, steps, warmup, stream, dev)
+    print(json.dumps({"case": name, "us": round(ms * 1e3, 3), "weight_bytes": wb,
+                      "weight_GBps": round(wb / (ms * 1e-3) / 1e9, 1), "copies": copies}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,13 +446,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--case", choices=sorted(CASES), help="time one workload (for profiler runs)")
+    ap.add_argument("--oracle-single-core", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.oracle_single_core:
+        print(json.dumps(oracle_single_core()), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: there is no multi-GPU path in this library "
               "(see the sharding design); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.case:
+        run_case(args.case, args.steps, args.warmup)
         return
 
     import torch
@@ -474,24 +603,38 @@ def main():
         torch.cuda.empty_cache()
         # MoE rows: 128 experts, top-8, 4-bit gs64 bf16.
         for T in (1, 64, 512):
-            ms_gu, ms_d, ms_ffn, touched, per_expert, graph = bench_moe(T, del_steps, 5, stream,
-                                                                        dev)
+            ms_gu, ms_d, ms_ffn, touched, per_expert, graph, rotation = bench_moe(
+                T, del_steps, 5, stream, dev)
             gu_bytes, d_bytes = 2 * touched * per_expert, touched * per_expert
+            gu_all, d_all, ffn_all = moe_call_bytes(T, touched, per_expert)
             rows[f"moe_t{T}"] = {
                 "experts_touched": touched,
+                "rotation_bytes": rotation,
                 "gate_up_silu_us": round(ms_gu * 1e3, 3),
                 "gate_up_weight_GBps": round(gu_bytes / (ms_gu * 1e-3) / 1e9, 1),
+                "gate_up_total_bytes": gu_all,
+                "gate_up_total_GBps": round(gu_all / (ms_gu * 1e-3) / 1e9, 1),
                 "down_us": round(ms_d * 1e3, 3),
                 "down_weight_GBps": round(d_bytes / (ms_d * 1e-3) / 1e9, 1),
+                "down_total_bytes": d_all,
+                "down_total_GBps": round(d_all / (ms_d * 1e-3) / 1e9, 1),
                 "tflops_total": round(2.0 * T * 8 * 3 * 768 * 2048 / ((ms_gu + ms_d) * 1e-3)
                                       / 1e12, 2),
                 "ffn_block_us": round(ms_ffn * 1e3, 3),
                 "ffn_block_weight_GBps": round(3 * touched * per_expert / (ms_ffn * 1e-3) / 1e9, 1),
+                "ffn_block_total_bytes": ffn_all,
+                "ffn_block_total_GBps": round(ffn_all / (ms_ffn * 1e-3) / 1e9, 1),
                 **{k: round(v * 1e3, 3) for k, v in graph.items()}}
         result["rows"] = rows
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(N, K, BITS, GS)
+        import subprocess
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        p = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-single-core"],
+                           capture_output=True, text=True, env=env, timeout=600)
+        if p.returncode == 0:
+            result["cpu_baseline"]["single_core"] = json.loads(p.stdout.strip().splitlines()[-1])
     print(json.dumps(result), flush=True)
 
 
