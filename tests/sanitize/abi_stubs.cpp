@@ -27,6 +27,7 @@ STUB(hipError_t launch_dequantize_mx(const DequantMxArgs&, hipStream_t))
 STUB(hipError_t launch_qmatmul_mx(const GemvMxArgs&, hipStream_t))
 STUB(hipError_t launch_qgemm_mx(const GemvMxArgs&, hipStream_t))
 STUB(hipError_t launch_moe(const MoeArgs&, hipStream_t))
+STUB(hipError_t launch_moe_pair(const MoeArgs&, const MoeArgs&, hipStream_t))
 STUB(hipError_t launch_qgemv_t(const QgemvTArgs&, hipStream_t))
 STUB(hipError_t launch_quantize_int8_tensor(const float*, int64_t, int8_t*, float*, hipStream_t))
 STUB(hipError_t launch_dequantize_int8_tensor(const int8_t*, int64_t, const float*, int, void*,

@@ -632,9 +632,7 @@ qp_status qgemv_moe_ffn(const void* a, qp_dtype a_dtype, const int32_t* ids,
         return s;
     if (qp_status s = moe_common(dn, what); s != QP_OK)
         return s;
-    if (hipError_t e = qp::launch_moe(gu, stream); e != hipSuccess)
-        return hip_result(e, what);
-    if (hipError_t e = qp::launch_moe(dn, stream); e != hipSuccess)
+    if (hipError_t e = qp::launch_moe_pair(gu, dn, stream); e != hipSuccess)
         return hip_result(e, what);
     qp::MoeCombineArgs c{o, ids, route_weights, n_tokens, top_k, d_model, num_experts,
                          (int)a_dtype, out};

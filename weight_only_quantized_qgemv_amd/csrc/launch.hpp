@@ -140,6 +140,10 @@ QP_MOE_DECL(6)
 QP_MOE_DECL(8)
 #undef QP_MOE_DECL
 hipError_t launch_moe(const MoeArgs& a, hipStream_t stream);
+// Two MoE calls over the same ids, pairs and experts, in stream order (the
+// FFN block's gate + up, then down): one routing pass when both take the same
+// tile height, two otherwise. Both use a's workspace for the tables.
+hipError_t launch_moe_pair(const MoeArgs& a, const MoeArgs& b, hipStream_t stream);
 
 // The transpose = false product (qgemv_t.hip): W stored [K, N], grouped along
 // N; fp32 partial sums of the K splits in `workspace`.

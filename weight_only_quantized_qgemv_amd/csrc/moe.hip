@@ -299,29 +299,26 @@ int moe_gemm_bm(const MoeArgs& a)
     return vec && sb && small ? 64 : 0;
 }
 
-hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
+MoeRouting moe_plan(const MoeArgs& a)
 {
     MoeRouting r{};
     const int64_t P = a.n_tokens * a.top_k;
     const int rm = moe_rowmfma_mt(a);
     const int bm = rm > 0 ? 0 : moe_gemm_bm(a);
     const int nb = rm > 0 || bm > 0 ? 0 : moe_mfma_nb(a);
-    const int mt = rm > 0 ? rm : bm > 0 ? bm : nb > 0 ? 16 * nb
-                                                       : moe_tile_height(P, a.E, a.bits, a.dt);
-    if (mt == 1) {
-        // One pair per tile: tile t is pair t itself, read straight from ids by
-        // the compute launch, and the routing launch is skipped.
-        r.mt = 1;
-        r.max_tiles = P;
-    } else {
-        hipError_t e = launch_moe_route(a, mt, &r, st);
-        if (e != hipSuccess)
-            return e;
-    }
+    r.mt = rm > 0 ? rm : bm > 0 ? bm : nb > 0 ? 16 * nb : moe_tile_height(P, a.E, a.bits, a.dt);
+    // One pair per tile: tile t is pair t itself, read straight from ids by
+    // the compute launch, and the routing launch is skipped.
+    r.max_tiles = P;
     r.nb = nb;
     r.gemm_bm = bm;
     r.rowmfma = rm;
     r.rowstream = moe_rowstream_ok(a, r.mt) ? 1 : 0;
+    return r;
+}
+
+hipError_t launch_moe_compute(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
+{
     const bool f = a.fused_silu;
     switch (a.bits) {
     case 2: return f ? launch_moe_b2_n2(a, r, st) : launch_moe_b2_n1(a, r, st);
@@ -331,6 +328,38 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
     case 8: return f ? launch_moe_b8_n2(a, r, st) : launch_moe_b8_n1(a, r, st);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
+{
+    MoeRouting r = moe_plan(a);
+    if (r.mt > 1)
+        if (hipError_t e = launch_moe_route(a, r.mt, &r, st); e != hipSuccess)
+            return e;
+    return launch_moe_compute(a, r, st);
+}
+
+hipError_t launch_moe_pair(const MoeArgs& a, const MoeArgs& b, hipStream_t st)
+{
+    MoeRouting ra = moe_plan(a), rb = moe_plan(b);
+    if (ra.mt > 1)
+        if (hipError_t e = launch_moe_route(a, ra.mt, &ra, st); e != hipSuccess)
+            return e;
+    if (hipError_t e = launch_moe_compute(a, ra, st); e != hipSuccess)
+        return e;
+    if (rb.mt > 1) {
+        if (rb.mt == ra.mt) {
+            // Same ids, pair count, expert count and tile height: the tables
+            // the first call's routing wrote are the second call's.
+            rb.n_tiles = ra.n_tiles;
+            rb.perm = ra.perm;
+            rb.tiles = ra.tiles;
+            rb.max_tiles = ra.max_tiles;
+        } else if (hipError_t e = launch_moe_route(b, rb.mt, &rb, st); e != hipSuccess) {
+            return e;
+        }
+    }
+    return launch_moe_compute(b, rb, st);
 }
 
 } // namespace qp
