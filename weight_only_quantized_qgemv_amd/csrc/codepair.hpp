@@ -13,7 +13,9 @@
 // m * 2^-9 and the first normal binade (8 + m) * 2^-9, so a byte holding a code
 // q < 16 converts to exactly q * 2^-9, and to q with the scale 2^9. E2M1
 // nibbles 0..3 are 0, 0.5, 1, 1.5: a 2-bit code converts to q with the scale 2.
-// 8-bit codes go through fp32 (v_cvt_f32_ubyteN, exact) and one pack.
+// 6- and 8-bit codes go through fp32 (v_cvt_f32_ubyteN, exact) and one pack
+// for bf16; for fp16 each code byte goes under the exponent byte of 1024 and
+// one packed subtraction of 1024 leaves it.
 //
 // Unit layout. A unit is 32 consecutive codes of a row (BITS words). Its 16
 // pairs come out in the order below; the activation pairs a kernel dots them
@@ -25,6 +27,12 @@
 //          nibble n, hi = (w >> 2) & 0x33333333 code 16i + 2n + 1; t = 0..3
 //          take byte t of lo, t = 4..7 byte t - 4 of hi (low nibble first).
 //   8-bit: word i, pair 2i + t: bytes 2t, 2t + 1 of word i.
+//   3-bit: slice j = bytes 3j .. 3j+2 of the unit (codes 8j .. 8j+7, LSB
+//          first across the word boundaries); its even codes spread to the
+//          bytes of one word and its odd codes to those of another, so the
+//          pairs are those of the 4-bit order.
+//   6-bit: slice j = bytes 6j .. 6j+5, its two 3-byte halves spread to bytes:
+//          pair p holds codes 2p, 2p + 1, the 8-bit order.
 //
 // Orientation. With b'' = fl(fl(qmax * s') + b') the weight of the top code
 // (computed as the dequantization computes it), the same group is also
@@ -59,6 +67,42 @@ template <> struct CodeOrder<8> {
     static constexpr int lo_code(int p) { return 4 * (p / 2) + 2 * (p % 2); }
     static constexpr int hi_code(int p) { return lo_code(p) + 1; }
 };
+template <> struct CodeOrder<3> : CodeOrder<4> {};
+template <> struct CodeOrder<6> : CodeOrder<8> {};
+
+// Bytes of 3- and 6-bit codes. A 24-bit piece s holds codes at bits 0, w, 2w,
+// ... (w = 3 or 6; bits above 24 are ignored). First the upper 12 bits move
+// up by 4 (one shift and one bit-field insert), so that the fields at 0, 6,
+// 16 and 22 (of this word or of it shifted right by 3) are the ones that go
+// to bytes 0..3: bytes 0 and 2 are already in place, and bytes 1 and 3 are
+// those of the word shifted left by 2, so one byte permute gathers them. A
+// last mask, with the codes complemented by `flip` in the same operation,
+// clears the neighbouring fields.
+__device__ __forceinline__ uint32_t code_stage(uint32_t s)
+{
+    return (s & 0xFFFu) | ((s << 4) & ~0xFFFu);
+}
+__device__ __forceinline__ uint32_t code_gather(uint32_t y, uint32_t flip, uint32_t mask)
+{
+    return (__builtin_amdgcn_perm(y << 2, y, 0x07020500u) ^ flip) & mask;
+}
+// The eight 3-bit codes of s: codes 0, 2, 4, 6 to bytes 0..3 of `even`, codes
+// 1, 3, 5, 7 to those of `odd`.
+__device__ __forceinline__ void code_bytes3(uint32_t s, uint32_t flip, uint32_t& even, uint32_t& odd)
+{
+    const uint32_t y = code_stage(s);
+    even = code_gather(y, flip, 0x07070707u);
+    odd = code_gather(y >> 3, flip, 0x07070707u);
+}
+// The four 6-bit codes of s to bytes 0..3. The empty asm hides that each
+// byte is below 64, which otherwise turns the byte conversions that follow
+// (v_cvt_f32_ubyteN) into a bit-field extract and a conversion each.
+__device__ __forceinline__ uint32_t code_bytes6(uint32_t s, uint32_t flip)
+{
+    uint32_t v = code_gather(code_stage(s), flip, 0x3F3F3F3Fu);
+    asm("" : "+v"(v));
+    return v;
+}
 
 template <int DT> struct ExactCvt;
 template <> struct ExactCvt<DT_BF16> {
@@ -74,6 +118,12 @@ template <> struct ExactCvt<DT_BF16> {
     {
         return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
     }
+    // Bytes 0, 1 (HI: 2, 3) of v, each a code, as an exact pair: through fp32.
+    template <bool HI> static __device__ __forceinline__ uint32_t bytes(uint32_t v)
+    {
+        return HI ? pack((float)((v >> 16) & 0xFFu), (float)(v >> 24))
+                  : pack((float)(v & 0xFFu), (float)((v >> 8) & 0xFFu));
+    }
 };
 template <> struct ExactCvt<DT_F16> {
     template <bool HI> static __device__ __forceinline__ uint32_t fp8(uint32_t w)
@@ -87,6 +137,15 @@ template <> struct ExactCvt<DT_F16> {
     static __device__ __forceinline__ uint32_t pack(float lo, float hi)
     {
         return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)lo, (_Float16)hi});
+    }
+    // Bytes 0, 1 (HI: 2, 3) of v, each a code, as an exact pair: the byte
+    // permute puts each code c under the exponent byte 0x64, which makes the
+    // half 1024 + c exactly (c < 1024), and one packed subtraction of 1024
+    // leaves c.
+    template <bool HI> static __device__ __forceinline__ uint32_t bytes(uint32_t v)
+    {
+        const uint32_t h = __builtin_amdgcn_perm(0x64646464u, v, HI ? 0x04030402u : 0x04010400u);
+        return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, h) - f16x2_t{1024.0f16, 1024.0f16});
     }
 };
 
@@ -120,13 +179,42 @@ __device__ __forceinline__ void code_pairs(const uint32_t* w, uint32_t flip, uin
             p[8 * i + 6] = C::template fp4<2>(hi);
             p[8 * i + 7] = C::template fp4<3>(hi);
         }
+    } else if constexpr (BITS == 3) {
+        // Slice j (24 bits, codes 8j .. 8j+7) in the low bits of s[j].
+        const uint32_t s[4] = {w[0], __builtin_amdgcn_alignbyte(w[1], w[0], 3),
+                               __builtin_amdgcn_alignbyte(w[2], w[1], 2), w[2] >> 8};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t even, odd;
+            code_bytes3(s[j], flip, even, odd);
+            p[4 * j + 0] = C::template fp8<false>(even);
+            p[4 * j + 1] = C::template fp8<true>(even);
+            p[4 * j + 2] = C::template fp8<false>(odd);
+            p[4 * j + 3] = C::template fp8<true>(odd);
+        }
+    } else if constexpr (BITS == 6) {
+        // Codes 4h .. 4h+3 (24 bits) in the low bits of s[h].
+        uint32_t s[8];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            s[4 * j + 0] = w[3 * j];
+            s[4 * j + 1] = __builtin_amdgcn_alignbyte(w[3 * j + 1], w[3 * j], 3);
+            s[4 * j + 2] = __builtin_amdgcn_alignbyte(w[3 * j + 2], w[3 * j + 1], 2);
+            s[4 * j + 3] = w[3 * j + 2] >> 8;
+        }
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            const uint32_t v = code_bytes6(s[h], flip);
+            p[2 * h + 0] = C::template bytes<false>(v);
+            p[2 * h + 1] = C::template bytes<true>(v);
+        }
     } else {
-        static_assert(BITS == 8, "2-, 4- and 8-bit codes");
+        static_assert(BITS == 8, "2-, 3-, 4-, 6- and 8-bit codes");
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t v = w[i] ^ flip;
-            p[2 * i + 0] = C::pack((float)(v & 0xFFu), (float)((v >> 8) & 0xFFu));
-            p[2 * i + 1] = C::pack((float)((v >> 16) & 0xFFu), (float)(v >> 24));
+            p[2 * i + 0] = C::template bytes<false>(v);
+            p[2 * i + 1] = C::template bytes<true>(v);
         }
     }
 }

@@ -156,7 +156,15 @@ template <int NW, int POLICY = 0>
 __device__ __forceinline__ void buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                              uint32_t (&w)[NW])
 {
-    if constexpr (NW % 4 == 0) {
+    if constexpr (NW == 3) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, POLICY);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+    } else if constexpr (NW == 6) {
+        const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+        const u32x2_t u = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off + 16, 0, POLICY));
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        w[4] = u.x; w[5] = u.y;
+    } else if constexpr (NW % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < NW; i += 4) {
             const u32x4_t v = __builtin_bit_cast(

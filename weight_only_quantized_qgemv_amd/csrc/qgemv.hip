@@ -296,7 +296,7 @@ hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
                 return e;
         }
     }
-    if constexpr ((BITS == 2 || BITS == 4 || BITS == 8) && DT != DT_F32) {
+    if constexpr (DT != DT_F32) {
         // 8-bit codes as well: measured 12.4 against 14.4 us on the slice
         // kernel below at 14336 x 4096, 8.1 against 12.7 at 4096 x 8192.
         if (a.M <= 2 && a.K % 32 == 0 && a.K <= 8 * 64 * 32) {

@@ -1,4 +1,4 @@
-// rowstream.hpp — the decode GEMV for 2-, 4- and 8-bit codes with a weight
+// rowstream.hpp — the decode GEMV for 2-, 3-, 4-, 6- and 8-bit codes with a weight
 // row per wave (or per 32-lane half of one, for rows of at most 32 units),
 // and its three- and four-row form on the 4x4x4 matrix instruction (emily
 // lib/emily/quantization.ex, `quantized_matmul/2`; affine codes of
@@ -8,9 +8,9 @@
 // Lane l of a row's KL lanes takes the 32-code units l, l + KL, ... of the
 // row, so its slice of the activation rows is fixed for the whole launch and
 // sits in registers. A unit is BITS code words; its 32 codes become 16 exact
-// 16-bit pairs (codepair.hpp: FP8 / FP4 conversion of split code bytes, or
-// bytes through fp32 at 8 bits), and the activation pairs are stored in the
-// same order. v_dot2 forms sum x q per unit, and the group's scale and bias,
+// 16-bit pairs (codepair.hpp: FP8 / FP4 conversion of split code bytes, the
+// 3-bit fields spread to bytes first; bytes through fp32 at 6 and 8 bits),
+// and the activation pairs are stored in the same order. v_dot2 forms sum x q per unit, and the group's scale and bias,
 // oriented so that the folded bias does not cancel against the codes, are
 // applied once per unit. D rows are loaded before any is reduced.
 //
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
     using PX = RowStreamPair<DT>;
     using E = Elem<DT>;
     using St = typename E::storage;
-    static_assert(BITS == 2 || BITS == 4 || BITS == 8, "codes in whole 16-bit halves");
+    static_assert(BITS == 2 || BITS == 3 || BITS == 4 || BITS == 6 || BITS == 8, "code widths");
     constexpr int D = rowstream_depth<BITS, UPL>();
     using CO = CodeOrder<BITS>;
     const int lane = threadIdx.x & 63;

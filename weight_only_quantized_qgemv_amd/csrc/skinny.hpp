@@ -139,19 +139,6 @@ __device__ __forceinline__ float rows_sum(float v)
     return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
 }
 
-// Three-bit fields at bits 0, 6, 12, 18 of s to the low bits of bytes 0..3.
-__device__ __forceinline__ uint32_t spread3(uint32_t s)
-{
-    const uint32_t y = (s & 0x1C7u) | ((s & 0x1C7000u) << 4);    // fields at 0, 6, 16, 22
-    return (y & 0x70007u) | ((y & 0x1C001C0u) << 2);
-}
-// Six-bit fields at bits 0, 6, 12, 18 of s to the low bits of bytes 0..3.
-__device__ __forceinline__ uint32_t spread6(uint32_t s)
-{
-    const uint32_t y = (s & 0xFFFu) | ((s & 0xFFF000u) << 4);    // fields at 0, 6, 16, 22
-    return (y & 0x3F003Fu) | ((y & 0xFC00FC0u) << 2);
-}
-
 // Per code width: UI units per item, LW registers per lane per item (the
 // lane's quarter of the item's row bytes, plus scratch), the activation slot
 // order, the exchange level XG the slices take for GU units per group, the
@@ -215,10 +202,8 @@ template <> struct SkW<8> {
     {
         using C = ExactCvt<DT>;
         const uint32_t a = w[2 * I] ^ flip, b = w[2 * I + 1] ^ flip;
-        return u32x4_t{C::pack((float)(a & 0xFFu), (float)((a >> 8) & 0xFFu)),
-                       C::pack((float)((a >> 16) & 0xFFu), (float)(a >> 24)),
-                       C::pack((float)(b & 0xFFu), (float)((b >> 8) & 0xFFu)),
-                       C::pack((float)((b >> 16) & 0xFFu), (float)(b >> 24))};
+        return u32x4_t{C::template bytes<false>(a), C::template bytes<true>(a), C::template bytes<false>(b),
+                       C::template bytes<true>(b)};
     }
 };
 template <> struct SkW<3> {
@@ -239,8 +224,8 @@ template <> struct SkW<3> {
     template <int DT, int I> __device__ __forceinline__ static u32x4_t frag(const uint32_t (&w)[LW], uint32_t flip)
     {
         using C = ExactCvt<DT>;
-        const uint32_t s = w[I] ^ flip;
-        const uint32_t even = spread3(s), odd = spread3(s >> 3);
+        uint32_t even, odd;
+        code_bytes3(w[I], flip, even, odd);
         return u32x4_t{C::template fp8<false>(even), C::template fp8<true>(even), C::template fp8<false>(odd),
                        C::template fp8<true>(odd)};
     }
@@ -272,11 +257,9 @@ template <> struct SkW<6> {
     template <int DT, int I> __device__ __forceinline__ static u32x4_t frag(const uint32_t (&w)[LW], uint32_t flip)
     {
         using C = ExactCvt<DT>;
-        const uint32_t a = spread6(w[2 * I] ^ flip), b = spread6(w[2 * I + 1] ^ flip);
-        return u32x4_t{C::pack((float)(a & 0xFFu), (float)((a >> 8) & 0xFFu)),
-                       C::pack((float)((a >> 16) & 0xFFu), (float)(a >> 24)),
-                       C::pack((float)(b & 0xFFu), (float)((b >> 8) & 0xFFu)),
-                       C::pack((float)((b >> 16) & 0xFFu), (float)(b >> 24))};
+        const uint32_t a = code_bytes6(w[2 * I], flip), b = code_bytes6(w[2 * I + 1], flip);
+        return u32x4_t{C::template bytes<false>(a), C::template bytes<true>(a), C::template bytes<false>(b),
+                       C::template bytes<true>(b)};
     }
 };
 
