@@ -128,7 +128,8 @@ def graph_ms(fn, n, stream, reps=5):
     return statistics.median(out)
 
 
-def bench_dense(N, K, M, bits, gs, dt, steps, warmup, stream, dev, seed=21, graph=False):
+def bench_dense(N, K, M, bits, gs, dt, steps, warmup, stream, dev, seed=21, graph=False,
+                graph_calls=None):
     import torch
     import weight_only_quantized_qgemv_amd as qp
     from weight_only_quantized_qgemv_amd import synth
@@ -145,7 +146,7 @@ def bench_dense(N, K, M, bits, gs, dt, steps, warmup, stream, dev, seed=21, grap
 
     ms = time_calls(step, steps, warmup, stream)
     if graph:
-        ms = (ms, graph_ms(step, 8 * copies, stream))
+        ms = (ms, graph_ms(step, graph_calls or 8 * copies, stream))
     del sets
     torch.cuda.empty_cache()
     return ms, wb, copies
@@ -471,7 +472,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
     bf16 = torch.bfloat16
     N, K, BITS, GS = 14336, 4096, 4, 64
-    ms, wb, copies = bench_dense(N, K, 1, BITS, GS, bf16, args.steps, args.warmup, stream, dev)
+    # The timed K steps: eager calls, back to back, rotating over the weight
+    # copies. Beside them, the same K calls captured once into a HIP graph and
+    # replayed (no host issue between launches).
+    (ms, ms_graph), wb, copies = bench_dense(N, K, 1, BITS, GS, bf16, args.steps, args.warmup,
+                                             stream, dev, graph=True, graph_calls=args.steps)
     gbs = wb / (ms * 1e-3) / 1e9
     traffic = None
     if TRAFFIC is not None and TRAFFIC.get("src_sha") == decode_src_sha():
@@ -484,6 +489,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
+        "ms_per_step_graph": round(ms_graph, 6),
+        "value_graph": round(wb / (ms_graph * 1e-3) / 1e9, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -505,19 +512,36 @@ def main():
     if not args.no_rows:
         rows = {}
         # Decode rows: W[14336,4096] gs64 bf16 at 4/8/2 bits, M = 1/4/16.
+        # Eager back-to-back calls, and the same calls replayed from a graph.
         for bits in (4, 8, 2):
             for M in (1, 4, 16):
-                ms_r, wb_r, _ = bench_dense(N, K, M, bits, 64, bf16, del_steps, 5, stream, dev)
+                (ms_r, ms_g), wb_r, _ = bench_dense(N, K, M, bits, 64, bf16, del_steps, 5, stream,
+                                                    dev, graph=True)
                 g = wb_r / (ms_r * 1e-3) / 1e9
                 rows[f"decode_b{bits}_m{M}"] = {
                     "us": round(ms_r * 1e3, 3), "weight_GBps": round(g, 1),
                     "frac_hbm": round(g / HBM_PEAK_GBS, 4),
-                    "tokens_per_s": round(M / (ms_r * 1e-3), 1)}
+                    "tokens_per_s": round(M / (ms_r * 1e-3), 1),
+                    "us_graph": round(ms_g * 1e3, 3),
+                    "weight_GBps_graph": round(wb_r / (ms_g * 1e-3) / 1e9, 1)}
         # The down-projection shape, W[4096,14336], 4-bit gs64 bf16, M = 1.
-        ms_r, wb_r, _ = bench_dense(4096, 14336, 1, 4, 64, bf16, del_steps, 5, stream, dev, seed=23)
+        (ms_r, ms_g), wb_r, _ = bench_dense(4096, 14336, 1, 4, 64, bf16, del_steps, 5, stream, dev,
+                                            seed=23, graph=True)
         g = wb_r / (ms_r * 1e-3) / 1e9
         rows["decode_b4_k14336_m1"] = {"us": round(ms_r * 1e3, 3), "weight_GBps": round(g, 1),
-                                       "frac_hbm": round(g / HBM_PEAK_GBS, 4)}
+                                       "frac_hbm": round(g / HBM_PEAK_GBS, 4),
+                                       "us_graph": round(ms_g * 1e3, 3),
+                                       "weight_GBps_graph": round(wb_r / (ms_g * 1e-3) / 1e9, 1)}
+        # Launch floor and the streaming rate: the 4-bit row kernel over N rows
+        # of K = 4096 (graph-replayed), from a 256-row matrix (about the fixed
+        # cost of one launch) to 114688 rows (264 MB).
+        sweep = {}
+        for n_s in (256, 4096, 14336, 57344, 114688):
+            (_, ms_g), wb_s, _ = bench_dense(n_s, K, 1, 4, 64, bf16, 20, 3, stream, dev, seed=25,
+                                             graph=True, graph_calls=400)
+            sweep[str(n_s)] = {"us_graph": round(ms_g * 1e3, 3),
+                               "weight_GBps": round(wb_s / (ms_g * 1e-3) / 1e9, 1)}
+        rows["decode_b4_rows_sweep"] = sweep
         # Cross-word rows: W[4096,4096] fp16 at 3/6 bits over gs 32/64/128, M = 1/8.
         for bits in (3, 6):
             for gs in (32, 64, 128):

@@ -101,7 +101,7 @@ def test_qmatmul_parity_small(bits, dt, k, m):
     assert_within(y, y_ref, S, dt, f"qmatmul b{bits} dt{dt} k{k} m{m}")
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("dt", [F16, BF16])
 @pytest.mark.parametrize("k,m,gs", [(14336, 1, 64), (11008, 1, 128), (8192, 2, 32), (6144, 2, 64),
                                     (2080, 1, 32), (16384, 2, 64), (12288, 1, 32), (2176, 2, 64),
@@ -109,10 +109,13 @@ def test_qmatmul_parity_small(bits, dt, k, m):
                                     (4096, 4, 64), (2176, 3, 64), (2112, 4, 64), (96, 3, 32),
                                     (1024, 4, 128), (9600, 1, 64), (5120, 2, 32)])
 def test_qmatmul_row_stream_units_per_lane(bits, dt, k, m, gs):
-    """2/4/8-bit decode on the row-per-wave kernel: 1 to 8 units of 32 codes
-    per lane, ragged unit counts (11008 = 344 units, 2176 = 68, 2080 = 65,
-    96 = 3), two rows per pass up to K = 8192 and one beyond, three and four
-    rows (activation slices read from LDS) up to K = 4096; rows with an
+    """Decode on the row-per-wave kernel at every code width (3- and 6-bit
+    units are 12 and 24 bytes, the fields spread to bytes first): 1 to 8
+    units of 32 codes per lane, ragged unit counts (11008 = 344 units, 2176
+    = 68, 2080 = 65, 96 = 3), two rows per pass up to K = 8192 and one
+    beyond, three and four rows (2/4/8-bit: activation slices read from LDS,
+    on the 4x4x4 matrix instruction; 3/6-bit: the skinny kernel) up to K =
+    4096; rows with an
     even number of groups (scales read as whole rows) and with an odd one
     (2080 / 32 = 65, 2112 / 64 = 33, 96 / 32 = 3); units per lane as the row
     needs them (9600 = 300 units: 5 per lane; 5120 = 160: 3; 11008: 6;

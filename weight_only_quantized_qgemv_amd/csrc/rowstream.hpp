@@ -61,10 +61,14 @@ template <> struct RowStreamPair<DT_F16> {
 // back-to-back launches): 4-bit 3 rows 8.0 us against 4 rows 8.6 us and 2
 // rows 8.2 us; 8-bit 1 row 11.8 us against 2 rows 12.2 us; 2-bit 4 rows 7.0
 // us against 3 rows 7.2 us and 6 rows 8.0 us; at K = 14336 (seven units per
-// lane) one row 10.3 us against two 11.1 us.
+// lane) one row 10.3 us against two 11.1 us. Three-bit units cost the most
+// VALU work per byte (the fields are spread to bytes first), so their waves
+// take half as many rows: 14336 x 4096 3-bit 8.7 us with 2 rows against 9.6
+// us with 4; at 6 bits one row (12.4 us) was slower than two (11.9 us).
 template <int BITS, int UPL> constexpr int rowstream_depth()
 {
-    return 24 / (BITS * UPL) < 1 ? 1 : (24 / (BITS * UPL) > 4 ? 4 : 24 / (BITS * UPL));
+    constexpr int B = BITS == 3 ? 12 : 24;
+    return B / (BITS * UPL) < 1 ? 1 : (B / (BITS * UPL) > 4 ? 4 : B / (BITS * UPL));
 }
 
 template <int BITS, int DT, int MT, int UPL, int WPB, bool WIDE, int KL>
