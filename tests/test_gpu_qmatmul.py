@@ -113,9 +113,9 @@ def test_qmatmul_row_stream_units_per_lane(bits, dt, k, m, gs):
     units are 12 and 24 bytes, the fields spread to bytes first): 1 to 8
     units of 32 codes per lane, ragged unit counts (11008 = 344 units, 2176
     = 68, 2080 = 65, 96 = 3), two rows per pass up to K = 8192 and one
-    beyond, three and four rows (2/4/8-bit: activation slices read from LDS,
-    on the 4x4x4 matrix instruction; 3/6-bit: the skinny kernel) up to K =
-    4096; rows with an
+    beyond, three and four rows up to K = 4096 (2/4/8-bit: activation
+    slices read from LDS, on the 4x4x4 matrix instruction; 3/6-bit: the four
+    rows' slices in registers, dot products); rows with an
     even number of groups (scales read as whole rows) and with an odd one
     (2080 / 32 = 65, 2112 / 64 = 33, 96 / 32 = 3); units per lane as the row
     needs them (9600 = 300 units: 5 per lane; 5120 = 160: 3; 11008: 6;

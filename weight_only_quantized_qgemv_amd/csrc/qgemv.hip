@@ -212,8 +212,10 @@ hipError_t run_rowstream_upl(const GemvArgs& a, int64_t m0, int mc, hipStream_t 
     constexpr bool exact = true;
     if (upl <= 1) return run_rowstream<BITS, DT, MT, 1>(a, m0, mc, st);
     if (upl <= 2) return run_rowstream<BITS, DT, MT, 2>(a, m0, mc, st);
-    if (exact && upl <= 3) return run_rowstream<BITS, DT, MT, 3>(a, m0, mc, st);
-    if (upl <= 4) return run_rowstream<BITS, DT, MT, 4>(a, m0, mc, st);
+    if constexpr (MT <= 2) {
+        if (exact && upl <= 3) return run_rowstream<BITS, DT, MT, 3>(a, m0, mc, st);
+        if (upl <= 4) return run_rowstream<BITS, DT, MT, 4>(a, m0, mc, st);
+    }
     if constexpr (MT == 1) {
         // Units per lane as the row needs them (K = 14336: 7), so that no
         // lane carries a whole unit of zeros through the dot products.
@@ -222,7 +224,9 @@ hipError_t run_rowstream_upl(const GemvArgs& a, int64_t m0, int mc, hipStream_t 
         if (exact && upl <= 7) return run_rowstream<BITS, DT, MT, 7>(a, m0, mc, st);
         return run_rowstream<BITS, DT, MT, 8>(a, m0, mc, st);
     }
-    return hipErrorInvalidValue;   // two rows only up to four units per lane
+    // Two rows' activation slices fit in registers up to four units per
+    // lane, four rows' up to two.
+    return hipErrorInvalidValue;
 }
 
 // Three or four activation rows with the products on the 4x4x4 matrix
@@ -285,6 +289,16 @@ hipError_t run_gemv(const GemvArgs& a, hipStream_t st)
         // (15.5 on the tile path below, 14.6 with dot products on four
         // activation rows); one and two rows stay on the dot-product stream
         // (9.0 against 11.3 us at one row).
+        if constexpr (BITS == 3 || BITS == 6) {
+            // Three and four rows of 3- and 6-bit codes on the row kernel,
+            // the four activation rows' slices in registers, where the matrix
+            // is small enough that the skinny kernel's set-up dominates:
+            // [4096, 4096] M = 4 measured 6.4 us at 3 bits against 8.6 on the
+            // skinny kernel, 7.5 against 10.9 at 6 bits; at 14336 rows the
+            // skinny kernel was faster (15.7 against 17.0 us at 3 bits).
+            if ((a.M == 3 || a.M == 4) && a.K % 32 == 0 && a.K <= 2 * 64 * 32 && a.N <= 8192)
+                return run_rowstream_upl<BITS, DT, 4>(a, 0, (int)a.M, st);
+        }
         if constexpr (BITS == 2 || BITS == 4 || BITS == 8) {
             if ((a.M == 3 || a.M == 4) && a.K % 32 == 0 && a.K <= 2 * 64 * 32)
                 return run_rowmfma<BITS, DT>(a, st);

@@ -1,7 +1,7 @@
-// rowstream.hpp — the decode GEMV for 2-, 3-, 4-, 6- and 8-bit codes with a weight
-// row per wave (or per 32-lane half of one, for rows of at most 32 units),
-// and its three- and four-row form on the 4x4x4 matrix instruction (emily
-// lib/emily/quantization.ex, `quantized_matmul/2`; affine codes of
+// rowstream.hpp — the decode GEMV for 2-, 3-, 4-, 6- and 8-bit codes with a
+// weight row per wave (or per 32-lane half of one, for rows of at most 32
+// units), and its three- and four-row form on the 4x4x4 matrix instruction
+// (emily lib/emily/quantization.ex, `quantized_matmul/2`; affine codes of
 // `dequantize_defn/1`):
 //   y[m, n] = sum_g s'[n,g] * sum_{k in g} x q + b'[n,g] * sum_{k in g} x.
 //
@@ -10,9 +10,12 @@
 // sits in registers. A unit is BITS code words; its 32 codes become 16 exact
 // 16-bit pairs (codepair.hpp: FP8 / FP4 conversion of split code bytes, the
 // 3-bit fields spread to bytes first; bytes through fp32 at 6 and 8 bits),
-// and the activation pairs are stored in the same order. v_dot2 forms sum x q per unit, and the group's scale and bias,
-// oriented so that the folded bias does not cancel against the codes, are
-// applied once per unit. D rows are loaded before any is reduced.
+// and the activation pairs are stored in the same order. v_dot2 forms
+// sum x q per unit, and the group's scale and bias, oriented so that the
+// folded bias does not cancel against the codes, are applied once per unit.
+// D rows are loaded before any is reduced. One or two activation rows share
+// a pass (and, for 3- and 6-bit codes on small matrices, up to four: their
+// slices in registers up to two units per lane).
 //
 // Every wave of a block needs the same activation slices, so the block
 // prepares them once: its threads load the raw activation units, permute
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
         }
     }
     __syncthreads();
-    static_assert(MT <= 2, "three and more activation rows use the matrix-core kernel");
+    static_assert(MT <= 4, "at most four activation rows' slices in registers");
     uint32_t xr[MT][UPL][16];
     float xs[MT][UPL];
 #pragma unroll
