@@ -305,6 +305,33 @@ def test_moe_routed_gemm_tiles(bits, dt, T, top_k, E, R, C, gs, Rd):
     assert_within(out_d, ref_d, S_d, dt, "routed down")
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_moe_routed_gemm_32_pair_tiles(bits, dt):
+    """Fewer than 16 pairs per expert on average (12 here), K a multiple of 64
+    and at most 1024: the plain form takes the routed GEMM in 32-pair tiles.
+    Expert 15 serves every token (48 pairs: a full tile and a partial one);
+    the other three picks of each token are uniform over experts 0..14."""
+    T, E, R, C, gs, Rd = 48, 16, 136, 512, 64, 192
+    log(f"moe routed gemm 32-pair tiles bits={bits} dt={dt}")
+    ids = np.concatenate([np.full((T, 1), E - 1), synth.moe_ids(T, 3, E - 1, seed=181)],
+                         axis=1).astype(np.int32).ravel()
+    top_k = 4
+    ids_d = torch.from_numpy(ids).to(dev())
+    gate_h, gate_d = stack(E, R, C, bits, gs, dt, 182 + bits)
+    a_s, a_d = activations((T, C), dt, 183)
+    g = qp.qgemv_moe_id(a_d, ids_d, T, top_k, C, 0, *gate_d, bits, gs)
+    torch.cuda.synchronize()
+    ref, S = qref.moe(a_s, dt, ids, T, top_k, C, 0, *gate_h, dt, E, R, C, bits, gs)
+    assert_within(g, ref, S, dt, "routed plain, 32-pair tiles")
+    down_h, down_d = stack(E, C, Rd, bits, 32, dt, 184 + bits)
+    h_s, h_d = activations((T * top_k, Rd), dt, 185)
+    out_d = qp.qgemv_moe_id(h_d, ids_d, T, top_k, top_k * Rd, Rd, *down_d, bits, 32)
+    torch.cuda.synchronize()
+    ref_d, S_d = qref.moe(h_s, dt, ids, T, top_k, top_k * Rd, Rd, *down_h, dt, E, C, Rd, bits, 32)
+    assert_within(out_d, ref_d, S_d, dt, "routed down, 32-pair tiles")
+
+
 def test_moe_routed_gemm_pair_order_does_not_change_values():
     """A pair's output does not depend on which tile slot it lands in: permuting
     the pairs permutes the outputs bit for bit."""

@@ -256,6 +256,8 @@ hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
             return run_rowstream_tiles<BITS, DT, NMAT>(k, r.max_tiles, st);
         if (r.gemm_bm == 64)
             return run_gemm_tiles<BITS, DT, NMAT, 64>(a, r, st);
+        if (r.gemm_bm == 32)
+            return run_gemm_tiles<BITS, DT, NMAT, 32>(a, r, st);
         if (r.nb > 0)
             return run_skinny_tiles<BITS, DT, NMAT>(k, r.max_tiles, st);
         if (!x_vec)
