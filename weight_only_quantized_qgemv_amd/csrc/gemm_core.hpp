@@ -14,8 +14,9 @@
 //    codes of its BN rows and their scales / biases in LDS by DMA; each lane
 //    then builds its MFMA B fragments in registers: it reads the 32 codes of
 //    one unit of its weight row (emily `dequantize_defn/1` layout), converts
-//    them with the byte-conversion instructions, applies q * s' + b' in fp32
-//    and rounds to the activation type. The contraction over the step's 64 k
+//    them exactly to fp32 (FP8 / FP4 pair conversions of code bytes or
+//    nibbles, or byte conversions), applies q * s' + b' in fp32 and rounds to
+//    the activation type. The contraction over the step's 64 k
 //    is taken in the order the units give: MFMA kk pairs k = 8 kk + i (lanes
 //    0-31) with k = 32 + 8 kk + i (lanes 32-63), and the activation fragments
 //    are read in the same order;
@@ -36,6 +37,7 @@
 // column in the same lane, and the epilogue writes SiLU(gate) * up.
 #pragma once
 
+#include "codepair.hpp"
 #include "common.hpp"
 #include "mx.hpp"
 
@@ -181,6 +183,69 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // only for what step kt + 1 reads early (the activations and codes / scales
 // of kt + 2): activation loads get NA - 2 steps to arrive and code loads
 // NC - 2, and the newest DMA stays in flight across the barrier.
+// Exact codes 8 kk .. 8 kk + 7 of a unit, in order, as fp32. 4- and 3-bit
+// codes go to bytes (a mask; for 3-bit the spreading of codepair.hpp) and
+// 2-bit codes to nibbles, and each FP8 / FP4 pair conversion (scale 2^9 / 2,
+// powers of two, so the values are the codes exactly) yields two of them;
+// 6- and 8-bit codes take one byte conversion each.
+template <int BITS> struct GemmCodes {
+    using CB = CodeBytes<BITS>;
+    static constexpr int NW = BITS == 4 ? 8 : BITS == 2 ? 4 : BITS == 3 ? 3 : CB::NBW;
+    static __device__ __forceinline__ void split(const uint32_t (&w)[BITS], uint32_t (&bw)[NW])
+    {
+        if constexpr (BITS == 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bw[2 * i] = and_opaque(w[i], 0x0F0F0F0Fu);           // codes 8i + 0, 2, 4, 6
+                bw[2 * i + 1] = and_opaque(w[i] >> 4, 0x0F0F0F0Fu);  // codes 8i + 1, 3, 5, 7
+            }
+        } else if constexpr (BITS == 2) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                bw[2 * i] = and_opaque(w[i], 0x33333333u);           // nibble n: code 16i + 2n
+                bw[2 * i + 1] = and_opaque(w[i] >> 2, 0x33333333u);  // nibble n: code 16i + 2n + 1
+            }
+        } else if constexpr (BITS == 3) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i) bw[i] = w[i];
+        } else {
+            CB::split(w, bw);
+        }
+    }
+    template <int KK> static __device__ __forceinline__ void codes8(const uint32_t (&bw)[NW], float (&q)[8])
+    {
+        if constexpr (BITS == 4 || BITS == 3) {
+            uint32_t even, odd;   // codes 0, 2, 4, 6 and 1, 3, 5, 7 of the eight, one per byte
+            if constexpr (BITS == 4) {
+                even = bw[2 * KK];
+                odd = bw[2 * KK + 1];
+            } else {
+                const uint32_t sl = KK == 0 ? bw[0]
+                                  : KK == 1 ? __builtin_amdgcn_alignbyte(bw[1], bw[0], 3)
+                                  : KK == 2 ? __builtin_amdgcn_alignbyte(bw[2], bw[1], 2)
+                                            : bw[2] >> 8;
+                code_bytes3(sl, 0u, even, odd);
+            }
+            const f32x2_t e01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(even, 512.0f, false);
+            const f32x2_t e23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(even, 512.0f, true);
+            const f32x2_t o01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(odd, 512.0f, false);
+            const f32x2_t o23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(odd, 512.0f, true);
+            q[0] = e01.x; q[1] = o01.x; q[2] = e01.y; q[3] = o01.y;
+            q[4] = e23.x; q[5] = o23.x; q[6] = e23.y; q[7] = o23.y;
+        } else if constexpr (BITS == 2) {
+            constexpr int i = KK / 2;
+            static_for<2>([&](auto BB) {
+                constexpr int bb = decltype(BB)::value, b = 2 * (KK % 2) + bb;
+                const f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(bw[2 * i], 2.0f, b);
+                const f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(bw[2 * i + 1], 2.0f, b);
+                q[4 * bb] = lo.x; q[4 * bb + 1] = hi.x; q[4 * bb + 2] = lo.y; q[4 * bb + 3] = hi.y;
+            });
+        } else {
+            static_for<8>([&](auto C) { q[decltype(C)::value] = CB::template code<8 * KK + decltype(C)::value>(bw); });
+        }
+    }
+};
+
 template <int BITS, int DT, int BM, int BN, int THREADS, int WMW, int NMAT, bool ROUTED, int NA,
           int NC, int MODE = 0>
 __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
@@ -190,7 +255,7 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     using T = MfmaTraits<DT>;
     using frag_t = typename T::frag_t;
     using CL = CodeLayout<BITS>;
-    using CB = CodeBytes<BITS>;
+    using GC = GemmCodes<BITS>;
     constexpr int WAVES = THREADS / 64;
     constexpr int WGN = WAVES / WMW;             // waves: WMW along M x WGN along N
     constexpr int WM = BM / WMW, WN = BN / WGN;  // wave tile
@@ -376,7 +441,7 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         const int row = n0 + bt[j] % BNO;
         b_gbase[j] = e_groups + (uint32_t)(row < N ? row : 0) * groups;
     }
-    uint32_t wcode[FN][CB::NBW];
+    uint32_t wcode[FN][GC::NW];
     float s_u[FN], b_u[FN];
     // Microscaled modes: the unit's raw code words, and its scale bytes (one,
     // or two for 16-wide groups).
@@ -433,7 +498,7 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         for (int j = 0; j < FN; ++j) {
             uint32_t w[BITS];
             read_unit(stage, bt[j], w);
-            CB::split(w, wcode[j]);
+            GC::split(w, wcode[j]);
             const char* sbp = sb_st + stage * SB_STAGE + bt[j] * 4;
             const uint32_t sd = *reinterpret_cast<const uint32_t*>(sbp);
             const uint32_t bd = *reinterpret_cast<const uint32_t*>(sbp + 4 * BN);
@@ -487,11 +552,13 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
             });
             return __builtin_bit_cast(frag_t, u32x4_t{packed[0], packed[1], packed[2], packed[3]});
         }
+        float q[8];
+        GC::template codes8<kk>(wcode[j], q);
         static_for<4>([&](auto P) {
-            constexpr int c = 8 * kk + 2 * decltype(P)::value;
-            const float w0 = __builtin_fmaf(CB::template code<c>(wcode[j]), s_u[j], b_u[j]);
-            const float w1 = __builtin_fmaf(CB::template code<c + 1>(wcode[j]), s_u[j], b_u[j]);
-            packed[decltype(P)::value] = T::pack2(w0, w1);
+            constexpr int p = decltype(P)::value;
+            const float w0 = __builtin_fmaf(q[2 * p], s_u[j], b_u[j]);
+            const float w1 = __builtin_fmaf(q[2 * p + 1], s_u[j], b_u[j]);
+            packed[p] = T::pack2(w0, w1);
         });
         return __builtin_bit_cast(frag_t, u32x4_t{packed[0], packed[1], packed[2], packed[3]});
     };
