@@ -45,7 +45,7 @@ CSRC = os.path.join(ROOT, "weight_only_quantized_qgemv_amd", "csrc")
 # (FETCH_SIZE, WRITE_SIZE) of `bench.py --case decode_b4_m1 --steps 20
 # --warmup 2`, each scaled by the same counter on a plain 1 GiB copy.
 # It holds only while the decode kernel's sources are the ones it was taken on.
-TRAFFIC = {"src_sha": "53f0d1d4b3460c6c", "fetch_bytes": 33204634, "write_bytes": 57344,
+TRAFFIC = {"src_sha": "d45f04b514375ebd", "fetch_bytes": 33204544, "write_bytes": 57344,
            "fetch_scale": 2.0, "write_scale": 1.0}
 DECODE_SOURCES = ("rowstream.hpp", "codepair.hpp", "gemv_core.hpp", "common.hpp", "qgemv.hip")
 
@@ -414,8 +414,10 @@ CASES = {
     "decode_b4_m1": (14336, 4096, 1, 4, 64, "bf16"),
     "skinny_b4_m16": (14336, 4096, 16, 4, 64, "bf16"),
     "skinny_b3_m8": (4096, 4096, 8, 3, 64, "f16"),
+    "rows_b3_m1": (4096, 4096, 1, 3, 64, "f16"),
     "prefill_b4_m2048": (14336, 4096, 2048, 4, 64, "bf16"),
     "moe_t1": 1,
+    "moe_t64": 64,
     "moe_t512": 512,
 }
 
