@@ -89,8 +89,11 @@ def test_edge_integral_widths(m, k, gs, bits, dt, act):
     edge_case(64, k, m, bits, gs, dt, seed=9000 + m + k + gs + bits, act=act)
 
 
-DENSE_CROSS = [(1, 4096, 32), (1, 4096, 128), (2, 4096, 64), (1, 14336, 64), (8, 4096, 64),
-               (40, 4096, 128)]
+# 3- and 6-bit codes: the row kernel at one and two rows (32-lane slots at K
+# <= 1024, seven units per lane at K = 14336) and at three and four rows
+# (their slices in registers), the skinny kernel, the tile GEMM.
+DENSE_CROSS = [(1, 4096, 32), (1, 4096, 128), (2, 4096, 64), (1, 14336, 64), (1, 1024, 32),
+               (3, 4096, 64), (4, 1024, 128), (8, 4096, 64), (40, 4096, 128)]
 
 
 @pytest.mark.parametrize("act", ACTS)
