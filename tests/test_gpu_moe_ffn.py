@@ -124,6 +124,36 @@ def test_moe_ffn_block_shape_sampled_tokens(T):
     check(y[tokens], out, bound, "ffn block shape")
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("dt", [BF16, F16])
+@pytest.mark.parametrize("T,top_k,E,F", [(1, 8, 16, 192), (3, 5, 16, 768), (2, 3, 8, 2048), (1, 4, 8, 4096)])
+def test_moe_ffn_fused_down_and_combine(bits, dt, T, top_k, E, F):
+    """At most one pair per expert on average: the down projection and the slot
+    combine run as one launch (rows of 6, 24, 64 and 128 units: 32- and 64-lane
+    slots, one and two units per lane)."""
+    c = ffn_case(T, top_k, E, 256, F, bits, 64, dt, 4500 + T + bits + F)
+    log(f"ffn fused down+combine: T={T} top_k={top_k} E={E} F={F} bits={bits} dt={dt}")
+    y = run_device(c)
+    torch.cuda.synchronize()
+    out, bound = reference_and_bound(c)
+    check(y, out, bound, "ffn fused down+combine")
+
+
+def test_moe_ffn_fused_invalid_ids_add_nothing():
+    """Invalid ids in the one-launch down + combine regime (8 pairs, 16 experts)."""
+    c = ffn_case(2, 4, 16, 256, 128, 4, 64, BF16, 4600)
+    ids = c["ids"].copy()
+    ids[[1, 6]] = [16, -3]                   # outside [0, 16)
+    y = run_device(c, ids=ids)
+    torch.cuda.synchronize()
+    ok_ids = ids.copy()
+    rw = c["rw"].copy()
+    bad = (ok_ids < 0) | (ok_ids >= 16)
+    ok_ids[bad], rw[bad] = 0, 0.0
+    out, bound = reference_and_bound(c, ids=ok_ids, rw=rw)
+    check(y, out, bound, "ffn fused invalid ids")
+
+
 def test_moe_ffn_invalid_ids_add_nothing():
     c = ffn_case(6, 4, 8, 256, 128, 4, 64, BF16, 4300)
     ids = c["ids"].copy()

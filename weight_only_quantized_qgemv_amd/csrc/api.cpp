@@ -632,6 +632,13 @@ qp_status qgemv_moe_ffn(const void* a, qp_dtype a_dtype, const int32_t* ids,
         return s;
     if (qp_status s = moe_common(dn, what); s != QP_OK)
         return s;
+    if (qp::moe_down_combine_ok(dn)) {
+        // Few tokens: the down projection and the slot combine in one launch,
+        // straight into `out` (the same values as the two launches below).
+        if (hipError_t e = qp::launch_moe(gu, stream); e != hipSuccess)
+            return hip_result(e, what);
+        return hip_result(qp::launch_moe_down_combine(dn, route_weights, out, stream), what);
+    }
     if (hipError_t e = qp::launch_moe_pair(gu, dn, stream); e != hipSuccess)
         return hip_result(e, what);
     qp::MoeCombineArgs c{o, ids, route_weights, n_tokens, top_k, d_model, num_experts,

@@ -195,4 +195,19 @@ struct MoeCombineArgs {
 };
 hipError_t launch_moe_combine(const MoeCombineArgs& a, hipStream_t stream);
 
+// The down projection of an MoE block fused with the slot combine, for few
+// tokens (one pair per tile; moe_rows.hpp, `qgemv_moe_rowcombine_kernel`):
+// out[t, r] = sum_j rw[t*top_k + j] * round(h[t*top_k + j] . W[ids][r]), the
+// same result as launch_moe on `dn` followed by launch_moe_combine. `dn` is the
+// plain (not fused) down call; out is [n_tokens, dn.n_rows] of dn.dt.
+constexpr int kMoeCombineMaxTopK = 8;
+bool moe_down_combine_ok(const MoeArgs& dn);
+hipError_t launch_moe_down_combine(const MoeArgs& dn, const float* rw, void* out, hipStream_t stream);
+#define QP_MOE_DC_DECL(B) \
+    hipError_t launch_moe_b##B##_dc(const MoeArgs& a, const float* rw, void* out, hipStream_t stream);
+QP_MOE_DC_DECL(2)
+QP_MOE_DC_DECL(4)
+QP_MOE_DC_DECL(8)
+#undef QP_MOE_DC_DECL
+
 } // namespace qp

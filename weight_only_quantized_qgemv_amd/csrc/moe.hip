@@ -337,6 +337,33 @@ hipError_t launch_moe_compute(const MoeArgs& a, const MoeRouting& r, hipStream_t
     return hipErrorInvalidValue;
 }
 
+bool moe_down_combine_ok(const MoeArgs& a)
+{
+    // Where the down projection would run on one-pair tiles (so the fused
+    // kernel reads each expert row once per token, as those tiles do), with
+    // at most kMoeCombineMaxTopK slots per token, and the whole stack, its
+    // scales and the output addressable with 32-bit offsets.
+    if (a.fused_silu || a.top_k < 1 || a.top_k > kMoeCombineMaxTopK)
+        return false;
+    if (!moe_rowstream_ok(a, 1) || moe_plan(a).rowstream == 0)
+        return false;
+    const int64_t es = 2;
+    const int64_t stack = a.E * a.n_rows;
+    return stack * (a.n_cols * a.bits / 8) < (int64_t(1) << 31) &&
+           stack * (a.n_cols / a.gs) * es < (int64_t(1) << 31) &&
+           a.n_tokens * a.n_rows * es < (int64_t(1) << 31);
+}
+
+hipError_t launch_moe_down_combine(const MoeArgs& a, const float* rw, void* out, hipStream_t st)
+{
+    switch (a.bits) {
+    case 2: return launch_moe_b2_dc(a, rw, out, st);
+    case 4: return launch_moe_b4_dc(a, rw, out, st);
+    case 8: return launch_moe_b8_dc(a, rw, out, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_moe(const MoeArgs& a, hipStream_t st)
 {
     MoeRouting r = moe_plan(a);

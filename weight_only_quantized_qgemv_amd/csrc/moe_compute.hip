@@ -270,7 +270,62 @@ hipError_t run_moe(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     }
 }
 
+#if QP_NMAT == 1 && (QP_BITS == 2 || QP_BITS == 4 || QP_BITS == 8)
+// The fused down projection and slot combine: grid x covers the output rows
+// (4 waves x 64 / KL rows per block), y the tokens.
+template <int BITS, int DT, int UPL, int KL>
+hipError_t run_rowcombine_upl(const GemvKernelArgs& k, const float* rw, int64_t n_tokens, hipStream_t st)
+{
+    constexpr int ROWS = 4 * (64 / KL);
+    int64_t gy = n_tokens < 65535 ? n_tokens : 65535;
+    gy = gy < 1 ? 1 : gy;
+    const dim3 grid((unsigned)((k.R + ROWS - 1) / ROWS), (unsigned)gy);
+    hipLaunchKernelGGL((qgemv_moe_rowcombine_kernel<BITS, DT, UPL, KL, kMoeCombineMaxTopK>), grid, dim3(256), 0,
+                       st, k, rw, n_tokens);
+    return hipGetLastError();
+}
+
+template <int BITS, int DT>
+hipError_t run_rowcombine(const MoeArgs& a, const float* rw, void* out, hipStream_t st)
+{
+    GemvKernelArgs k{};
+    k.x = a.a;
+    k.top_k = a.top_k;
+    k.outer = a.a_outer;
+    k.inner = a.a_inner;
+    k.ids = a.ids;
+    k.n_pairs = (int)(a.n_tokens * a.top_k);
+    k.n_experts = (int)a.E;
+    k.wq[0] = k.wq[1] = a.wq[0];
+    k.scales[0] = k.scales[1] = a.scales[0];
+    k.biases[0] = k.biases[1] = a.biases[0];
+    k.R = a.n_rows;
+    k.K = a.n_cols;
+    k.gs = a.gs;
+    k.out = out;
+    k.out_bytes = (uint32_t)(a.n_tokens * a.n_rows * 2);
+    k.x_bytes = (uint32_t)(((a.n_tokens - 1) * a.a_outer + (a.top_k - 1) * a.a_inner + a.n_cols) * 2);
+    const int64_t units = a.n_cols / 32;
+    if (units <= 32) return run_rowcombine_upl<BITS, DT, 1, 32>(k, rw, a.n_tokens, st);
+    if (units <= 64) return run_rowcombine_upl<BITS, DT, 1, 64>(k, rw, a.n_tokens, st);
+    if (units <= 128) return run_rowcombine_upl<BITS, DT, 2, 64>(k, rw, a.n_tokens, st);
+    return hipErrorInvalidValue;
+}
+#endif
+
 } // namespace
+
+#if QP_NMAT == 1 && (QP_BITS == 2 || QP_BITS == 4 || QP_BITS == 8)
+hipError_t QP_CAT(QP_CAT(launch_moe_b, QP_BITS), _dc)(const MoeArgs& a, const float* rw, void* out,
+                                                      hipStream_t st)
+{
+    switch (a.dt) {
+    case DT_F16: return run_rowcombine<QP_BITS, DT_F16>(a, rw, out, st);
+    case DT_BF16: return run_rowcombine<QP_BITS, DT_BF16>(a, rw, out, st);
+    }
+    return hipErrorInvalidValue;
+}
+#endif
 
 hipError_t QP_CAT(QP_CAT(QP_CAT(launch_moe_b, QP_BITS), _n), QP_NMAT)(const MoeArgs& a,
                                                                        const MoeRouting& r,

@@ -403,4 +403,159 @@ __global__ __launch_bounds__(256) void qgemv_moe_rowstream_kernel(GemvKernelArgs
     }
 }
 
+// The down projection of an MoE block fused with its close, for few tokens
+// (each pair its own tile): output row r of token t is
+//   out[t, r] = sum_j rw[t*top_k + j] * o_j[r],  o_j = h[t*top_k + j] . W[e_j][r]
+// (the ferrum-kernels MoE dispatch docs leave this weighted sum of a token's
+// slots to the FFN; router weights come from the caller). A slot of KL lanes
+// owns one row r and, for each of the token's top_k <= KM slots, loads that
+// expert's row r (one resource over the whole stack), forms o_j exactly as
+// the one-pair kernel above does (same units per lane, same dot chain, same
+// lane reduction), rounds it to the activation type as the stored o would be,
+// and sums the slots in slot order in fp32: the result is that of the two
+// separate launches, with one launch and no o round trip. The block gathers
+// all the token's pair rows into LDS as permuted slices with their sums.
+// Slots whose id is outside [0, E) read zeros and add nothing.
+template <int BITS, int DT, int UPL, int KL, int KM>
+__global__ __launch_bounds__(256) void qgemv_moe_rowcombine_kernel(GemvKernelArgs a, const float* __restrict__ rw,
+                                                                  int64_t n_tokens)
+{
+    using PX = RowStreamPair<DT>;
+    using E = Elem<DT>;
+    using St = typename E::storage;
+    static_assert(BITS == 2 || BITS == 4 || BITS == 8, "codes in whole 16-bit halves");
+    using CO = CodeOrder<BITS>;
+    static_assert(KL == 32 || KL == 64, "32 or 64 lanes per row");
+    constexpr int S = 64 / KL;                       // row slots per wave
+    constexpr int UNITS = KL * UPL;                  // unit slots of one pair's row
+    constexpr int ENTRIES = KM * UNITS;              // (slot, unit) slices of a token
+    constexpr int EPT = (ENTRIES + 255) / 256;
+    constexpr int SB = (int)sizeof(St);
+    __shared__ u32x4_t xl[KM][4][UNITS];
+    __shared__ float sl[KM][UNITS];
+
+    const int lane = threadIdx.x & 63;
+    const int kl = lane % KL, slot = lane / KL;
+    const int wv = (int)(threadIdx.x >> 6);
+    const int r0 = ((int)blockIdx.x * 4 + wv) * S + slot;   // the slot's output row
+    const int Rr = (int)a.R;
+    const int k = (int)a.top_k;
+    const uint32_t units_row = (uint32_t)(a.K / 32);
+    const uint32_t row_bytes = (uint32_t)a.K * BITS / 8;
+    const uint32_t groups_row = (uint32_t)(a.K / a.gs);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out, a.out_bytes);
+    const __amdgpu_buffer_rsrc_t rwq = make_rsrc(a.wq[0], (uint32_t)(a.n_experts * a.R) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales[0], (uint32_t)(a.n_experts * a.R) * groups_row * SB);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.biases[0], (uint32_t)(a.n_experts * a.R) * groups_row * SB);
+    uint32_t gofs[UPL];
+#pragma unroll
+    for (int j = 0; j < UPL; ++j)
+        gofs[j] = (uint32_t)((32 * (kl + KL * j)) / a.gs) * SB;
+
+    for (int64_t t = blockIdx.y; t < n_tokens; t += gridDim.y) {
+        // The token's experts (the same in every thread); -1 for an absent or
+        // invalid slot.
+        int ex[KM];
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            const int e = j < k ? a.ids[t * k + j] : -1;
+            ex[j] = (e >= 0 && e < a.n_experts) ? e : -1;
+        }
+        uint32_t raw[EPT][16];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int idx = (int)threadIdx.x + 256 * e, j = idx / UNITS, u = idx % UNITS;
+            uint32_t off = OOB;
+            if (idx < ENTRIES && u < (int)units_row) {
+                int ej = -1;
+#pragma unroll
+                for (int jj = 0; jj < KM; ++jj)
+                    ej = jj == j ? ex[jj] : ej;
+                if (ej >= 0) {
+                    const uint32_t xrow = (uint32_t)t * (uint32_t)a.outer + (uint32_t)j * (uint32_t)a.inner;
+                    off = (xrow + 32u * (uint32_t)u) * (uint32_t)SB;
+                }
+            }
+            buffer_words<16>(rx, off, raw[e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        uint32_t w[KM][UPL][BITS];
+        St sv[KM][UPL], bv[KM][UPL];
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+#pragma unroll
+            for (int jj = 0; jj < UPL; ++jj) {
+                const int u = kl + KL * jj;
+                const bool live = ex[j] >= 0 && u < (int)units_row && r0 < Rr;
+                const uint32_t row = (uint32_t)(ex[j] < 0 ? 0 : ex[j]) * (uint32_t)Rr + (uint32_t)r0;
+                buffer_words<BITS, BITS == 8 ? 0 : kStreamPolicy>(
+                    rwq, live ? row * row_bytes + (uint32_t)u * (4 * BITS) : OOB, w[j][jj]);
+                const uint32_t so = live ? row * groups_row * SB + gofs[jj] : OOB;
+                sv[j][jj] = buffer_elem<DT>(rs, so);
+                bv[j][jj] = buffer_elem<DT>(rb, so);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int idx = (int)threadIdx.x + 256 * e, j = idx / UNITS, u = idx % UNITS;
+            if (idx < ENTRIES) {
+                uint32_t q4[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int k0 = CO::lo_code(q), k1 = CO::hi_code(q);
+                    const uint32_t lo = (raw[e][k0 / 2] >> (16 * (k0 & 1))) & 0xFFFFu;
+                    const uint32_t hi = (raw[e][k1 / 2] >> (16 * (k1 & 1))) & 0xFFFFu;
+                    q4[q] = lo | (hi << 16);
+                }
+                float sum = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 32; ++c)
+                    sum += E::to_f32((uint16_t)(raw[e][c / 2] >> (16 * (c & 1))));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xl[j][q][u] = u32x4_t{q4[4 * q], q4[4 * q + 1], q4[4 * q + 2], q4[4 * q + 3]};
+                sl[j][u] = sum;
+            }
+        }
+        __syncthreads();
+
+        float acc[KM];
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            float total = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < UPL; ++jj) {
+                const int u = kl + KL * jj;
+                const Orient o = orient<BITS>(E::to_f32(sv[j][jj]), E::to_f32(bv[j][jj]));
+                uint32_t cp[16];
+                code_pairs<BITS, DT>(w[j][jj], o.flip, cp);
+                float part = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4_t v = xl[j][q][u];
+                    part = PX::dot(cp[4 * q], v.x, part);
+                    part = PX::dot(cp[4 * q + 1], v.y, part);
+                    part = PX::dot(cp[4 * q + 2], v.z, part);
+                    part = PX::dot(cp[4 * q + 3], v.w, part);
+                }
+                total = __builtin_fmaf(o.s, part, __builtin_fmaf(o.b, sl[j][u], total));
+            }
+            acc[j] = total;
+        }
+        reduce_slots<KM, KL>(acc);
+        if (kl == KL - 1 && r0 < Rr) {
+            float v = 0.0f;
+#pragma unroll
+            for (int j = 0; j < KM; ++j)
+                if (ex[j] >= 0)
+                    v = __builtin_fmaf(rw[t * k + j], E::to_f32(E::from_f32(acc[j])), v);
+            buffer_store_elem<DT>(E::from_f32(v), ro, ((uint32_t)t * (uint32_t)Rr + (uint32_t)r0) * (uint32_t)SB);
+        }
+        __syncthreads();   // the slices are rebuilt for the next token
+    }
+}
+
 } // namespace qp
