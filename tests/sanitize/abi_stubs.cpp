@@ -34,7 +34,11 @@ STUB(hipError_t launch_dequantize_int8_tensor(const int8_t*, int64_t, const floa
                                               hipStream_t))
 STUB(hipError_t launch_qmatmul_int8_tensor(const Int8TensorArgs&, hipStream_t))
 STUB(hipError_t launch_moe_combine(const MoeCombineArgs&, hipStream_t))
+STUB(hipError_t launch_moe_down_combine(const MoeArgs&, const float*, void*, hipStream_t))
 #undef STUB
+
+// The FFN block takes its two-launch close in this build.
+bool moe_down_combine_ok(const MoeArgs&) { return false; }
 
 bool qgemm_mx_fits(const GemvMxArgs&) { return false; }
 // Sizes only need to be positive and grow with the problem here.
