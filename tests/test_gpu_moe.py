@@ -374,3 +374,32 @@ def test_moe_routed_scales_not_dword_aligned():
     ref, S = qref.moe(a_s, BF16, ids, P, 1, C, 0, *h, BF16, E, R, C, bits, gs)
     assert_within(out, ref, S, BF16, "scales 2 mod 4")
     assert_within(out_al, ref, S, BF16, "scales aligned")
+
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_moe_routed_gemm_persistent_blocks_walk_several_items(dt):
+    """More (tile, row block) items than the GPU holds routed-GEMM blocks at
+    once (two per CU at 4-bit, about 512), so every persistent block walks two
+    or three items of its XCD's stretch of the work list: 64 experts with 32
+    pairs each (one 64-pair tile per expert) times 23 row blocks is 1472
+    items, 184 per XCD, which the 64 blocks of an XCD do not divide."""
+    T, top_k, E, C, bits, gs = 256, 8, 64, 128, 4, 64
+    log(f"moe routed gemm persistent dt={dt}")
+    ids = synth.moe_ids(T, top_k, E, seed=191).ravel()
+    assert np.bincount(ids, minlength=E).min() >= 16
+    ids_d = torch.from_numpy(ids).to(dev())
+    a_s, a_d = activations((T, C), dt, 192)
+    R = 23 * 256                      # plain form: 256 rows per item
+    w_h, w_d = stack(E, R, C, bits, gs, dt, 193)
+    g = qp.qgemv_moe_id(a_d, ids_d, T, top_k, C, 0, *w_d, bits, gs)
+    torch.cuda.synchronize()
+    ref, S = qref.moe(a_s, dt, ids, T, top_k, C, 0, *w_h, dt, E, R, C, bits, gs)
+    assert_within(g, ref, S, dt, "routed plain, persistent blocks")
+    del w_d
+    Rf = 23 * 128                     # fused form: 128 gate + 128 up rows per item
+    gate_h, gate_d = stack(E, Rf, C, bits, gs, dt, 194)
+    up_h, up_d = stack(E, Rf, C, bits, gs, dt, 195)
+    out = qp.qgemv_moe_id_gate_up_silu(a_d, ids_d, T, top_k, C, 0, gate_d, up_d, bits, gs)
+    torch.cuda.synchronize()
+    ref_f = qref.moe_gate_up_silu(a_s, dt, ids, T, top_k, C, 0, gate_h, up_h, dt, E, Rf, C, bits, gs)
+    check_fused(out, ref_f, dt, "routed gate_up, persistent blocks")

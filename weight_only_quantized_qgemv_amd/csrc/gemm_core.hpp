@@ -297,17 +297,22 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     const uint32_t wrow_bytes = (uint32_t)K * BITS / 8;
     const uint32_t groups = (uint32_t)(K / ga.gs);
 
-    // Tile of this block, XCD by XCD.
+    // Tile of this block, XCD by XCD. The routed form is persistent: its
+    // grid is at most what the GPU holds at once, and block l of XCD x takes
+    // the items x * per_xcd + l, + B, + 2B, ... of the device-written work
+    // list (B = blocks per XCD), so each XCD runs one contiguous stretch of
+    // the list (an expert's row blocks side by side). The dense form takes
+    // one tile per block.
     const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+    for (int iter = 0;; ++iter) {
     int m0 = 0, n0, expert = 0, start = 0, count = 0;
     if constexpr (ROUTED) {
-        // The grid covers the largest possible tile list; the real one is
-        // spread evenly over the XCDs and the remaining blocks exit.
         const int work = *ga.n_tiles * ga.tiles_n;
         const int per_xcd = (work + 7) / 8;
-        if (local >= per_xcd)
+        const int l = local + iter * (int)(gridDim.x / 8);
+        if (l >= per_xcd)
             return;
-        const int w = xcd * per_xcd + local;
+        const int w = xcd * per_xcd + l;
         if (w >= work)
             return;
         const TileDesc d = ga.tdesc[w / ga.tiles_n];
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         count = d.count;
         n0 = (w % ga.tiles_n) * BNO;
     } else {
-        if (local >= ga.per_xcd)
+        if (iter > 0 || local >= ga.per_xcd)
             return;
         const int tile = xcd * ga.per_xcd + local;
         if (tile >= ga.tiles)
@@ -640,7 +645,8 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
         a_cur = a_nxt;
         c_cur = c_nxt;
     }
-    // No DMA may still be writing this block's LDS when the block ends.
+    // No DMA of this tile may still be writing the block's LDS when the
+    // block ends or its next tile's DMA starts.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
     // Epilogue: lane l, register r of a 32 x 32 tile holds
@@ -671,6 +677,9 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
                 __builtin_amdgcn_raw_buffer_store_b16(Elem<DT>::from_f32(v), ry, off, 0, 0);
             }
         }
+    }
+    // Every wave leaves the tile before any starts the next one's DMA.
+    __builtin_amdgcn_s_barrier();
     }
 }
 

@@ -7,7 +7,33 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qp {
+
+// Compute units of the current device, asked of the runtime once per device
+// and kept (persistent grids are sized from it).
+inline hipError_t device_cu_count(int* cus)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return hipSuccess;
+        }
+    }
+    e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess && cached && *cus > 0)
+        cache[dev].store(*cus, std::memory_order_relaxed);
+    return e;
+}
 
 struct GemvArgs {
     const void* x;          // [M, K] activations

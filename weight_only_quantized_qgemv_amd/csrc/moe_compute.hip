@@ -91,10 +91,12 @@ hipError_t run_skinny_tiles(GemvKernelArgs k, int64_t max_tiles, hipStream_t st)
 
 // Routed GEMM (gemm_core.hpp): tiles of BM pairs of one expert times BN / NMAT
 // rows of each of its NMAT matrices, four waves side by side along the rows
-// (each weight fragment is built by one wave only); grid x covers every
-// (tile, row block) of the largest possible tile list, XCD by XCD. Three
-// activation stages and four code / scale stages: 64 KB of LDS at 4-bit, so
-// two blocks share a CU (four activation stages measured the same).
+// (each weight fragment is built by one wave only). The blocks are
+// persistent: the grid is the smaller of the largest possible work list
+// ((tile, row block) items) and the blocks the GPU holds at once, and each
+// block walks its XCD's stretch of the device-written list. Three activation
+// stages and four code / scale stages: 64 KB of LDS at 4-bit, so two blocks
+// share a CU (four activation stages measured the same).
 #ifndef QP_MOE_GEMM_NA
 #define QP_MOE_GEMM_NA 3
 #endif
@@ -114,8 +116,12 @@ hipError_t run_gemm_tiles(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     const void* kern = reinterpret_cast<const void*>(
         &gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, 1, NMAT, true, NA, NC>);
     static bool attr_set = false; // per instantiation; set before its first launch
+    static int per_cu = 0;        // blocks of this kernel one CU holds at once
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        if (e != hipSuccess)
+            return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, NT, LDS);
         if (e != hipSuccess)
             return e;
         attr_set = true;
@@ -144,7 +150,12 @@ hipError_t run_gemm_tiles(const MoeArgs& a, const MoeRouting& r, hipStream_t st)
     g.top_k = (int)a.top_k;
     g.outer_b = (uint32_t)(a.a_outer * 2);
     g.inner_b = (uint32_t)(a.a_inner * 2);
-    const int64_t blocks = (r.max_tiles * g.tiles_n + 7) / 8 * 8;
+    int cus = 0;
+    hipError_t e = device_cu_count(&cus);
+    if (e != hipSuccess)
+        return e;
+    const int64_t resident = std::max<int64_t>(8, (int64_t)std::max(per_cu, 1) * cus / 8 * 8);
+    const int64_t blocks = std::min((r.max_tiles * g.tiles_n + 7) / 8 * 8, resident);
     hipLaunchKernelGGL((gemm::qgemm_tile_kernel<BITS, DT, BM, BN, NT, 1, NMAT, true, NA, NC>),
                        dim3((unsigned)blocks), dim3(NT), LDS, st, g);
     return hipGetLastError();
