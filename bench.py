@@ -78,9 +78,43 @@ def copies_for(nbytes):
     return max(2, -(-ROTATE_BYTES // nbytes))
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def hold_stream(stream, calls, us_per_call=10.0):
+    """Keeps `stream` busy on a device spin (torch's sleep kernel) for about
+    `calls` x `us_per_call` microseconds, so that the host has queued all of
+    the timed calls before the start event that follows it is reached. The
+    timed region then holds device work only: without it, its first call
+    starts one host issue time (about 5 us) after the start event, which at
+    20 timed calls adds about 0.25 us to every call. The spin runs before the
+    start event and is not part of any timed region."""
+    import torch
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        probe = 2_000_000
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(probe)   # first launch (module load), untimed
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(probe)
+        b.record(stream)
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = probe / max(a.elapsed_time(b), 1e-3)
+    cycles = int(_SLEEP_CYCLES_PER_MS * calls * us_per_call * 1e-3)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(max(cycles, 1))
+
+
 def time_calls(fn, steps, warmup, stream, reps=5):
     """Median over `reps` of the mean ms per call over `steps` back-to-back
-    calls, HIP events recorded on `stream` (the stream the kernels run on)."""
+    calls, HIP events recorded on `stream` (the stream the kernels run on).
+    Each repetition starts from a synchronized device, holds the stream
+    (`hold_stream`) while the host queues the calls, and times exactly the
+    `steps` calls between its two events."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -89,6 +123,7 @@ def time_calls(fn, steps, warmup, stream, reps=5):
     for _ in range(reps):
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
+        hold_stream(stream, steps, 12.0)
         start.record(stream)
         for i in range(steps):
             fn(i)
@@ -119,6 +154,7 @@ def graph_ms(fn, n, stream, reps=5):
     for _ in range(reps):
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
+        hold_stream(stream, 1, 50.0)
         start.record(stream)
         g.replay()
         end.record(stream)
