@@ -186,7 +186,10 @@ def test_qmatmul_tiny_config_full(m):
     assert_within(y, y_ref, S, F32, "tiny")
 
 
-def sampled_check(y, xs, dt, rq, rs, rb, k, bits, gs, n_samples=3000, seed=0, tau=None):
+def sampled_check(y, xs, dt, rq, rs, rb, k, bits, gs, n_samples=3000, seed=0, tau=None, blocks=()):
+    """Random outputs, the four corners, and every output of each 256 x 256
+    block (m0, n0) in `blocks` (whole tiles of the matrix-core GEMM, so every
+    lane, register and wave position of a tile is checked)."""
     m, n = y.shape
     g = synth.rng(seed)
     mi = g.integers(0, m, n_samples)
@@ -194,6 +197,11 @@ def sampled_check(y, xs, dt, rq, rs, rb, k, bits, gs, n_samples=3000, seed=0, ta
     # Always include the corners and the last row (ragged tails).
     mi = np.concatenate([mi, [0, m - 1, 0, m - 1]])
     ni = np.concatenate([ni, [0, 0, n - 1, n - 1]])
+    for (m0, n0) in blocks:
+        bm, bn = np.meshgrid(np.arange(m0, min(m0 + 256, m)), np.arange(n0, min(n0 + 256, n)),
+                             indexing="ij")
+        mi = np.concatenate([mi, bm.ravel()])
+        ni = np.concatenate([ni, bn.ravel()])
     y_ref, S = qref.qmatmul_sampled(xs, dt, rq, rs, rb, dt, k, bits, gs, mi, ni)
     yv = values(y)[mi, ni]
     assert_within(torch.from_numpy(yv), y_ref, S, dt, "sampled", tau=tau)
@@ -254,13 +262,17 @@ def test_qmatmul_many_rows_k_not_multiple_of_64(k, bits, dt):
     ((2048, 14336), (4096, 14336), 44, 42),
 ])
 def test_qmatmul_prefill_config_sampled(shape_x, shape_w, xseed, wseed):
+    """3,000 random outputs and four whole 256 x 256 blocks (the first, the
+    last, and two interior ones at different XCD positions of the tile grid)."""
     log(f"prefill config x={shape_x} w={shape_w}")
     w = synth.normal_f32(shape_w, 0.02, wseed)
     (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, 4, 64, BF16)
     xs, xt = activations(shape_x, BF16, xseed)
     y = qp.qmatmul(xt, gq, gs_, gb, 4, 64)
     torch.cuda.synchronize()
-    sampled_check(y, xs, BF16, rq, rs, rb, shape_w[1], 4, 64, seed=xseed)
+    m, n = shape_x[0], shape_w[0]
+    blocks = [(0, 0), (m - 256, n - 256), (768, 1280), (1536, n // 2 + 256)]
+    sampled_check(y, xs, BF16, rq, rs, rb, shape_w[1], 4, 64, seed=xseed, blocks=blocks)
 
 
 def test_qmatmul_k_zero_writes_zeros():
