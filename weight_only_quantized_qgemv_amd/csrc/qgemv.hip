@@ -181,7 +181,7 @@ hipError_t run_skinny(const GemvArgs& a, hipStream_t st, bool* done)
 template <int BITS, int DT, int MT, int UPL>
 hipError_t run_rowstream(const GemvArgs& a, int64_t m0, int mc, hipStream_t st)
 {
-    constexpr int D = rowstream_depth<BITS, UPL>();
+    constexpr int D = rowstream_depth<BITS, UPL, MT>();
     RowStreamArgs k{};
     k.x = static_cast<const char*>(a.x) + m0 * a.K * 2;
     k.wq = a.wq;

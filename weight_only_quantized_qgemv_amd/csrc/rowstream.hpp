@@ -68,10 +68,21 @@ template <> struct RowStreamPair<DT_F16> {
 // VALU work per byte (the fields are spread to bytes first), so their waves
 // take half as many rows: 14336 x 4096 3-bit 8.7 us with 2 rows against 9.6
 // us with 4; at 6 bits one row (12.4 us) was slower than two (11.9 us).
-template <int BITS, int UPL> constexpr int rowstream_depth()
+// Two activation rows double the dot products per row, and two rows per wave
+// measured best for them at up to two units per lane (14336 x 4096, M = 2:
+// 4-bit 9.85 us against 10.5 with three rows, 8-bit 13.1 against 14.7 with
+// one, 2-bit 8.9 against 9.5 with four). Two-bit rows of seven or eight units
+// per lane take two rows rather than one (4096 x 14336: 8.3 us against 9.7).
+template <int BITS, int UPL, int MT = 1> constexpr int rowstream_depth()
 {
     constexpr int B = BITS == 3 ? 12 : 24;
-    return B / (BITS * UPL) < 1 ? 1 : (B / (BITS * UPL) > 4 ? 4 : B / (BITS * UPL));
+    constexpr int d = B / (BITS * UPL) < 1 ? 1 : (B / (BITS * UPL) > 4 ? 4 : B / (BITS * UPL));
+    if constexpr (MT == 2 && UPL <= 2 && (BITS == 2 || BITS == 4 || BITS == 8))
+        return 2;
+    else if constexpr (BITS == 2 && d < 2)
+        return 2;
+    else
+        return d;
 }
 
 template <int BITS, int DT, int MT, int UPL, int WPB, bool WIDE, int KL>
@@ -81,7 +92,7 @@ __global__ __launch_bounds__(64 * WPB) void qgemv_rowstream_kernel(RowStreamArgs
     using E = Elem<DT>;
     using St = typename E::storage;
     static_assert(BITS == 2 || BITS == 3 || BITS == 4 || BITS == 6 || BITS == 8, "code widths");
-    constexpr int D = rowstream_depth<BITS, UPL>();
+    constexpr int D = rowstream_depth<BITS, UPL, MT>();
     using CO = CodeOrder<BITS>;
     const int lane = threadIdx.x & 63;
     // A wave is S slots of KL lanes (KL = 32 for rows of at most 32 units, so
