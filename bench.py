@@ -49,6 +49,14 @@ TRAFFIC = {"src_sha": "019072a3f4a4daa1", "fetch_bytes": 33197056, "write_bytes"
            "fetch_scale": 2.0, "write_scale": 1.0}
 DECODE_SOURCES = ("rowstream.hpp", "codepair.hpp", "gemv_core.hpp", "common.hpp", "qgemv.hip")
 
+# Shader clock under the prefill's own load, from rocprofv3 --pmc GRBM_GUI_ACTIVE
+# (summed over the 8 XCDs) against the kernel trace of the same command
+# (`bench.py --case NAME --steps 10 --warmup 2`): the chip runs the matrix
+# cores below the 2.4 GHz of the nominal peak. The prefill rows report their
+# fraction of the bf16 matrix peak at this clock beside the nominal one.
+PROFILED_CLOCK_GHZ = {"prefill_m2048_n14336_k4096": 1.77, "prefill_m2048_n4096_k14336": None}
+NOMINAL_CLOCK_GHZ = 2.4
+
 
 def decode_src_sha() -> str:
     h = hashlib.sha256()
@@ -452,6 +460,7 @@ CASES = {
     "skinny_b3_m8": (4096, 4096, 8, 3, 64, "f16"),
     "rows_b3_m1": (4096, 4096, 1, 3, 64, "f16"),
     "prefill_b4_m2048": (14336, 4096, 2048, 4, 64, "bf16"),
+    "prefill_b4_m2048_k14336": (4096, 14336, 2048, 4, 64, "bf16"),
     "moe_t1": 1,
     "moe_t64": 64,
     "moe_t512": 512,
@@ -511,10 +520,12 @@ def main():
     bf16 = torch.bfloat16
     N, K, BITS, GS = 14336, 4096, 4, 64
     # The timed K steps: eager calls, back to back, rotating over the weight
-    # copies. Beside them, the same K calls captured once into a HIP graph and
-    # replayed (no host issue between launches).
+    # copies. Beside them, the same calls (at least 136 of them, so that the
+    # graph's own start-up is spread thin) captured once into a HIP graph and
+    # replayed (no launch API between the kernels).
     (ms, ms_graph), wb, copies = bench_dense(N, K, 1, BITS, GS, bf16, args.steps, args.warmup,
-                                             stream, dev, graph=True, graph_calls=args.steps)
+                                             stream, dev, graph=True,
+                                             graph_calls=max(args.steps, 136))
     gbs = wb / (ms * 1e-3) / 1e9
     traffic = None
     if TRAFFIC is not None and TRAFFIC.get("src_sha") == decode_src_sha():
@@ -597,10 +608,16 @@ def main():
         for (n, k) in ((14336, 4096), (4096, 14336)):
             ms_r, _, _ = bench_dense(n, k, 2048, 4, 64, bf16, 20, 3, stream, dev, seed=41)
             tf = 2.0 * 2048 * n * k / (ms_r * 1e-3) / 1e12
-            rows[f"prefill_m2048_n{n}_k{k}"] = {
+            key = f"prefill_m2048_n{n}_k{k}"
+            rows[key] = {
                 "us": round(ms_r * 1e3, 2), "tflops": round(tf, 1),
                 "frac_bf16_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                 "tokens_per_s": round(2048 / (ms_r * 1e-3), 1)}
+            clk = PROFILED_CLOCK_GHZ.get(key)
+            if clk:
+                rows[key]["profiled_clock_ghz"] = clk
+                rows[key]["frac_bf16_mfma_at_profiled_clock"] = round(
+                    tf / (MFMA_BF16_PEAK_TFLOPS * clk / NOMINAL_CLOCK_GHZ), 4)
         # Unfused rows: dequantize to a dense bf16 weight, then torch.matmul, on
         # the decode and prefill shapes, beside the fused call measured above.
         for M, fused_key in ((1, "decode_b4_m1"), (2048, "prefill_m2048_n14336_k4096")):
