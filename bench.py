@@ -99,6 +99,8 @@ def hold_stream(stream, calls, us_per_call=10.0):
     start event and is not part of any timed region."""
     import torch
     global _SLEEP_CYCLES_PER_MS
+    if not hasattr(torch.cuda, "_sleep"):
+        return   # no sleep kernel in this torch: time without the hold
     if _SLEEP_CYCLES_PER_MS is None:
         probe = 2_000_000
         with torch.cuda.stream(stream):
