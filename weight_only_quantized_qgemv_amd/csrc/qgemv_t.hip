@@ -106,18 +106,39 @@ __global__ __launch_bounds__(64 * kWaves) void qgemv_t_partial_kernel(QgemvTArgs
                 xsv[m] = xv * s;
                 accb[m] = __builtin_fmaf(xv, b, accb[m]);
             }
+            if constexpr (BITS == 4) {
+                // Codes 8v .. 8v + 7 of word v, exact in fp32 two at a time:
+                // a mask per nibble parity puts them in bytes, and the FP8
+                // (E4M3) pair conversion with scale 2^9 returns each byte
+                // b <= 15 as b itself.
 #pragma unroll
-            for (int c = 0; c < C::CODES; ++c) {
-                const int bit = c * BITS, wi = bit / 32, sh = bit % 32;
-                uint32_t qc;
-                if (sh + BITS <= 32)
-                    qc = (w[u][wi] >> sh) & mask;
-                else
-                    qc = __builtin_amdgcn_alignbit(w[u][wi + 1], w[u][wi], sh) & mask;
-                const float q = (float)qc;
+                for (int v = 0; v < C::WORDS; ++v) {
+                    const uint32_t ev = w[u][v] & 0x0F0F0F0Fu, od = (w[u][v] >> 4) & 0x0F0F0F0Fu;
+                    const f32x2_t e01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 512.0f, false);
+                    const f32x2_t e23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 512.0f, true);
+                    const f32x2_t o01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(od, 512.0f, false);
+                    const f32x2_t o23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(od, 512.0f, true);
+                    const float q[8] = {e01.x, o01.x, e01.y, o01.y, e23.x, o23.x, e23.y, o23.y};
 #pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    acc[m][c] = __builtin_fmaf(q, xsv[m], acc[m][c]);
+                    for (int j = 0; j < 8; ++j)
+#pragma unroll
+                        for (int m = 0; m < MT; ++m)
+                            acc[m][8 * v + j] = __builtin_fmaf(q[j], xsv[m], acc[m][8 * v + j]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < C::CODES; ++c) {
+                    const int bit = c * BITS, wi = bit / 32, sh = bit % 32;
+                    uint32_t qc;
+                    if (sh + BITS <= 32)
+                        qc = (w[u][wi] >> sh) & mask;
+                    else
+                        qc = __builtin_amdgcn_alignbit(w[u][wi + 1], w[u][wi], sh) & mask;
+                    const float q = (float)qc;
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        acc[m][c] = __builtin_fmaf(q, xsv[m], acc[m][c]);
+                }
             }
         }
     }
