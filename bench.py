@@ -705,6 +705,9 @@ def main():
                 "ffn_block_weight_GBps": round(3 * touched * per_expert / (ms_ffn * 1e-3) / 1e9, 1),
                 "ffn_block_total_bytes": ffn_all,
                 "ffn_block_total_GBps": round(ffn_all / (ms_ffn * 1e-3) / 1e9, 1),
+                "tokens_per_s": {"gate_up_silu": round(T / (ms_gu * 1e-3), 1),
+                                 "down": round(T / (ms_d * 1e-3), 1),
+                                 "ffn_block": round(T / (ms_ffn * 1e-3), 1)},
                 **{k: round(v * 1e3, 3) for k, v in graph.items()}}
         result["rows"] = rows
 
