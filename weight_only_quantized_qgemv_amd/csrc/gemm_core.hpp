@@ -304,7 +304,7 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     // the list (an expert's row blocks side by side). The dense form takes
     // one tile per block.
     const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-    for (int iter = 0;; ++iter) {
+    for (int iter = 0;; ++iter) { // the tile loop, through the epilogue below
     int m0 = 0, n0, expert = 0, start = 0, count = 0;
     if constexpr (ROUTED) {
         const int work = *ga.n_tiles * ga.tiles_n;
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(THREADS) void qgemm_tile_kernel(GemmArgs ga)
     }
     // Every wave leaves the tile before any starts the next one's DMA.
     __builtin_amdgcn_s_barrier();
-    }
+    } // the tile loop (its body is left at the kernel's indentation)
 }
 
 } // namespace gemm
