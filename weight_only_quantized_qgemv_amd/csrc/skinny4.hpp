@@ -1,6 +1,6 @@
-// skinny4.hpp — skinny products (M = 5..16 activation rows) of 4-bit codes on
-// the 16x16x32 matrix instruction, with row-contiguous code loads (emily
-// lib/emily/quantization.ex, `quantized_matmul/2`; affine codes of
+// skinny4.hpp — skinny products (M = 3..16 activation rows) of 4- and 2-bit
+// codes on the 16x16x32 matrix instruction, with row-contiguous code loads
+// (emily lib/emily/quantization.ex, `quantized_matmul/2`; affine codes of
 // `dequantize_defn/1`):
 //   y[m, n] = sum_g s'[n,g] * sum_{k in g} x q + b'[n,g] * sum_{k in g} x.
 //
@@ -11,35 +11,45 @@
 // orientation it applies are that row's own.
 //
 // A wave owns a K-slice of 16 units and up to four row groups of 16 weight
-// rows. A row group's codes (16 rows x 16 units x 16 bytes) arrive as four
-// loads per lane, each covering four rows with 256 contiguous bytes of each
-// (16 lanes per row); the wave writes them to its own LDS, [row][slice][unit]
-// dwords, and every lane reads back its row's 16 dwords of k-slice kg: the
-// eight codes of one instruction per unit. A row group's scales and biases
-// over the slice are one or two 16-byte loads per lane (its row's groups).
-// Two row groups are in flight while one is computed. The activations of the
-// slice are staged through the same LDS first (as in skinny.hpp), and the
-// row groups' sums meet across the K-slice waves at the end.
+// rows. A row group's codes (16 rows x 16 units x 16 or 8 bytes) arrive as
+// four loads per lane, each covering four rows with 256 (128) contiguous
+// bytes of each (16 lanes per row); the wave writes them to its own LDS,
+// [row][dword of the unit][unit], and every lane reads back its row's 16
+// dwords holding k-slice kg of each unit (at 2 bits a dword holds two
+// k-slices, 16 bits each): the eight codes of one instruction per unit. A
+// row group's scales and biases over the slice are one or two 16-byte loads
+// per lane (its row's groups). Two row groups are in flight while one is
+// computed. The activations of the slice are staged through the same LDS
+// first (as in skinny.hpp), and the row groups' sums meet across the K-slice
+// waves at the end.
 #pragma once
 
 #include "skinny.hpp"
 
 namespace qp {
 
-constexpr uint32_t kSk4CodeRow = 68;                       // dwords per weight row in LDS (64 + 4: banks)
-constexpr uint32_t kSk4CodeBuf = 16 * kSk4CodeRow * 4;     // bytes of one row group's codes
+// Dwords per weight row in LDS: the slice's 16 units (4 dwords each at 4
+// bits, 2 at 2 bits) plus 4 against bank conflicts; bytes of one row group's codes.
+template <int BITS> __host__ __device__ constexpr uint32_t sk4_code_row() { return 16u * BITS + 4u; }
+template <int BITS> __host__ __device__ constexpr uint32_t sk4_code_buf() { return 16u * sk4_code_row<BITS>() * 4u; }
 __host__ __device__ constexpr uint32_t skinny4_wave_lds()
 {
     // Activation staging (later two code buffers, then the partial sums),
     // then the group sums of the slice's activations.
     return 16u * kSkinnyXRow + 1024u;
 }
-static_assert(2 * kSk4CodeBuf <= 16 * kSkinnyXRow && (uint32_t)kSkinnyRG * 1024u <= 16 * kSkinnyXRow,
+static_assert(2 * sk4_code_buf<4>() <= 16 * kSkinnyXRow && (uint32_t)kSkinnyRG * 1024u <= 16 * kSkinnyXRow,
               "code buffers and partial sums within the staging region");
 
-template <int DT, int GU>
+template <int BITS, int DT, int GU>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(GemvKernelArgs a, SkinnyShape sh)
 {
+    static_assert(BITS == 2 || BITS == 4, "2- and 4-bit codes");
+    // A lane's piece of a row per row quad: 16 bytes (4-bit) or 8 (2-bit),
+    // 4 or 2 dwords, each holding one k-slice (4-bit) or two (2-bit, 16 bits
+    // each) of the unit.
+    constexpr int PW = BITS;                        // dwords per unit
+    constexpr uint32_t CR = sk4_code_row<BITS>();
     using M16 = SkMfma<DT>;
     using frag_t = typename M16::frag_t;
     using E = Elem<DT>;
@@ -58,7 +68,7 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
     const int g = lane >> 4, l16 = lane & 15;
     const int R = (int)a.R;
     const int K = (int)a.K;
-    const uint32_t row_bytes = (uint32_t)K / 2;
+    const uint32_t row_bytes = (uint32_t)K * BITS / 8;
     const uint32_t G = (uint32_t)(K / a.gs);
     constexpr uint32_t WL = skinny4_wave_lds();
     char* const xst = lds + (uint32_t)wave * WL;            // staging; code buffers; partial sums
@@ -102,10 +112,10 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
         __builtin_amdgcn_sched_barrier(0);
 
         // The ring: row group rgi (rows 16 (wri + wr rgi) .. + 15 of the block).
-        // Load q of lane l: row 4 q + l / 16 of the group, bytes 16 (l % 16)
-        // of the slice's 256; the row's scale and bias dwords over the slice.
+        // Load q of lane l: row 4 q + l / 16 of the group, unit l % 16 of the
+        // slice (16 or 8 bytes); the row's scale and bias dwords over the slice.
         struct Slot {
-            u32x4_t c[4];
+            uint32_t c[4][PW];
             uint32_t s[SBW], b[SBW];
         };
         auto fetch = [&](int rgi, Slot& sl) {
@@ -113,8 +123,14 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t row = rg0 + 4u * (uint32_t)q + (uint32_t)g;
-                sl.c[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                    rw, row * row_bytes + (uint32_t)u0 * 16u + 16u * (uint32_t)l16, 0, 0));
+                const uint32_t off = row * row_bytes + ((uint32_t)u0 + (uint32_t)l16) * (4u * PW);
+                if constexpr (PW == 4) {
+                    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+                    sl.c[q][0] = v.x; sl.c[q][1] = v.y; sl.c[q][2] = v.z; sl.c[q][3] = v.w;
+                } else {
+                    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, 0));
+                    sl.c[q][0] = v.x; sl.c[q][1] = v.y;
+                }
             }
             const uint32_t soff = ((rg0 + (uint32_t)l16) * G + (uint32_t)(u0 / GU)) * SB;
             if constexpr (SBW == 8) {
@@ -178,25 +194,26 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
         static_for<kSkinnyRG>([&](auto RGI) {
             constexpr int rgi = decltype(RGI)::value;
             Slot& sl = ring[rgi % 2];
-            char* const cb = xst + (uint32_t)(rgi % 2) * kSk4CodeBuf;   // the staging is done with
+            char* const cb = xst + (uint32_t)(rgi % 2) * sk4_code_buf<BITS>();   // the staging is done with
             __builtin_amdgcn_sched_barrier(0);
-            // Codes to LDS as [row][k-slice][unit] dwords, then this lane's
-            // row (l16) at k-slice g: 16 consecutive dwords, one per unit.
+            // Codes to LDS as [row][dword of the unit][unit], then this
+            // lane's row (l16) at its k-slice g: 16 consecutive dwords, one
+            // per unit (dword g at 4 bits; dword g / 2 at 2 bits, whose half
+            // g % 2 is the slice).
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t row = 4u * (uint32_t)q + (uint32_t)g;
-                const u32x4_t v = sl.c[q];
-                uint32_t* const d = reinterpret_cast<uint32_t*>(cb) + row * kSk4CodeRow + (uint32_t)l16;
-                d[0] = v.x;
-                d[16] = v.y;
-                d[32] = v.z;
-                d[48] = v.w;
+                uint32_t* const d = reinterpret_cast<uint32_t*>(cb) + row * CR + (uint32_t)l16;
+#pragma unroll
+                for (int j = 0; j < PW; ++j)
+                    d[16 * j] = sl.c[q][j];
             }
+            const uint32_t gd = BITS == 4 ? (uint32_t)g : (uint32_t)g >> 1;
             uint32_t dw[kSkinnyKW];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
-                    cb + ((uint32_t)l16 * kSk4CodeRow + 16u * (uint32_t)g + 4u * (uint32_t)i) * 4u);
+                    cb + ((uint32_t)l16 * CR + 16u * gd + 4u * (uint32_t)i) * 4u);
                 dw[4 * i] = v.x; dw[4 * i + 1] = v.y; dw[4 * i + 2] = v.z; dw[4 * i + 3] = v.w;
             }
             uint32_t sv[SBW], bv[SBW];
@@ -213,15 +230,26 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
                 static_for<NGS>([&](auto GI) {
                     constexpr int gi = decltype(GI)::value;
                     const uint32_t sw = sv[gi / 2], bw = bv[gi / 2];
-                    const Orient o = orient<4>(E::to_f32((St)(sw >> (16 * (gi % 2)))),
-                                               E::to_f32((St)(bw >> (16 * (gi % 2)))));
+                    const Orient o = orient<BITS>(E::to_f32((St)(sw >> (16 * (gi % 2)))),
+                                                  E::to_f32((St)(bw >> (16 * (gi % 2)))));
                     f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int u = gi * GU; u < gi * GU + GU; ++u) {
-                        const uint32_t lo = (dw[u] ^ o.flip) & 0x0F0F0F0Fu;
-                        const uint32_t hi = ((dw[u] >> 4) ^ o.flip) & 0x0F0F0F0Fu;
-                        const u32x4_t bfr = u32x4_t{C::template fp8<false>(lo), C::template fp8<true>(lo),
-                                                    C::template fp8<false>(hi), C::template fp8<true>(hi)};
+                        u32x4_t bfr;
+                        if constexpr (BITS == 4) {
+                            const uint32_t lo = (dw[u] ^ o.flip) & 0x0F0F0F0Fu;
+                            const uint32_t hi = ((dw[u] >> 4) ^ o.flip) & 0x0F0F0F0Fu;
+                            bfr = u32x4_t{C::template fp8<false>(lo), C::template fp8<true>(lo),
+                                          C::template fp8<false>(hi), C::template fp8<true>(hi)};
+                        } else {
+                            // The slice's 16 bits; even codes to nibbles 0..3 of
+                            // lo, odd ones of hi, FP4 pairs per byte: the same
+                            // pair order as the 4-bit codes.
+                            const uint32_t h = (dw[u] >> (16u * ((uint32_t)g & 1u))) ^ o.flip;
+                            const uint32_t lo = h & 0x3333u, hi = (h >> 2) & 0x3333u;
+                            bfr = u32x4_t{C::template fp4<0>(lo), C::template fp4<1>(lo),
+                                          C::template fp4<0>(hi), C::template fp4<1>(hi)};
+                        }
                         d = M16::mma(xa[u], __builtin_bit_cast(frag_t, bfr), d);
                     }
                     const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(xsw + (uint32_t)((gi * 16 + 4 * g) * 4));
@@ -261,12 +289,12 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
     }
 }
 
-template <int DT, int GU>
+template <int BITS, int DT, int GU>
 hipError_t skinny4_launch_one(const GemvKernelArgs& k, const SkinnyShape& sh, dim3 grid, hipStream_t st)
 {
     static bool attr_set = false;   // per instantiation; set before its first launch
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemv_skinny4_kernel<DT, GU>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemv_skinny4_kernel<BITS, DT, GU>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(kSkinnyMaxWaves * skinny4_wave_lds()));
         if (e != hipSuccess)
@@ -274,17 +302,17 @@ hipError_t skinny4_launch_one(const GemvKernelArgs& k, const SkinnyShape& sh, di
         attr_set = true;
     }
     const int waves = sh.ks * sh.wr;
-    hipLaunchKernelGGL((qgemv_skinny4_kernel<DT, GU>), grid, dim3(64 * waves), waves * skinny4_wave_lds(), st, k, sh);
+    hipLaunchKernelGGL((qgemv_skinny4_kernel<BITS, DT, GU>), grid, dim3(64 * waves), waves * skinny4_wave_lds(), st, k, sh);
     return hipGetLastError();
 }
 
-template <int DT>
+template <int BITS, int DT>
 hipError_t skinny4_launch(const GemvKernelArgs& k, const SkinnyShape& sh, dim3 grid, hipStream_t st)
 {
     switch (k.gs) {
-    case 32: return skinny4_launch_one<DT, 1>(k, sh, grid, st);
-    case 64: return skinny4_launch_one<DT, 2>(k, sh, grid, st);
-    case 128: return skinny4_launch_one<DT, 4>(k, sh, grid, st);
+    case 32: return skinny4_launch_one<BITS, DT, 1>(k, sh, grid, st);
+    case 64: return skinny4_launch_one<BITS, DT, 2>(k, sh, grid, st);
+    case 128: return skinny4_launch_one<BITS, DT, 4>(k, sh, grid, st);
     }
     return hipErrorInvalidValue;
 }
