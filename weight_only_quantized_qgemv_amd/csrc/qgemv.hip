@@ -154,13 +154,15 @@ hipError_t run_skinny(const GemvArgs& a, hipStream_t st, bool* done)
     for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
         const int rows = (int)((a.M - m0) < 16 ? (a.M - m0) : 16);
         GemvKernelArgs k = dense_args(a, m0, rows, (int)sizeof(St<DT>), 0);
-        if constexpr ((BITS == 4 || BITS == 2) && DT != DT_F32) {
-            // 4- and 2-bit codes with rows of scales and codes in whole
-            // 16-byte pieces: the row-contiguous form (skinny4.hpp). Measured
-            // (graph-replayed): 14336 x 4096 M = 16 13.2 us against 15.4, M = 8
-            // 12.2 against 14.6; 4096 x 14336 M = 16 18.3 against 25.5; 2-bit
+        if constexpr ((BITS == 2 || BITS == 3 || BITS == 4) && DT != DT_F32) {
+            // 4-, 3- and 2-bit codes with rows of scales in whole 16-byte
+            // pieces: the row-contiguous form (skinny4.hpp). Measured (graph-
+            // replayed): 14336 x 4096 M = 16 13.2 us against 15.4, M = 8 12.2
+            // against 14.6; 4096 x 14336 M = 16 18.3 against 25.5; 2-bit
             // 14336 x 4096 M = 16 11.9 against 12.5, 4096 x 14336 M = 16 18.3
-            // against 21.7. 8-bit codes measured no faster this way.
+            // against 21.7; 3-bit (queued launches) 14336 x 4096 M = 16 14.2
+            // against 16.7, 4096 x 4096 M = 8 8.3 against 9.6 at gs 64. 8-bit
+            // codes measured no faster this way.
             const bool fit = (2 * (a.K / a.gs)) % 16 == 0 && reinterpret_cast<uintptr_t>(a.scales) % 16 == 0 &&
                              reinterpret_cast<uintptr_t>(a.biases) % 16 == 0 &&
                              reinterpret_cast<uintptr_t>(a.wq) % 16 == 0 && sh.rows_per_block % 16 == 0;

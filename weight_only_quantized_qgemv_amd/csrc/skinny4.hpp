@@ -1,5 +1,5 @@
-// skinny4.hpp — skinny products (M = 3..16 activation rows) of 4- and 2-bit
-// codes on the 16x16x32 matrix instruction, with row-contiguous code loads
+// skinny4.hpp — skinny products (M = 3..16 activation rows) of 4-, 3- and
+// 2-bit codes on the 16x16x32 matrix instruction, with row-contiguous code loads
 // (emily lib/emily/quantization.ex, `quantized_matmul/2`; affine codes of
 // `dequantize_defn/1`):
 //   y[m, n] = sum_g s'[n,g] * sum_{k in g} x q + b'[n,g] * sum_{k in g} x.
@@ -11,12 +11,13 @@
 // orientation it applies are that row's own.
 //
 // A wave owns a K-slice of 16 units and up to four row groups of 16 weight
-// rows. A row group's codes (16 rows x 16 units x 16 or 8 bytes) arrive as
-// four loads per lane, each covering four rows with 256 (128) contiguous
-// bytes of each (16 lanes per row); the wave writes them to its own LDS,
-// [row][dword of the unit][unit], and every lane reads back its row's 16
-// dwords holding k-slice kg of each unit (at 2 bits a dword holds two
-// k-slices, 16 bits each): the eight codes of one instruction per unit. A
+// rows. A row group's codes (16 rows x 16 units x 16, 12 or 8 bytes) arrive
+// as four loads per lane, each covering four rows with 256 (192, 128)
+// contiguous bytes of each (16 lanes per row); the wave writes them to its
+// own LDS, [row][dword of the unit][unit], and every lane reads back its
+// row's dwords holding k-slice kg of each unit (at 2 bits a dword holds two
+// k-slices, 16 bits each; at 3 bits a 24-bit slice is aligned out of the two
+// dwords it spans): the eight codes of one instruction per unit. A
 // row group's scales and biases over the slice are one or two 16-byte loads
 // per lane (its row's groups). Two row groups are in flight while one is
 // computed. The activations of the slice are staged through the same LDS
@@ -44,10 +45,11 @@ static_assert(2 * sk4_code_buf<4>() <= 16 * kSkinnyXRow && (uint32_t)kSkinnyRG *
 template <int BITS, int DT, int GU>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(GemvKernelArgs a, SkinnyShape sh)
 {
-    static_assert(BITS == 2 || BITS == 4, "2- and 4-bit codes");
-    // A lane's piece of a row per row quad: 16 bytes (4-bit) or 8 (2-bit),
-    // 4 or 2 dwords, each holding one k-slice (4-bit) or two (2-bit, 16 bits
-    // each) of the unit.
+    static_assert(BITS == 2 || BITS == 3 || BITS == 4, "2-, 3- and 4-bit codes");
+    // A lane's piece of a row per row quad: one unit, 16 bytes (4-bit), 12
+    // (3-bit) or 8 (2-bit). A dword holds one k-slice at 4 bits and two (16
+    // bits each) at 2; at 3 bits the 24-bit slices straddle the unit's three
+    // dwords.
     constexpr int PW = BITS;                        // dwords per unit
     constexpr uint32_t CR = sk4_code_row<BITS>();
     using M16 = SkMfma<DT>;
@@ -127,6 +129,9 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
                 if constexpr (PW == 4) {
                     const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
                     sl.c[q][0] = v.x; sl.c[q][1] = v.y; sl.c[q][2] = v.z; sl.c[q][3] = v.w;
+                } else if constexpr (PW == 3) {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b96(rw, off, 0, 0);
+                    sl.c[q][0] = v[0]; sl.c[q][1] = v[1]; sl.c[q][2] = v[2];
                 } else {
                     const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, 0));
                     sl.c[q][0] = v.x; sl.c[q][1] = v.y;
@@ -208,13 +213,26 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
                 for (int j = 0; j < PW; ++j)
                     d[16 * j] = sl.c[q][j];
             }
-            const uint32_t gd = BITS == 4 ? (uint32_t)g : (uint32_t)g >> 1;
-            uint32_t dw[kSkinnyKW];
+            // At 3 bits, slice g starts at bit 24 g: dword 3g / 4, byte 3g % 4,
+            // and runs into the next dword (the last slice ends its dword).
+            const uint32_t gd = BITS == 4 ? (uint32_t)g : BITS == 2 ? (uint32_t)g >> 1 : (3u * (uint32_t)g) >> 2;
+            auto read16 = [&](uint32_t j, uint32_t (&v16)[kSkinnyKW]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
-                    cb + ((uint32_t)l16 * CR + 16u * gd + 4u * (uint32_t)i) * 4u);
-                dw[4 * i] = v.x; dw[4 * i + 1] = v.y; dw[4 * i + 2] = v.z; dw[4 * i + 3] = v.w;
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+                        cb + ((uint32_t)l16 * CR + 16u * j + 4u * (uint32_t)i) * 4u);
+                    v16[4 * i] = v.x; v16[4 * i + 1] = v.y; v16[4 * i + 2] = v.z; v16[4 * i + 3] = v.w;
+                }
+            };
+            uint32_t dw[kSkinnyKW];
+            read16(gd, dw);
+            if constexpr (BITS == 3) {
+                uint32_t nx[kSkinnyKW];
+                read16(gd < 2u ? gd + 1u : 2u, nx);
+                const uint32_t sh = (3u * (uint32_t)g) & 3u;
+#pragma unroll
+                for (int u = 0; u < kSkinnyKW; ++u)
+                    dw[u] = __builtin_amdgcn_alignbyte(nx[u], dw[u], sh);   // slice g in the low 24 bits
             }
             uint32_t sv[SBW], bv[SBW];
 #pragma unroll
@@ -241,6 +259,13 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
                             const uint32_t hi = ((dw[u] >> 4) ^ o.flip) & 0x0F0F0F0Fu;
                             bfr = u32x4_t{C::template fp8<false>(lo), C::template fp8<true>(lo),
                                           C::template fp8<false>(hi), C::template fp8<true>(hi)};
+                        } else if constexpr (BITS == 3) {
+                            // The slice's 24 bits to bytes (even and odd codes),
+                            // complemented by the flip: the 4-bit pair order.
+                            uint32_t even, odd;
+                            code_bytes3(dw[u], o.flip, even, odd);
+                            bfr = u32x4_t{C::template fp8<false>(even), C::template fp8<true>(even),
+                                          C::template fp8<false>(odd), C::template fp8<true>(odd)};
                         } else {
                             // The slice's 16 bits; even codes to nibbles 0..3 of
                             // lo, odd ones of hi, FP4 pairs per byte: the same
