@@ -45,7 +45,7 @@ CSRC = os.path.join(ROOT, "weight_only_quantized_qgemv_amd", "csrc")
 # (FETCH_SIZE, WRITE_SIZE) of `bench.py --case decode_b4_m1 --steps 20
 # --warmup 2`, each scaled by the same counter on a plain 1 GiB copy.
 # It holds only while the decode kernel's sources are the ones it was taken on.
-TRAFFIC = {"src_sha": "95a929ce0a07a1f6", "fetch_bytes": 33205395, "write_bytes": 57344,
+TRAFFIC = {"src_sha": "f3905fab68b2293d", "fetch_bytes": 33205382, "write_bytes": 57344,
            "fetch_scale": 2.0, "write_scale": 1.0}
 DECODE_SOURCES = ("rowstream.hpp", "codepair.hpp", "gemv_core.hpp", "common.hpp", "qgemv.hip")
 

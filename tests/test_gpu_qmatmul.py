@@ -126,15 +126,15 @@ def test_qmatmul_row_stream_units_per_lane(bits, dt, k, m, gs):
     assert_within(y, y_ref, S, dt, f"row stream b{bits} k{k} m{m}")
 
 
-@pytest.mark.parametrize("bits", [4, 3, 8, 2])
+@pytest.mark.parametrize("bits", [4, 3, 8, 2, 6])
 @pytest.mark.parametrize("dt", [F16, BF16])
 @pytest.mark.parametrize("n,k,m,gs", [(301, 14336, 16, 128), (50, 14336, 7, 64),
                                       (130, 160, 11, 32), (1000, 4096, 2, 64)])
 def test_qmatmul_skinny_tiles(bits, dt, n, k, m, gs):
     """2..16 activation rows: ragged row counts, K not a multiple of the
     K-split quads, and K long enough that the activation rows go to LDS in
-    several chunks (K = 14336); 2- and 4-bit codes take the row-contiguous
-    form where the scales allow it (K = 14336 at gs 64 and 128)."""
+    several chunks (K = 14336); 2-, 3-, 4- and 6-bit codes take the
+    row-contiguous form where the scales allow it (K = 14336 at gs 64 and 128)."""
     log(f"skinny bits={bits} dt={dt} n={n} k={k} m={m} gs={gs}")
     y, y_ref, S = run_case(n, k, m, bits, gs, dt, seed=5000 + n + k + m + bits)
     assert_within(y, y_ref, S, dt, f"skinny b{bits} n{n} k{k} m{m}")
@@ -208,11 +208,14 @@ def sampled_check(y, xs, dt, rq, rs, rb, k, bits, gs, n_samples=3000, seed=0, ta
     assert_within(torch.from_numpy(yv), y_ref, S, dt, "sampled", tau=tau)
 
 
-@pytest.mark.parametrize("bits", [4, 8, 2])
+@pytest.mark.parametrize("bits", [4, 8, 2, 3, 6])
 @pytest.mark.parametrize("m", [1, 4, 16])
 def test_qmatmul_decode_config_full(bits, m):
     """W [14336, 4096] N(0, 0.02) (seed 21), gs64, bf16 scales; x bf16 [m, 4096]
-    (seed 22). Every output against the oracle (at most 16 x 14336 of them)."""
+    (seed 22). Every output against the oracle (at most 16 x 14336 of them).
+    At 16 rows (at 4 too for 3- and 6-bit codes) 2-, 3-, 4- and 6-bit codes
+    take the row-contiguous skinny form; 6-bit codes take it from 2^25 codes,
+    which this matrix has."""
     log(f"decode config bits={bits} m={m}")
     w = synth.normal_f32((14336, 4096), 0.02, 21)
     (rq, rs, rb), (gq, gs_, gb) = quantize_both(w, bits, 64, BF16)

@@ -154,16 +154,21 @@ hipError_t run_skinny(const GemvArgs& a, hipStream_t st, bool* done)
     for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
         const int rows = (int)((a.M - m0) < 16 ? (a.M - m0) : 16);
         GemvKernelArgs k = dense_args(a, m0, rows, (int)sizeof(St<DT>), 0);
-        if constexpr ((BITS == 2 || BITS == 3 || BITS == 4) && DT != DT_F32) {
-            // 4-, 3- and 2-bit codes with rows of scales in whole 16-byte
+        if constexpr ((BITS == 2 || BITS == 3 || BITS == 4 || BITS == 6) && DT != DT_F32) {
+            // 6-, 4-, 3- and 2-bit codes with rows of scales in whole 16-byte
             // pieces: the row-contiguous form (skinny4.hpp). Measured (graph-
             // replayed): 14336 x 4096 M = 16 13.2 us against 15.4, M = 8 12.2
             // against 14.6; 4096 x 14336 M = 16 18.3 against 25.5; 2-bit
             // 14336 x 4096 M = 16 11.9 against 12.5, 4096 x 14336 M = 16 18.3
             // against 21.7; 3-bit (queued launches) 14336 x 4096 M = 16 14.2
-            // against 16.7, 4096 x 4096 M = 8 8.3 against 9.6 at gs 64. 8-bit
-            // codes measured no faster this way.
-            const bool fit = (2 * (a.K / a.gs)) % 16 == 0 && reinterpret_cast<uintptr_t>(a.scales) % 16 == 0 &&
+            // against 16.7, 4096 x 4096 M = 8 8.3 against 9.6 at gs 64; 6-bit
+            // 4096 x 14336 M = 16 26.7 against 30.6, 14336 x 4096 M = 16 18.2
+            // against 18.7, but 4096 x 4096 M = 8 10.7 against 10.2 and, at
+            // gs 32 (whose scales and biases take 16 more registers, which
+            // spills), 14.4 against 11.3: so 6-bit codes take it from gs 64 and
+            // 2^25 codes. 8-bit codes measured no faster this way.
+            const bool wide = BITS != 6 || (a.gs >= 64 && (int64_t)a.N * a.K >= (int64_t(1) << 25));
+            const bool fit = wide && (2 * (a.K / a.gs)) % 16 == 0 && reinterpret_cast<uintptr_t>(a.scales) % 16 == 0 &&
                              reinterpret_cast<uintptr_t>(a.biases) % 16 == 0 &&
                              reinterpret_cast<uintptr_t>(a.wq) % 16 == 0 && sh.rows_per_block % 16 == 0;
             if (fit) {

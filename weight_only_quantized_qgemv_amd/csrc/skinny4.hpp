@@ -1,5 +1,5 @@
-// skinny4.hpp — skinny products (M = 3..16 activation rows) of 4-, 3- and
-// 2-bit codes on the 16x16x32 matrix instruction, with row-contiguous code loads
+// skinny4.hpp — skinny products (M = 3..16 activation rows) of 6-, 4-, 3-
+// and 2-bit codes on the 16x16x32 matrix instruction, with row-contiguous code loads
 // (emily lib/emily/quantization.ex, `quantized_matmul/2`; affine codes of
 // `dequantize_defn/1`):
 //   y[m, n] = sum_g s'[n,g] * sum_{k in g} x q + b'[n,g] * sum_{k in g} x.
@@ -11,12 +11,13 @@
 // orientation it applies are that row's own.
 //
 // A wave owns a K-slice of 16 units and up to four row groups of 16 weight
-// rows. A row group's codes (16 rows x 16 units x 16, 12 or 8 bytes) arrive
-// as four loads per lane, each covering four rows with 256 (192, 128)
-// contiguous bytes of each (16 lanes per row); the wave writes them to its
+// rows. A row group's codes (16 rows x 16 units x 24, 16, 12 or 8 bytes)
+// arrive as four loads per lane, each covering four rows with 384 (256, 192,
+// 128) contiguous bytes of each (16 lanes per row); the wave writes them to its
 // own LDS, [row][dword of the unit][unit], and every lane reads back its
 // row's dwords holding k-slice kg of each unit (at 2 bits a dword holds two
 // k-slices, 16 bits each; at 3 bits a 24-bit slice is aligned out of the two
+// dwords it spans, at 6 bits a 48-bit one is two 24-bit halves of the two
 // dwords it spans): the eight codes of one instruction per unit. A
 // row group's scales and biases over the slice are one or two 16-byte loads
 // per lane (its row's groups). Two row groups are in flight while one is
@@ -29,8 +30,8 @@
 
 namespace qp {
 
-// Dwords per weight row in LDS: the slice's 16 units (4 dwords each at 4
-// bits, 2 at 2 bits) plus 4 against bank conflicts; bytes of one row group's codes.
+// Dwords per weight row in LDS: the slice's 16 units (BITS dwords each) plus
+// 4 against bank conflicts; bytes of one row group's codes.
 template <int BITS> __host__ __device__ constexpr uint32_t sk4_code_row() { return 16u * BITS + 4u; }
 template <int BITS> __host__ __device__ constexpr uint32_t sk4_code_buf() { return 16u * sk4_code_row<BITS>() * 4u; }
 __host__ __device__ constexpr uint32_t skinny4_wave_lds()
@@ -39,17 +40,17 @@ __host__ __device__ constexpr uint32_t skinny4_wave_lds()
     // then the group sums of the slice's activations.
     return 16u * kSkinnyXRow + 1024u;
 }
-static_assert(2 * sk4_code_buf<4>() <= 16 * kSkinnyXRow && (uint32_t)kSkinnyRG * 1024u <= 16 * kSkinnyXRow,
+static_assert(2 * sk4_code_buf<6>() <= 16 * kSkinnyXRow && (uint32_t)kSkinnyRG * 1024u <= 16 * kSkinnyXRow,
               "code buffers and partial sums within the staging region");
 
 template <int BITS, int DT, int GU>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(GemvKernelArgs a, SkinnyShape sh)
 {
-    static_assert(BITS == 2 || BITS == 3 || BITS == 4, "2-, 3- and 4-bit codes");
-    // A lane's piece of a row per row quad: one unit, 16 bytes (4-bit), 12
-    // (3-bit) or 8 (2-bit). A dword holds one k-slice at 4 bits and two (16
-    // bits each) at 2; at 3 bits the 24-bit slices straddle the unit's three
-    // dwords.
+    static_assert(BITS == 2 || BITS == 3 || BITS == 4 || BITS == 6, "2-, 3-, 4- and 6-bit codes");
+    // A lane's piece of a row per row quad: one unit, 24 bytes (6-bit), 16
+    // (4-bit), 12 (3-bit) or 8 (2-bit). A dword holds one k-slice at 4 bits
+    // and two (16 bits each) at 2; at 3 and 6 bits the 24- and 48-bit slices
+    // straddle the unit's dwords.
     constexpr int PW = BITS;                        // dwords per unit
     constexpr uint32_t CR = sk4_code_row<BITS>();
     using M16 = SkMfma<DT>;
@@ -126,7 +127,12 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
             for (int q = 0; q < 4; ++q) {
                 const uint32_t row = rg0 + 4u * (uint32_t)q + (uint32_t)g;
                 const uint32_t off = row * row_bytes + ((uint32_t)u0 + (uint32_t)l16) * (4u * PW);
-                if constexpr (PW == 4) {
+                if constexpr (PW == 6) {
+                    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+                    const u32x2_t t = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, off + 16u, 0, 0));
+                    sl.c[q][0] = v.x; sl.c[q][1] = v.y; sl.c[q][2] = v.z; sl.c[q][3] = v.w;
+                    sl.c[q][4] = t.x; sl.c[q][5] = t.y;
+                } else if constexpr (PW == 4) {
                     const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
                     sl.c[q][0] = v.x; sl.c[q][1] = v.y; sl.c[q][2] = v.z; sl.c[q][3] = v.w;
                 } else if constexpr (PW == 3) {
@@ -175,10 +181,13 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
         for (int u = 0; u < kSkinnyKW; ++u) {
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xst + (uint32_t)l16 * kSkinnyXRow +
                                                                  (uint32_t)(u * 32 + 8 * g) * 2u);
-            xa[u] = __builtin_bit_cast(frag_t, u32x4_t{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u),
-                                                       __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
-                                                       __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
-                                                       __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)});
+            if constexpr (BITS == 6)   // byte codes keep the natural order
+                xa[u] = __builtin_bit_cast(frag_t, v);
+            else                       // the pair order 0, 2, 4, 6, 1, 3, 5, 7
+                xa[u] = __builtin_bit_cast(frag_t, u32x4_t{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u),
+                                                           __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                                                           __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
+                                                           __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)});
         }
         static_for<NGS>([&](auto GI) {
             constexpr int gi = decltype(GI)::value;
@@ -215,7 +224,12 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
             }
             // At 3 bits, slice g starts at bit 24 g: dword 3g / 4, byte 3g % 4,
             // and runs into the next dword (the last slice ends its dword).
-            const uint32_t gd = BITS == 4 ? (uint32_t)g : BITS == 2 ? (uint32_t)g >> 1 : (3u * (uint32_t)g) >> 2;
+            // At 6 bits, slice g starts at bit 48 g: dword 3g / 2, at its bit 0
+            // (g even) or 16 (g odd), and ends in the next dword.
+            const uint32_t gd = BITS == 4   ? (uint32_t)g
+                                : BITS == 2 ? (uint32_t)g >> 1
+                                : BITS == 3 ? (3u * (uint32_t)g) >> 2
+                                            : (3u * (uint32_t)g) >> 1;
             auto read16 = [&](uint32_t j, uint32_t (&v16)[kSkinnyKW]) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -226,6 +240,18 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
             };
             uint32_t dw[kSkinnyKW];
             read16(gd, dw);
+            uint32_t dx[BITS == 6 ? kSkinnyKW : 1];   // 6-bit: codes 4..7 of the slice
+            if constexpr (BITS == 6) {
+                uint32_t nx[kSkinnyKW];
+                read16(gd + 1u, nx);
+                const bool odd = (g & 1) != 0;
+#pragma unroll
+                for (int u = 0; u < kSkinnyKW; ++u) {
+                    const uint32_t a0 = __builtin_amdgcn_alignbyte(nx[u], dw[u], odd ? 2u : 0u);
+                    dx[u] = odd ? nx[u] >> 8 : __builtin_amdgcn_alignbyte(nx[u], dw[u], 3u);
+                    dw[u] = a0;   // codes 0..3 of the slice in the low 24 bits
+                }
+            }
             if constexpr (BITS == 3) {
                 uint32_t nx[kSkinnyKW];
                 read16(gd < 2u ? gd + 1u : 2u, nx);
@@ -259,6 +285,12 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
                             const uint32_t hi = ((dw[u] >> 4) ^ o.flip) & 0x0F0F0F0Fu;
                             bfr = u32x4_t{C::template fp8<false>(lo), C::template fp8<true>(lo),
                                           C::template fp8<false>(hi), C::template fp8<true>(hi)};
+                        } else if constexpr (BITS == 6) {
+                            // Codes 0..3 and 4..7 of the slice to bytes, complemented
+                            // by the flip; byte pairs in the natural order.
+                            const uint32_t c03 = code_bytes6(dw[u], o.flip), c47 = code_bytes6(dx[u], o.flip);
+                            bfr = u32x4_t{C::template bytes<false>(c03), C::template bytes<true>(c03),
+                                          C::template bytes<false>(c47), C::template bytes<true>(c47)};
                         } else if constexpr (BITS == 3) {
                             // The slice's 24 bits to bytes (even and odd codes),
                             // complemented by the flip: the 4-bit pair order.
