@@ -110,3 +110,12 @@ def test_edge_cross_word_widths(m, k, gs, bits, dt, act):
 def test_edge_fp32(m, k, bits, act):
     log(f"edge fp32 bits={bits} m={m} k={k} act={act}")
     edge_case(64, k, m, bits, 64, F32, seed=9800 + m + k + bits, act=act)
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("gs,dt", [(64, BF16), (128, F16)])
+def test_edge_six_bit_row_contiguous(gs, dt, act):
+    """6-bit codes take the row-contiguous skinny form from 2^25 codes:
+    2368 x 14336 rows of the edge pattern, eight activation rows."""
+    log(f"edge six-bit row-contiguous gs={gs} dt={dt} act={act}")
+    edge_case(2368, 14336, 8, 6, gs, dt, seed=9700 + gs, act=act)

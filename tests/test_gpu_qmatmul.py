@@ -226,6 +226,19 @@ def test_qmatmul_decode_config_full(bits, m):
     assert_within(y, y_ref, S, BF16, f"decode config b{bits} m{m}")
 
 
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("gs", [64, 128])
+@pytest.mark.parametrize("m", [5, 16])
+def test_qmatmul_six_bit_row_contiguous(dt, gs, m):
+    """6-bit codes on the row-contiguous skinny form, which they take from
+    2^25 codes: 2403 x 14336 (34.4 M codes; the last block's row groups are
+    ragged), every output against the oracle."""
+    n, k = 2403, 14336
+    log(f"six-bit row-contiguous dt={dt} gs={gs} m={m}")
+    y, y_ref, S = run_case(n, k, m, 6, gs, dt, seed=5600 + gs + m)
+    assert_within(y, y_ref, S, dt, f"six-bit row-contiguous gs{gs} m{m}")
+
+
 @pytest.mark.parametrize("bits", [3, 6])
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("m", [1, 8])
