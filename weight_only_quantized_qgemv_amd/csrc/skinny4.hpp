@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void qgemv_skinny4_kernel(Gem
 
         // The ring: row group rgi (rows 16 (wri + wr rgi) .. + 15 of the block).
         // Load q of lane l: row 4 q + l / 16 of the group, unit l % 16 of the
-        // slice (16 or 8 bytes); the row's scale and bias dwords over the slice.
+        // slice (4 BITS bytes); the row's scale and bias dwords over the slice.
         struct Slot {
             uint32_t c[4][PW];
             uint32_t s[SBW], b[SBW];
