@@ -129,12 +129,15 @@ def test_qmatmul_row_stream_units_per_lane(bits, dt, k, m, gs):
 @pytest.mark.parametrize("bits", [4, 3, 8, 2, 6])
 @pytest.mark.parametrize("dt", [F16, BF16])
 @pytest.mark.parametrize("n,k,m,gs", [(301, 14336, 16, 128), (50, 14336, 7, 64),
-                                      (130, 160, 11, 32), (1000, 4096, 2, 64)])
+                                      (130, 160, 11, 32), (1000, 4096, 2, 64),
+                                      (200, 768, 6, 32), (137, 1280, 16, 32)])
 def test_qmatmul_skinny_tiles(bits, dt, n, k, m, gs):
     """2..16 activation rows: ragged row counts, K not a multiple of the
     K-split quads, and K long enough that the activation rows go to LDS in
-    several chunks (K = 14336); 2-, 3-, 4- and 6-bit codes take the
-    row-contiguous form where the scales allow it (K = 14336 at gs 64 and 128)."""
+    several chunks (K = 14336); 2-, 3- and 4-bit codes take the row-contiguous
+    form where the scales allow it (K = 14336 at gs 64 and 128, and K = 768
+    and 1280 at gs 32, whose last K-slice of 16 units is half empty), 6-bit
+    codes only on larger matrices."""
     log(f"skinny bits={bits} dt={dt} n={n} k={k} m={m} gs={gs}")
     y, y_ref, S = run_case(n, k, m, bits, gs, dt, seed=5000 + n + k + m + bits)
     assert_within(y, y_ref, S, dt, f"skinny b{bits} n{n} k{k} m{m}")
