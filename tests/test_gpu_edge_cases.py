@@ -71,9 +71,11 @@ ACTS = ["pos", "neg", "normal"]
 
 # (m, k, gs): the row kernel at one and two rows (1 to 8 units per lane, 32-lane
 # slots at K <= 1024), the four-row matrix-instruction kernel, the skinny
-# matrix-core kernel, the tile GEMM.
+# matrix-core kernel (its row-contiguous form at gs 32, 64 and 128), the tile
+# GEMM.
 DENSE_16 = [(1, 16384, 128), (1, 4096, 64), (1, 1024, 32), (2, 8192, 64), (2, 16384, 128),
-            (3, 4096, 64), (4, 4096, 128), (8, 4096, 64), (16, 14336, 64), (40, 4096, 64)]
+            (3, 4096, 64), (4, 4096, 128), (8, 4096, 64), (12, 2048, 32), (16, 14336, 64),
+            (40, 4096, 64)]
 
 
 def with_dtypes(cases):
@@ -93,7 +95,7 @@ def test_edge_integral_widths(m, k, gs, bits, dt, act):
 # <= 1024, seven units per lane at K = 14336) and at three and four rows
 # (their slices in registers), the skinny kernel, the tile GEMM.
 DENSE_CROSS = [(1, 4096, 32), (1, 4096, 128), (2, 4096, 64), (1, 14336, 64), (1, 1024, 32),
-               (3, 4096, 64), (4, 1024, 128), (8, 4096, 64), (40, 4096, 128)]
+               (3, 4096, 64), (4, 1024, 128), (8, 4096, 64), (12, 2048, 32), (40, 4096, 128)]
 
 
 @pytest.mark.parametrize("act", ACTS)
