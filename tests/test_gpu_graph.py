@@ -1,5 +1,5 @@
-"""The calls under HIP graph capture: a captured sequence (decode qmatmul,
-prefill qmatmul, both MoE forms with and without the routing launch) replayed
+"""The calls under HIP graph capture: a captured sequence (decode qmatmul at
+one, four and eight activation rows, prefill qmatmul, both MoE forms with and without the routing launch) replayed
 several times, with eager work and synchronisations between the replays,
 gives bit-identical outputs to the eager calls every time. The library
 allocates nothing and records no memset, so its launches can be captured
@@ -24,11 +24,13 @@ def quantized(n, k, seed):
 
 
 def test_graph_replays_match_eager():
-    log("graph capture: decode, prefill, MoE")
+    log("graph capture: decode (1, 4, 8 rows), prefill, MoE")
     N, K = 1024, 512
     wq, s, b = quantized(N, K, 501)
     _, x1 = activations((1, K), BF16, 502)
     _, x64 = activations((96, K), BF16, 503)
+    _, x4 = activations((4, K), BF16, 509)
+    _, x8 = activations((8, K), BF16, 510)
     E, R, C = 8, 128, 256
     g = tuple(t.reshape(E, R, -1) for t in quantized(E * R, C, 504))
     u = tuple(t.reshape(E, R, -1) for t in quantized(E * R, C, 505))
@@ -40,6 +42,8 @@ def test_graph_replays_match_eager():
     outs = {
         "y1": torch.empty((1, N), dtype=torch.bfloat16, device=dev()),
         "y64": torch.empty((96, N), dtype=torch.bfloat16, device=dev()),
+        "y4": torch.empty((4, N), dtype=torch.bfloat16, device=dev()),
+        "y8": torch.empty((8, N), dtype=torch.bfloat16, device=dev()),
         "h1": torch.empty((2, R), dtype=torch.bfloat16, device=dev()),
         "hT": torch.empty((128, R), dtype=torch.bfloat16, device=dev()),
         "pT": torch.empty((128, R), dtype=torch.bfloat16, device=dev()),
@@ -48,6 +52,8 @@ def test_graph_replays_match_eager():
     def run():
         qp.qmatmul(x1, wq, s, b, 4, 64, out=outs["y1"])
         qp.qmatmul(x64, wq, s, b, 4, 64, out=outs["y64"])
+        qp.qmatmul(x4, wq, s, b, 4, 64, out=outs["y4"])
+        qp.qmatmul(x8, wq, s, b, 4, 64, out=outs["y8"])
         qp.qgemv_moe_id_gate_up_silu(a1, ids1, 1, 2, 0, 0, g, u, 4, 64, out=outs["h1"],
                                      workspace=ws)
         qp.qgemv_moe_id_gate_up_silu(aT, idsT, 64, 2, C, 0, g, u, 4, 64, out=outs["hT"],
